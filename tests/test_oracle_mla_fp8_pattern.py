@@ -1,0 +1,250 @@
+"""Pins for the oracle's sparse MLA, E4M3 codec, layer pattern and IndexShare group (CPU only)."""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import workloads as W
+
+
+# ---------------------------------------------------------------- sparse MLA
+def _dense_sdpa_f64(q_lat, q_rope, kv, length, scale):
+    """Dense causal attention over positions 0..length-1 with torch's SDPA in
+    float64 on the CPU: query = [q_lat | q_rope], key = [c | kr], value = c."""
+    c = torch.from_numpy(kv[:length, :512])
+    kr = torch.from_numpy(kv[:length, 512:])
+    q = torch.cat([torch.from_numpy(q_lat), torch.from_numpy(q_rope)], dim=-1)[None]  # [1,H,256]
+    k = torch.cat([c, kr], dim=-1)[None, None].expand(1, q.shape[1], length, 576)
+    v = c[None, None].expand(1, q.shape[1], length, 512)
+    out = torch.nn.functional.scaled_dot_product_attention(
+        q[:, :, None, :].contiguous(), k.contiguous(), v.contiguous(), scale=scale)
+    return out[0, :, 0, :].numpy()
+
+
+def test_mla_equals_dense_attention_when_prefix_fits():
+    rng = np.random.default_rng(5)
+    h, n = 8, 300
+    kv = rng.normal(size=(1, n, 576))
+    q_lat = rng.normal(size=(3, h, 512))
+    q_rope = rng.normal(size=(3, h, 64))
+    pos = [0, 17, n - 1]
+    sc = rng.normal(size=(3, n))
+    idx = oracle.topk_select(sc, pos, 2048)        # prefix <= K: every position kept
+    out, lse = oracle.sparse_mla(q_lat, q_rope, kv, [0, 0, 0], idx, 1 / 16)
+    for i, p in enumerate(pos):
+        want = _dense_sdpa_f64(q_lat[i], q_rope[i], kv[0], p + 1, 1 / 16)
+        np.testing.assert_allclose(out[i], want, rtol=1e-12, atol=1e-12)
+
+
+def test_mla_single_key_returns_that_row():
+    rng = np.random.default_rng(6)
+    kv = rng.normal(size=(2, 10, 576))
+    idx = np.full((1, 2048), -1)
+    idx[0, 0] = 7
+    out, lse = oracle.sparse_mla(rng.normal(size=(1, 4, 512)), rng.normal(size=(1, 4, 64)),
+                                 kv, [1], idx, 1 / 16)
+    assert np.array_equal(out[0], np.broadcast_to(kv[1, 7, :512], (4, 512)))
+
+
+def test_mla_zero_query_is_mean_and_lse_is_log_count():
+    rng = np.random.default_rng(7)
+    kv = rng.normal(size=(1, 50, 576))
+    sel = np.array([3, 9, 10, 44])
+    idx = np.full((1, 2048), -1)
+    idx[0, :4] = sel
+    out, lse = oracle.sparse_mla(np.zeros((1, 2, 512)), np.zeros((1, 2, 64)), kv, [0], idx, 1 / 16)
+    np.testing.assert_allclose(out[0], np.broadcast_to(kv[0, sel, :512].mean(0), (2, 512)), rtol=1e-14)
+    np.testing.assert_allclose(lse[0], math.log(4.0), rtol=1e-14)
+
+
+def test_mla_rope_term_and_scale_matter():
+    """A query whose latent part is zero must still attend through the RoPE key."""
+    kv = np.zeros((1, 2, 576))
+    kv[0, 0, :512] = 1.0
+    kv[0, 1, :512] = -1.0
+    kv[0, 1, 512] = 16.0          # only row 1 has a RoPE key
+    q_rope = np.zeros((1, 1, 64))
+    q_rope[0, 0, 0] = 1.0
+    idx = np.array([[0, 1] + [-1] * 2046])
+    out, lse = oracle.sparse_mla(np.zeros((1, 1, 512)), q_rope, kv, [0], idx, 1 / 16)
+    # z = (0, 1): p1 = e/(1+e)
+    p1 = math.e / (1 + math.e)
+    np.testing.assert_allclose(out[0, 0, 0], (1 - p1) * 1.0 + p1 * -1.0, rtol=1e-14)
+    np.testing.assert_allclose(lse[0, 0], math.log(1 + math.e), rtol=1e-14)
+
+
+def test_mla_invariant_to_index_order_and_lse_consistent():
+    rng = np.random.default_rng(8)
+    kv = rng.normal(size=(1, 5000, 576))
+    ql, qr = rng.normal(size=(1, 4, 512)), rng.normal(size=(1, 4, 64))
+    idx = np.sort(rng.choice(5000, 2048, replace=False))[None]
+    out1, lse1 = oracle.sparse_mla(ql, qr, kv, [0], idx, 1 / 16)
+    out2, lse2 = oracle.sparse_mla(ql, qr, kv, [0], rng.permutation(idx[0])[None], 1 / 16)
+    np.testing.assert_allclose(out1, out2, rtol=1e-12, atol=1e-13)
+    rows = kv[0, idx[0]]
+    z = (ql[0] @ rows[:, :512].T + qr[0] @ rows[:, 512:].T) / 16
+    np.testing.assert_allclose(lse1[0], np.log(np.exp(z).sum(1)), rtol=1e-12)
+
+
+def test_mla_no_valid_index():
+    out, lse = oracle.sparse_mla(np.ones((1, 2, 512)), np.ones((1, 2, 64)), np.ones((1, 4, 576)),
+                                 [0], np.full((1, 2048), -1), 1 / 16)
+    assert np.all(out == 0) and np.all(lse == -np.inf)
+
+
+# ---------------------------------------------------------------- E4M3
+def test_e4m3_decode_all_codes_match_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    assert np.array_equal(ours[~np.isnan(ours)], ref[~np.isnan(ref)])
+    assert oracle.e4m3_decode(np.array([0x7E]))[0] == 448.0
+    assert oracle.e4m3_decode(np.array([0x01]))[0] == 2.0 ** -9
+
+
+def test_e4m3_encode_matches_torch_in_range():
+    rng = np.random.default_rng(9)
+    x = np.concatenate([rng.normal(size=200000) * s for s in (1e-3, 0.1, 3, 60)])
+    x = x.astype(np.float32).astype(np.float64)          # torch casts from fp32
+    x = x[np.abs(x) < 448]
+    ref = torch.from_numpy(x.astype(np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.array_equal(oracle.e4m3_encode(x), ref)
+
+
+def test_e4m3_round_half_even_and_saturation():
+    # between 1.0 (code 0x38) and 1.125 (0x39) the midpoint 1.0625 goes to the even code 0x38
+    assert oracle.e4m3_encode(np.array([1.0625, 1.1875, 449.0, -1e6, -0.0]))[:].tolist() == \
+        [0x38, 0x3A, 0x7E, 0xFE, 0x80]
+    # every code re-encodes to itself (except NaN)
+    codes = np.array([c for c in range(256) if c not in (0x7F, 0xFF)], dtype=np.uint8)
+    assert np.array_equal(oracle.e4m3_encode(oracle.e4m3_decode(codes)), codes)
+
+
+def test_block_quantisation_rule():
+    from oracle.e4m3 import block_exponent
+    assert block_exponent(4.0) == -6            # 4 <= 448 * 2^-6 = 7, 4 > 3.5
+    assert block_exponent(448.0) == 0 and block_exponent(448.0001) == 1
+    assert block_exponent(0.0) == 0
+    assert block_exponent(7.0) == -6 and block_exponent(7.001) == -5
+    rng = np.random.default_rng(10)
+    x = rng.integers(-4, 5, (50, 256)).astype(np.float64)
+    codes, scales = oracle.quantize_blocks(x)
+    assert scales.shape == (50, 2)
+    assert np.array_equal(oracle.dequantize_blocks(codes, scales), x)       # integers are exact
+    y = rng.normal(size=(40, 128)) * 10
+    c2, s2 = oracle.quantize_blocks(y)
+    deq = oracle.dequantize_blocks(c2, s2)
+    # relative error of E4M3 RNE is at most 2^-4 for normals
+    big = np.abs(y) > s2 * 2 ** -6
+    assert np.all(np.abs(deq - y)[big] <= np.abs(y)[big] * 2 ** -4 + 1e-300)
+    assert np.all(np.abs(y).max(-1) <= 448 * s2[:, 0]) and np.all(np.abs(y).max(-1) > 224 * s2[:, 0])
+
+
+def test_fp8_scores_equal_bf16_scores_on_integer_inputs():
+    wl = W.Workload("t", 2, 700, 2, 1, "fp8")
+    q, w = W.indexer_queries(wl, 1, 0)
+    k = W.indexer_keys(wl, 1, 0)
+    q_seq, q_pos = W.query_layout(wl)
+    from oracle.group import indexer_inputs_fp8
+    qd, kd = indexer_inputs_fp8(q.float().numpy(), k.float().numpy())
+    a = oracle.indexer_score(qd, w.numpy(), kd, q_seq.numpy(), q_pos.numpy())
+    b = oracle.indexer_score(q.float().numpy(), w.numpy(), k.float().numpy(), q_seq.numpy(), q_pos.numpy())
+    assert np.array_equal(a, b)
+
+
+# ---------------------------------------------------------------- layer pattern
+def test_pattern_matches_page_table(golden_dir):
+    tab = json.load(open(os.path.join(golden_dir, "indexer_types_table.json")))
+    pat = oracle.layer_pattern(78)
+    for row in tab["rows"]:
+        for l in row["layers"]:
+            assert pat[l] == row["type"], l
+    assert pat.count("full") == tab["totals"]["full"] and pat.count("shared") == tab["totals"]["shared"]
+    src = oracle.shared_source(pat)
+    for s, f in tab["reuse"]["pairs"]:
+        assert src[s] == f
+    assert src[77] == 74 and src[76] == 74 and src[75] == 74
+    # a full layer uses its own indices; a shared layer the nearest full layer before it
+    for l, t in enumerate(pat):
+        if t == "full":
+            assert src[l] == l
+        else:
+            assert pat[src[l]] == "full" and all(pat[j] == "shared" for j in range(src[l] + 1, l + 1))
+    full = [i for i, t in enumerate(pat) if t == "full"]
+    assert full == [0, 1, 2] + list(range(6, 75, 4))
+
+
+def test_page_constants_match_workload_shapes(golden_dir):
+    c = json.load(open(os.path.join(golden_dir, "page_constants.json")))
+    assert (W.INDEX_HEADS, W.INDEX_DIM, W.TOPK) == (c["index_n_heads"], c["index_head_dim"], c["index_topk"])
+    assert W.MLA_HEADS == c["attention_heads"] and W.LATENT_DIM == c["kv_lora_rank"]
+    assert W.ROPE_DIM == c["qk_rope_dim"] and W.QK_DIM == c["qk_nope_dim"] + c["qk_rope_dim"]
+    assert W.KV_ROW * 2 == c["kv_bytes_per_token_per_layer_bf16"]
+    # the page's 1M totals are in GiB: 78 layers x 2^20 tokens x bytes
+    assert round(78 * 2 ** 20 * 1152 / 2 ** 30) == c["kv_total_1m_bf16_gb"]
+    assert int(78 * 2 ** 20 * 656 / 2 ** 30) == c["kv_total_1m_fp8_gb"]
+    pat = oracle.layer_pattern(78)
+    assert round(pat.count("full") / 78, 3) == c["indexer_flops_ratio_21_over_78"]
+    t2 = float(2 ** 20) ** 2
+    assert round(78 * t2 / 1e13, 1) == c["indexer_T2_term_1m_without"] / 1e13
+    assert round(pat.count("full") * t2 / 1e13, 1) == c["indexer_T2_term_1m_with"] / 1e13
+
+
+# ---------------------------------------------------------------- IndexShare group
+def _tiny_group(seed=0, n_layers=4):
+    wl = W.Workload("t", 2, 2600, 2, n_layers, "bf16")
+    return wl, W.group_inputs(wl, seed, n_layers=n_layers)
+
+
+def _np(t):
+    return t.float().numpy() if t.dtype == torch.bfloat16 else t.numpy()
+
+
+def test_group_s_layers_reuse_f_indices_and_match_independent_mla():
+    wl, g = _tiny_group()
+    layers = [tuple(_np(t) for t in L) for L in g.layers]
+    scores, idx, outs = oracle.indexshare_group(_np(g.q_idx), _np(g.w), _np(g.k_idx),
+                                                _np(g.q_seq), _np(g.q_pos), layers)
+    for l in range(1, 4):
+        ql, qr, kv = layers[l]
+        o, s = oracle.sparse_mla(ql, qr, kv, _np(g.q_seq), idx, 1 / 16)
+        assert np.array_equal(outs[l][0], o) and np.array_equal(outs[l][1], s)
+    # F-layer index is the top-k of the F-layer score
+    assert np.array_equal(idx, oracle.topk_select(scores, _np(g.q_pos), 2048))
+
+
+def test_group_with_no_shared_layers_is_per_layer_dsa():
+    wl, g = _tiny_group(n_layers=1)
+    layers = [tuple(_np(t) for t in L) for L in g.layers]
+    scores, idx, outs = oracle.indexshare_group(_np(g.q_idx), _np(g.w), _np(g.k_idx),
+                                                _np(g.q_seq), _np(g.q_pos), layers)
+    sc = oracle.indexer_score(_np(g.q_idx), _np(g.w), _np(g.k_idx), _np(g.q_seq), _np(g.q_pos))
+    o, s = oracle.sparse_mla(*layers[0], _np(g.q_seq), oracle.topk_select(sc, _np(g.q_pos)), 1 / 16)
+    assert np.array_equal(outs[0][0], o)
+
+
+def test_stack_uses_latest_full_layer():
+    wl = W.Workload("t", 1, 300, 1, 12, "bf16")
+    q_seq, q_pos = W.query_layout(wl)
+    pat = oracle.layer_pattern(12)
+    ind = {}
+    for f in [i for i, t in enumerate(pat) if t == "full"]:
+        q, w = W.indexer_queries(wl, 0, f)
+        ind[f] = (_np(q), _np(w), _np(W.indexer_keys(wl, 0, f, lo=-1, hi=1)))
+    mla = {}
+    for l in range(12):
+        ql, qr = W.mla_queries(wl, 0, l)
+        mla[l] = (_np(ql), _np(qr), _np(W.mla_cache(wl, 0, l)))
+    # shorten the context so top-k is a real selection: K = 64
+    idx_of, outs = oracle.layer_stack(ind, mla, _np(q_seq), _np(q_pos), n_layers=12, k=64)
+    src = oracle.shared_source(pat)
+    assert sorted(idx_of) == [0, 1, 2, 6, 10]
+    for l in range(12):
+        o, _ = oracle.sparse_mla(*mla[l], _np(q_seq), idx_of[src[l]], 1 / 16)
+        assert np.array_equal(outs[l][0], o)
+    assert src[3:6] == [2, 2, 2] and src[7:10] == [6, 6, 6] and src[11] == 10
