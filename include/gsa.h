@@ -1,0 +1,205 @@
+/*
+ * gsa.h — C ABI of libgsa: GLM-5.2's DSA lightning indexer, IndexShare and
+ * absorbed sparse MLA on one AMD Instinct MI355X (gfx950).
+ *
+ * Sources (page titles as published):
+ *   [Overview]  "GLM-5.2 总览" (t6page), table tbl-glm52-config and glossary.
+ *   [Arch]      "GLM-5.2 架构深度拆解" (pillumina), CH2 §2.1-§2.4, §7.3.
+ *   [Q&A]       "GLM-5.2架构与基准" (lzwjava), §2 IndexShare / IndexCache.
+ *   [Serving]   "GLM-5→5.1→5.2：稀疏索引、Agent 后训练与 1M 上下文服务"
+ *               (papers-3lj), §10 operator-level changes.
+ *
+ * Conventions for every call:
+ *   - Pointers named *_dev are device pointers (HBM); everything else is host.
+ *     All device buffers are owned and allocated by the caller; the library
+ *     never allocates, frees or synchronises.
+ *   - Work is enqueued on `stream` (a hipStream_t; NULL = the default stream)
+ *     and the call returns without waiting for it.
+ *   - Arguments are validated on the host before anything is enqueued; a
+ *     failed check returns GSA_ERR_INVALID_ARG / GSA_ERR_UNSUPPORTED /
+ *     GSA_ERR_WORKSPACE and enqueues nothing. A launch failure returns
+ *     GSA_ERR_HIP. gsa_last_error() gives the calling thread's last message.
+ *   - Device pointers must be 16-byte aligned. Tensors are dense row-major
+ *     unless a leading dimension is given.
+ *   - Values the library cannot check without reading device memory (indices,
+ *     positions, sequence ids) must lie in the documented ranges; violating
+ *     them is undefined behaviour.
+ *   - Calls are re-entrant; calls that share a workspace must not overlap.
+ */
+#ifndef GSA_H
+#define GSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum gsa_status {
+    GSA_OK = 0,
+    GSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, ... */
+    GSA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. k != 2048) */
+    GSA_ERR_WORKSPACE = 3,     /* workspace missing or too small */
+    GSA_ERR_HIP = 4            /* a HIP launch failed */
+} gsa_status;
+
+typedef enum gsa_dtype {
+    GSA_BF16 = 0,              /* bfloat16 */
+    GSA_FP8_E4M3 = 1           /* OCP E4M3FN bytes with fp32 per-128-block scales */
+} gsa_dtype;
+
+/* Fixed shapes of the GLM-5.2 indexer and MLA ([Overview] tbl-glm52-config;
+ * [Arch] §1.1: index_n_heads 32, index_head_dim 128, index_topk 2048; 64 heads;
+ * kv_lora_rank 512; qk_rope_head_dim 64). */
+#define GSA_INDEX_HEADS 32
+#define GSA_INDEX_DIM 128
+#define GSA_TOPK 2048
+#define GSA_LATENT_DIM 512
+#define GSA_ROPE_DIM 64
+#define GSA_KV_ROW 576          /* 512 latent + 64 RoPE bf16 = 1152 B per token */
+
+const char* gsa_status_string(gsa_status s);
+const char* gsa_last_error(void);
+const char* gsa_version(void);
+
+/*
+ * gsa_quantize_e4m3 — per-block FP8 quantisation of indexer q or k
+ * ([Overview] sub-document index row 02: FP8 per-block; glossary: E4M3).
+ *
+ * x_dev      bf16 [n_blocks, 128]: each 128-element row is one block (one
+ *            indexer key row, or one (query, head) vector).
+ * codes_dev  uint8 [n_blocks, 128] out: E4M3FN, round to nearest even,
+ *            saturating at +-448.
+ * scales_dev fp32 [n_blocks] out: 2^e with e the smallest integer such that
+ *            max|x| <= 448 * 2^e, clamped to [-126, 127]; 1 for a zero block.
+ * Errors: null pointers, n_blocks < 0 (0 is a no-op).
+ */
+gsa_status gsa_quantize_e4m3(const void* x_dev, int64_t n_blocks,
+                             uint8_t* codes_dev, float* scales_dev, void* stream);
+
+/*
+ * gsa_indexer_score — the full (F) layer's lightning-indexer score
+ * ([Arch] §2.2: an F layer scores each query against every history token
+ * with 32 heads x 128 dims; [Overview] sub-document index: ReLU).
+ *
+ *   scores[i, s] = sum_h w[i,h] * max(0, q[i,h,:] . k[q_seq[i], s, :])  s <= q_pos[i]
+ *   scores[i, s] = -inf                                                q_pos[i] < s < n_cap
+ *   columns n_cap .. ld_scores-1 are not written.
+ *
+ * dt         GSA_BF16 or GSA_FP8_E4M3.
+ * q_dev      [n_q, 32, 128] bf16, or E4M3 bytes when dt is FP8.
+ * q_scale_dev fp32 [n_q, 32] per-(query, head) block scales (FP8 only, else NULL).
+ * w_dev      fp32 [n_q, 32] per-(query, head) weights.
+ * k_dev      [batch, n_cap, 128] bf16 or E4M3 bytes: one key per position,
+ *            shared by all heads.
+ * k_scale_dev fp32 [batch, n_cap] per-key-row block scales (FP8 only, else NULL).
+ *            FP8 scales must be powers of two (as gsa_quantize_e4m3 makes them);
+ *            only their exponent is used.
+ * q_seq_dev  int32 [n_q], each in [0, batch). q_pos_dev int32 [n_q], each in
+ *            [0, n_cap). Queries of one sequence should be adjacent (any order
+ *            is correct; adjacency lets them share key reads).
+ * scores_dev fp32 [n_q, ld_scores], ld_scores >= n_cap, ld_scores % 4 == 0.
+ * Errors: null pointers, n_q < 1, batch < 1, n_cap < 1, bad ld, bad dtype,
+ *         missing scales for FP8, n_cap > 2^31 - 1.
+ */
+gsa_status gsa_indexer_score(gsa_dtype dt,
+                             const void* q_dev, const float* q_scale_dev, const float* w_dev,
+                             const void* k_dev, const float* k_scale_dev,
+                             const int32_t* q_seq_dev, const int32_t* q_pos_dev,
+                             int n_q, int batch, int64_t n_cap,
+                             float* scores_dev, int64_t ld_scores, void* stream);
+
+/*
+ * gsa_topk — causal top-k over each score row ([Arch] §2.2 and §1.1:
+ * index_topk 2048, the selected tokens are the layer's sparse attention set).
+ *
+ * For row i, among positions s = 0..q_pos[i], keeps the min(k, q_pos[i]+1)
+ * largest scores; ties go to the lower position; -0.0 ties with +0.0.
+ * idx_dev int32 [n_q, k] out: the kept positions in ascending order, then -1.
+ * NaN scores are not supported.
+ * scores_dev fp32 [n_q, ld_scores] (ld_scores % 4 == 0, >= max q_pos + 1).
+ * workspace_dev: at least gsa_topk_workspace_bytes(n_q, ld_scores, k) bytes,
+ *            16-byte aligned; its contents on entry do not matter.
+ * Errors: k != 2048 (GSA_ERR_UNSUPPORTED), null pointers, small workspace.
+ */
+size_t gsa_topk_workspace_bytes(int n_q, int64_t ld_scores, int k);
+gsa_status gsa_topk(const float* scores_dev, int64_t ld_scores, const int32_t* q_pos_dev,
+                    int n_q, int k, int32_t* idx_dev,
+                    void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * gsa_sparse_mla_attn — absorbed MLA over the selected positions of one layer
+ * ([Overview] tbl-glm52-config: 64 heads, QK dim 256 = 192 + 64, latent 512,
+ * cache row 512 + 64 in BF16 = 1152 B; sub-document index: decode in latent
+ * space; [Serving] §10: each layer gathers the selected entries of its own
+ * K/V cache, then sparse attention).
+ *
+ * For query i, head h, selected rows s_j = idx[i, j] (entries < 0 skipped):
+ *   z_j = scale * (q_lat[i,h,:] . c[s_j] + q_rope[i,h,:] . kr[s_j])
+ *   out[i,h,:] = sum_j softmax(z)_j * c[s_j];  lse[i,h] = log sum_j exp(z_j)
+ * (c = kv[..., :512], kr = kv[..., 512:]). A row with no valid index gives
+ * out = 0 and lse = -inf.
+ *
+ * q_lat_dev  bf16 [n_q, n_heads, 512]; q_rope_dev bf16 [n_q, n_heads, 64].
+ * kv_dev     bf16 [batch, n_cap, 576] (packed 1152-byte rows).
+ * q_seq_dev  int32 [n_q] in [0, batch). idx_dev int32 [n_q, k], each
+ *            entry -1 or in [0, n_cap).
+ * n_heads    must be 64. k must be 2048.
+ * out_dev    fp32 [n_q, n_heads, 512]; lse_dev fp32 [n_q, n_heads] or NULL.
+ * workspace_dev: at least gsa_mla_workspace_bytes(n_q, n_heads, k) bytes.
+ */
+size_t gsa_mla_workspace_bytes(int n_q, int n_heads, int k);
+gsa_status gsa_sparse_mla_attn(const void* q_lat_dev, const void* q_rope_dev, const void* kv_dev,
+                               const int32_t* q_seq_dev, const int32_t* idx_dev, int k,
+                               int n_q, int n_heads, int batch, int64_t n_cap, float scale,
+                               float* out_dev, float* lse_dev,
+                               void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
+ * gsa_indexshare_group — one IndexShare group: a full layer and the shared
+ * layers that reuse its indices ([Arch] §2.2 and §2.4: the F layer runs the
+ * indexer and writes the shared top-k buffer, S layers skip the indexer and
+ * read it; [Serving] §10: indexer once per group, buffer written once, every
+ * layer gathers from its own cache; [Arch] §7.3: with no shared layers this is
+ * per-layer DSA; [Arch] §2.4: MTP steps may reuse the buffer).
+ *
+ * compute_index = 1: score + top-k run and write index_buf_dev, then every
+ *                    layer in `layers` attends over it (layers[0] is the F layer).
+ * compute_index = 0: the caller supplies index_buf_dev (e.g. an earlier F
+ *                    layer's, or for MTP draft steps); only attention runs, and
+ *                    the indexer fields are ignored.
+ * index_buf_dev int32 [n_q, k], owned by the caller, who keeps it consistent
+ *                    with the prefix and positions it was computed for.
+ * scores_dev   fp32 [n_q, ld_scores] scratch for the F layer's scores.
+ * workspace    at least gsa_group_workspace_bytes(n_q, ld_scores, k, n_heads).
+ */
+typedef struct gsa_mla_layer {
+    const void* q_lat_dev;     /* bf16 [n_q, n_heads, 512] */
+    const void* q_rope_dev;    /* bf16 [n_q, n_heads, 64] */
+    const void* kv_dev;        /* bf16 [batch, n_cap, 576] */
+    float* out_dev;            /* fp32 [n_q, n_heads, 512] */
+    float* lse_dev;            /* fp32 [n_q, n_heads] or NULL */
+} gsa_mla_layer;
+
+typedef struct gsa_group_desc {
+    int compute_index;
+    gsa_dtype dt;
+    const void* q_idx_dev; const float* q_scale_dev; const float* w_dev;
+    const void* k_idx_dev; const float* k_scale_dev;
+    float* scores_dev; int64_t ld_scores;
+    const int32_t* q_seq_dev; const int32_t* q_pos_dev;
+    int n_q; int batch; int64_t n_cap; int k;
+    int32_t* index_buf_dev;
+    int n_layers; const gsa_mla_layer* layers;   /* host array of n_layers */
+    int n_heads; float scale;
+    void* workspace_dev; size_t workspace_bytes;
+} gsa_group_desc;
+
+size_t gsa_group_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads);
+gsa_status gsa_indexshare_group(const gsa_group_desc* desc, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* GSA_H */

@@ -1,0 +1,246 @@
+"""Python binding of libgsa: GLM-5.2's DSA lightning indexer, IndexShare and
+absorbed sparse MLA on one MI355X.
+
+Argument marshalling only: every step runs in the HIP kernels of libgsa.so
+(built in this directory by `build.py`). PyTorch supplies device memory and
+the current stream. Importing this package does not load the library; the
+first call does, and raises if the library is missing or a call fails. There
+is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgsa.so")
+HEADER = os.path.join(_HERE, "..", "include", "gsa.h")
+
+INDEX_HEADS, INDEX_DIM, TOPK = 32, 128, 2048
+MLA_HEADS, LATENT_DIM, ROPE_DIM, KV_ROW = 64, 512, 64, 576
+BF16, FP8_E4M3 = 0, 1
+
+_lib = None
+
+
+class GsaError(RuntimeError):
+    pass
+
+
+class _MlaLayer(ctypes.Structure):
+    _fields_ = [("q_lat_dev", ctypes.c_void_p), ("q_rope_dev", ctypes.c_void_p),
+                ("kv_dev", ctypes.c_void_p), ("out_dev", ctypes.c_void_p),
+                ("lse_dev", ctypes.c_void_p)]
+
+
+class _GroupDesc(ctypes.Structure):
+    _fields_ = [("compute_index", ctypes.c_int), ("dt", ctypes.c_int),
+                ("q_idx_dev", ctypes.c_void_p), ("q_scale_dev", ctypes.c_void_p),
+                ("w_dev", ctypes.c_void_p), ("k_idx_dev", ctypes.c_void_p),
+                ("k_scale_dev", ctypes.c_void_p), ("scores_dev", ctypes.c_void_p),
+                ("ld_scores", ctypes.c_int64), ("q_seq_dev", ctypes.c_void_p),
+                ("q_pos_dev", ctypes.c_void_p), ("n_q", ctypes.c_int), ("batch", ctypes.c_int),
+                ("n_cap", ctypes.c_int64), ("k", ctypes.c_int), ("index_buf_dev", ctypes.c_void_p),
+                ("n_layers", ctypes.c_int), ("layers", ctypes.POINTER(_MlaLayer)),
+                ("n_heads", ctypes.c_int), ("scale", ctypes.c_float),
+                ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
+def _declare(lib):
+    P, I, I64, SZ, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+    sig = {
+        "gsa_status_string": (ctypes.c_char_p, [I]),
+        "gsa_last_error": (ctypes.c_char_p, []),
+        "gsa_version": (ctypes.c_char_p, []),
+        "gsa_quantize_e4m3": (I, [P, I64, P, P, P]),
+        "gsa_indexer_score": (I, [I, P, P, P, P, P, P, P, I, I, I64, P, I64, P]),
+        "gsa_topk_workspace_bytes": (SZ, [I, I64, I]),
+        "gsa_topk": (I, [P, I64, P, I, I, P, P, SZ, P]),
+        "gsa_mla_workspace_bytes": (SZ, [I, I, I]),
+        "gsa_sparse_mla_attn": (I, [P, P, P, P, P, I, I, I, I, I64, F, P, P, P, SZ, P]),
+        "gsa_group_workspace_bytes": (SZ, [I, I64, I, I]),
+        "gsa_indexshare_group": (I, [ctypes.POINTER(_GroupDesc), P]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype, fn.argtypes = res, args
+    return lib
+
+
+def lib():
+    """Load libgsa.so (built by build.py); raise if it is not there."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise GsaError(f"{LIB_PATH} is missing: build it with `python -m long_context_sparse_02_amd.build`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def header_symbols():
+    """Function names declared in include/gsa.h."""
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(gsa_[a-z0-9_]+)\s*\(", text)))
+
+
+def _check(status):
+    if status != 0:
+        L = lib()
+        raise GsaError(f"{L.gsa_status_string(status).decode()}: {L.gsa_last_error().decode()}")
+
+
+def _p(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t, name, dtype, shape=None):
+    if t.dtype != dtype:
+        raise GsaError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_cuda or not t.is_contiguous():
+        raise GsaError(f"{name} must be a contiguous device tensor")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise GsaError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
+# ---------------------------------------------------------------- entry points
+def quantize_e4m3(x):
+    """x bf16 [..., 128] -> (codes uint8 same shape, scales fp32 [...])."""
+    _need(x, "x", torch.bfloat16)
+    n = x.numel() // 128
+    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+    scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    _check(lib().gsa_quantize_e4m3(_p(x), n, _p(codes), _p(scales), _stream(x.device)))
+    return codes, scales
+
+
+def indexer_score(q, w, k, q_seq, q_pos, q_scale=None, k_scale=None, scores=None, ld=None):
+    """q [n_q,32,128], k [B,N,128] (bf16, or uint8 E4M3 codes with scales);
+    w fp32 [n_q,32]; q_seq/q_pos int32 [n_q]. Returns fp32 scores [n_q, ld]."""
+    fp8 = q.dtype == torch.uint8
+    n_q, batch, n_cap = q.shape[0], k.shape[0], k.shape[1]
+    _need(q, "q", torch.uint8 if fp8 else torch.bfloat16, (n_q, INDEX_HEADS, INDEX_DIM))
+    _need(k, "k", q.dtype, (batch, n_cap, INDEX_DIM))
+    _need(w, "w", torch.float32, (n_q, INDEX_HEADS))
+    _need(q_seq, "q_seq", torch.int32, (n_q,))
+    _need(q_pos, "q_pos", torch.int32, (n_q,))
+    if fp8:
+        _need(q_scale, "q_scale", torch.float32, (n_q, INDEX_HEADS))
+        _need(k_scale, "k_scale", torch.float32, (batch, n_cap))
+    if ld is None:
+        ld = (n_cap + 3) // 4 * 4
+    if scores is None:
+        scores = torch.empty((n_q, ld), dtype=torch.float32, device=q.device)
+    _need(scores, "scores", torch.float32)
+    _check(lib().gsa_indexer_score(FP8_E4M3 if fp8 else BF16, _p(q), _p(q_scale), _p(w), _p(k),
+                                   _p(k_scale), _p(q_seq), _p(q_pos), n_q, batch, n_cap,
+                                   _p(scores), scores.shape[1], _stream(q.device)))
+    return scores
+
+
+def topk_workspace_bytes(n_q, ld, k=TOPK):
+    return int(lib().gsa_topk_workspace_bytes(n_q, ld, k))
+
+
+def mla_workspace_bytes(n_q, n_heads=MLA_HEADS, k=TOPK):
+    return int(lib().gsa_mla_workspace_bytes(n_q, n_heads, k))
+
+
+def group_workspace_bytes(n_q, ld, k=TOPK, n_heads=MLA_HEADS):
+    return int(lib().gsa_group_workspace_bytes(n_q, ld, k, n_heads))
+
+
+def _workspace(nbytes, device, ws):
+    if ws is None:
+        ws = torch.empty(max(16, nbytes), dtype=torch.uint8, device=device)
+    return ws
+
+
+def topk(scores, q_pos, k=TOPK, idx=None, workspace=None):
+    """scores fp32 [n_q, ld]; q_pos int32 [n_q] -> idx int32 [n_q, k]."""
+    n_q, ld = scores.shape
+    _need(scores, "scores", torch.float32)
+    _need(q_pos, "q_pos", torch.int32, (n_q,))
+    if idx is None:
+        idx = torch.empty((n_q, k), dtype=torch.int32, device=scores.device)
+    _need(idx, "idx", torch.int32, (n_q, k))
+    ws = _workspace(topk_workspace_bytes(n_q, ld, k), scores.device, workspace)
+    _check(lib().gsa_topk(_p(scores), ld, _p(q_pos), n_q, k, _p(idx), _p(ws), ws.numel(),
+                          _stream(scores.device)))
+    return idx
+
+
+def sparse_mla_attn(q_lat, q_rope, kv, q_seq, idx, scale=1.0 / 16.0, out=None, lse=None,
+                    workspace=None, want_lse=True):
+    """q_lat bf16 [n_q,64,512], q_rope bf16 [n_q,64,64], kv bf16 [B,N,576],
+    q_seq int32 [n_q], idx int32 [n_q, 2048] -> (out fp32 [n_q,64,512], lse fp32 [n_q,64])."""
+    n_q, n_h = q_lat.shape[0], q_lat.shape[1]
+    batch, n_cap = kv.shape[0], kv.shape[1]
+    _need(q_lat, "q_lat", torch.bfloat16, (n_q, n_h, LATENT_DIM))
+    _need(q_rope, "q_rope", torch.bfloat16, (n_q, n_h, ROPE_DIM))
+    _need(kv, "kv", torch.bfloat16, (batch, n_cap, KV_ROW))
+    _need(q_seq, "q_seq", torch.int32, (n_q,))
+    _need(idx, "idx", torch.int32)
+    k = idx.shape[1]
+    if out is None:
+        out = torch.empty((n_q, n_h, LATENT_DIM), dtype=torch.float32, device=q_lat.device)
+    if lse is None and want_lse:
+        lse = torch.empty((n_q, n_h), dtype=torch.float32, device=q_lat.device)
+    ws = _workspace(mla_workspace_bytes(n_q, n_h, k), q_lat.device, workspace)
+    _check(lib().gsa_sparse_mla_attn(_p(q_lat), _p(q_rope), _p(kv), _p(q_seq), _p(idx), k, n_q, n_h,
+                                     batch, n_cap, scale, _p(out), _p(lse), _p(ws), ws.numel(),
+                                     _stream(q_lat.device)))
+    return out, lse
+
+
+def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_idx=None,
+                     q_scale=None, k_scale=None, scores=None, compute_index=True,
+                     scale=1.0 / 16.0, workspace=None, outs=None):
+    """One IndexShare group: layers = [(q_lat, q_rope, kv), ...], F layer first.
+    With compute_index the F layer's indexer + top-k write index_buf, then every
+    layer attends over it. Returns [(out, lse)] per layer."""
+    L = lib()
+    n_q = q_seq.shape[0]
+    kv0 = layers[0][2]
+    batch, n_cap = kv0.shape[0], kv0.shape[1]
+    k = index_buf.shape[1]
+    dev = q_seq.device
+    fp8 = compute_index and q_idx.dtype == torch.uint8
+    if compute_index:
+        if scores is None:
+            scores = torch.empty((n_q, (n_cap + 3) // 4 * 4), dtype=torch.float32, device=dev)
+        ld = scores.shape[1]
+    else:
+        ld = 4
+    if outs is None:
+        outs = [(torch.empty((n_q, MLA_HEADS, LATENT_DIM), dtype=torch.float32, device=dev),
+                 torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)) for _ in layers]
+    arr = (_MlaLayer * len(layers))()
+    for i, ((ql, qr, kv), (o, s)) in enumerate(zip(layers, outs)):
+        arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
+                           None if s is None else s.data_ptr())
+    nbytes = group_workspace_bytes(n_q, ld, k) if compute_index else mla_workspace_bytes(n_q, MLA_HEADS, k)
+    ws = _workspace(nbytes, dev, workspace)
+    d = _GroupDesc()
+    d.compute_index = 1 if compute_index else 0
+    d.dt = FP8_E4M3 if fp8 else BF16
+    if compute_index:
+        d.q_idx_dev, d.w_dev, d.k_idx_dev = q_idx.data_ptr(), w.data_ptr(), k_idx.data_ptr()
+        d.q_scale_dev = q_scale.data_ptr() if fp8 else None
+        d.k_scale_dev = k_scale.data_ptr() if fp8 else None
+        d.scores_dev, d.q_pos_dev = scores.data_ptr(), q_pos.data_ptr()
+    d.ld_scores = ld
+    d.q_seq_dev = q_seq.data_ptr()
+    d.n_q, d.batch, d.n_cap, d.k = n_q, batch, n_cap, k
+    d.index_buf_dev = index_buf.data_ptr()
+    d.n_layers, d.layers = len(layers), ctypes.cast(arr, ctypes.POINTER(_MlaLayer))
+    d.n_heads, d.scale = MLA_HEADS, scale
+    d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
+    _check(L.gsa_indexshare_group(ctypes.byref(d), _stream(dev)))
+    return outs

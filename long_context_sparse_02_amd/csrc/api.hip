@@ -1,0 +1,215 @@
+// C ABI of libgsa (declared in include/gsa.h): host-side argument checks,
+// then launches on the caller's stream. Nothing here allocates, frees or
+// synchronises; no C++ exception crosses the boundary.
+#include <stdarg.h>
+#include <stdio.h>
+
+#include "../../include/gsa.h"
+#include "launch.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+gsa_status fail(gsa_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+gsa_status hip_result(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(GSA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    g_err[0] = 0;
+    return GSA_OK;
+}
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+#define REQUIRE(cond, ...) \
+    do { if (!(cond)) return fail(GSA_ERR_INVALID_ARG, __VA_ARGS__); } while (0)
+#define REQUIRE_PTR(p) \
+    do { if ((p) == nullptr) return fail(GSA_ERR_INVALID_ARG, "%s is NULL", #p); \
+         if (!aligned16(p)) return fail(GSA_ERR_INVALID_ARG, "%s is not 16-byte aligned", #p); } while (0)
+
+constexpr int kMaxGridY = 65535;
+
+gsa_status check_score(gsa_dtype dt, const void* q, const float* qs, const float* w, const void* k,
+                       const float* ks, const int32_t* q_seq, const int32_t* q_pos, int n_q,
+                       int batch, int64_t n_cap, const float* scores, int64_t ld) {
+    if (dt != GSA_BF16 && dt != GSA_FP8_E4M3) return fail(GSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
+    REQUIRE_PTR(q); REQUIRE_PTR(w); REQUIRE_PTR(k); REQUIRE_PTR(q_seq); REQUIRE_PTR(q_pos);
+    REQUIRE_PTR(scores);
+    if (dt == GSA_FP8_E4M3) { REQUIRE_PTR(qs); REQUIRE_PTR(ks); }
+    REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
+    REQUIRE(batch >= 1, "batch must be >= 1 (got %d)", batch);
+    REQUIRE(n_cap >= 1 && n_cap <= 0x7fffffff, "n_cap must be in [1, 2^31-1] (got %lld)", (long long)n_cap);
+    REQUIRE(ld >= n_cap, "ld_scores (%lld) must be >= n_cap (%lld)", (long long)ld, (long long)n_cap);
+    REQUIRE(ld % 4 == 0, "ld_scores must be a multiple of 4 (got %lld)", (long long)ld);
+    if (n_q > kMaxGridY) return fail(GSA_ERR_UNSUPPORTED, "n_q must be <= %d (got %d)", kMaxGridY, n_q);
+    return GSA_OK;
+}
+
+gsa_status check_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
+                      const int32_t* idx, const void* ws, size_t ws_bytes) {
+    REQUIRE_PTR(scores); REQUIRE_PTR(q_pos); REQUIRE_PTR(idx);
+    REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
+    if (n_q > kMaxGridY) return fail(GSA_ERR_UNSUPPORTED, "n_q must be <= %d (got %d)", kMaxGridY, n_q);
+    if (k != GSA_TOPK) return fail(GSA_ERR_UNSUPPORTED, "k must be %d (got %d)", GSA_TOPK, k);
+    REQUIRE(ld >= 1 && ld % 4 == 0, "ld_scores must be a positive multiple of 4 (got %lld)", (long long)ld);
+    REQUIRE(ld <= 0x7fffffff, "ld_scores must be < 2^31");
+    const size_t need = gsa::topk_workspace_bytes(n_q, ld, k);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(GSA_ERR_WORKSPACE, "top-k workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                    ws == nullptr ? ", NULL" : "");
+    REQUIRE(aligned16(ws), "workspace is not 16-byte aligned");
+    return GSA_OK;
+}
+
+gsa_status check_mla(const void* q_lat, const void* q_rope, const void* kv, const int32_t* q_seq,
+                     const int32_t* idx, int k, int n_q, int n_heads, int batch, int64_t n_cap,
+                     float scale, const float* out, const float* lse, const void* ws, size_t ws_bytes) {
+    REQUIRE_PTR(q_lat); REQUIRE_PTR(q_rope); REQUIRE_PTR(kv); REQUIRE_PTR(q_seq); REQUIRE_PTR(idx);
+    REQUIRE_PTR(out);
+    if (lse != nullptr) REQUIRE(aligned16(lse), "lse is not 16-byte aligned");
+    REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
+    if (n_q > kMaxGridY) return fail(GSA_ERR_UNSUPPORTED, "n_q must be <= %d (got %d)", kMaxGridY, n_q);
+    REQUIRE(batch >= 1, "batch must be >= 1 (got %d)", batch);
+    REQUIRE(n_cap >= 1, "n_cap must be >= 1");
+    if (n_heads != 64) return fail(GSA_ERR_UNSUPPORTED, "n_heads must be 64 (got %d)", n_heads);
+    if (k != GSA_TOPK) return fail(GSA_ERR_UNSUPPORTED, "k must be %d (got %d)", GSA_TOPK, k);
+    REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
+    const size_t need = gsa::mla_workspace_bytes(n_q, n_heads, k);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+        return fail(GSA_ERR_WORKSPACE, "attention workspace needs %zu bytes (got %zu)", need, ws_bytes);
+    if (need > 0) REQUIRE(aligned16(ws), "workspace is not 16-byte aligned");
+    return GSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* gsa_status_string(gsa_status s) {
+    switch (s) {
+        case GSA_OK: return "GSA_OK";
+        case GSA_ERR_INVALID_ARG: return "GSA_ERR_INVALID_ARG";
+        case GSA_ERR_UNSUPPORTED: return "GSA_ERR_UNSUPPORTED";
+        case GSA_ERR_WORKSPACE: return "GSA_ERR_WORKSPACE";
+        case GSA_ERR_HIP: return "GSA_ERR_HIP";
+    }
+    return "GSA_ERR_UNKNOWN";
+}
+
+const char* gsa_last_error(void) { return g_err; }
+
+const char* gsa_version(void) { return "gsa 0.1 gfx950"; }
+
+gsa_status gsa_quantize_e4m3(const void* x, int64_t n_blocks, uint8_t* codes, float* scales,
+                             void* stream) {
+    REQUIRE_PTR(x); REQUIRE_PTR(codes); REQUIRE_PTR(scales);
+    REQUIRE(n_blocks >= 0, "n_blocks must be >= 0");
+    return hip_result(gsa::launch_quantize_e4m3(x, n_blocks, codes, scales, (hipStream_t)stream),
+                      "quantize_e4m3");
+}
+
+gsa_status gsa_indexer_score(gsa_dtype dt, const void* q, const float* q_scale, const float* w,
+                             const void* k, const float* k_scale, const int32_t* q_seq,
+                             const int32_t* q_pos, int n_q, int batch, int64_t n_cap,
+                             float* scores, int64_t ld, void* stream) {
+    gsa_status st = check_score(dt, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, batch, n_cap, scores, ld);
+    if (st != GSA_OK) return st;
+    return hip_result(gsa::launch_indexer_score(dt == GSA_FP8_E4M3, q, q_scale, w, k, k_scale, q_seq,
+                                                q_pos, n_q, batch, n_cap, scores, ld, (hipStream_t)stream),
+                      "indexer_score");
+}
+
+size_t gsa_topk_workspace_bytes(int n_q, int64_t ld, int k) {
+    if (n_q < 1 || ld < 1) return 0;
+    return gsa::topk_workspace_bytes(n_q, ld, k);
+}
+
+gsa_status gsa_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
+                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    gsa_status st = check_topk(scores, ld, q_pos, n_q, k, idx, ws, ws_bytes);
+    if (st != GSA_OK) return st;
+    return hip_result(gsa::launch_topk(scores, ld, q_pos, n_q, k, idx, ws, (hipStream_t)stream), "topk");
+}
+
+size_t gsa_mla_workspace_bytes(int n_q, int n_heads, int k) {
+    if (n_q < 1 || n_heads != 64 || k != GSA_TOPK) return 0;
+    return gsa::mla_workspace_bytes(n_q, n_heads, k);
+}
+
+gsa_status gsa_sparse_mla_attn(const void* q_lat, const void* q_rope, const void* kv,
+                               const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
+                               int batch, int64_t n_cap, float scale, float* out, float* lse,
+                               void* ws, size_t ws_bytes, void* stream) {
+    gsa_status st = check_mla(q_lat, q_rope, kv, q_seq, idx, k, n_q, n_heads, batch, n_cap, scale,
+                              out, lse, ws, ws_bytes);
+    if (st != GSA_OK) return st;
+    return hip_result(gsa::launch_sparse_mla(q_lat, q_rope, kv, q_seq, idx, k, n_q, n_heads, n_cap,
+                                             scale, out, lse, ws, (hipStream_t)stream),
+                      "sparse_mla_attn");
+}
+
+size_t gsa_group_workspace_bytes(int n_q, int64_t ld, int k, int n_heads) {
+    const size_t a = gsa_topk_workspace_bytes(n_q, ld, k);
+    const size_t b = gsa_mla_workspace_bytes(n_q, n_heads, k);
+    return a > b ? a : b;     // top-k finishes (stream order) before attention reuses the space
+}
+
+gsa_status gsa_indexshare_group(const gsa_group_desc* d, void* stream) {
+    if (d == nullptr) return fail(GSA_ERR_INVALID_ARG, "desc is NULL");
+    REQUIRE_PTR(d->index_buf_dev); REQUIRE_PTR(d->q_seq_dev);
+    REQUIRE(d->n_layers >= 0, "n_layers must be >= 0");
+    REQUIRE(d->n_layers == 0 || d->layers != nullptr, "layers is NULL");
+    REQUIRE(d->compute_index == 0 || d->compute_index == 1, "compute_index must be 0 or 1");
+    const size_t need = gsa_group_workspace_bytes(d->n_q, d->ld_scores, d->k, d->n_heads);
+    // validate every step before enqueuing any of them
+    if (d->compute_index) {
+        gsa_status st = check_score(d->dt, d->q_idx_dev, d->q_scale_dev, d->w_dev, d->k_idx_dev,
+                                    d->k_scale_dev, d->q_seq_dev, d->q_pos_dev, d->n_q, d->batch,
+                                    d->n_cap, d->scores_dev, d->ld_scores);
+        if (st != GSA_OK) return st;
+        st = check_topk(d->scores_dev, d->ld_scores, d->q_pos_dev, d->n_q, d->k, d->index_buf_dev,
+                        d->workspace_dev, d->workspace_bytes);
+        if (st != GSA_OK) return st;
+    }
+    for (int l = 0; l < d->n_layers; ++l) {
+        const gsa_mla_layer& L = d->layers[l];
+        gsa_status st = check_mla(L.q_lat_dev, L.q_rope_dev, L.kv_dev, d->q_seq_dev, d->index_buf_dev,
+                                  d->k, d->n_q, d->n_heads, d->batch, d->n_cap, d->scale, L.out_dev,
+                                  L.lse_dev, d->workspace_dev, d->workspace_bytes);
+        if (st != GSA_OK) {
+            char tmp[512];
+            snprintf(tmp, sizeof(tmp), "layer %d: %s", l, g_err);
+            snprintf(g_err, sizeof(g_err), "%s", tmp);
+            return st;
+        }
+    }
+    (void)need;
+    hipStream_t s = (hipStream_t)stream;
+    if (d->compute_index) {
+        hipError_t e = gsa::launch_indexer_score(d->dt == GSA_FP8_E4M3, d->q_idx_dev, d->q_scale_dev,
+                                                 d->w_dev, d->k_idx_dev, d->k_scale_dev, d->q_seq_dev,
+                                                 d->q_pos_dev, d->n_q, d->batch, d->n_cap,
+                                                 d->scores_dev, d->ld_scores, s);
+        if (e != hipSuccess) return hip_result(e, "group: indexer_score");
+        e = gsa::launch_topk(d->scores_dev, d->ld_scores, d->q_pos_dev, d->n_q, d->k, d->index_buf_dev,
+                             d->workspace_dev, s);
+        if (e != hipSuccess) return hip_result(e, "group: topk");
+    }
+    for (int l = 0; l < d->n_layers; ++l) {
+        const gsa_mla_layer& L = d->layers[l];
+        hipError_t e = gsa::launch_sparse_mla(L.q_lat_dev, L.q_rope_dev, L.kv_dev, d->q_seq_dev,
+                                              d->index_buf_dev, d->k, d->n_q, d->n_heads, d->n_cap,
+                                              d->scale, L.out_dev, L.lse_dev, d->workspace_dev, s);
+        if (e != hipSuccess) return hip_result(e, "group: sparse_mla_attn");
+    }
+    g_err[0] = 0;
+    return GSA_OK;
+}
+
+}  // extern "C"

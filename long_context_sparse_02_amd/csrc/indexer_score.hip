@@ -1,0 +1,224 @@
+// Lightning-indexer score of a full (F) layer on gfx950 MFMA.
+//
+// "GLM-5.2 架构深度拆解" CH2 §2.2: an F layer scores each query against every
+// history token with 32 heads x 128 dims; "GLM-5.2 总览" sub-document index:
+// the indexer applies a ReLU (and FP8 per-block q/k as one variant).
+//
+//   score[i, s] = sum_h w[i,h] * max(0, q[i,h,:] . k[seq(i), s, :])   (s <= pos(i))
+//
+// Mapping to CDNA4. The 32 heads of one query are the 32 rows (M) of a
+// 32x32 MFMA tile and 32 consecutive keys its columns (N); the 128 dims are the
+// contraction. bf16 uses v_mfma_f32_32x32x16_bf16 (8 k-steps); fp8 uses
+// v_mfma_scale_f32_32x32x64_f8f6f4 (2 k-steps) with the per-block power-of-two
+// scales fed as E8M0 operand scales, so no dequantisation pass exists.
+// Because the contraction order is free, lane group g of a tile owns dims
+// [64g, 64g+64) in both operands. The epilogue (ReLU, head weight, sum over
+// heads) stays in registers: each lane holds 16 heads of one key and one
+// cross-lane add finishes the sum, so only the final fp32 score reaches HBM.
+//
+// Keys stream through LDS in 128-key tiles: coalesced 16-byte global loads
+// (each wave instruction reads 1 KiB contiguous), XOR-swizzled 16-byte chunks
+// so the MFMA-layout ds_read_b128 is conflict-free, and the next tile's loads
+// are in flight while the current tile is multiplied. Queries of one sequence
+// that share a work-group (QB of them) reuse each key tile from LDS.
+#include <type_traits>
+
+#include "device_common.h"
+#include "launch.h"
+
+namespace gsa {
+namespace {
+
+constexpr int kHeads = 32;
+constexpr int kDim = 128;
+constexpr int kTile = 128;      // keys per LDS tile
+constexpr int kThreads = 256;   // 4 waves
+
+template <bool FP8>
+struct KeyTile {
+    static constexpr int kRowBytes = FP8 ? kDim : kDim * 2;
+    static constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per key row
+    static constexpr int kBytes = kTile * kRowBytes;
+    static constexpr int kLoads = kBytes / (kThreads * 16);     // 16-byte loads per thread
+    // byte offset of chunk c of tile row r (XOR swizzle over the row's chunks)
+    __device__ static __forceinline__ int off(int r, int c) {
+        return r * kRowBytes + ((c ^ (r & (kChunks - 1))) << 4);
+    }
+};
+
+template <int QB, bool FP8>
+__global__ __launch_bounds__(kThreads) void indexer_score_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int n_q, int64_t n_cap,
+    float* __restrict__ scores, int64_t ld, int chunk) {
+    using T = KeyTile<FP8>;
+    constexpr int QPW = QB >= 4 ? QB / 4 : 1;   // queries per wave
+    constexpr int KSTEPS = FP8 ? 2 : 8;         // MFMA steps over 128 dims
+    using AVec = std::conditional_t<FP8, i32x8, bf16x8>;
+
+    __shared__ __attribute__((aligned(16))) uint8_t tile[T::kBytes];
+    __shared__ int key_e8[kTile];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int qb0 = blockIdx.y * QB;
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    if (c0 >= n_cap) return;
+    const int64_t c1 = min(c0 + (int64_t)chunk, n_cap);
+
+    // This wave owns the (query, 32-key subtile) pairs [wave*QB, wave*QB + QB):
+    // pair p -> query p/4 of the block, subtile p%4 of the 128-key tile.
+    const int jw0 = (wave * QB) / 4;
+
+    AVec a[QPW][KSTEPS];
+    float wr[QPW][16];
+    int apos[QPW], a_e8[QPW];
+#pragma unroll
+    for (int jj = 0; jj < QPW; ++jj) {
+        const int qi = qb0 + jw0 + jj;
+        const bool ok = qi < n_q;
+        const int qr = ok ? qi : 0;
+        apos[jj] = ok ? q_pos[qi] : -1;
+        // A operand: row = head n, this lane group's 64 dims [64g, 64g+64)
+        const uint8_t* qh = q + ((int64_t)qr * kHeads + n) * T::kRowBytes;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            if constexpr (FP8) {
+                const i32x4* p = (const i32x4*)(qh + 64 * g + 32 * t);
+                const i32x4 lo = p[0], hi = p[1];
+                a[jj][t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                a[jj][t] = *(const bf16x8*)(qh + 2 * (64 * g + 8 * t));
+            }
+        }
+        // accumulator register i of a 32x32 tile holds row 8*(i/4) + 4*g + i%4
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int h = 8 * (i >> 2) + 4 * g + (i & 3);
+            wr[jj][i] = ok ? w[(int64_t)qr * kHeads + h] : 0.f;
+        }
+        if constexpr (FP8) a_e8[jj] = e8m0_of(q_scale[(int64_t)qr * kHeads + n]);
+        else a_e8[jj] = 127;
+    }
+
+    // Queries of the block are processed in runs that share a sequence.
+    int j0 = 0;
+    while (j0 < QB && qb0 + j0 < n_q) {
+        const int seq = q_seq[qb0 + j0];
+        int j1 = j0 + 1;
+        int maxpos = q_pos[qb0 + j0];
+        while (j1 < QB && qb0 + j1 < n_q && q_seq[qb0 + j1] == seq) {
+            maxpos = max(maxpos, (int)q_pos[qb0 + j1]);
+            ++j1;
+        }
+        const uint8_t* kb = k + (int64_t)seq * n_cap * T::kRowBytes;
+        const float* ksb = FP8 ? k_scale + (int64_t)seq * n_cap : nullptr;
+
+        i32x4 pf[T::kLoads];
+        auto load_tile = [&](int64_t t0) {
+#pragma unroll
+            for (int i = 0; i < T::kLoads; ++i) {
+                const int lin = i * kThreads + tid;
+                const int r = lin / T::kChunks, c = lin % T::kChunks;
+                pf[i] = (t0 + r < c1) ? *(const i32x4*)(kb + (t0 + r) * T::kRowBytes + c * 16)
+                                      : i32x4{0, 0, 0, 0};
+            }
+        };
+        if (c0 <= maxpos) load_tile(c0);
+
+        for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
+            const bool active = t0 <= maxpos;   // uniform over the work-group
+            if (active) {
+                __syncthreads();                 // readers of the previous tile are done
+#pragma unroll
+                for (int i = 0; i < T::kLoads; ++i) {
+                    const int lin = i * kThreads + tid;
+                    *(i32x4*)(tile + T::off(lin / T::kChunks, lin % T::kChunks)) = pf[i];
+                }
+                if constexpr (FP8) {
+                    if (tid < kTile) key_e8[tid] = (t0 + tid < c1) ? e8m0_of(ksb[t0 + tid]) : 127;
+                }
+                __syncthreads();
+                const int64_t tn = t0 + kTile;
+                if (tn < c1 && tn <= maxpos) load_tile(tn);   // in flight during the MFMAs
+            }
+#pragma unroll
+            for (int p = 0; p < QB; ++p) {
+                const int pp = wave * QB + p;
+                const int j = pp >> 2, nt = pp & 3;
+                const int jj = j - jw0;
+                if (j < j0 || j >= j1) continue;         // other run (wave-uniform)
+                const int64_t s0 = t0 + nt * 32;
+                const int64_t s = s0 + n;
+                float res = neg_inf();
+                if (active && s0 <= apos[jj]) {
+                    f32x16 acc = {};
+                    const int row = nt * 32 + n;
+#pragma unroll
+                    for (int t = 0; t < KSTEPS; ++t) {
+                        if constexpr (FP8) {
+                            const i32x4 lo = *(const i32x4*)(tile + T::off(row, 4 * g + 2 * t));
+                            const i32x4 hi = *(const i32x4*)(tile + T::off(row, 4 * g + 2 * t + 1));
+                            const i32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                a[jj][t], b, acc, 0, 0, 0, a_e8[jj], 0, key_e8[row]);
+                        } else {
+                            const bf16x8 b = *(const bf16x8*)(tile + T::off(row, 8 * g + t));
+                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jj][t], b, acc, 0, 0, 0);
+                        }
+                    }
+                    float part = 0.f;
+#pragma unroll
+                    for (int i = 0; i < 16; ++i) part = fmaf(wr[jj][i], fmaxf(acc[i], 0.f), part);
+                    part += shfl_xor(part, 32);
+                    res = (s <= apos[jj]) ? part : neg_inf();
+                }
+                if (g == 0 && s < c1) scores[(int64_t)(qb0 + j) * ld + s] = res;
+            }
+        }
+        j0 = j1;
+    }
+}
+
+template <int QB>
+hipError_t launch_qb(bool fp8, dim3 grid, hipStream_t st, const void* q, const float* qs,
+                     const float* w, const void* k, const float* ks, const int32_t* q_seq,
+                     const int32_t* q_pos, int n_q, int64_t n_cap, float* scores, int64_t ld,
+                     int chunk) {
+    if (fp8)
+        hipLaunchKernelGGL((indexer_score_kernel<QB, true>), grid, dim3(kThreads), 0, st,
+                           (const uint8_t*)q, qs, w, (const uint8_t*)k, ks, q_seq, q_pos, n_q,
+                           n_cap, scores, ld, chunk);
+    else
+        hipLaunchKernelGGL((indexer_score_kernel<QB, false>), grid, dim3(kThreads), 0, st,
+                           (const uint8_t*)q, qs, w, (const uint8_t*)k, ks, q_seq, q_pos, n_q,
+                           n_cap, scores, ld, chunk);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, const float* w,
+                                const void* k, const float* k_scale, const int32_t* q_seq,
+                                const int32_t* q_pos, int n_q, int batch, int64_t n_cap,
+                                float* scores, int64_t ld, hipStream_t stream) {
+    // Queries per work-group: the typical number of queries per sequence.
+    const int per_seq = n_q / (batch > 0 ? batch : 1);
+    const int qb = per_seq >= 8 ? 8 : per_seq >= 4 ? 4 : per_seq >= 2 ? 2 : 1;
+    const int64_t n_qblk = (n_q + qb - 1) / qb;
+    // Key chunk per work-group: aim for >= 2048 work-groups, chunks of 1K..16K keys.
+    int64_t chunk = 16384;
+    while (chunk > 1024 && n_qblk * ((n_cap + chunk - 1) / chunk) < 2048) chunk >>= 1;
+    const dim3 grid((unsigned)((n_cap + chunk - 1) / chunk), (unsigned)n_qblk);
+    switch (qb) {
+        case 8: return launch_qb<8>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
+        case 4: return launch_qb<4>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
+        case 2: return launch_qb<2>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
+        default: return launch_qb<1>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
+    }
+}
+
+}  // namespace gsa

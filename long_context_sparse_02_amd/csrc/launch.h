@@ -1,0 +1,29 @@
+// Host-side launchers of the gfx950 kernels (internal to libgsa; the C ABI in
+// include/gsa.h validates arguments and then calls these).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace gsa {
+
+hipError_t launch_quantize_e4m3(const void* x, int64_t n_blocks, uint8_t* codes, float* scales,
+                                hipStream_t stream);
+
+hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, const float* w,
+                                const void* k, const float* k_scale, const int32_t* q_seq,
+                                const int32_t* q_pos, int n_q, int batch, int64_t n_cap,
+                                float* scores, int64_t ld, hipStream_t stream);
+
+size_t topk_workspace_bytes(int n_q, int64_t ld, int k);
+hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
+                       int32_t* idx, void* ws, hipStream_t stream);
+
+size_t mla_workspace_bytes(int n_q, int n_heads, int k);
+hipError_t launch_sparse_mla(const void* q_lat, const void* q_rope, const void* kv,
+                             const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
+                             int64_t n_cap, float scale, float* out, float* lse, void* ws,
+                             hipStream_t stream);
+
+}  // namespace gsa

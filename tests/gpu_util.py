@@ -1,0 +1,42 @@
+"""Helpers shared by the GPU parity tests (marshalling between torch and numpy)."""
+import sys
+
+import numpy as np
+import torch
+
+# Attention tolerance: bf16 inputs, fp32 accumulation, P rounded to bf16 before
+# P.V (relative error <= 2^-9 per weight); outputs are O(0.1), so the expected
+# max-abs error is ~1e-3. The bar is 1e-2 max-abs.
+ATOL_OUT = 1e-2
+ATOL_LSE = 1e-2
+
+
+def np32(t):
+    """torch (any device) -> numpy float32 (bf16 widens exactly); ints stay ints."""
+    t = t.detach().cpu()
+    if t.dtype in (torch.bfloat16, torch.float16):
+        t = t.float()
+    return t.numpy()
+
+
+def dev():
+    return torch.device("cuda", 0)
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def assert_scores_equal(gpu_row, oracle_row, label=""):
+    g = np.asarray(gpu_row, dtype=np.float64)
+    o = np.asarray(oracle_row, dtype=np.float64)
+    bad = np.nonzero(~((g == o) | (np.isneginf(g) & np.isneginf(o))))[0]
+    assert bad.size == 0, f"{label}: {bad.size} mismatches, first at {bad[:5]}: gpu {g[bad[:5]]} oracle {o[bad[:5]]}"
+
+
+def max_abs(a, b):
+    a = np.asarray(a, np.float64)
+    b = np.asarray(b, np.float64)
+    both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
+    d = np.where(both_inf, 0.0, np.abs(a - b))
+    return float(np.max(d)) if d.size else 0.0

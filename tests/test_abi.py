@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports what include/gsa.h declares, and rejects bad
+arguments on the host before touching a GPU (CPU only: no compute calls)."""
+import ctypes
+import os
+
+import pytest
+
+import long_context_sparse_02_amd as gsa
+
+pytestmark = pytest.mark.skipif(not os.path.exists(gsa.LIB_PATH),
+                                reason="libgsa.so not built (run __graft_entry__.build())")
+
+OK, INVALID, UNSUPPORTED, WORKSPACE = 0, 1, 2, 3
+FAKE = ctypes.c_void_p(0x10000)          # aligned, never dereferenced on these paths
+MISALIGNED = ctypes.c_void_p(0x10004)
+
+
+def test_exports_every_declared_symbol():
+    L = gsa.lib()
+    declared = gsa.header_symbols()
+    assert {"gsa_indexer_score", "gsa_topk", "gsa_sparse_mla_attn", "gsa_indexshare_group"} <= set(declared)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings_and_version():
+    L = gsa.lib()
+    assert L.gsa_status_string(0) == b"GSA_OK"
+    assert L.gsa_status_string(3) == b"GSA_ERR_WORKSPACE"
+    assert b"gfx950" in L.gsa_version()
+
+
+def _score(**kw):
+    a = dict(dt=0, q=FAKE, qs=None, w=FAKE, k=FAKE, ks=None, q_seq=FAKE, q_pos=FAKE, n_q=4, batch=1,
+             n_cap=4096, scores=FAKE, ld=4096)
+    a.update(kw)
+    return gsa.lib().gsa_indexer_score(a["dt"], a["q"], a["qs"], a["w"], a["k"], a["ks"], a["q_seq"],
+                                       a["q_pos"], a["n_q"], a["batch"], a["n_cap"], a["scores"],
+                                       a["ld"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), INVALID), (dict(w=None), INVALID), (dict(scores=None), INVALID),
+    (dict(k=MISALIGNED), INVALID), (dict(n_q=0), INVALID), (dict(batch=0), INVALID),
+    (dict(n_cap=0), INVALID), (dict(ld=4095), INVALID), (dict(ld=4098), INVALID),
+    (dict(dt=7), INVALID), (dict(dt=1), INVALID),              # fp8 without scales
+    (dict(n_q=70000), UNSUPPORTED),
+])
+def test_indexer_score_rejects(kw, code):
+    assert _score(**kw) == code
+    assert gsa.lib().gsa_last_error() != b""
+
+
+def test_topk_rejects():
+    L = gsa.lib()
+    need = L.gsa_topk_workspace_bytes(4, 4096, 2048)
+    assert need > 0
+    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 1024, FAKE, FAKE, need, None) == UNSUPPORTED
+    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 2048, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 2048, FAKE, None, need, None) == WORKSPACE
+    assert L.gsa_topk(None, 4096, FAKE, 4, 2048, FAKE, FAKE, need, None) == INVALID
+    assert L.gsa_topk(FAKE, 4094, FAKE, 4, 2048, FAKE, FAKE, need, None) == INVALID
+
+
+def test_sparse_mla_rejects():
+    L = gsa.lib()
+    need = L.gsa_mla_workspace_bytes(8, 64, 2048)
+    assert need > 0          # a small batch is split across work-groups
+    args = [FAKE, FAKE, FAKE, FAKE, FAKE, 2048, 8, 64, 1, 4096, 1 / 16, FAKE, None, FAKE, need, None]
+    bad = list(args); bad[7] = 32
+    assert L.gsa_sparse_mla_attn(*bad) == UNSUPPORTED
+    bad = list(args); bad[5] = 512
+    assert L.gsa_sparse_mla_attn(*bad) == UNSUPPORTED
+    bad = list(args); bad[14] = need - 16
+    assert L.gsa_sparse_mla_attn(*bad) == WORKSPACE
+    bad = list(args); bad[10] = -1.0
+    assert L.gsa_sparse_mla_attn(*bad) == INVALID
+    bad = list(args); bad[2] = None
+    assert L.gsa_sparse_mla_attn(*bad) == INVALID
+
+
+def test_group_validates_every_layer_before_launching():
+    L = gsa.lib()
+    layers = (gsa._MlaLayer * 2)()
+    layers[0] = gsa._MlaLayer(0x10000, 0x10000, 0x10000, 0x10000, None)
+    layers[1] = gsa._MlaLayer(0x10000, None, 0x10000, 0x10000, None)     # second layer broken
+    d = gsa._GroupDesc()
+    d.compute_index = 0
+    d.q_seq_dev = d.index_buf_dev = 0x10000
+    d.n_q, d.batch, d.n_cap, d.k = 64, 64, 4096, 2048
+    d.n_layers, d.layers = 2, ctypes.cast(layers, ctypes.POINTER(gsa._MlaLayer))
+    d.n_heads, d.scale = 64, 1 / 16
+    assert L.gsa_indexshare_group(ctypes.byref(d), None) == WORKSPACE    # n_q = 64 splits rows
+    assert b"layer 0" in L.gsa_last_error()
+    d.workspace_dev, d.workspace_bytes = 0x10000, 1 << 30
+    assert L.gsa_indexshare_group(ctypes.byref(d), None) == INVALID
+    assert b"layer 1" in L.gsa_last_error()
+    assert L.gsa_indexshare_group(None, None) == INVALID
+    d.compute_index = 2
+    assert L.gsa_indexshare_group(ctypes.byref(d), None) == INVALID
+
+
+def test_quantize_rejects():
+    L = gsa.lib()
+    assert L.gsa_quantize_e4m3(None, 10, FAKE, FAKE, None) == INVALID
+    assert L.gsa_quantize_e4m3(FAKE, -1, FAKE, FAKE, None) == INVALID

@@ -1,0 +1,235 @@
+"""HIP path vs the CPU oracle on the same seeded inputs (small and ragged sizes).
+
+Scores and indices must match bit for bit on integer-valued indexer inputs;
+attention within 1e-2 max-abs. Every call goes through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+import long_context_sparse_02_amd as gsa
+import oracle
+import workloads as W
+from gpu_util import ATOL_LSE, ATOL_OUT, assert_scores_equal, dev, max_abs, np32, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    gsa.lib()
+
+
+# ------------------------------------------------------------------ quantiser
+def test_quantize_e4m3_matches_oracle():
+    g = torch.Generator().manual_seed(11)
+    ints = torch.randint(-4, 5, (300, 128), generator=g).float()
+    normal = torch.randn((300, 128), generator=g) * torch.logspace(-30, 30, 300)[:, None]
+    special = torch.zeros((4, 128))
+    special[1, 5] = 3.0e38
+    special[2] = torch.linspace(-1e-38, 1e-38, 128)
+    special[3, ::2] = -0.0
+    x = torch.cat([ints, normal, special]).to(torch.bfloat16)
+    codes, scales = gsa.quantize_e4m3(x.to(dev()))
+    torch.cuda.synchronize()
+    oc, osc = oracle.quantize_blocks(np32(x))
+    assert np.array_equal(np32(scales).astype(np.float64), osc[:, 0])
+    assert np.array_equal(np32(codes), oc)
+
+
+# ------------------------------------------------------------------ indexer score
+def _score_case(wl, seed, ld=None, dtype="bf16", perm=None):
+    q, w = W.indexer_queries(wl, seed, 0)
+    k = W.indexer_keys(wl, seed, 0)
+    q_seq, q_pos = W.query_layout(wl)
+    if perm is not None:
+        q, w, q_seq, q_pos = q[perm], w[perm], q_seq[perm], q_pos[perm]
+    d = dev()
+    ld = ld or (wl.n_ctx + 3) // 4 * 4
+    scores = torch.full((wl.n_q, ld), 12345.0, device=d)
+    if dtype == "fp8":
+        qc, qs = gsa.quantize_e4m3(q.to(d))
+        kc, ks = gsa.quantize_e4m3(k.to(d))
+        gsa.indexer_score(qc, w.to(d), kc, q_seq.to(d), q_pos.to(d), q_scale=qs, k_scale=ks, scores=scores)
+    else:
+        gsa.indexer_score(q.to(d), w.to(d), k.to(d), q_seq.to(d), q_pos.to(d), scores=scores)
+    torch.cuda.synchronize()
+    want = oracle.indexer_score(np32(q), np32(w), np32(k), np32(q_seq), np32(q_pos))
+    got = np32(scores)
+    for i in range(wl.n_q):
+        assert_scores_equal(got[i, : wl.n_ctx], want[i], f"query {i}")
+    assert np.all(got[:, wl.n_ctx:] == 12345.0), "columns past n_cap were written"
+    return got
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_score_tiny_group(dtype):
+    _score_case(W.WORKLOADS["group_b1_n4096_q4"], 0, dtype=dtype)
+
+
+@pytest.mark.parametrize("q_per_seq", [1, 2, 3, 4, 8, 11])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_score_ragged_and_query_blocks(q_per_seq, dtype):
+    # n_cap not a multiple of the 128-key tile; several sequences; ld padded
+    wl = W.Workload("ragged", 3, 1000 + 37 * q_per_seq, q_per_seq, 1, dtype)
+    _score_case(wl, q_per_seq, ld=(wl.n_ctx + 12 + 3) // 4 * 4, dtype=dtype)
+
+
+def test_score_unsorted_sequences_and_positions():
+    wl = W.Workload("mixed", 4, 700, 5, 1, "bf16")
+    perm = torch.randperm(wl.n_q, generator=torch.Generator().manual_seed(3))
+    q, w = W.indexer_queries(wl, 5, 0)
+    k = W.indexer_keys(wl, 5, 0)
+    q_seq = torch.randint(0, 4, (wl.n_q,), generator=torch.Generator().manual_seed(4), dtype=torch.int32)
+    q_pos = torch.tensor([0, 1, 127, 128, 129, 699, 300, 5, 64, 255, 256, 511, 512, 2, 3, 698, 640,
+                          641, 10, 600][: wl.n_q], dtype=torch.int32)
+    d = dev()
+    s = gsa.indexer_score(q.to(d), w.to(d), k.to(d), q_seq.to(d), q_pos.to(d))
+    torch.cuda.synchronize()
+    want = oracle.indexer_score(np32(q), np32(w), np32(k), np32(q_seq), np32(q_pos))
+    for i in range(wl.n_q):
+        assert_scores_equal(np32(s)[i, :700], want[i], f"query {i}")
+    del perm
+
+
+def test_score_negative_weights_and_float_inputs():
+    g = torch.Generator().manual_seed(9)
+    q = (torch.randn((6, 32, 128), generator=g)).to(torch.bfloat16)
+    k = (torch.randn((2, 900, 128), generator=g)).to(torch.bfloat16)
+    w = torch.randn((6, 32), generator=g)
+    q_seq = torch.tensor([0, 0, 0, 1, 1, 1], dtype=torch.int32)
+    q_pos = torch.tensor([899, 450, 3, 899, 128, 0], dtype=torch.int32)
+    d = dev()
+    s = np32(gsa.indexer_score(q.to(d), w.to(d), k.to(d), q_seq.to(d), q_pos.to(d)))
+    want = oracle.indexer_score(np32(q), np32(w), np32(k), np32(q_seq), np32(q_pos))
+    fin = np.isfinite(want)
+    assert np.array_equal(np.isfinite(s[:, :900]), fin)
+    # fp32 accumulation over 128 products then 32 heads, against float64
+    err = np.abs(s[:, :900][fin] - want[fin])
+    assert np.all(err <= 1e-4 * (1 + np.abs(want[fin]))), err.max()
+
+
+# ------------------------------------------------------------------ top-k
+@pytest.mark.parametrize("kind", W.SCORE_KINDS)
+def test_topk_matches_oracle(kind):
+    n = 40000                                          # 3 chunks, ragged tail
+    pos = torch.tensor([39999, 20000, 16383, 16384, 2047, 2048, 2049, 0, 5000], dtype=torch.int32)
+    s = W.score_matrix(kind, pos.numel(), n, seed=7)
+    d = dev()
+    idx = gsa.topk(s.to(d), pos.to(d))
+    torch.cuda.synchronize()
+    want = oracle.topk_select(np32(s), np32(pos), 2048)
+    got = np32(idx)
+    for i in range(pos.numel()):
+        assert np.array_equal(got[i], want[i]), f"{kind} row {i} (pos {int(pos[i])})"
+
+
+def test_topk_one_million_row():
+    n = 1 << 20
+    s = W.score_matrix("int_ties", 2, n, seed=8)
+    pos = torch.tensor([n - 1, n // 2 + 3], dtype=torch.int32)
+    idx = np32(gsa.topk(s.to(dev()), pos.to(dev())))
+    want = oracle.topk_select(np32(s), np32(pos), 2048)
+    assert np.array_equal(idx, want)
+
+
+def test_topk_ld_padding_is_ignored():
+    s = W.score_matrix("normal", 3, 5000, seed=2)
+    s[:, 4990:] = 1e30                                 # beyond every q_pos: must not be selected
+    pos = torch.tensor([4989, 3000, 100], dtype=torch.int32)
+    idx = np32(gsa.topk(s.to(dev()), pos.to(dev())))
+    assert np.array_equal(idx, oracle.topk_select(np32(s), np32(pos), 2048))
+
+
+# ------------------------------------------------------------------ sparse MLA
+def _mla_case(n_q, batch, n_ctx, seed, idx_fn=None):
+    wl = W.Workload("mla", batch, n_ctx, n_q // batch, 1, "bf16")
+    q_lat, q_rope = W.mla_queries(wl, seed, 0)
+    kv = W.mla_cache(wl, seed, 0)
+    q_seq, q_pos = W.query_layout(wl)
+    g = torch.Generator().manual_seed(seed)
+    if idx_fn is None:
+        s = torch.randn((wl.n_q, n_ctx), generator=g)
+        idx = torch.from_numpy(oracle.topk_select(s.numpy(), np32(q_pos), 2048))
+    else:
+        idx = idx_fn(wl, g)
+    d = dev()
+    out, lse = gsa.sparse_mla_attn(q_lat.to(d), q_rope.to(d), kv.to(d), q_seq.to(d), idx.to(d))
+    torch.cuda.synchronize()
+    o_want, l_want = oracle.sparse_mla(np32(q_lat), np32(q_rope), np32(kv), np32(q_seq), np32(idx), 1 / 16)
+    eo, el = max_abs(np32(out), o_want), max_abs(np32(lse), l_want)
+    say(f"mla n_q={n_q}: max|out-oracle|={eo:.2e} max|lse-oracle|={el:.2e}")
+    assert eo <= ATOL_OUT and el <= ATOL_LSE
+    return out, lse
+
+
+@pytest.mark.parametrize("n_q,batch", [(4, 1), (8, 2), (64, 4), (256, 2)])   # splits 32, 32, 4, 1
+def test_mla_matches_oracle(n_q, batch):
+    _mla_case(n_q, batch, 5000, seed=n_q)
+
+
+def test_mla_scattered_invalid_indices_and_empty_rows():
+    def idx_fn(wl, g):
+        idx = torch.randint(0, wl.n_ctx, (wl.n_q, 2048), generator=g, dtype=torch.int32)
+        drop = torch.rand((wl.n_q, 2048), generator=g) < 0.3
+        idx[drop] = -1
+        idx[1] = -1                                    # a query with nothing to attend
+        idx[2, :] = -1
+        idx[2, 777] = 42                               # a single valid row
+        return idx
+    out, lse = _mla_case(4, 1, 3000, seed=21, idx_fn=idx_fn)
+    assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
+
+
+def test_mla_short_prefix_equals_dense():
+    # prefix <= 2048: top-k keeps every position, so sparse attention is dense attention
+    def idx_fn(wl, g):
+        pos = torch.tensor([0, 1, 700, 2047])
+        idx = torch.full((4, 2048), -1, dtype=torch.int32)
+        for i, p in enumerate(pos):
+            idx[i, : p + 1] = torch.arange(p + 1)
+        return idx
+    _mla_case(4, 1, 2048, seed=5, idx_fn=idx_fn)
+
+
+# ------------------------------------------------------------------ IndexShare group
+def _group_case(wl, seed, dtype="bf16"):
+    g = W.group_inputs(wl, seed, n_layers=4)
+    d = dev()
+    layers = [tuple(t.to(d) for t in L) for L in g.layers]
+    idx = torch.full((wl.n_q, 2048), -7, dtype=torch.int32, device=d)
+    kw = {}
+    q_idx, k_idx = g.q_idx.to(d), g.k_idx.to(d)
+    if dtype == "fp8":
+        q_idx, kw["q_scale"] = gsa.quantize_e4m3(q_idx)
+        k_idx, kw["k_scale"] = gsa.quantize_e4m3(k_idx)
+    outs = gsa.indexshare_group(layers, g.q_seq.to(d), idx, q_pos=g.q_pos.to(d), q_idx=q_idx,
+                                w=g.w.to(d), k_idx=k_idx, **kw)
+    torch.cuda.synchronize()
+    sc, oidx, oouts = oracle.indexshare_group(
+        np32(g.q_idx), np32(g.w), np32(g.k_idx), np32(g.q_seq), np32(g.q_pos),
+        [tuple(np32(t) for t in L) for L in g.layers])
+    assert np.array_equal(np32(idx), oidx)
+    for l, ((o, s), (wo, ws)) in enumerate(zip(outs, oouts)):
+        eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
+        say(f"group layer {l}: max|out|err={eo:.2e} lse err={el:.2e}")
+        assert eo <= ATOL_OUT and el <= ATOL_LSE
+    return idx, outs
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+def test_group_tiny(dtype):
+    _group_case(W.WORKLOADS["group_b1_n4096_q4"], 0, dtype)
+
+
+def test_group_s_only_call_reuses_buffer_and_is_deterministic():
+    wl = W.WORKLOADS["group_b1_n4096_q4"]
+    idx, outs = _group_case(wl, 1)
+    g = W.group_inputs(wl, 1, n_layers=4)
+    d = dev()
+    layers = [tuple(t.to(d) for t in L) for L in g.layers[1:]]
+    outs2 = gsa.indexshare_group(layers, g.q_seq.to(d), idx, compute_index=False)
+    torch.cuda.synchronize()
+    for (o1, s1), (o2, s2) in zip(outs[1:], outs2):
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
