@@ -9,43 +9,130 @@
 //
 //   z_j = scale * (q_lat . c[s_j] + q_rope . kr[s_j]);  out = sum_j softmax(z)_j c[s_j]
 //
-// One work-group (4 waves, 16 heads each) takes one query and a contiguous
-// slice of its selected rows ("split"); slices are merged with their
-// log-sum-exp when a query is split. Per 32-row block:
-//   gather  each thread pulls 16-byte pieces of two adjacent rows (wave loads
-//           cover whole 128-byte lines) into LDS twice: row-major for Q.K,
-//           and as bf16 pairs (row 2p, row 2p+1) per latent dim for P.V, the
-//           pairing done in registers with v_perm. The next block's loads are
-//           in flight while the current block is multiplied.
+// One work-group (8 waves) takes one query and a contiguous slice of its
+// selected rows ("split"); slices are merged with their log-sum-exp when a
+// query is split. Wave w serves heads 16*(w%4) .. +15 and latent half w/4; the
+// two waves of a head group split both contractions: each takes Q.K over half
+// of the 576 dims and P.V over half of the 512 latent dims, and they swap
+// their fp32 partial scores through LDS (a + b == b + a, so both hold the
+// identical S and run the identical softmax). Per wave that is 36 registers
+// of Q and 64 of O, which leaves room for two waves per SIMD; the LDS reads
+// per 32-row block (each head group reads the block once for Q.K and once
+// for P.V) are what bounds this kernel.
+// Per 32-row block:
+//   gather  global_load_lds_dwordx4 copies the block's 32 x 1152 bytes straight
+//           into LDS (no staging registers); each wave instruction moves 1 KiB
+//           of whole 128-byte lines. A ring of kRing LDS blocks keeps
+//           kRing - 1 blocks in flight per CU. Rows sit at a 1168-byte pitch
+//           (16 bytes of padding), which spreads the 16 rows read by a 16-lane
+//           group over distinct banks and lets every LDS address be one base
+//           register plus an immediate. Indices of -1 load a static zero row.
 //   Q.K     S^T (rows x heads) on v_mfma_f32_16x16x32_bf16 with Q resident in
 //           registers; in that layout a lane holds 8 rows of one head, so the
 //           softmax max/sum need only two cross-lane steps.
 //   softmax online, base 2; the running max moves only when a block max
 //           exceeds it by more than 2^8, so the O rescale is rare.
 //   P.V     P (bf16) is the MFMA A operand straight from registers; the V
-//           operand comes from the pair-transposed copy; O (16 heads x 512)
-//           stays in accumulators for the whole slice.
+//           operand is read from the same block with the gfx950 LDS transpose
+//           read (ds_read_b64_tr_b16: 16 lanes' 4x16 block comes back as
+//           16x4), so no transposed copy is stored.
 #include "device_common.h"
 #include "launch.h"
 
 namespace gsa {
+
+// A 1152-byte all-zero cache row: gather source for index -1 (never written).
+__device__ __attribute__((aligned(16))) uint8_t g_zero_row[1152];
+
 namespace {
 
 constexpr int kHeads = 64;
 constexpr int kLat = 512;
-constexpr int kRowElems = 576;
-constexpr int kRowBytes = kRowElems * 2;      // 1152
-constexpr int kBlk = 32;                      // rows per block
-constexpr int kThreads = 256;
-constexpr int kRowStride = kRowBytes + 16;    // LDS row pitch (bank spread)
-constexpr int kCtStride = 72;                 // bytes per latent dim: 16 pairs x 4 B + 8 pad
-constexpr int kRowBuf = kBlk * kRowStride;
-constexpr int kCtBuf = kLat * kCtStride;
-constexpr int kBuf = kRowBuf + kCtBuf;
+constexpr int kRowBytes = 1152;                 // 576 bf16
+constexpr int kChunksPerRow = kRowBytes / 16;   // 72
+constexpr int kBlk = 32;                        // rows per block
+constexpr int kWaves = 8;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kPitch = kRowBytes + 16;          // LDS row pitch
+constexpr int kChunksPerPitch = kPitch / 16;    // 73 (the last one is padding)
+constexpr int kDmaPerBlock = (kBlk * kPitch + 1023) / 1024;   // 37 one-KiB LDS-DMA instructions
+constexpr int kBuf = kDmaPerBlock * 1024;       // 37 KiB per ring slot
+constexpr int kDmaBig = kDmaPerBlock - kWaves * (kDmaPerBlock / kWaves);   // waves issuing one more (5)
+constexpr int kDmaLo = kDmaPerBlock / kWaves;   // 4
+constexpr int kDmaHi = kDmaLo + 1;              // 5
+constexpr int kRing = 3;                        // LDS blocks in the ring
 constexpr int kMaxRows = 2048;
-constexpr float kRescale = 8.0f;              // lazy-rescale threshold (log2 units)
+constexpr float kRescale = 8.0f;                // lazy-rescale threshold (log2 units)
+
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+__shared__ __attribute__((aligned(16))) uint8_t g_ring[kRing * kBuf];
+__shared__ int32_t g_rows[kMaxRows];
+__shared__ f32x4 g_xs[kWaves][2][64];           // partial S^T of each wave (2 KiB per wave)
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// One 16-byte LDS-DMA load per lane: lane l's 16 bytes from `src` land at LDS
+// address lds_base + 16*l (one wait state between the M0 write and the
+// load, as the M0 -> LDS-DMA hazard requires). Issued through asm so that the
+// compiler's wait insertion does not treat later LDS reads as depending on it
+// (it would wait for every DMA in flight); the ring's own vmcnt waits and
+// barriers order these loads against the reads of the slot they fill, so the
+// asm carries no memory clobber and the index reads feeding it can be batched
+// ahead of it.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "m0");
+}
+
+// Work-group barrier without the memory fence of __syncthreads(): that fence
+// would wait for every outstanding LDS-DMA load, including the blocks still
+// meant to be in flight. Each wave first waits (vmcnt) for its own part of
+// the block it is about to read; the empty asm statements keep the compiler
+// from moving memory accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+// s_waitcnt lgkmcnt(0) alone: this wave's LDS writes have landed
+__device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
+
+// Cross-lane max / sum over lanes l and l^16 (l^32): the gfx950 permlane swaps
+// return, for every lane, its own value and its partner's, in some order.
+__device__ __forceinline__ float max_x16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float max_x32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_x16(float v) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float sum_x32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+template <int PER>
+__device__ __forceinline__ void wait_block(int later) {
+    if (later >= 2) wait_vmcnt<2 * PER>();
+    else if (later == 1) wait_vmcnt<PER>();
+    else wait_vmcnt<0>();
+}
 
 __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     const uint8_t* __restrict__ q_lat, const uint8_t* __restrict__ q_rope,
@@ -53,11 +140,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     const int32_t* __restrict__ idx, int k, int64_t n_cap, float scale_log2, int rows_per_split,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
     float* __restrict__ part_ml) {
-    extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-    int32_t* rows_s = (int32_t*)(smem + 2 * kBuf);
-
+    int32_t* rows_s = g_rows;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
+    const int hg = wave & 3, hf = wave >> 2;           // head group, latent half
     const int q = blockIdx.y, split = blockIdx.x, n_split = gridDim.x;
     const int r0 = split * rows_per_split;
     const int nrows = rows_per_split;
@@ -66,88 +152,76 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 
     for (int i = tid; i < nrows; i += kThreads) rows_s[i] = idx[(int64_t)q * k + r0 + i];
 
-    // Q of this wave's 16 heads as the B operand: head = 16*wave + l16, dims 32t + 8g
-    const int head = 16 * wave + l16;
-    bf16x8 qr[18];
+    // Q as the B operand: head 16*hg + l16, K-steps t = 9*hf .. 9*hf+8 of the
+    // 576 dims (dims 32t + 8g .. +8; steps 16 and 17 are the RoPE dims)
+    const int head = 16 * hg + l16;
+    bf16x8 qr[9];
     {
         const uint8_t* ql = q_lat + ((int64_t)q * kHeads + head) * (kLat * 2);
         const uint8_t* qp = q_rope + ((int64_t)q * kHeads + head) * (64 * 2);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) qr[t] = *(const bf16x8*)(ql + 2 * (32 * t + 8 * g));
-#pragma unroll
-        for (int t = 0; t < 2; ++t) qr[16 + t] = *(const bf16x8*)(qp + 2 * (32 * t + 8 * g));
+        for (int j = 0; j < 9; ++j) {
+            const int t = 9 * hf + j;
+            qr[j] = t < 16 ? *(const bf16x8*)(ql + 2 * (32 * t + 8 * g))
+                           : *(const bf16x8*)(qp + 2 * (32 * (t - 16) + 8 * g));
+        }
     }
+    wait_vmcnt<0>();     // Q is in registers before any ring load is counted
     __syncthreads();
 
-    // gather registers: 4 latent units (2 rows x 16 B each) + 1 RoPE unit
-    i32x4 gl[4][2], gr;
-    auto gather = [&](int b) {
+    // 16-byte LDS position s = 64*i + lane of a block holds row s / 73, chunk s % 73
+    // (chunk 72 and positions past row 31 are padding, filled from the zero row)
+    const bool big = wave < kDmaBig;
+    const int i0 = big ? kDmaHi * wave : kDmaHi * kDmaBig + kDmaLo * (wave - kDmaBig);
+    auto issue = [&](int b, int slot) __attribute__((always_inline)) {
+        const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)g_ring + slot * kBuf;
+        const int nload = big ? kDmaHi : kDmaLo;
+        int srow[kDmaHi];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int u = i * kThreads + tid;
-            const int p = u & 15, c = u >> 4;          // row pair, 16-byte latent chunk
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int s = rows_s[b * kBlk + 2 * p + h];
-                gl[i][h] = s >= 0 ? *(const i32x4*)(kvs + (int64_t)s * kRowBytes + 16 * c)
-                                  : i32x4{0, 0, 0, 0};
-            }
+        for (int j = 0; j < kDmaHi; ++j) {              // every index read first, one wait
+            const int pos = 64 * (i0 + j) + lane;
+            const int row = pos / kChunksPerPitch;
+            const int c = pos - row * kChunksPerPitch;
+            srow[j] = (j < nload && row < kBlk && c < kChunksPerRow) ? rows_s[b * kBlk + row] : -1;
         }
-        const int r = tid >> 3, c = tid & 7;
-        const int s = rows_s[b * kBlk + r];
-        gr = s >= 0 ? *(const i32x4*)(kvs + (int64_t)s * kRowBytes + 1024 + 16 * c)
-                    : i32x4{0, 0, 0, 0};
-    };
-    auto stash = [&](uint8_t* buf) {
-        uint8_t* rowb = buf;
-        uint8_t* ctb = buf + kRowBuf;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int u = i * kThreads + tid;
-            const int p = u & 15, c = u >> 4;
-            *(i32x4*)(rowb + (2 * p) * kRowStride + 16 * c) = gl[i][0];
-            *(i32x4*)(rowb + (2 * p + 1) * kRowStride + 16 * c) = gl[i][1];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const uint32_t x = (uint32_t)gl[i][0][e], y = (uint32_t)gl[i][1][e];
-                const uint32_t lo = __builtin_amdgcn_perm(y, x, 0x05040100u);   // dim 8c+2e
-                const uint32_t hi = __builtin_amdgcn_perm(y, x, 0x07060302u);   // dim 8c+2e+1
-                *(uint32_t*)(ctb + (8 * c + 2 * e) * kCtStride + 4 * p) = lo;
-                *(uint32_t*)(ctb + (8 * c + 2 * e + 1) * kCtStride + 4 * p) = hi;
-            }
+        for (int j = 0; j < kDmaHi; ++j) {
+            if (j == kDmaHi - 1 && !big) break;
+            const int pos = 64 * (i0 + j) + lane;
+            const int row = pos / kChunksPerPitch;
+            const int c = pos - row * kChunksPerPitch;
+            const uint8_t* src = srow[j] >= 0 ? kvs + (int64_t)srow[j] * kRowBytes + 16 * c : g_zero_row;
+            lds_dma16(src, dst + 1024 * (i0 + j));
         }
-        const int r = tid >> 3, c = tid & 7;
-        *(i32x4*)(rowb + r * kRowStride + 1024 + 16 * c) = gr;
     };
 
-    f32x4 o[32];
+    f32x4 o[16];
 #pragma unroll
-    for (int d = 0; d < 32; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int d = 0; d < 16; ++d) o[d] = f32x4{0.f, 0.f, 0.f, 0.f};
     float m_run = neg_inf();      // running max (log2 units) of head `head`
     float l_part = 0.f;           // this lane's share of the running sum
 
-    const int nblk = nrows / kBlk;
-    if (nblk > 0) gather(0);
-    for (int b = 0; b < nblk; ++b) {
-        uint8_t* buf = smem + (b & 1) * kBuf;
-        stash(buf);
-        __syncthreads();
-        if (b + 1 < nblk) gather(b + 1);
-
-        // S^T tiles: rows 16tt + 4g + i, head l16 of this wave
-        const uint8_t* rowb = buf;
-        f32x4 sacc[2];
+    auto compute = [&](int b, const lds_u8* buf) __attribute__((always_inline)) {
+        // rows of this block with a valid index (bit r), one LDS read per lane
+        const uint64_t valid = __builtin_amdgcn_ballot_w64(rows_s[b * kBlk + (lane & 31)] >= 0);
+        // partial S^T over this wave's 9 K-steps: rows 16tt + 4g + i, head l16
+        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+        const lds_u8* arow = buf + l16 * kPitch + 16 * g + 64 * 9 * hf;
 #pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            const uint8_t* arow = rowb + (16 * tt + l16) * kRowStride + 16 * g;
+        for (int j = 0; j < 9; ++j) {
 #pragma unroll
-            for (int t = 0; t < 18; ++t) {
-                const bf16x8 a = *(const bf16x8*)(arow + 64 * t);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qr[t], acc, 0, 0, 0);
+            for (int tt = 0; tt < 2; ++tt) {
+                const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(arow + 16 * tt * kPitch + 64 * j);
+                sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qr[j], sacc[tt], 0, 0, 0);
             }
-            sacc[tt] = acc;
         }
+        // swap partial scores with the partner wave (same heads, other half)
+        g_xs[wave][0][lane] = sacc[0];
+        g_xs[wave][1][lane] = sacc[1];
+        wait_lgkm0();
+        ring_barrier();
+        sacc[0] += g_xs[wave ^ 4][0][lane];
+        sacc[1] += g_xs[wave ^ 4][1][lane];
         float z[8];
         float mb = neg_inf();
 #pragma unroll
@@ -155,15 +229,15 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int r = 16 * tt + 4 * g + i;
-                const bool ok = rows_s[b * kBlk + r] >= 0;
+                const bool ok = (valid >> r) & 1u;
                 const float v = ok ? sacc[tt][i] * scale_log2 : neg_inf();
                 z[tt * 4 + i] = v;
                 mb = fmaxf(mb, v);
             }
-        mb = fmaxf(mb, shfl_xor(mb, 16));
-        mb = fmaxf(mb, shfl_xor(mb, 32));
-        const bool move = mb > m_run + kRescale || (m_run == neg_inf() && mb != neg_inf());
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {   // wave-uniform branch
+        mb = max_x16(mb);
+        mb = max_x32(mb);
+        const bool move = mb > m_run + kRescale;
+        if (__builtin_amdgcn_ballot_w64(move) != 0) {   // wave-uniform branch, rare
             const float m_new = move ? mb : m_run;
             const float alpha = move ? exp2_(m_run - m_new) : 1.f;   // exp2(-inf) = 0
             l_part *= alpha;
@@ -172,7 +246,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 #pragma unroll
             for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
-            for (int d = 0; d < 32; ++d)
+            for (int d = 0; d < 16; ++d)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) o[d][i] *= al[i];
         }
@@ -184,20 +258,37 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             l_part += p;
             pa[e] = (__bf16)p;
         }
-        // P.V: O[heads][16 dims] += P[heads][32 rows] * V[32 rows][16 dims]
-        const uint8_t* ctb = buf + kRowBuf + l16 * kCtStride + 8 * g;
+        // P.V over this wave's 256 latent dims: O[heads][16 dims] += P[heads][32 rows] *
+        // V[32 rows][16 dims]. The V operand of lane (dim l16, group g) is rows
+        // {4g..4g+3, 16+4g..16+4g+3}: two transpose reads in which lane j of the group
+        // supplies row 4g + j/4 (+16), dims 16d + 4(j%4) .. +3.
+        const lds_u8* vb = buf + (4 * g + (l16 >> 2)) * kPitch + 8 * (l16 & 3) + 512 * hf;
 #pragma unroll
-        for (int d = 0; d < 32; ++d) {
-            const uint8_t* cp = ctb + 16 * d * kCtStride;
-            const uint2 lo = *(const uint2*)(cp);        // rows 4g..4g+3
-            const uint2 hi = *(const uint2*)(cp + 32);   // rows 16+4g..16+4g+3
-            const i32x4 bi = {(int)lo.x, (int)lo.y, (int)hi.x, (int)hi.y};
-            o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, __builtin_bit_cast(bf16x8, bi), o[d], 0, 0, 0);
+        for (int d = 0; d < 16; ++d) {
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 32 * d));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 16 * kPitch + 32 * d));
+            const bf16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[d], 0, 0, 0);
         }
+    };
+
+    const int nblk = nrows / kBlk;
+#pragma unroll
+    for (int p = 0; p < kRing - 1; ++p)
+        if (p < nblk) issue(p, p);
+    for (int b = 0; b < nblk; ++b) {
+        // this wave's loads of block b are done once at most the later issued
+        // blocks (b+1 .. min(nblk, b+kRing-1) - 1) remain outstanding
+        const int later = min(nblk, b + kRing - 1) - b - 1;
+        if (big) wait_block<kDmaHi>(later);
+        else wait_block<kDmaLo>(later);
+        ring_barrier();    // every wave's part of block b is in; block b-1's readers are done
+        if (b + kRing - 1 < nblk) issue(b + kRing - 1, (b + kRing - 1) % kRing);
+        compute(b, (const lds_u8*)g_ring + (b % kRing) * kBuf);
     }
 
-    float l_tot = l_part + shfl_xor(l_part, 16);
-    l_tot += shfl_xor(l_tot, 32);
+    const float l_tot = sum_x32(sum_x16(l_part));
+    const int dim0 = 256 * hf;
     if (n_split == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
         float iv[4];
@@ -205,20 +296,21 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         for (int i = 0; i < 4; ++i) iv[i] = __shfl(inv, 4 * g + i, 64);
         float* oq = out + (int64_t)q * kHeads * kLat;
 #pragma unroll
-        for (int d = 0; d < 32; ++d)
+        for (int d = 0; d < 16; ++d)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                oq[(16 * wave + 4 * g + i) * kLat + 16 * d + l16] = o[d][i] * iv[i];
-        if (lse != nullptr && g == 0)
+                oq[(16 * hg + 4 * g + i) * kLat + dim0 + 16 * d + l16] = o[d][i] * iv[i];
+        if (lse != nullptr && g == 0 && hf == 0)
             lse[(int64_t)q * kHeads + head] =
                 l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : neg_inf();
     } else {
         float* po = part_o + ((int64_t)q * n_split + split) * kHeads * kLat;
 #pragma unroll
-        for (int d = 0; d < 32; ++d)
+        for (int d = 0; d < 16; ++d)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) po[(16 * wave + 4 * g + i) * kLat + 16 * d + l16] = o[d][i];
-        if (g == 0) {
+            for (int i = 0; i < 4; ++i)
+                po[(16 * hg + 4 * g + i) * kLat + dim0 + 16 * d + l16] = o[d][i];
+        if (g == 0 && hf == 0) {
             float* pm = part_ml + ((int64_t)q * n_split + split) * kHeads * 2;
             pm[2 * head] = m_run;
             pm[2 * head + 1] = l_tot;
@@ -226,33 +318,35 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     }
 }
 
-// Combine the per-split partial results of each query with their log-sum-exp.
-__global__ __launch_bounds__(kThreads) void sparse_mla_merge(const float* __restrict__ part_o,
+// Combine the per-split partial results with their log-sum-exp. Grid
+// (n_q, 16): a work-group merges 4 heads x 512 dims of one query.
+__global__ __launch_bounds__(256) void sparse_mla_merge(const float* __restrict__ part_o,
                                                              const float* __restrict__ part_ml,
                                                              int n_split, float* __restrict__ out,
                                                              float* __restrict__ lse) {
     const int q = blockIdx.x;
-    const int dim4 = threadIdx.x & 127;        // float4 column
-    for (int h = threadIdx.x >> 7; h < kHeads; h += 2) {
-        float mx = neg_inf();
-        for (int s = 0; s < n_split; ++s)
-            mx = fmaxf(mx, part_ml[(((int64_t)q * n_split + s) * kHeads + h) * 2]);
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-        float lsum = 0.f;
-        if (mx != neg_inf()) {
-            for (int s = 0; s < n_split; ++s) {
-                const float* pm = part_ml + (((int64_t)q * n_split + s) * kHeads + h) * 2;
-                const float wgt = exp2_(pm[0] - mx);
-                lsum += wgt * pm[1];
-                const f32x4 v = *(const f32x4*)(part_o + (((int64_t)q * n_split + s) * kHeads + h) * kLat + 4 * dim4);
-                acc += wgt * v;
-            }
+    const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
+    const int c = threadIdx.x & 63;              // float4 columns c and c + 64
+    const float* pm = part_ml + ((int64_t)q * n_split * kHeads + h) * 2;
+    float mx = neg_inf();
+    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, pm[(int64_t)s * kHeads * 2]);
+    f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
+    float lsum = 0.f;
+    if (mx != neg_inf()) {
+        for (int s = 0; s < n_split; ++s) {
+            const float wgt = exp2_(pm[(int64_t)s * kHeads * 2] - mx);
+            lsum += wgt * pm[(int64_t)s * kHeads * 2 + 1];
+            const f32x4* po = (const f32x4*)(part_o + (((int64_t)q * n_split + s) * kHeads + h) * kLat);
+            a0 += wgt * po[c];
+            a1 += wgt * po[c + 64];
         }
-        const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
-        *(f32x4*)(out + ((int64_t)q * kHeads + h) * kLat + 4 * dim4) = acc * inv;
-        if (lse != nullptr && dim4 == 0)
-            lse[(int64_t)q * kHeads + h] = lsum > 0.f ? (mx + log2f(lsum)) * 0.69314718055994531f : neg_inf();
     }
+    const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
+    f32x4* oo = (f32x4*)(out + ((int64_t)q * kHeads + h) * kLat);
+    oo[c] = a0 * inv;
+    oo[c + 64] = a1 * inv;
+    if (lse != nullptr && c == 0)
+        lse[(int64_t)q * kHeads + h] = lsum > 0.f ? (mx + log2f(lsum)) * 0.69314718055994531f : neg_inf();
 }
 
 int choose_split(int n_q, int k) {
@@ -276,23 +370,15 @@ hipError_t launch_sparse_mla(const void* q_lat, const void* q_rope, const void* 
     (void)n_heads;
     const int s = choose_split(n_q, k);
     const int rows = k / s;
-    const size_t lds = 2 * kBuf + kMaxRows * sizeof(int32_t);
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute((const void*)sparse_mla_kernel,
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
     float* part_o = (float*)ws;
     float* part_ml = s > 1 ? part_o + (size_t)n_q * s * kHeads * kLat : nullptr;
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, n_q), dim3(kThreads), lds, st,
+    hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, n_q), dim3(kThreads), 0, st,
                        (const uint8_t*)q_lat, (const uint8_t*)q_rope, (const uint8_t*)kv, q_seq, idx,
                        k, n_cap, scale_log2, rows, out, lse, part_o, part_ml);
     if (s > 1)
-        hipLaunchKernelGGL(sparse_mla_merge, dim3(n_q), dim3(kThreads), 0, st, part_o, part_ml, s,
-                           out, lse);
+        hipLaunchKernelGGL(sparse_mla_merge, dim3(n_q, kHeads / 4), dim3(256), 0, st, part_o,
+                           part_ml, s, out, lse);
     return hipGetLastError();
 }
 
