@@ -32,4 +32,56 @@ __device__ __forceinline__ int e8m0_of(float s) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// ---- LDS-DMA rings ---------------------------------------------------------
+// One 16-byte LDS-DMA load per lane: lane l's 16 bytes from `src` land at LDS
+// address lds_base + 16*l (one wait state between the M0 write and the load,
+// as the M0 -> LDS-DMA hazard requires). Issued through asm so that the
+// compiler's wait insertion does not treat later LDS reads as depending on it
+// (it would wait for every DMA in flight); each ring's own vmcnt waits and
+// barriers order these loads against the reads of the slot they fill, so the
+// asm carries no memory clobber and the index reads feeding it can be batched.
+__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "m0");
+}
+// The same with 4 bytes per lane (64 lanes fill 256 contiguous LDS bytes).
+__device__ __forceinline__ void lds_dma4(const void* src, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dword %0, off"
+                 :
+                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                 : "m0");
+}
+
+// Work-group barrier without the memory fence of __syncthreads(): that fence
+// would wait for every outstanding LDS-DMA load, including those meant to stay
+// in flight. Each wave first waits (vmcnt) for its own part of the slot it is
+// about to read; the empty asm statements keep the compiler from moving
+// memory accesses across the barrier.
+__device__ __forceinline__ void ring_barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Run-time count: waits until at most n (clamped to [0, 63]) vector-memory
+// operations of this wave are outstanding. A smaller n only waits longer.
+template <int N = 63>
+__device__ __forceinline__ void wait_vmcnt_le(int n) {
+    if constexpr (N == 0) {
+        wait_vmcnt<0>();
+    } else {
+        if (n >= N) wait_vmcnt<N>();
+        else wait_vmcnt_le<N - 1>(n);
+    }
+}
+
 }  // namespace gsa

@@ -16,11 +16,13 @@
 // heads) stays in registers: each lane holds 16 heads of one key and one
 // cross-lane add finishes the sum, so only the final fp32 score reaches HBM.
 //
-// Keys stream through LDS in 128-key tiles: coalesced 16-byte global loads
-// (each wave instruction reads 1 KiB contiguous), XOR-swizzled 16-byte chunks
-// so the MFMA-layout ds_read_b128 is conflict-free, and the next tile's loads
-// are in flight while the current tile is multiplied. Queries of one sequence
-// that share a work-group (QB of them) reuse each key tile from LDS.
+// Keys stream through LDS in 128-key tiles with LDS-DMA (global_load_lds:
+// whole 1 KiB key blocks per wave instruction, no staging registers) into a
+// ring of kRing slots, so kRing - 1 tiles are in flight per work-group. The
+// DMA source chunk of each lane is chosen so that 16-byte chunks land XOR-
+// swizzled inside their key row, which makes the MFMA-layout ds_read_b128
+// conflict-free. Queries of one sequence that share a work-group (QB of them)
+// reuse each key tile from LDS.
 #include <type_traits>
 
 #include "device_common.h"
@@ -33,14 +35,19 @@ constexpr int kHeads = 32;
 constexpr int kDim = 128;
 constexpr int kTile = 128;      // keys per LDS tile
 constexpr int kThreads = 256;   // 4 waves
+constexpr int kRing = 4;        // LDS tile slots
 
 template <bool FP8>
 struct KeyTile {
     static constexpr int kRowBytes = FP8 ? kDim : kDim * 2;
     static constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per key row
     static constexpr int kBytes = kTile * kRowBytes;
-    static constexpr int kLoads = kBytes / (kThreads * 16);     // 16-byte loads per thread
-    // byte offset of chunk c of tile row r (XOR swizzle over the row's chunks)
+    static constexpr int kRowsPerDma = 1024 / kRowBytes;        // key rows per 1 KiB DMA
+    static constexpr int kDma = kBytes / 1024;                  // 32 (bf16) or 16 (fp8)
+    static constexpr int kDmaPerWave = kDma / 4;
+    static constexpr int kScaleBytes = FP8 ? 512 : 0;           // fp32 scale per key (2 x 256 B DMA)
+    static constexpr int kSlot = kBytes + kScaleBytes;
+    // byte offset of logical chunk c of tile row r (XOR swizzle over the row's chunks)
     __device__ static __forceinline__ int off(int r, int c) {
         return r * kRowBytes + ((c ^ (r & (kChunks - 1))) << 4);
     }
@@ -57,9 +64,9 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     constexpr int QPW = QB >= 4 ? QB / 4 : 1;   // queries per wave
     constexpr int KSTEPS = FP8 ? 2 : 8;         // MFMA steps over 128 dims
     using AVec = std::conditional_t<FP8, i32x8, bf16x8>;
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-    __shared__ __attribute__((aligned(16))) uint8_t tile[T::kBytes];
-    __shared__ int key_e8[kTile];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * T::kSlot];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -103,6 +110,11 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
         if constexpr (FP8) a_e8[jj] = e8m0_of(q_scale[(int64_t)qr * kHeads + n]);
         else a_e8[jj] = 127;
     }
+    wait_vmcnt<0>();   // operands are in registers before any ring load is counted
+
+    // DMA instructions per tile issued by this wave (wave 0 also moves the fp8 scales)
+    const int per = T::kDmaPerWave + ((FP8 && wave == 0) ? 2 : 0);
+    const uint32_t ring_base = (uint32_t)(uintptr_t)(lds_u8*)ring;
 
     // Queries of the block are processed in runs that share a sequence.
     int j0 = 0;
@@ -116,34 +128,55 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
         }
         const uint8_t* kb = k + (int64_t)seq * n_cap * T::kRowBytes;
         const float* ksb = FP8 ? k_scale + (int64_t)seq * n_cap : nullptr;
-
-        i32x4 pf[T::kLoads];
-        auto load_tile = [&](int64_t t0) {
+        // tiles [0, na) hold keys at or before the run's last position; later ones are masked
+        const int64_t t_end = min(c1, (int64_t)maxpos + 1);
+        const int na = t_end > c0 ? (int)((t_end - c0 + kTile - 1) / kTile) : 0;
+        const int nt_all = (int)((c1 - c0 + kTile - 1) / kTile);
+        // score stores this wave issues per tile in this run (one per owned pair in the run)
+        int stores = 0;
 #pragma unroll
-            for (int i = 0; i < T::kLoads; ++i) {
-                const int lin = i * kThreads + tid;
-                const int r = lin / T::kChunks, c = lin % T::kChunks;
-                pf[i] = (t0 + r < c1) ? *(const i32x4*)(kb + (t0 + r) * T::kRowBytes + c * 16)
-                                      : i32x4{0, 0, 0, 0};
+        for (int p = 0; p < QB; ++p) {
+            const int j = (wave * QB + p) >> 2;
+            stores += (j >= j0 && j < j1) ? 1 : 0;
+        }
+
+        auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
+            const int64_t t0 = c0 + (int64_t)ti * kTile;
+            const uint32_t dst = ring_base + slot * T::kSlot;
+#pragma unroll
+            for (int jd = 0; jd < T::kDmaPerWave; ++jd) {
+                const int i = wave * T::kDmaPerWave + jd;
+                const int r = i * T::kRowsPerDma + lane / T::kChunks;
+                const int p = lane % T::kChunks;                     // physical chunk in the row
+                const int c = p ^ (r & (T::kChunks - 1));            // logical chunk stored there
+                const int64_t krow = min(t0 + r, c1 - 1);            // rows past the chunk: any valid row
+                lds_dma16(kb + krow * T::kRowBytes + 16 * c, dst + 1024 * i);
+            }
+            if constexpr (FP8) {
+                if (wave == 0) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int64_t krow = min(t0 + 64 * h + lane, c1 - 1);
+                        lds_dma4(ksb + krow, dst + T::kBytes + 256 * h);
+                    }
+                }
             }
         };
-        if (c0 <= maxpos) load_tile(c0);
 
-        for (int64_t t0 = c0; t0 < c1; t0 += kTile) {
-            const bool active = t0 <= maxpos;   // uniform over the work-group
+        for (int p = 0; p < kRing - 1; ++p)
+            if (p < na) issue(p, p);
+        for (int ti = 0; ti < nt_all; ++ti) {
+            const int64_t t0 = c0 + (int64_t)ti * kTile;
+            const bool active = ti < na;                 // uniform over the work-group
+            const lds_u8* tile = (const lds_u8*)ring + (ti % kRing) * T::kSlot;
             if (active) {
-                __syncthreads();                 // readers of the previous tile are done
-#pragma unroll
-                for (int i = 0; i < T::kLoads; ++i) {
-                    const int lin = i * kThreads + tid;
-                    *(i32x4*)(tile + T::off(lin / T::kChunks, lin % T::kChunks)) = pf[i];
-                }
-                if constexpr (FP8) {
-                    if (tid < kTile) key_e8[tid] = (t0 + tid < c1) ? e8m0_of(ksb[t0 + tid]) : 127;
-                }
-                __syncthreads();
-                const int64_t tn = t0 + kTile;
-                if (tn < c1 && tn <= maxpos) load_tile(tn);   // in flight during the MFMAs
+                // wait for this wave's DMAs of tile ti: the later issued ones are the
+                // DMAs of tiles ti+1 .. min(na, ti+kRing-1)-1 and the score stores of
+                // the iterations since tile ti was issued
+                const int later = min(na, ti + kRing - 1) - ti - 1;
+                wait_vmcnt_le<2 * 8 + 3 * 8>(later * per + stores * min(ti, kRing - 1));
+                ring_barrier();   // every wave's part of tile ti landed; tile ti-1's readers are done
+                if (ti + kRing - 1 < na) issue(ti + kRing - 1, (ti + kRing - 1) % kRing);
             }
 #pragma unroll
             for (int p = 0; p < QB; ++p) {
@@ -160,13 +193,14 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 #pragma unroll
                     for (int t = 0; t < KSTEPS; ++t) {
                         if constexpr (FP8) {
-                            const i32x4 lo = *(const i32x4*)(tile + T::off(row, 4 * g + 2 * t));
-                            const i32x4 hi = *(const i32x4*)(tile + T::off(row, 4 * g + 2 * t + 1));
+                            const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(tile + T::off(row, 4 * g + 2 * t));
+                            const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(tile + T::off(row, 4 * g + 2 * t + 1));
                             const i32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            const float ks = *(const __attribute__((address_space(3))) float*)(tile + T::kBytes + 4 * row);
                             acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                a[jj][t], b, acc, 0, 0, 0, a_e8[jj], 0, key_e8[row]);
+                                a[jj][t], b, acc, 0, 0, 0, a_e8[jj], 0, e8m0_of(ks));
                         } else {
-                            const bf16x8 b = *(const bf16x8*)(tile + T::off(row, 8 * g + t));
+                            const bf16x8 b = *(const __attribute__((address_space(3))) bf16x8*)(tile + T::off(row, 8 * g + t));
                             acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jj][t], b, acc, 0, 0, 0);
                         }
                     }
@@ -179,6 +213,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
                 if (g == 0 && s < c1) scores[(int64_t)(qb0 + j) * ld + s] = res;
             }
         }
+        ring_barrier();     // the next run refills slots this run's last tiles were read from
         j0 = j1;
     }
 }

@@ -73,38 +73,6 @@ __shared__ f32x4 g_xs[kWaves][2][64];           // partial S^T of each wave (2 K
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// One 16-byte LDS-DMA load per lane: lane l's 16 bytes from `src` land at LDS
-// address lds_base + 16*l (one wait state between the M0 write and the
-// load, as the M0 -> LDS-DMA hazard requires). Issued through asm so that the
-// compiler's wait insertion does not treat later LDS reads as depending on it
-// (it would wait for every DMA in flight); the ring's own vmcnt waits and
-// barriers order these loads against the reads of the slot they fill, so the
-// asm carries no memory clobber and the index reads feeding it can be batched
-// ahead of it.
-__device__ __forceinline__ void lds_dma16(const void* src, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(src), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-                 : "m0");
-}
-
-// Work-group barrier without the memory fence of __syncthreads(): that fence
-// would wait for every outstanding LDS-DMA load, including the blocks still
-// meant to be in flight. Each wave first waits (vmcnt) for its own part of
-// the block it is about to read; the empty asm statements keep the compiler
-// from moving memory accesses across the barrier.
-__device__ __forceinline__ void ring_barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-    static_assert(N >= 0 && N < 64, "vmcnt range");
-    __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 // s_waitcnt lgkmcnt(0) alone: this wave's LDS writes have landed
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
 

@@ -92,6 +92,31 @@ __device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* scr
     __syncthreads();
 }
 
+// A thread's share of one chunk: kPer float4 loads issued together before any
+// is used (each thread owns float4 slots tid, tid + 256, ...), so a pass costs
+// one memory round trip instead of kPer. Slots past the valid range read as
+// -inf and are skipped by the callers' bounds test.
+constexpr int kPer = kChunk / (4 * kThreads);   // 16 float4 per thread
+__device__ __forceinline__ void load_chunk(const float* row, int64_t s0, int64_t s1, f32x4 (&v)[kPer]) {
+    const f32x4* r4 = (const f32x4*)(row + s0);
+    const int64_t n4 = (s1 - s0 + 3) >> 2;           // float4 slots touching [s0, s1)
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t j = (int64_t)i * kThreads + threadIdx.x;
+        if (j < n4) {
+            if (s0 + 4 * j + 4 <= s1) v[i] = r4[j];
+            else {                                      // ragged tail of the row
+                f32x4 t = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+                for (int e = 0; e < 4; ++e)
+                    if (s0 + 4 * j + e < s1) t[e] = row[s0 + 4 * j + e];
+                v[i] = t;
+            }
+        } else {
+            v[i] = f32x4{neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+        }
+    }
+}
+
 __global__ __launch_bounds__(kThreads) void topk_zero(uint32_t* hist, int n_q) {
     const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
     const int64_t n = (int64_t)n_q * kB1;
@@ -142,19 +167,20 @@ __global__ __launch_bounds__(kThreads) void topk_hist(const float* __restrict__ 
     __syncthreads();
 
     const float* row = scores + (int64_t)q * ld;
-    auto add = [&](float f) {
-        const uint32_t key = score_key(f);
-        if (PASS == 1) atomicAdd(&h[key >> 21], 1u);
-        else if (PASS == 2) { if ((key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u); }
-        else { if ((key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u); }
-    };
-    const int64_t n4 = (s1 - s0) >> 2;
-    const f32x4* r4 = (const f32x4*)(row + s0);
-    for (int64_t i = threadIdx.x; i < n4; i += kThreads) {
-        const f32x4 v = r4[i];
-        add(v[0]); add(v[1]); add(v[2]); add(v[3]);
+    f32x4 v[kPer];
+    load_chunk(row, s0, s1, v);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t p0 = s0 + 4 * ((int64_t)i * kThreads + threadIdx.x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (p0 + e >= s1) continue;
+            const uint32_t key = score_key(v[i][e]);
+            if (PASS == 1) atomicAdd(&h[key >> 21], 1u);
+            else if (PASS == 2) { if ((key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u); }
+            else { if ((key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u); }
+        }
     }
-    for (int64_t s = s0 + (n4 << 2) + threadIdx.x; s < s1; s += kThreads) add(row[s]);
     __syncthreads();
     uint32_t* dst = hq + (PASS == 1 ? 0 : PASS == 2 ? kB1 : kB1 + kB2);
     for (int i = threadIdx.x; i < NB; i += kThreads)
@@ -190,18 +216,19 @@ __global__ __launch_bounds__(kThreads) void topk_count(const float* __restrict__
 
     const float* row = scores + (int64_t)q * ld;
     uint32_t gt = 0, eq = 0;
-    auto cnt = [&](float f) {
-        const uint32_t key = score_key(f);
-        gt += key > T;
-        eq += key == T;
-    };
-    const int64_t n4 = (s1 - s0) >> 2;
-    const f32x4* r4 = (const f32x4*)(row + s0);
-    for (int64_t i = threadIdx.x; i < n4; i += kThreads) {
-        const f32x4 v = r4[i];
-        cnt(v[0]); cnt(v[1]); cnt(v[2]); cnt(v[3]);
+    f32x4 v[kPer];
+    load_chunk(row, s0, s1, v);
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t p0 = s0 + 4 * ((int64_t)i * kThreads + threadIdx.x);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            if (p0 + e >= s1) continue;
+            const uint32_t key = score_key(v[i][e]);
+            gt += key > T;
+            eq += key == T;
+        }
     }
-    for (int64_t s = s0 + (n4 << 2) + threadIdx.x; s < s1; s += kThreads) cnt(row[s]);
     uint32_t tg, te;
     block_excl_scan(gt, scratch, tg);
     block_excl_scan(eq, scratch + 4, te);
@@ -254,15 +281,21 @@ __global__ __launch_bounds__(kThreads) void topk_compact(const float* __restrict
     uint32_t eq_run = eq_before;                          // equal keys seen before the sub-block
 
     const float* row = scores + (int64_t)q * ld;
-    // sub-blocks of 4 consecutive scores per thread keep position order across threads
-    for (int64_t b0 = s0; b0 < s1; b0 += 4 * kThreads) {
+    f32x4 v[kPer];
+    load_chunk(row, s0, s1, v);
+    // sub-block i holds 4 consecutive scores per thread, so thread order is
+    // position order inside it and sub-blocks follow each other
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int64_t b0 = s0 + (int64_t)i * 4 * kThreads;
+        if (b0 >= s1) break;                                 // uniform over the block
         const int64_t p0 = b0 + 4 * threadIdx.x;
         uint32_t key[4];
         bool valid[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             valid[e] = p0 + e < s1;
-            key[e] = valid[e] ? score_key(row[p0 + e]) : 0u;
+            key[e] = valid[e] ? score_key(v[i][e]) : 0u;
         }
         uint32_t n_eq = 0;
 #pragma unroll
