@@ -3,350 +3,353 @@
 // "GLM-5.2 架构深度拆解" §1.1 and CH2 §2.2: an F layer keeps the 2048
 // highest-scoring history positions of each query as its sparse attention set.
 //
-// Method: exact radix select on order-preserving uint32 keys of the fp32
-// scores (-0 folded onto +0), then an ordered compaction.
-//   pass 1  histogram of key bits 31..21 (2048 bins) over positions 0..pos
-//   pass 2  histogram of bits 20..10 among keys in the pass-1 threshold bin
-//   pass 3  histogram of bits 9..0 among keys in the pass-2 threshold bin
-//           -> T, the k-th largest key, n_gt keys above it, need = k - n_gt
-//   count   per chunk: keys > T and keys == T
-//   compact per chunk, in position order: keys > T, and keys == T whose rank
-//           among equal keys (in position order) is below `need`
-// Every row is split into 16K-score chunks, one work-group each, so a single
-// 1M-long row spreads over 64 CUs. Cross-chunk state is integer histograms
-// built with atomic adds (order-free, hence deterministic) and per-chunk
-// counts combined in chunk order, so the output is the same on every run.
-// Output positions are ascending; rows with <= k valid positions select all
-// of them and pad with -1.
+// Order: (score descending, position ascending) is a strict total order on the
+// positions 0..pos of a row, so the top-k set is unique, and it is contained in
+// the union of the top-k sets of any partition of the row. The selection runs
+// as a tree over that fact:
+//   level 1  one work-group per 16K-score chunk: each wave holds 2048
+//            consecutive scores in registers (32 per lane) as order-preserving
+//            uint32 keys (-0 folded onto +0). The k-th largest key T is found
+//            by bisection over [min, max]: every step counts keys >= mid with
+//            one ballot and popcount per 64 keys plus an 8-wave sum, so no
+//            histogram or atomic is involved; ties at T keep the lowest
+//            positions. An ordered compaction (ballot ranks) writes the
+//            chunk's top-k as (key, position) pairs in position order;
+//   level 2+ one work-group merges up to 8 lists of a row (concatenated in
+//            chunk order, hence in position order) with the same selection,
+//            until one list remains.
+// The last level writes the positions (ascending) and pads with -1. The row is
+// read from HBM once; no counter or histogram is shared between work-groups,
+// so the result is the same on every run.
 #include "device_common.h"
 #include "launch.h"
 
 namespace gsa {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kChunk = 16384;       // scores per work-group
-constexpr int kB1 = 2048, kB2 = 2048, kB3 = 1024;
-constexpr int kHistWords = kB1 + kB2 + kB3;
+constexpr int kK = 2048;
+constexpr int kChunk = 16384;                  // scores per level-1 work-group
+constexpr int kFan = 8;                        // lists per merge work-group
+constexpr int kMaxItems = kFan * kK;           // = kChunk
+constexpr int kThreads = 512;
+constexpr int kWaves = kThreads / 64;
+constexpr size_t kListBytes = 16 + (size_t)kK * 8; // count (16-byte slot) + (key, position) pairs
 
-struct Ws {
-    uint32_t* hist;     // [n_q][kHistWords]
-    uint32_t* counts;   // [n_q][n_chunks][2]  (gt, eq)
-    uint32_t* state;    // [n_q][4]  (T, n_gt, need, valid)
+constexpr int kPer = kMaxItems / kThreads;      // items per lane (32)
+constexpr int kSeg = 64 * kPer;                 // items per wave (2048)
+
+constexpr int kBins = 256;                     // 8-bit radix digit
+
+struct Scratch {
+    uint32_t hist[2][kWaves][kBins];            // per-wave digit histograms, double-buffered
+    uint32_t wsum[kWaves];
+    uint32_t wmin[kWaves];
+    uint32_t wmax[kWaves];
+    uint32_t wtot[4];
+    uint32_t pick[3];                           // chosen bin, count above it, count in it
 };
 
-__device__ __forceinline__ Ws ws_of(void* base, int n_q, int n_chunks) {
-    Ws w;
-    w.hist = (uint32_t*)base;
-    w.counts = w.hist + (size_t)n_q * kHistWords;
-    w.state = w.counts + (size_t)n_q * n_chunks * 2;
-    return w;
+__device__ __forceinline__ uint32_t wave_max(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+__device__ __forceinline__ uint32_t wave_min(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+// number of set bits of `mask` in lanes below this one
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
-// Exclusive prefix sum over the 256 threads of the block (in thread order);
-// also returns the block total. `scratch` holds >= 4 words.
-__device__ __forceinline__ uint32_t block_excl_scan(uint32_t v, uint32_t* scratch, uint32_t& total) {
+// Sum over the block of a per-wave value (uniform inside each wave).
+__device__ __forceinline__ uint32_t block_sum(uint32_t wave_val, Scratch& sc, uint32_t* before = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    uint32_t x = v;
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-        const uint32_t y = __shfl_up(x, o, 64);
-        if (lane >= o) x += y;
-    }
-    if (lane == 63) scratch[wave] = x;
+    if (lane == 0) sc.wsum[wave] = wave_val;
     __syncthreads();
-    uint32_t before = 0;
-    total = 0;
+    uint32_t tot = 0, bef = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const uint32_t t = scratch[i];
-        if (i < wave) before += t;
-        total += t;
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t t = sc.wsum[w];
+        bef += w < wave ? t : 0u;
+        tot += t;
     }
     __syncthreads();
-    return before + x - v;
+    if (before) *before = bef;
+    return tot;
 }
 
-// In a histogram `h` (LDS, nb bins), find the bin b where the count of keys in
-// bins >= b first reaches `need`, scanning from the top. Returns b and the
-// count strictly above it (through LDS, visible to all threads).
-__device__ void find_bin(const uint32_t* h, int nb, uint32_t need, uint32_t* scratch,
-                         int* out_bin, uint32_t* out_above) {
-    const int per = nb / kThreads;          // 8 or 4 consecutive bins per thread
-    const int t = threadIdx.x;
-    if (t == 0) { *out_bin = 0; *out_above = 0; }
-    // thread t owns bins [nb - per*(t+1), nb - per*t): thread order = descending bins
-    const int hi = nb - per * t;
-    uint32_t s = 0;
-    for (int b = hi - 1; b >= hi - per; --b) s += h[b];
-    uint32_t total;
-    uint32_t run = block_excl_scan(s, scratch, total);   // count in bins above this thread's range
-    for (int b = hi - 1; b >= hi - per; --b) {
-        const uint32_t c = h[b];
-        if (run < need && run + c >= need) {
-            *out_bin = b;
-            *out_above = run;
+__device__ __forceinline__ void clear_hist(Scratch& sc, int b) {
+    uint4* h = (uint4*)&sc.hist[b][0][0];                       // kWaves*kBins/4 = kThreads
+    h[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Item i = kSeg*wave + 64*r + lane of the block is v[r] of that lane (valid for
+// i < n; kFull: n = kMaxItems). The items are in position order. Selects the
+// min(k, n) largest by (key desc, position asc) and emits them in position
+// order through emit(slot, i, r). Returns the number emitted.
+//
+// Threshold: the k-th largest key T is found by radix selection on keys
+// relative to the block minimum: each pass histograms the next 8 bits of the
+// candidates (the keys inside the bin chosen by the previous pass), then keeps
+// the bin where the count of larger keys first reaches k. A pass ends the
+// search early when its bin is taken whole; otherwise the last pass leaves a
+// single key value T and the number `need` of its copies to keep, which are
+// the lowest positions among them.
+template <bool kFull, typename Emit>
+__device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scratch& sc, Emit emit) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int seg0 = kSeg * wave;
+    auto valid = [&](int r) { return kFull || seg0 + 64 * r + lane < n; };
+    if (!kFull && n <= kK) {                                  // everything is kept
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid(r)));
+        uint32_t slot;
+        block_sum(c, sc, &slot);
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(valid(r));
+            if (valid(r)) emit(slot + lanes_below(m), seg0 + 64 * r + lane, r);
+            slot += __builtin_popcountll(m);
         }
-        run += c;
+        return n < 0 ? 0 : n;
     }
-    __syncthreads();
-}
-
-// A thread's share of one chunk: kPer float4 loads issued together before any
-// is used (each thread owns float4 slots tid, tid + 256, ...), so a pass costs
-// one memory round trip instead of kPer. Slots past the valid range read as
-// -inf and are skipped by the callers' bounds test.
-constexpr int kPer = kChunk / (4 * kThreads);   // 16 float4 per thread
-__device__ __forceinline__ void load_chunk(const float* row, int64_t s0, int64_t s1, f32x4 (&v)[kPer]) {
-    const f32x4* r4 = (const f32x4*)(row + s0);
-    const int64_t n4 = (s1 - s0 + 3) >> 2;           // float4 slots touching [s0, s1)
+    // ---- min / max of the valid keys
+    uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int64_t j = (int64_t)i * kThreads + threadIdx.x;
-        if (j < n4) {
-            if (s0 + 4 * j + 4 <= s1) v[i] = r4[j];
-            else {                                      // ragged tail of the row
-                f32x4 t = {neg_inf(), neg_inf(), neg_inf(), neg_inf()};
-                for (int e = 0; e < 4; ++e)
-                    if (s0 + 4 * j + e < s1) t[e] = row[s0 + 4 * j + e];
-                v[i] = t;
-            }
-        } else {
-            v[i] = f32x4{neg_inf(), neg_inf(), neg_inf(), neg_inf()};
+    for (int r = 0; r < kPer; ++r)
+        if (valid(r)) { mn = min(mn, v[r]); mx = max(mx, v[r]); }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) { sc.wmin[wave] = mn; sc.wmax[wave] = mx; }
+    clear_hist(sc, 0);
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) { mn = min(mn, sc.wmin[w]); mx = max(mx, sc.wmax[w]); }
+
+    // ---- radix passes: candidates are keys in [base, base + 2^nb)
+    uint32_t base = mn, need = kK, in_bin = 0;
+    int nb = mx == mn ? 0 : 32 - __builtin_clz(mx - mn);
+    bool whole = false;                                        // the last bin was taken whole
+    int buf = 0;
+    while (nb > 0) {                                           // uniform over the block
+        const int db = min(8, nb), sh = nb - db;
+        uint32_t* h = sc.hist[buf][wave];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const uint32_t d = (v[r] - base) >> sh;
+            if (valid(r) && d < (1u << db)) atomicAdd(&h[d], 1u);
         }
-    }
-}
-
-__global__ __launch_bounds__(kThreads) void topk_zero(uint32_t* hist, int n_q) {
-    const int64_t i = (int64_t)blockIdx.x * kThreads + threadIdx.x;
-    const int64_t n = (int64_t)n_q * kB1;
-    if (i < n) hist[(i / kB1) * kHistWords + (i % kB1)] = 0u;
-}
-
-// pass 1..3: histogram of one radix digit over the chunk's valid positions.
-template <int PASS>
-__global__ __launch_bounds__(kThreads) void topk_hist(const float* __restrict__ scores, int64_t ld,
-                                                      const int32_t* __restrict__ q_pos, int n_q,
-                                                      int k, int n_chunks, void* ws_base) {
-    __shared__ uint32_t h[2048];
-    __shared__ uint32_t hprev[2048];
-    __shared__ uint32_t scratch[8];
-    __shared__ int sbin[2];
-    __shared__ uint32_t sabove[2];
-    const int q = blockIdx.y, c = blockIdx.x;
-    Ws w = ws_of(ws_base, n_q, n_chunks);
-    const int64_t len = (int64_t)q_pos[q] + 1;
-    if (len <= k) return;                             // selects everything; nothing to rank
-    const int64_t s0 = (int64_t)c * kChunk;
-    const int64_t s1 = min(s0 + kChunk, len);
-    uint32_t* hq = w.hist + (size_t)q * kHistWords;
-    // the pass that follows accumulates into the next histogram: clear it now
-    if (c == 0 && PASS < 3) {
-        uint32_t* nxt = hq + (PASS == 1 ? kB1 : kB1 + kB2);
-        const int nb = PASS == 1 ? kB2 : kB3;
-        for (int i = threadIdx.x; i < nb; i += kThreads) nxt[i] = 0u;
-    }
-    if (s0 >= s1) return;
-    constexpr int NB = PASS == 3 ? kB3 : 2048;
-    for (int i = threadIdx.x; i < NB; i += kThreads) h[i] = 0u;
-
-    // threshold prefix from the earlier passes
-    uint32_t prefix = 0;
-    if (PASS >= 2) {
-        for (int i = threadIdx.x; i < kB1; i += kThreads) hprev[i] = hq[i];
         __syncthreads();
-        find_bin(hprev, kB1, (uint32_t)k, scratch, &sbin[0], &sabove[0]);
-        prefix = (uint32_t)sbin[0];
-        if (PASS == 3) {
-            for (int i = threadIdx.x; i < kB2; i += kThreads) hprev[i] = hq[kB1 + i];
-            __syncthreads();
-            find_bin(hprev, kB2, (uint32_t)k - sabove[0], scratch, &sbin[1], &sabove[1]);
-            prefix = (prefix << 11) | (uint32_t)sbin[1];
+        clear_hist(sc, buf ^ 1);
+        uint32_t tot = 0, sfx = 0;
+        if (threadIdx.x < kBins) {
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) tot += sc.hist[buf][w][threadIdx.x];
+            sfx = tot;                                         // suffix sum within the wave
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t t = (uint32_t)__shfl_down((int)sfx, o, 64);
+                if (lane + o < 64) sfx += t;
+            }
+            if (lane == 0) sc.wtot[wave] = sfx;
+        }
+        __syncthreads();
+        if (threadIdx.x < kBins) {
+#pragma unroll
+            for (int w = 0; w < 4; ++w) sfx += w > wave ? sc.wtot[w] : 0u;
+            // count(key in bins >= t) = sfx; the chosen bin is the one where it reaches need
+            if (sfx >= need && sfx - tot < need) {
+                sc.pick[0] = threadIdx.x;
+                sc.pick[1] = sfx - tot;
+                sc.pick[2] = tot;
+            }
+        }
+        __syncthreads();
+        const uint32_t b = sc.pick[0];
+        need -= sc.pick[1];
+        in_bin = sc.pick[2];
+        base += b << sh;
+        nb = sh;
+        buf ^= 1;
+        if (in_bin == need) { whole = true; break; }
+    }
+    // Selection. whole: every key >= base (exactly k of them). Otherwise the
+    // search ended on one key value T = base with `in_bin` copies: keys > T,
+    // plus the first `need` copies of T by position (all of them if need = in_bin).
+    uint32_t T = base;
+    if (!whole && mx == mn) in_bin = kFull ? (uint32_t)kMaxItems : (uint32_t)n;
+    const bool partial = !whole && need != in_bin;
+    uint32_t eq_before = 0;
+    if (partial) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+            c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid(r) && v[r] == T));
+        block_sum(c, sc, &eq_before);
+    }
+    auto take = [&](int r, uint32_t& eq_run) {                 // wave-uniform call
+        if (!partial) return valid(r) && v[r] >= T;
+        const bool in = valid(r);
+        const uint64_t eqm = __builtin_amdgcn_ballot_w64(in && v[r] == T);
+        const bool s = in && (v[r] > T || (v[r] == T && eq_run + lanes_below(eqm) < need));
+        eq_run += __builtin_popcountll(eqm);
+        return s;
+    };
+    uint32_t n_sel = 0;
+    {
+        uint32_t eq_run = eq_before;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) n_sel += __builtin_popcountll(__builtin_amdgcn_ballot_w64(take(r, eq_run)));
+    }
+    uint32_t slot;
+    const uint32_t n_out = block_sum(n_sel, sc, &slot);
+    {
+        uint32_t eq_run = eq_before;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const bool s = take(r, eq_run);
+            const uint64_t sm = __builtin_amdgcn_ballot_w64(s);
+            const uint32_t my = slot + lanes_below(sm);
+            if (s && my < (uint32_t)kK) emit(my, seg0 + 64 * r + lane, r);   // guard: never past k slots
+            slot += __builtin_popcountll(sm);
         }
     }
-    __syncthreads();
-
-    const float* row = scores + (int64_t)q * ld;
-    f32x4 v[kPer];
-    load_chunk(row, s0, s1, v);
-#pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int64_t p0 = s0 + 4 * ((int64_t)i * kThreads + threadIdx.x);
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (p0 + e >= s1) continue;
-            const uint32_t key = score_key(v[i][e]);
-            if (PASS == 1) atomicAdd(&h[key >> 21], 1u);
-            else if (PASS == 2) { if ((key >> 21) == prefix) atomicAdd(&h[(key >> 10) & 2047u], 1u); }
-            else { if ((key >> 10) == prefix) atomicAdd(&h[key & 1023u], 1u); }
-        }
-    }
-    __syncthreads();
-    uint32_t* dst = hq + (PASS == 1 ? 0 : PASS == 2 ? kB1 : kB1 + kB2);
-    for (int i = threadIdx.x; i < NB; i += kThreads)
-        if (h[i]) atomicAdd(&dst[i], h[i]);
+    return (int)min(n_out, (uint32_t)kK);
 }
 
-// Resolve T from the three histograms; count keys > T and == T per chunk.
-__global__ __launch_bounds__(kThreads) void topk_count(const float* __restrict__ scores, int64_t ld,
-                                                       const int32_t* __restrict__ q_pos, int n_q,
-                                                       int k, int n_chunks, void* ws_base) {
-    __shared__ uint32_t hprev[2048];
-    __shared__ uint32_t scratch[8];
-    __shared__ int sbin[3];
-    __shared__ uint32_t sabove[3];
+__device__ __forceinline__ void write_final_pad(int32_t* out, int count) {
+    for (int j = count + threadIdx.x; j < kK; j += kThreads) out[j] = -1;
+}
+
+// Level 1: chunk c of row q.
+__global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__ scores, int64_t ld,
+                                                       const int32_t* __restrict__ q_pos, int n_chunks,
+                                                       uint8_t* __restrict__ lists, int32_t* __restrict__ idx) {
+    __shared__ Scratch sc;
     const int q = blockIdx.y, c = blockIdx.x;
-    Ws w = ws_of(ws_base, n_q, n_chunks);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int64_t len = (int64_t)q_pos[q] + 1;
     const int64_t s0 = (int64_t)c * kChunk;
-    if (len <= k || s0 >= len) return;
-    const int64_t s1 = min(s0 + kChunk, len);
-    const uint32_t* hq = w.hist + (size_t)q * kHistWords;
-    for (int i = threadIdx.x; i < kB1; i += kThreads) hprev[i] = hq[i];
-    __syncthreads();
-    find_bin(hprev, kB1, (uint32_t)k, scratch, &sbin[0], &sabove[0]);
-    for (int i = threadIdx.x; i < kB2; i += kThreads) hprev[i] = hq[kB1 + i];
-    __syncthreads();
-    find_bin(hprev, kB2, (uint32_t)k - sabove[0], scratch, &sbin[1], &sabove[1]);
-    for (int i = threadIdx.x; i < kB3; i += kThreads) hprev[i] = hq[kB1 + kB2 + i];
-    __syncthreads();
-    find_bin(hprev, kB3, (uint32_t)k - sabove[0] - sabove[1], scratch, &sbin[2], &sabove[2]);
-    const uint32_t T = ((uint32_t)sbin[0] << 21) | ((uint32_t)sbin[1] << 10) | (uint32_t)sbin[2];
-    const uint32_t n_gt = sabove[0] + sabove[1] + sabove[2];
-
-    const float* row = scores + (int64_t)q * ld;
-    uint32_t gt = 0, eq = 0;
-    f32x4 v[kPer];
-    load_chunk(row, s0, s1, v);
+    const int n = (int)max((int64_t)0, min(s0 + kChunk, len) - s0);
+    const float* row = scores + (int64_t)q * ld + s0;
+    // lane holds items kSeg*wave + 64r + lane: each wave load reads 256 contiguous bytes.
+    // Loads are unconditional (clamped address) so all 32 are in flight together; a
+    // branch around each would make the compiler wait for each one at the join.
+    uint32_t v[kPer];
+    if (n > 0) {
+        float x[kPer];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int64_t p0 = s0 + 4 * ((int64_t)i * kThreads + threadIdx.x);
+        for (int r = 0; r < kPer; ++r) x[r] = row[min(kSeg * wave + 64 * r + lane, n - 1)];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            if (p0 + e >= s1) continue;
-            const uint32_t key = score_key(v[i][e]);
-            gt += key > T;
-            eq += key == T;
-        }
+        for (int r = 0; r < kPer; ++r) v[r] = kSeg * wave + 64 * r + lane < n ? score_key(x[r]) : 0u;
+    } else {
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) v[r] = 0u;
     }
-    uint32_t tg, te;
-    block_excl_scan(gt, scratch, tg);
-    block_excl_scan(eq, scratch + 4, te);
-    if (threadIdx.x == 0) {
-        w.counts[((size_t)q * n_chunks + c) * 2 + 0] = tg;
-        w.counts[((size_t)q * n_chunks + c) * 2 + 1] = te;
-        if (c == 0) {
-            w.state[q * 4 + 0] = T;
-            w.state[q * 4 + 1] = n_gt;
-            w.state[q * 4 + 2] = (uint32_t)k - n_gt;
-        }
+    if (n_chunks == 1) {
+        int32_t* out = idx + (int64_t)q * kK;
+        auto em = [&](uint32_t slot, int i, int) { out[slot] = (int32_t)(s0 + i); };
+        const int cnt = n == kMaxItems ? select_regs<true>(v, n, sc, em) : select_regs<false>(v, n, sc, em);
+        write_final_pad(out, cnt);
+    } else {
+        uint8_t* L = lists + ((size_t)q * n_chunks + c) * kListBytes;
+        uint2* items = (uint2*)(L + 16);
+        auto em = [&](uint32_t slot, int i, int r) { items[slot] = make_uint2(v[r], (uint32_t)(s0 + i)); };
+        const int cnt = n == kMaxItems ? select_regs<true>(v, n, sc, em) : select_regs<false>(v, n, sc, em);
+        if (threadIdx.x == 0) *(uint32_t*)L = (uint32_t)cnt;
     }
 }
 
-// Ordered compaction: every selected position, ascending, into idx[q][...].
-__global__ __launch_bounds__(kThreads) void topk_compact(const float* __restrict__ scores, int64_t ld,
-                                                         const int32_t* __restrict__ q_pos, int n_q,
-                                                         int k, int n_chunks, void* ws_base,
-                                                         int32_t* __restrict__ idx) {
-    __shared__ uint32_t scratch[8];
-    __shared__ uint32_t sbase[2];
-    const int q = blockIdx.y, c = blockIdx.x;
-    Ws w = ws_of(ws_base, n_q, n_chunks);
-    const int64_t len = (int64_t)q_pos[q] + 1;
-    int32_t* out = idx + (int64_t)q * k;
-    const int64_t s0 = (int64_t)c * kChunk;
-    if (len <= k) {
-        // every valid position is selected; pad with -1
-        if (c == 0)
-            for (int j = threadIdx.x; j < k; j += kThreads) out[j] = j < len ? j : -1;
-        return;
-    }
-    if (s0 >= len) return;
-    const int64_t s1 = min(s0 + kChunk, len);
-    const uint32_t T = w.state[q * 4 + 0];
-    const uint32_t need = w.state[q * 4 + 2];
-    // counts of the chunks before this one (in chunk order)
+// Level 2+: lists [kFan*g, kFan*g + kFan) of row q (n_in lists per row) into one.
+__global__ __launch_bounds__(kThreads) void topk_merge(const uint8_t* __restrict__ in, int n_in,
+                                                       uint8_t* __restrict__ out_lists, int n_out,
+                                                       int32_t* __restrict__ idx) {
+    __shared__ Scratch sc;
+    __shared__ uint32_t base[kFan + 1];
+    const int q = blockIdx.y, g = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int l0 = g * kFan;
+    const int nl = min(kFan, n_in - l0);
     if (threadIdx.x == 0) {
-        uint32_t gb = 0, eb = 0;
-        for (int cc = 0; cc < c; ++cc) {
-            gb += w.counts[((size_t)q * n_chunks + cc) * 2 + 0];
-            eb += w.counts[((size_t)q * n_chunks + cc) * 2 + 1];
+        uint32_t b = 0;
+        for (int l = 0; l < nl; ++l) {
+            base[l] = b;
+            b += min(*(const uint32_t*)(in + ((size_t)q * n_in + l0 + l) * kListBytes), (uint32_t)kK);
         }
-        sbase[0] = gb;
-        sbase[1] = eb;
+        base[nl] = b;
     }
     __syncthreads();
-    const uint32_t eq_before = sbase[1];
-    uint32_t out_run = sbase[0] + min(eq_before, need);   // output slot of the next selected key
-    uint32_t eq_run = eq_before;                          // equal keys seen before the sub-block
-
-    const float* row = scores + (int64_t)q * ld;
-    f32x4 v[kPer];
-    load_chunk(row, s0, s1, v);
-    // sub-block i holds 4 consecutive scores per thread, so thread order is
-    // position order inside it and sub-blocks follow each other
+    const int n = (int)base[nl];
+    // item i of the concatenation (lists in order) is item i - base[l] of list l
+    uint32_t v[kPer], p[kPer];
+    uint32_t bl[kFan];
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int64_t b0 = s0 + (int64_t)i * 4 * kThreads;
-        if (b0 >= s1) break;                                 // uniform over the block
-        const int64_t p0 = b0 + 4 * threadIdx.x;
-        uint32_t key[4];
-        bool valid[4];
+    for (int j = 0; j < kFan; ++j) bl[j] = j < nl ? base[j] : 0xffffffffu;
+    {
+        uint2 it[kPer];
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            valid[e] = p0 + e < s1;
-            key[e] = valid[e] ? score_key(v[i][e]) : 0u;
+        for (int r = 0; r < kPer; ++r) {        // unconditional loads: all in flight together
+            const int i = min(kSeg * wave + 64 * r + lane, max(n - 1, 0));
+            int l = 0;
+#pragma unroll
+            for (int j = 1; j < kFan; ++j) l += (uint32_t)i >= bl[j] ? 1 : 0;
+            it[r] = ((const uint2*)(in + ((size_t)q * n_in + l0 + l) * kListBytes + 16))[i - bl[l]];
         }
-        uint32_t n_eq = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) n_eq += valid[e] && key[e] == T;
-        uint32_t eq_tot;
-        uint32_t eq_rank = eq_run + block_excl_scan(n_eq, scratch, eq_tot);
-        bool sel[4];
-        uint32_t n_sel = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            bool s = false;
-            if (valid[e]) {
-                if (key[e] > T) s = true;
-                else if (key[e] == T) { s = eq_rank < need; ++eq_rank; }
-            }
-            sel[e] = s;
-            n_sel += s;
+        for (int r = 0; r < kPer; ++r) {
+            const bool ok = kSeg * wave + 64 * r + lane < n;
+            v[r] = ok ? it[r].x : 0u;
+            p[r] = ok ? it[r].y : 0u;
         }
-        uint32_t sel_tot;
-        uint32_t o = out_run + block_excl_scan(n_sel, scratch + 4, sel_tot);
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            if (sel[e]) {
-                if (o < (uint32_t)k) out[o] = (int32_t)(p0 + e);   // guard: never past the row
-                ++o;
-            }
-        out_run += sel_tot;
-        eq_run += eq_tot;
+    }
+    if (n_out == 1) {
+        int32_t* out = idx + (int64_t)q * kK;
+        auto em = [&](uint32_t slot, int, int r) { out[slot] = (int32_t)p[r]; };
+        const int cnt = n == kMaxItems ? select_regs<true>(v, n, sc, em) : select_regs<false>(v, n, sc, em);
+        write_final_pad(out, cnt);
+    } else {
+        uint8_t* L = out_lists + ((size_t)q * n_out + g) * kListBytes;
+        uint2* items = (uint2*)(L + 16);
+        auto em = [&](uint32_t slot, int, int r) { items[slot] = make_uint2(v[r], p[r]); };
+        const int cnt = n == kMaxItems ? select_regs<true>(v, n, sc, em) : select_regs<false>(v, n, sc, em);
+        if (threadIdx.x == 0) *(uint32_t*)L = (uint32_t)cnt;
     }
 }
+
+int n_chunks_of(int64_t ld) { return (int)((ld + kChunk - 1) / kChunk); }
 
 }  // namespace
 
 size_t topk_workspace_bytes(int n_q, int64_t ld, int k) {
     (void)k;
-    const int64_t n_chunks = (ld + kChunk - 1) / kChunk;
-    return ((size_t)n_q * kHistWords + (size_t)n_q * n_chunks * 2 + (size_t)n_q * 4) * 4;
+    const int nc = n_chunks_of(ld);
+    if (nc <= 1) return 16;
+    const int n2 = (nc + kFan - 1) / kFan;
+    return (size_t)n_q * (nc + n2) * kListBytes;
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
                        int32_t* idx, void* ws, hipStream_t st) {
-    const int n_chunks = (int)((ld + kChunk - 1) / kChunk);
-    const dim3 grid(n_chunks, n_q), block(kThreads);
-    const int64_t nz = (int64_t)n_q * kB1;
-    hipLaunchKernelGGL(topk_zero, dim3((unsigned)((nz + kThreads - 1) / kThreads)), block, 0, st,
-                       (uint32_t*)ws, n_q);
-    hipLaunchKernelGGL(topk_hist<1>, grid, block, 0, st, scores, ld, q_pos, n_q, k, n_chunks, ws);
-    hipLaunchKernelGGL(topk_hist<2>, grid, block, 0, st, scores, ld, q_pos, n_q, k, n_chunks, ws);
-    hipLaunchKernelGGL(topk_hist<3>, grid, block, 0, st, scores, ld, q_pos, n_q, k, n_chunks, ws);
-    hipLaunchKernelGGL(topk_count, grid, block, 0, st, scores, ld, q_pos, n_q, k, n_chunks, ws);
-    hipLaunchKernelGGL(topk_compact, grid, block, 0, st, scores, ld, q_pos, n_q, k, n_chunks, ws, idx);
+    (void)k;
+    const int nc = n_chunks_of(ld);
+    uint8_t* a = (uint8_t*)ws;                                  // level-1 lists (n_q x nc)
+    uint8_t* b = a + (size_t)n_q * nc * kListBytes;            // level-2 lists (n_q x nc/8)
+    hipLaunchKernelGGL(topk_chunk, dim3(nc, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, nc, a, idx);
+    int n = nc;
+    uint8_t* in = a;
+    uint8_t* out = b;
+    while (n > 1) {
+        const int ng = (n + kFan - 1) / kFan;
+        hipLaunchKernelGGL(topk_merge, dim3(ng, n_q), dim3(kThreads), 0, st, in, n, out, ng, idx);
+        n = ng;
+        uint8_t* t = in;
+        in = out;
+        out = t;
+    }
     return hipGetLastError();
 }
 
