@@ -17,8 +17,10 @@ launch stream. `cpu_baseline` times the CPU oracle on a bounded sample.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -48,6 +50,29 @@ def score_bytes(wl, fp8):
 def mla_bytes(wl):
     """Per layer: gathered rows + indices + q_lat/q_rope + fp32 output (per query)."""
     return wl.n_q * (2048 * 1152 + 2048 * 4 + 64 * 576 * 2 + 64 * 512 * 4)
+
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SCORE_SOURCES = ("long_context_sparse_02_amd/csrc/indexer_score.hip", "long_context_sparse_02_amd/csrc/device_common.h")
+
+
+def measured_traffic(wl):
+    """HBM bytes per indexer-score launch from the committed counter summary of
+    this workload (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated), or None
+    when there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(HERE, "profiles", f"indexer_score_{wl.name}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    t = re.search(r"^traffic_bytes_per_launch:\s*(\d+)", text, re.M)
+    h = re.search(r"^sources_sha256:\s*([0-9a-f]{64})", text, re.M)
+    if not t or not h:
+        return None
+    sha = hashlib.sha256()
+    for f in SCORE_SOURCES:
+        with open(os.path.join(HERE, f), "rb") as fh:
+            sha.update(fh.read())
+    return int(t.group(1)) if sha.hexdigest() == h.group(1) else None
 
 
 def build_inputs(wl, seed, dev):
@@ -146,7 +171,8 @@ def run_bench(args):
                          "sparse_mla_all_layers": round(mla_ms, 4)},
         "roofline": {"kernel": "indexer_score", "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": None, "bytes_per_launch": sb, "avg_launch_ms": round(score_ms, 4)},
+                     "traffic": measured_traffic(wl), "traffic_unit": "HBM bytes per launch (rocprofv3 counters)",
+                     "bytes_per_launch": sb, "avg_launch_ms": round(score_ms, 4)},
         "mla_achieved_GBs": None if mla_gbs is None else round(mla_gbs, 1),
     }
     if not args.no_cpu_baseline:
