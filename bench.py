@@ -1,15 +1,22 @@
 #!/usr/bin/env python3
 """Benchmark of the DSA lightning indexer + IndexShare + sparse MLA hot path on one MI355X.
 
-One step = one IndexShare group over one batch of synthetic input: the full
-layer's indexer score and top-2048, then absorbed sparse MLA for that layer and
-its 3 shared layers (4 layers). Default workload: decode, 64 sequences x 131072
-cached tokens, one query per sequence (bf16 indexer, bf16 latent cache).
+One step = one pass of the measured unit over one batch of synthetic input:
+  group workloads   one IndexShare group: the full layer's indexer score and
+                    top-2048, then absorbed sparse MLA for it and its 3 shared
+                    layers (4 layers);
+  prefill workloads the full layer's indexer score and top-2048 (index buffer
+                    written), no attention;
+  stack workloads   the 78-layer attention stack: 21 full layers (score +
+                    top-2048 each) and 78 sparse MLA layers, in layer order.
+Default workload: decode, 64 sequences x 131072 cached tokens, one query per
+sequence (bf16 indexer, bf16 latent cache), one group per step.
 
 Prints ONE JSON line. `value` is query-tokens/s over the timed steps, inputs
-resident in HBM. `roofline` covers the dominant kernel (the indexer score):
-algorithmic bytes per launch / its average launch time from HIP events on the
-launch stream. `cpu_baseline` times the CPU oracle on a bounded sample.
+resident in HBM. `roofline` covers the kernel with the largest share of the
+step: algorithmic bytes per launch / its average launch time from HIP events
+recorded between the calls on the launch stream. `cpu_baseline` times the CPU
+oracle on a bounded sample of the same workload.
 
     python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
@@ -33,34 +40,54 @@ import workloads as W
 METRIC = "query-tokens/s via indexer+top-2048+sparse MLA at 128K/1M; % of roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 SCALE = 1.0 / 16.0           # 1/sqrt(QK dim 256)
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = "long_context_sparse_02_amd/csrc/"
+KERNEL_SOURCES = {
+    "indexer_score": (CSRC + "indexer_score.hip", CSRC + "device_common.h"),
+    "topk": (CSRC + "topk.hip", CSRC + "device_common.h"),
+    "sparse_mla": (CSRC + "sparse_mla.hip", CSRC + "device_common.h"),
+}
 
 
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
 
+def is_stack(wl):
+    return wl.mla and wl.n_layers > 4
+
+
+# ---- algorithmic bytes per launch ---------------------------------------------
 def score_bytes(wl, fp8):
-    """Algorithmic HBM bytes of one indexer-score launch: every causal key once
-    per sequence (queries of a sequence share it) + q + w."""
+    """One indexer-score launch: every causal key once per sequence (the queries
+    of a sequence share it) + q + w (+ scales)."""
     key_row = (128 + 4) if fp8 else 256
     q_bytes = wl.n_q * (32 * 128 * (1 if fp8 else 2) + (32 * 4 if fp8 else 0) + 32 * 4)
     return wl.batch * wl.n_ctx * key_row + q_bytes
 
 
+def topk_bytes(wl):
+    """One top-k launch: each query's causal scores read once + its indices written."""
+    first = wl.n_ctx - wl.q_per_seq + 1                     # causal length of the first query
+    causal = wl.batch * sum(first + j for j in range(wl.q_per_seq))
+    return causal * 4 + wl.n_q * 2048 * 4
+
+
 def mla_bytes(wl):
-    """Per layer: gathered rows + indices + q_lat/q_rope + fp32 output (per query)."""
+    """One sparse-MLA launch: gathered rows + indices + q_lat/q_rope + fp32 output."""
     return wl.n_q * (2048 * 1152 + 2048 * 4 + 64 * 576 * 2 + 64 * 512 * 4)
 
 
-HERE = os.path.dirname(os.path.abspath(__file__))
-SCORE_SOURCES = ("long_context_sparse_02_amd/csrc/indexer_score.hip", "long_context_sparse_02_amd/csrc/device_common.h")
+def launch_bytes(kind, wl, fp8):
+    return {"indexer_score": lambda: score_bytes(wl, fp8), "topk": lambda: topk_bytes(wl),
+            "sparse_mla": lambda: mla_bytes(wl)}[kind]()
 
 
-def measured_traffic(wl):
-    """HBM bytes per indexer-score launch from the committed counter summary of
-    this workload (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated), or None
-    when there is none or the kernel sources changed since it was taken."""
-    path = os.path.join(HERE, "profiles", f"indexer_score_{wl.name}.md")
+def measured_traffic(kind, wl):
+    """HBM bytes per launch of `kind` from the committed counter summary of this
+    workload (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated), or None when
+    there is none or the kernel sources changed since it was taken."""
+    path = os.path.join(HERE, "profiles", f"{kind}_{wl.name}.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -69,33 +96,95 @@ def measured_traffic(wl):
     if not t or not h:
         return None
     sha = hashlib.sha256()
-    for f in SCORE_SOURCES:
+    for f in KERNEL_SOURCES[kind]:
         with open(os.path.join(HERE, f), "rb") as fh:
             sha.update(fh.read())
     return int(t.group(1)) if sha.hexdigest() == h.group(1) else None
 
 
+# ---- inputs and the step ----------------------------------------------------------
 def build_inputs(wl, seed, dev):
+    """Device inputs of the workload, drawn by the seeded generators in `workloads`."""
     t0 = time.time()
     q_seq, q_pos = W.query_layout(wl, dev)
-    q_idx, w = W.indexer_queries(wl, seed, 0, dev)
-    k_idx = W.indexer_keys(wl, seed, 0, dev)
     fp8 = wl.indexer_dtype == "fp8"
-    q_scale = k_scale = None
-    if fp8:
-        q_idx, q_scale = gsa.quantize_e4m3(q_idx)
-        k_idx8, k_scale = gsa.quantize_e4m3(k_idx)
-        del k_idx
-        k_idx = k_idx8
+    if is_stack(wl):
+        src = gsa.layer_pattern(wl.n_layers)
+    else:                                      # one group: layer 0 full, the rest shared
+        src = [0] * (wl.n_layers if wl.mla else 1)
+    full_layers = [l for l, s in enumerate(src) if s == l]
+    indexers = []
+    for f in full_layers:
+        q_idx, w = W.indexer_queries(wl, seed, f, dev)
+        k_idx = W.indexer_keys(wl, seed, f, dev)
+        q_scale = k_scale = None
+        if fp8:
+            q_idx, q_scale = gsa.quantize_e4m3(q_idx)
+            k8, k_scale = gsa.quantize_e4m3(k_idx)
+            del k_idx
+            k_idx = k8
+        indexers.append((q_idx, w, k_idx, q_scale, k_scale))
     layers = []
     if wl.mla:
         for l in range(wl.n_layers):
             q_lat, q_rope = W.mla_queries(wl, seed, l, dev)
             layers.append((q_lat, q_rope, W.mla_cache(wl, seed, l, dev)))
     torch.cuda.synchronize()
-    log(f"[bench] inputs for {wl.name} generated in {time.time() - t0:.1f}s")
-    return dict(q_seq=q_seq, q_pos=q_pos, q_idx=q_idx, w=w, k_idx=k_idx, q_scale=q_scale,
-                k_scale=k_scale, layers=layers, fp8=fp8)
+    log(f"[bench] inputs for {wl.name} generated in {time.time() - t0:.1f}s "
+        f"({len(full_layers)} full layers, {len(layers)} attention layers)")
+    ordinal = {f: j for j, f in enumerate(full_layers)}
+    return dict(q_seq=q_seq, q_pos=q_pos, indexers=indexers, full_layers=full_layers,
+                src=[ordinal[s] for s in src], layers=layers, fp8=fp8)
+
+
+def make_step(wl, inp, dev):
+    """The measured unit as the sequence of library calls gsa_indexshare_group /
+    gsa_layer_stack make (same kernels, order and stream), so that events can
+    be recorded between the calls. Returns (step, buffers, kinds): step(evs)
+    records evs[i] before call i and evs[-1] after the last."""
+    ld = (wl.n_ctx + 3) // 4 * 4
+    n_full = len(inp["full_layers"])
+    bufs = dict(
+        scores=torch.empty((wl.n_q, ld), dtype=torch.float32, device=dev),
+        idx=torch.empty((n_full, wl.n_q, 2048), dtype=torch.int32, device=dev),
+        ws=torch.empty(max(gsa.group_workspace_bytes(wl.n_q, ld), 16), dtype=torch.uint8, device=dev),
+        outs=[(torch.empty((wl.n_q, 64, 512), dtype=torch.float32, device=dev),
+               torch.empty((wl.n_q, 64), dtype=torch.float32, device=dev)) for _ in inp["layers"]])
+    calls = []                                  # (kind, fn)
+    q_seq, q_pos = inp["q_seq"], inp["q_pos"]
+
+    def score_call(j):
+        q, w, k, qs, ks = inp["indexers"][j]
+        return lambda: gsa.indexer_score(q, w, k, q_seq, q_pos, q_scale=qs, k_scale=ks,
+                                         scores=bufs["scores"])
+
+    def topk_call(j):
+        return lambda: gsa.topk(bufs["scores"], q_pos, idx=bufs["idx"][j], workspace=bufs["ws"])
+
+    def mla_call(l):
+        (ql, qr, kv), (o, s) = inp["layers"][l], bufs["outs"][l]
+        j = inp["src"][l]
+        return lambda: gsa.sparse_mla_attn(ql, qr, kv, q_seq, bufs["idx"][j], SCALE, out=o, lse=s,
+                                           workspace=bufs["ws"])
+
+    n_units = max(len(inp["layers"]), 1)
+    for l in range(n_units):
+        j = inp["src"][l]
+        if inp["full_layers"][j] == l:
+            calls += [("indexer_score", score_call(j)), ("topk", topk_call(j))]
+        if inp["layers"]:
+            calls.append(("sparse_mla", mla_call(l)))
+    kinds = [k for k, _ in calls]
+
+    def step(evs=None):
+        for i, (_, fn) in enumerate(calls):
+            if evs is not None:
+                evs[i].record()
+            fn()
+        if evs is not None:
+            evs[-1].record()
+
+    return step, bufs, kinds
 
 
 def run_bench(args):
@@ -103,33 +192,11 @@ def run_bench(args):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = build_inputs(wl, args.seed, dev)
-    ld = (wl.n_ctx + 3) // 4 * 4
-    scores = torch.empty((wl.n_q, ld), dtype=torch.float32, device=dev)
-    idx = torch.empty((wl.n_q, 2048), dtype=torch.int32, device=dev)
-    ws = torch.empty(max(gsa.group_workspace_bytes(wl.n_q, ld), 16), dtype=torch.uint8, device=dev)
-    outs = [(torch.empty((wl.n_q, 64, 512), dtype=torch.float32, device=dev),
-             torch.empty((wl.n_q, 64), dtype=torch.float32, device=dev)) for _ in inp["layers"]]
-
-    def step(ev=None):
-        # same kernels, order and stream as gsa_indexshare_group; events bracket each call
-        if ev is not None:
-            ev[0].record()
-        gsa.indexer_score(inp["q_idx"], inp["w"], inp["k_idx"], inp["q_seq"], inp["q_pos"],
-                          q_scale=inp["q_scale"], k_scale=inp["k_scale"], scores=scores)
-        if ev is not None:
-            ev[1].record()
-        gsa.topk(scores, inp["q_pos"], idx=idx, workspace=ws)
-        if ev is not None:
-            ev[2].record()
-        for (ql, qr, kv), (o, s) in zip(inp["layers"], outs):
-            gsa.sparse_mla_attn(ql, qr, kv, inp["q_seq"], idx, SCALE, out=o, lse=s, workspace=ws)
-        if ev is not None:
-            ev[3].record()
-
+    step, bufs, kinds = make_step(wl, inp, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -140,17 +207,20 @@ def run_bench(args):
     t_end.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
-    total_ms = t_start.elapsed_time(t_end)
-    ms_step = total_ms / args.steps
-    score_ms = float(np.mean([e[0].elapsed_time(e[1]) for e in evs]))
-    topk_ms = float(np.mean([e[1].elapsed_time(e[2]) for e in evs]))
-    mla_ms = float(np.mean([e[2].elapsed_time(e[3]) for e in evs])) if inp["layers"] else 0.0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    per_kind = {}                              # kind -> list of launch durations (ms)
+    for e in evs:
+        for i, k in enumerate(kinds):
+            per_kind.setdefault(k, []).append(e[i].elapsed_time(e[i + 1]))
+    launches = {k: kinds.count(k) for k in per_kind}
+    step_share = {k: float(np.mean(v)) * launches[k] for k, v in per_kind.items()}
+    dom = max(step_share, key=step_share.get)
+    avg_ms = float(np.mean(per_kind[dom]))
+    nbytes = launch_bytes(dom, wl, inp["fp8"])
+    achieved = nbytes / (avg_ms / 1e3) / 1e9
     value = wl.n_q / (ms_step / 1e3)
-    sb = score_bytes(wl, inp["fp8"])
-    achieved = sb / (score_ms / 1e3) / 1e9
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); "
-        f"score {score_ms:.3f} ms, top-k {topk_ms:.3f} ms, {len(outs)}x MLA {mla_ms:.3f} ms")
-    mla_gbs = (mla_bytes(wl) * len(outs)) / (mla_ms / 1e3) / 1e9 if mla_ms > 0 else None
+    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); " +
+        ", ".join(f"{k} {launches[k]}x {np.mean(v) * 1e3:.1f} us" for k, v in per_kind.items()))
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -165,61 +235,84 @@ def run_bench(args):
         "dtype": "fp8" if inp["fp8"] else "bf16",
         "data": "synthetic (seeded; integer indexer q/k in [-4,4], w in [1,4]; N(0,1) bf16 latents)",
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.n_ctx,
-                   "queries": wl.n_q, "layers_per_step": len(outs) if wl.mla else 0,
-                   "indexer": wl.indexer_dtype, "topk": 2048, "mla_heads": 64, "seed": args.seed},
-        "breakdown_ms": {"indexer_score": round(score_ms, 4), "topk": round(topk_ms, 4),
-                         "sparse_mla_all_layers": round(mla_ms, 4)},
-        "roofline": {"kernel": "indexer_score", "bound": "hbm", "achieved": round(achieved, 1),
+                   "queries": wl.n_q, "full_layers": len(inp["full_layers"]),
+                   "attention_layers": len(inp["layers"]), "indexer": wl.indexer_dtype,
+                   "topk": 2048, "mla_heads": 64, "seed": args.seed},
+        "breakdown_ms_per_step": {k: round(v, 4) for k, v in step_share.items()},
+        "avg_launch_us": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in per_kind.items()},
+        "achieved_GBs": {k: round(launch_bytes(k, wl, inp["fp8"]) / (float(np.mean(v)) / 1e3) / 1e9, 1)
+                         for k, v in per_kind.items()},
+        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(wl), "traffic_unit": "HBM bytes per launch (rocprofv3 counters)",
-                     "bytes_per_launch": sb, "avg_launch_ms": round(score_ms, 4)},
-        "mla_achieved_GBs": None if mla_gbs is None else round(mla_gbs, 1),
+                     "traffic": measured_traffic(dom, wl),
+                     "traffic_unit": "HBM bytes per launch (rocprofv3 counters)",
+                     "bytes_per_launch": nbytes, "avg_launch_ms": round(avg_ms, 4)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args)
     return result
 
 
+# ---- the oracle on the host ---------------------------------------------------------
+def host_indexer_inputs(wl, inp, j, qi, seed):
+    """Host copies of full layer j's indexer inputs for query qi: (q [1,32,128],
+    w [1,32], keys [N,128]) as the oracle reads them. For the fp8 workload the
+    original integer values are redrawn on the device (same generator, same
+    values) and the oracle applies its own e4m3 block quantisation."""
+    import oracle
+    b = int(inp["q_seq"][qi])
+    q, w, k, _, _ = inp["indexers"][j]
+    if inp["fp8"]:
+        f = inp["full_layers"][j]
+        qv, wv = W.indexer_queries(wl, seed, f, q.device)
+        qh = qv[qi:qi + 1].float().cpu().numpy()
+        kh = W.indexer_keys_seq(wl, seed, f, b, q.device).float().cpu().numpy()
+        qh, kh = oracle.indexer_inputs_fp8(qh, kh)
+        return qh, wv[qi:qi + 1].cpu().numpy(), kh
+    return q[qi:qi + 1].float().cpu().numpy(), w[qi:qi + 1].cpu().numpy(), k[b].float().cpu().numpy()
+
+
+def host_rows(kv, b, sel):
+    """The latent rows `sel` (valid entries) of sequence b, fetched by torch's
+    index_select on the device, and the local indices that address them."""
+    v = sel >= 0
+    rows = np.zeros((len(sel), 576), np.float32)
+    rows[v] = kv[b].index_select(0, torch.from_numpy(sel[v]).to(kv.device).long()).float().cpu().numpy()
+    return rows[None], np.where(v, np.arange(len(sel)), -1)[None]
+
+
 def cpu_baseline(wl, inp, args):
-    """The CPU oracle on a bounded sample of the same workload: the full group
-    (score over every causal key, top-2048, then 4 layers of sparse MLA) for
-    the first `--cpu-queries` queries. Host copies are made before timing."""
+    """The CPU oracle on a bounded sample of the same workload: the first
+    `--cpu-queries` queries through the whole measured unit (every full
+    layer's score over all causal keys and top-2048, then every attention
+    layer over the oracle's own selection). Host copies are made untimed."""
     import oracle                                  # test infrastructure: baseline leg only
     n = min(args.cpu_queries, wl.n_q)
     threads = len(os.sched_getaffinity(0))
     torch.set_num_threads(threads)
-    qs = inp["q_seq"][:n].cpu().numpy()
-    qp = inp["q_pos"][:n].cpu().numpy()
-    if inp["fp8"]:
-        raise SystemExit("cpu baseline for the fp8 workload is not wired in bench.py")
-    q = inp["q_idx"][:n].float().cpu().numpy()
-    w = inp["w"][:n].cpu().numpy()
-    seqs = sorted(set(int(s) for s in qs))
-    remap = {s: i for i, s in enumerate(seqs)}
-    keys = np.stack([inp["k_idx"][s].float().cpu().numpy() for s in seqs])
-    qs_local = np.array([remap[int(s)] for s in qs])
-    t0 = time.perf_counter()
-    sc = oracle.indexer_score(q, w, keys, qs_local, qp)
-    sel = oracle.topk_select(sc, qp, 2048)
-    t_sel = time.perf_counter() - t0
-    # the oracle attends over the rows its own indices select; fetch just those rows
-    t_mla = 0.0
-    for (ql, qr, kv) in inp["layers"]:
-        rows = np.zeros((n, 2048, 576), np.float32)
-        for i in range(n):
-            v = sel[i] >= 0
-            rows[i, v] = kv[int(qs[i])][torch.from_numpy(sel[i][v]).to(kv.device).long()].float().cpu().numpy()
-        local_idx = np.where(sel >= 0, np.arange(2048)[None, :], -1)
-        qln, qrn = ql[:n].float().cpu().numpy(), qr[:n].float().cpu().numpy()
-        t1 = time.perf_counter()
-        for i in range(n):
-            oracle.sparse_mla(qln[i:i + 1], qrn[i:i + 1], rows[i:i + 1], [0], local_idx[i:i + 1], SCALE)
-        t_mla += time.perf_counter() - t1
-    secs = t_sel + t_mla
-    log(f"[bench] oracle: {n} queries in {secs:.2f}s (score+top-k {t_sel:.2f}s, MLA {t_mla:.2f}s) on {threads} threads")
+    secs = 0.0
+    for qi in range(n):
+        b = int(inp["q_seq"][qi])
+        pos = np.array([int(inp["q_pos"][qi])], np.int32)
+        sels = []
+        for j in range(len(inp["full_layers"])):
+            qh, wh, kh = host_indexer_inputs(wl, inp, j, qi, args.seed)
+            t0 = time.perf_counter()
+            sc = oracle.indexer_score(qh, wh, kh[None], np.zeros(1, np.int32), pos)
+            sels.append(oracle.topk_select(sc, pos, 2048)[0])
+            secs += time.perf_counter() - t0
+        for l, (ql, qr, kv) in enumerate(inp["layers"]):
+            rows, local = host_rows(kv, b, sels[inp["src"][l]])
+            qln = ql[qi:qi + 1].float().cpu().numpy()
+            qrn = qr[qi:qi + 1].float().cpu().numpy()
+            t0 = time.perf_counter()
+            oracle.sparse_mla(qln, qrn, rows, np.zeros(1, np.int32), local, SCALE)
+            secs += time.perf_counter() - t0
+    log(f"[bench] oracle: {n} queries in {secs:.2f}s on {threads} threads")
     return {"value": round(n / secs, 3), "unit": "query-tokens/s", "cores": threads, "kind": "oracle",
-            "sample": f"first {n} of {wl.n_q} queries of {wl.name}: full group (score over all causal keys, "
-                      f"top-2048, {len(inp['layers'])} layers of sparse MLA); host copies untimed",
+            "sample": f"first {n} of {wl.n_q} queries of {wl.name} through the whole unit "
+                      f"({len(inp['full_layers'])} x score over all causal keys + top-2048, "
+                      f"{len(inp['layers'])} x sparse MLA); host copies untimed",
             "seconds": round(secs, 3)}
 
 

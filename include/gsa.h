@@ -199,6 +199,59 @@ typedef struct gsa_group_desc {
 size_t gsa_group_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads);
 gsa_status gsa_indexshare_group(const gsa_group_desc* desc, void* stream);
 
+/*
+ * gsa_layer_pattern — which layers run the indexer in GLM-5.2's layer stack
+ * ([Arch] §2.1 table: layers 0, 1, 2 are full, then every fourth layer from 6
+ * (6, 10, ..., 74) is full and the three after it are shared; 21 full and 57
+ * shared of 78; §1.2: index_topk_freq = 4). A shared layer uses the indices of
+ * the latest full layer before it; the §2.1 table makes layer 76 shared, so
+ * layer 77 uses layer 74 (not "L76" as the §1.3 diagram labels it).
+ *
+ * src (host, n_layers int32, or NULL): src[i] = the full layer whose indices
+ * layer i attends over (i itself when layer i is full).
+ * Returns the number of full layers, or -1 when n_layers < 1.
+ */
+int gsa_layer_pattern(int n_layers, int32_t* src);
+
+/*
+ * gsa_layer_stack — the attention stack of n_layers layers under that pattern:
+ * one IndexShare group per full layer (score + top-k into its index buffer,
+ * then attention for it and the shared layers after it), in layer order on
+ * `stream` ([Arch] §2.1-§2.4; [Serving] §10). Every group is validated before
+ * the first is enqueued; the groups then run as gsa_indexshare_group would.
+ *
+ * indexers      host array, one gsa_indexer_layer per full layer, in layer
+ *               order (gsa_layer_pattern(n_layers, NULL) entries).
+ * layers        host array of n_layers gsa_mla_layer (each layer's own cache).
+ * scores_dev    fp32 [n_q, ld_scores], scratch reused by every full layer.
+ * index_buf_dev int32: full layer number f (its ordinal among full layers)
+ *               writes [n_q, k] at index_buf_dev + f * index_stride.
+ *               index_stride = 0 reuses one buffer (enough for the stack
+ *               itself, since each group reads only its own full layer's
+ *               indices); otherwise index_stride >= n_q * k, a multiple of 4.
+ * workspace     at least gsa_group_workspace_bytes(n_q, ld_scores, k, n_heads).
+ * The other fields mean what they mean in gsa_group_desc.
+ */
+typedef struct gsa_indexer_layer {
+    const void* q_idx_dev; const float* q_scale_dev; const float* w_dev;
+    const void* k_idx_dev; const float* k_scale_dev;
+} gsa_indexer_layer;
+
+typedef struct gsa_stack_desc {
+    int n_layers;
+    gsa_dtype dt;
+    const gsa_indexer_layer* indexers;
+    const gsa_mla_layer* layers;
+    float* scores_dev; int64_t ld_scores;
+    const int32_t* q_seq_dev; const int32_t* q_pos_dev;
+    int n_q; int batch; int64_t n_cap; int k;
+    int32_t* index_buf_dev; int64_t index_stride;
+    int n_heads; float scale;
+    void* workspace_dev; size_t workspace_bytes;
+} gsa_stack_desc;
+
+gsa_status gsa_layer_stack(const gsa_stack_desc* desc, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -49,6 +49,23 @@ class _GroupDesc(ctypes.Structure):
                 ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
+class _IndexerLayer(ctypes.Structure):
+    _fields_ = [("q_idx_dev", ctypes.c_void_p), ("q_scale_dev", ctypes.c_void_p),
+                ("w_dev", ctypes.c_void_p), ("k_idx_dev", ctypes.c_void_p),
+                ("k_scale_dev", ctypes.c_void_p)]
+
+
+class _StackDesc(ctypes.Structure):
+    _fields_ = [("n_layers", ctypes.c_int), ("dt", ctypes.c_int),
+                ("indexers", ctypes.POINTER(_IndexerLayer)), ("layers", ctypes.POINTER(_MlaLayer)),
+                ("scores_dev", ctypes.c_void_p), ("ld_scores", ctypes.c_int64),
+                ("q_seq_dev", ctypes.c_void_p), ("q_pos_dev", ctypes.c_void_p),
+                ("n_q", ctypes.c_int), ("batch", ctypes.c_int), ("n_cap", ctypes.c_int64),
+                ("k", ctypes.c_int), ("index_buf_dev", ctypes.c_void_p),
+                ("index_stride", ctypes.c_int64), ("n_heads", ctypes.c_int), ("scale", ctypes.c_float),
+                ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+
+
 def _declare(lib):
     P, I, I64, SZ, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
     sig = {
@@ -63,6 +80,8 @@ def _declare(lib):
         "gsa_sparse_mla_attn": (I, [P, P, P, P, P, I, I, I, I, I64, F, P, P, P, SZ, P]),
         "gsa_group_workspace_bytes": (SZ, [I, I64, I, I]),
         "gsa_indexshare_group": (I, [ctypes.POINTER(_GroupDesc), P]),
+        "gsa_layer_pattern": (I, [I, P]),
+        "gsa_layer_stack": (I, [ctypes.POINTER(_StackDesc), P]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -82,7 +101,7 @@ def lib():
 
 def header_symbols():
     """Function names declared in include/gsa.h."""
-    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", " ", open(HEADER).read(), flags=re.S)   # declarations only
     return sorted(set(re.findall(r"\b(gsa_[a-z0-9_]+)\s*\(", text)))
 
 
@@ -243,4 +262,64 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     d.n_heads, d.scale = MLA_HEADS, scale
     d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
     _check(L.gsa_indexshare_group(ctypes.byref(d), _stream(dev)))
+    return outs
+
+
+def layer_pattern(n_layers=78):
+    """src[i] = the full layer whose indices layer i uses (i when full), from libgsa."""
+    src = (ctypes.c_int32 * max(n_layers, 1))()
+    n_full = lib().gsa_layer_pattern(n_layers, ctypes.cast(src, ctypes.c_void_p))
+    if n_full < 0:
+        raise GsaError(f"invalid n_layers {n_layers}")
+    return list(src)[:n_layers]
+
+
+def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_stride=None,
+                scale=1.0 / 16.0, workspace=None, outs=None):
+    """The attention stack: indexers = [(q_idx, w, k_idx, q_scale, k_scale)] per full
+    layer in layer order (scales None for bf16); layers = [(q_lat, q_rope, kv)] per
+    layer. index_buf: int32 [n_full, n_q, k] (each full layer's indices kept) or
+    [n_q, k] (one buffer reused). Returns [(out, lse)] per layer."""
+    L = lib()
+    n_q = q_seq.shape[0]
+    kv0 = layers[0][2]
+    batch, n_cap = kv0.shape[0], kv0.shape[1]
+    k = index_buf.shape[-1]
+    dev = q_seq.device
+    if not index_buf.is_contiguous():
+        raise GsaError("index_buf must be contiguous")
+    if index_stride is None:
+        index_stride = n_q * k if index_buf.dim() == 3 else 0
+    n_full = L.gsa_layer_pattern(len(layers), None)
+    if len(indexers) != n_full:
+        raise GsaError(f"{len(layers)} layers have {n_full} full layers, got {len(indexers)} indexers")
+    if index_stride and index_buf.numel() < (n_full - 1) * index_stride + n_q * k:
+        raise GsaError("index_buf is too small for one [n_q, k] buffer per full layer")
+    fp8 = indexers[0][0].dtype == torch.uint8
+    if scores is None:
+        scores = torch.empty((n_q, (n_cap + 3) // 4 * 4), dtype=torch.float32, device=dev)
+    ld = scores.shape[1]
+    if outs is None:
+        outs = [(torch.empty((n_q, MLA_HEADS, LATENT_DIM), dtype=torch.float32, device=dev),
+                 torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)) for _ in layers]
+    xs = (_IndexerLayer * len(indexers))()
+    for i, (qi, w, ki, qs, ks) in enumerate(indexers):
+        xs[i] = _IndexerLayer(qi.data_ptr(), None if qs is None else qs.data_ptr(), w.data_ptr(),
+                              ki.data_ptr(), None if ks is None else ks.data_ptr())
+    arr = (_MlaLayer * len(layers))()
+    for i, ((ql, qr, kv), (o, s)) in enumerate(zip(layers, outs)):
+        arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
+                           None if s is None else s.data_ptr())
+    ws = _workspace(group_workspace_bytes(n_q, ld, k), dev, workspace)
+    d = _StackDesc()
+    d.n_layers, d.dt = len(layers), FP8_E4M3 if fp8 else BF16
+    d.indexers = ctypes.cast(xs, ctypes.POINTER(_IndexerLayer))
+    d.layers = ctypes.cast(arr, ctypes.POINTER(_MlaLayer))
+    d.scores_dev, d.ld_scores = scores.data_ptr(), ld
+    d.q_seq_dev, d.q_pos_dev = q_seq.data_ptr(), q_pos.data_ptr()
+    d.n_q, d.batch, d.n_cap, d.k = n_q, batch, n_cap, k
+    d.index_buf_dev, d.index_stride = index_buf.data_ptr(), index_stride
+    d.n_heads, d.scale = MLA_HEADS, scale
+    d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
+    _check(L.gsa_layer_stack(ctypes.byref(d), _stream(dev)))
     return outs

@@ -160,14 +160,17 @@ size_t gsa_group_workspace_bytes(int n_q, int64_t ld, int k, int n_heads) {
     return a > b ? a : b;     // top-k finishes (stream order) before attention reuses the space
 }
 
-gsa_status gsa_indexshare_group(const gsa_group_desc* d, void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Host-side checks of one group; enqueues nothing.
+gsa_status validate_group(const gsa_group_desc* d) {
     if (d == nullptr) return fail(GSA_ERR_INVALID_ARG, "desc is NULL");
     REQUIRE_PTR(d->index_buf_dev); REQUIRE_PTR(d->q_seq_dev);
     REQUIRE(d->n_layers >= 0, "n_layers must be >= 0");
     REQUIRE(d->n_layers == 0 || d->layers != nullptr, "layers is NULL");
     REQUIRE(d->compute_index == 0 || d->compute_index == 1, "compute_index must be 0 or 1");
-    const size_t need = gsa_group_workspace_bytes(d->n_q, d->ld_scores, d->k, d->n_heads);
-    // validate every step before enqueuing any of them
     if (d->compute_index) {
         gsa_status st = check_score(d->dt, d->q_idx_dev, d->q_scale_dev, d->w_dev, d->k_idx_dev,
                                     d->k_scale_dev, d->q_seq_dev, d->q_pos_dev, d->n_q, d->batch,
@@ -189,8 +192,11 @@ gsa_status gsa_indexshare_group(const gsa_group_desc* d, void* stream) {
             return st;
         }
     }
-    (void)need;
-    hipStream_t s = (hipStream_t)stream;
+    return GSA_OK;
+}
+
+// Enqueues a validated group: score -> top-k (F layer) -> attention per layer.
+gsa_status enqueue_group(const gsa_group_desc* d, hipStream_t s) {
     if (d->compute_index) {
         hipError_t e = gsa::launch_indexer_score(d->dt == GSA_FP8_E4M3, d->q_idx_dev, d->q_scale_dev,
                                                  d->w_dev, d->k_idx_dev, d->k_scale_dev, d->q_seq_dev,
@@ -207,6 +213,78 @@ gsa_status gsa_indexshare_group(const gsa_group_desc* d, void* stream) {
                                               d->index_buf_dev, d->k, d->n_q, d->n_heads, d->n_cap,
                                               d->scale, L.out_dev, L.lse_dev, d->workspace_dev, s);
         if (e != hipSuccess) return hip_result(e, "group: sparse_mla_attn");
+    }
+    return GSA_OK;
+}
+
+// Layer i is full when i < 3 or i = 2 (mod 4); a shared layer uses the latest
+// full layer before it.
+bool layer_is_full(int i) { return i < 3 || i % 4 == 2; }
+
+}  // namespace
+
+extern "C" {
+
+gsa_status gsa_indexshare_group(const gsa_group_desc* d, void* stream) {
+    gsa_status st = validate_group(d);
+    if (st != GSA_OK) return st;
+    st = enqueue_group(d, (hipStream_t)stream);
+    if (st == GSA_OK) g_err[0] = 0;
+    return st;
+}
+
+int gsa_layer_pattern(int n_layers, int32_t* src) {
+    if (n_layers < 1) return -1;
+    int n_full = 0, last = 0;
+    for (int i = 0; i < n_layers; ++i) {
+        if (layer_is_full(i)) { last = i; ++n_full; }
+        if (src) src[i] = last;
+    }
+    return n_full;
+}
+
+gsa_status gsa_layer_stack(const gsa_stack_desc* d, void* stream) {
+    if (d == nullptr) return fail(GSA_ERR_INVALID_ARG, "desc is NULL");
+    REQUIRE(d->n_layers >= 1, "n_layers must be >= 1");
+    REQUIRE(d->layers != nullptr && d->indexers != nullptr, "layers / indexers is NULL");
+    REQUIRE(d->index_stride == 0 || d->index_stride >= (int64_t)d->n_q * d->k,
+            "index_stride must be 0 or >= n_q * k");
+    REQUIRE(d->index_stride % 4 == 0, "index_stride must be a multiple of 4 (16-byte rows)");
+    // one group per full layer: the full layer and the shared layers after it
+    auto group_at = [&](int i, int f) {                   // i: a full layer, f: its ordinal
+        const gsa_indexer_layer& X = d->indexers[f];
+        gsa_group_desc g{};
+        g.compute_index = 1;
+        g.dt = d->dt;
+        g.q_idx_dev = X.q_idx_dev; g.q_scale_dev = X.q_scale_dev; g.w_dev = X.w_dev;
+        g.k_idx_dev = X.k_idx_dev; g.k_scale_dev = X.k_scale_dev;
+        g.scores_dev = d->scores_dev; g.ld_scores = d->ld_scores;
+        g.q_seq_dev = d->q_seq_dev; g.q_pos_dev = d->q_pos_dev;
+        g.n_q = d->n_q; g.batch = d->batch; g.n_cap = d->n_cap; g.k = d->k;
+        g.index_buf_dev = d->index_buf_dev + (int64_t)f * d->index_stride;
+        g.n_layers = 1;
+        while (i + g.n_layers < d->n_layers && !layer_is_full(i + g.n_layers)) ++g.n_layers;
+        g.layers = d->layers + i;
+        g.n_heads = d->n_heads; g.scale = d->scale;
+        g.workspace_dev = d->workspace_dev; g.workspace_bytes = d->workspace_bytes;
+        return g;
+    };
+    for (int i = 0, f = 0; i < d->n_layers; ++i) {      // validate all before enqueuing any
+        if (!layer_is_full(i)) continue;
+        const gsa_group_desc g = group_at(i, f++);
+        const gsa_status st = validate_group(&g);
+        if (st != GSA_OK) {
+            char tmp[512];
+            snprintf(tmp, sizeof(tmp), "group of full layer %d: %s", i, g_err);
+            snprintf(g_err, sizeof(g_err), "%s", tmp);
+            return st;
+        }
+    }
+    for (int i = 0, f = 0; i < d->n_layers; ++i) {
+        if (!layer_is_full(i)) continue;
+        const gsa_group_desc g = group_at(i, f++);
+        const gsa_status st = enqueue_group(&g, (hipStream_t)stream);
+        if (st != GSA_OK) return st;
     }
     g_err[0] = 0;
     return GSA_OK;

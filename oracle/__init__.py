@@ -30,10 +30,10 @@ from .indexer import indexer_score
 from .topk import topk_select
 from .mla import sparse_mla
 from .pattern import layer_pattern, shared_source
-from .group import indexshare_group, layer_stack
+from .group import indexer_inputs_fp8, indexshare_group, layer_stack
 
 __all__ = [
     "e4m3_decode", "e4m3_encode", "quantize_blocks", "dequantize_blocks",
     "indexer_score", "topk_select", "sparse_mla", "layer_pattern",
-    "shared_source", "indexshare_group", "layer_stack",
+    "shared_source", "indexshare_group", "layer_stack", "indexer_inputs_fp8",
 ]

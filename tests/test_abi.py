@@ -104,3 +104,57 @@ def test_quantize_rejects():
     L = gsa.lib()
     assert L.gsa_quantize_e4m3(None, 10, FAKE, FAKE, None) == INVALID
     assert L.gsa_quantize_e4m3(FAKE, -1, FAKE, FAKE, None) == INVALID
+
+
+def test_layer_pattern_matches_oracle():
+    import oracle
+    L = gsa.lib()
+    for n in (1, 2, 3, 4, 5, 6, 7, 10, 78, 101):
+        src = gsa.layer_pattern(n)
+        assert src == oracle.shared_source(oracle.layer_pattern(n)), n
+        assert L.gsa_layer_pattern(n, None) == sum(1 for i, s in enumerate(src) if s == i)
+    assert L.gsa_layer_pattern(78, None) == 21
+    assert L.gsa_layer_pattern(0, None) == -1
+    with pytest.raises(gsa.GsaError):
+        gsa.layer_pattern(0)
+
+
+def _stack_desc(n_layers, layers, indexers):
+    d = gsa._StackDesc()
+    d.n_layers, d.dt = n_layers, 0
+    d.indexers = ctypes.cast(indexers, ctypes.POINTER(gsa._IndexerLayer))
+    d.layers = ctypes.cast(layers, ctypes.POINTER(gsa._MlaLayer))
+    d.scores_dev, d.ld_scores = 0x10000, 4096
+    d.q_seq_dev = d.q_pos_dev = d.index_buf_dev = 0x10000
+    d.n_q, d.batch, d.n_cap, d.k = 64, 64, 4096, 2048
+    d.index_stride = 64 * 2048
+    d.n_heads, d.scale = 64, 1 / 16
+    d.workspace_dev, d.workspace_bytes = 0x10000, 1 << 30
+    return d
+
+
+def test_stack_validates_every_group_before_launching():
+    L = gsa.lib()
+    n = 78
+    layers = (gsa._MlaLayer * n)()
+    for i in range(n):
+        layers[i] = gsa._MlaLayer(0x10000, 0x10000, 0x10000, 0x10000, None)
+    layers[77] = gsa._MlaLayer(0x10000, None, 0x10000, 0x10000, None)    # last layer broken
+    xs = (gsa._IndexerLayer * 21)()
+    for f in range(21):
+        xs[f] = gsa._IndexerLayer(0x10000, None, 0x10000, 0x10000, None)
+    d = _stack_desc(n, layers, xs)
+    assert L.gsa_layer_stack(ctypes.byref(d), None) == INVALID
+    msg = L.gsa_last_error()
+    assert b"group of full layer 74" in msg and b"layer 3" in msg    # 77 is the 4th layer of 74's group
+    xs[20] = gsa._IndexerLayer(0x10000, None, None, 0x10000, None)      # full layer 74: no w
+    layers[77] = gsa._MlaLayer(0x10000, 0x10000, 0x10000, 0x10000, None)
+    assert L.gsa_layer_stack(ctypes.byref(d), None) == INVALID
+    assert b"group of full layer 74" in L.gsa_last_error()
+    xs[20] = gsa._IndexerLayer(0x10000, None, 0x10000, 0x10000, None)
+    d.index_stride = 100                                                 # < n_q * k
+    assert L.gsa_layer_stack(ctypes.byref(d), None) == INVALID
+    d.index_stride = 64 * 2048
+    d.n_layers = 0
+    assert L.gsa_layer_stack(ctypes.byref(d), None) == INVALID
+    assert L.gsa_layer_stack(None, None) == INVALID
