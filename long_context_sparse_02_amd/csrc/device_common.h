@@ -32,6 +32,12 @@ __device__ __forceinline__ int e8m0_of(float s) {
 
 __device__ __forceinline__ float shfl_xor(float v, int m) { return __shfl_xor(v, m, kWave); }
 
+// v(l) + v(l ^ 32) with the gfx950 permlane32 swap (VALU only, no LDS).
+__device__ __forceinline__ float sum_x32(float v) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // ---- LDS-DMA rings ---------------------------------------------------------
 // One 16-byte LDS-DMA load per lane: lane l's 16 bytes from `src` land at LDS
 // address lds_base + 16*l (one wait state between the M0 write and the load,

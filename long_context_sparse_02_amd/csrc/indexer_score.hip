@@ -207,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
                     float part = 0.f;
 #pragma unroll
                     for (int i = 0; i < 16; ++i) part = fmaf(wr[jj][i], fmaxf(acc[i], 0.f), part);
-                    part += shfl_xor(part, 32);
+                    part = sum_x32(part);
                     res = (s <= apos[jj]) ? part : neg_inf();
                 }
                 if (g == 0 && s < c1) scores[(int64_t)(qb0 + j) * ld + s] = res;
@@ -216,6 +216,297 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
         ring_barrier();     // the next run refills slots this run's last tiles were read from
         j0 = j1;
     }
+}
+
+// Several queries of one sequence per work-group (MTP verify, chunked prefill).
+// Here the MFMA rate, not HBM, bounds the kernel, so the key tile in LDS must
+// feed as many MFMAs per LDS read as registers allow, and each SIMD needs a
+// second wave to issue MFMAs while the first waits on LDS or runs the epilogue.
+// 8 waves (2 per SIMD). Wave w holds the A operands of 2 queries (pair qp =
+// w mod QB/2) and takes NSUB of the 4 32-key subtiles of every tile; each key
+// fragment read from LDS feeds the MFMAs of both queries.
+constexpr int kMqWaves = 8;
+constexpr int kMqThreads = 64 * kMqWaves;
+
+template <int QB, bool FP8>
+__global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int n_q, int64_t n_cap,
+    float* __restrict__ scores, int64_t ld, int chunk) {
+    using T = KeyTile<FP8>;
+    constexpr int QPW = 2;                       // queries per wave
+    constexpr int NQP = QB / QPW;                // query pairs per work-group
+    constexpr int NSUB = 4 * NQP / kMqWaves;     // subtiles per wave per tile
+    static_assert(QB == 4 || QB == 8 || QB == 16, "QB");
+    constexpr int KSTEPS = FP8 ? 2 : 8;
+    constexpr int kDmaPerWave = T::kDma / kMqWaves;
+    using AVec = std::conditional_t<FP8, i32x8, bf16x8>;
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * T::kSlot];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // scalar: wave-uniform values stay in SGPRs
+    const int n = lane & 31, g = lane >> 5;
+    const int qb0 = blockIdx.y * QB;
+    const int64_t c0 = (int64_t)blockIdx.x * chunk;
+    if (c0 >= n_cap) return;
+    const int64_t c1 = min(c0 + (int64_t)chunk, n_cap);
+    const int jw0 = (wave % NQP) * QPW;          // this wave's first query in the block
+    const int sub0 = (wave / NQP) * NSUB;        // and first subtile
+    // LDS byte offset, inside a 32-key subtile, of the 16-byte chunks this lane
+    // reads (row n; the row's swizzle depends on n only, as subtiles are 32 rows)
+    constexpr int kReads = FP8 ? 2 * KSTEPS : KSTEPS;
+    uint32_t lds_off[kReads];
+#pragma unroll
+    for (int t = 0; t < kReads; ++t) lds_off[t] = T::off(n, FP8 ? 4 * g + t : 8 * g + t);
+
+    AVec a[QPW][KSTEPS];
+    float wr[QPW][16];
+    int apos[QPW], a_e8[QPW];
+#pragma unroll
+    for (int jj = 0; jj < QPW; ++jj) {
+        const int qi = qb0 + jw0 + jj;
+        const bool ok = qi < n_q;
+        const int qr = ok ? qi : 0;
+        apos[jj] = ok ? q_pos[qi] : -1;
+        const uint8_t* qh = q + ((int64_t)qr * kHeads + n) * T::kRowBytes;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            if constexpr (FP8) {
+                const i32x4* p = (const i32x4*)(qh + 64 * g + 32 * t);
+                const i32x4 lo = p[0], hi = p[1];
+                a[jj][t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                a[jj][t] = *(const bf16x8*)(qh + 2 * (64 * g + 8 * t));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const int h = 8 * (i >> 2) + 4 * g + (i & 3);
+            wr[jj][i] = ok ? w[(int64_t)qr * kHeads + h] : 0.f;
+        }
+        if constexpr (FP8) a_e8[jj] = e8m0_of(q_scale[(int64_t)qr * kHeads + n]);
+        else a_e8[jj] = 127;
+    }
+    wait_vmcnt<0>();
+
+    const int per = kDmaPerWave + ((FP8 && wave == 0) ? 2 : 0);
+    const uint32_t ring_base = (uint32_t)(uintptr_t)(lds_u8*)ring;
+
+    int j0 = 0;
+    while (j0 < QB && qb0 + j0 < n_q) {
+        const int seq = q_seq[qb0 + j0];
+        int j1 = j0 + 1;
+        int maxpos = q_pos[qb0 + j0];
+        while (j1 < QB && qb0 + j1 < n_q && q_seq[qb0 + j1] == seq) {
+            maxpos = max(maxpos, (int)q_pos[qb0 + j1]);
+            ++j1;
+        }
+        const uint8_t* kb = k + (int64_t)seq * n_cap * T::kRowBytes;
+        const float* ksb = FP8 ? k_scale + (int64_t)seq * n_cap : nullptr;
+        const int64_t t_end = min(c1, (int64_t)maxpos + 1);
+        const int na = t_end > c0 ? (int)((t_end - c0 + kTile - 1) / kTile) : 0;
+        const int nt_all = (int)((c1 - c0 + kTile - 1) / kTile);
+        bool inrun[QPW];
+        int nin = 0;
+#pragma unroll
+        for (int jj = 0; jj < QPW; ++jj) {
+            inrun[jj] = jw0 + jj >= j0 && jw0 + jj < j1;
+            nin += inrun[jj] ? 1 : 0;
+        }
+        const int stores = nin * NSUB;           // score stores of this wave per tile
+
+        auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
+            const int64_t t0 = c0 + (int64_t)ti * kTile;
+            const uint32_t dst = ring_base + slot * T::kSlot;
+#pragma unroll
+            for (int jd = 0; jd < kDmaPerWave; ++jd) {
+                const int i = wave * kDmaPerWave + jd;
+                const int r = i * T::kRowsPerDma + lane / T::kChunks;
+                const int p = lane % T::kChunks;
+                const int c = p ^ (r & (T::kChunks - 1));
+                const int64_t krow = min(t0 + r, c1 - 1);
+                lds_dma16(kb + krow * T::kRowBytes + 16 * c, dst + 1024 * i);
+            }
+            if constexpr (FP8) {
+                if (wave == 0) {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const int64_t krow = min(t0 + 64 * h + lane, c1 - 1);
+                        lds_dma4(ksb + krow, dst + T::kBytes + 256 * h);
+                    }
+                }
+            }
+        };
+
+        for (int p = 0; p < kRing - 1; ++p)
+            if (p < na) issue(p, p);
+        for (int ti = 0; ti < nt_all; ++ti) {
+            const int64_t t0 = c0 + (int64_t)ti * kTile;
+            const bool active = ti < na;
+            const lds_u8* tile = (const lds_u8*)ring + (ti % kRing) * T::kSlot;
+            if (active) {
+                const int later = min(na, ti + kRing - 1) - ti - 1;
+                wait_vmcnt_le<63>(later * per + stores * min(ti, kRing - 1));
+                ring_barrier();
+                if (ti + kRing - 1 < na) issue(ti + kRing - 1, (ti + kRing - 1) % kRing);
+            }
+            if (nin == 0) continue;                       // wave-uniform
+            const uint32_t tile_addr = ring_base + (ti % kRing) * T::kSlot;
+            // Fast path: both queries in the run and every key of this wave's
+            // subtiles causal for both. Straight-line code in which the epilogue of
+            // subtile ns - 1 is interleaved with the MFMAs of subtile ns, so the VALU
+            // work runs while the matrix core is busy.
+            const int64_t s_first = t0 + sub0 * 32, s_last = s_first + NSUB * 32 - 1;
+            bool fast = active && nin == QPW && s_last < c1;
+#pragma unroll
+            for (int jj = 0; jj < QPW; ++jj) fast = fast && s_last <= apos[jj];
+            if (fast) {
+                f32x16 acc[2][QPW];
+                auto mfmas = [&](int ns, f32x16 (&c)[QPW]) __attribute__((always_inline)) {
+                    const int nt = sub0 + ns;
+                    const lds_u8* base = (const lds_u8*)(uintptr_t)(tile_addr + nt * 32 * T::kRowBytes);
+#pragma unroll
+                    for (int t = 0; t < KSTEPS; ++t) {
+                        if constexpr (FP8) {
+                            const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(base + lds_off[2 * t]);
+                            const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(base + lds_off[2 * t + 1]);
+                            const i32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            const int ke = e8m0_of(*(const __attribute__((address_space(3))) float*)(
+                                (const lds_u8*)(uintptr_t)(tile_addr + T::kBytes + nt * 128) + 4 * n));
+#pragma unroll
+                            for (int jj = 0; jj < QPW; ++jj)
+                                c[jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    a[jj][t], b, t == 0 ? f32x16{} : c[jj], 0, 0, 0, a_e8[jj], 0, ke);
+                        } else {
+                            const bf16x8 b = *(const __attribute__((address_space(3))) bf16x8*)(base + lds_off[t]);
+#pragma unroll
+                            for (int jj = 0; jj < QPW; ++jj)
+                                c[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    a[jj][t], b, t == 0 ? f32x16{} : c[jj], 0, 0, 0);
+                        }
+                    }
+                };
+                // epilogue in two parts: the per-lane head sums (VALU only, scheduled
+                // between the MFMAs) and the cross-half add + store after them
+                auto head_sums = [&](const f32x16 (&c)[QPW], float (&part)[QPW]) __attribute__((always_inline)) {
+#pragma unroll
+                    for (int jj = 0; jj < QPW; ++jj) {
+                        float acc_s = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)
+                            acc_s = fmaf(wr[jj][i], __int_as_float(max(__float_as_int(c[jj][i]), 0)), acc_s);
+                        part[jj] = acc_s;
+                    }
+                };
+                auto finish = [&](int ns, const float (&part)[QPW]) __attribute__((always_inline)) {
+                    const int64_t s0 = t0 + (sub0 + ns) * 32;
+#pragma unroll
+                    for (int jj = 0; jj < QPW; ++jj)            // both half-waves hold the sum
+                        scores[(int64_t)(qb0 + jw0 + jj) * ld + s0 + n] = sum_x32(part[jj]);
+                };
+                mfmas(0, acc[0]);
+#pragma unroll
+                for (int ns = 1; ns < NSUB; ++ns) {
+                    float part[QPW];
+                    mfmas(ns, acc[ns & 1]);
+                    head_sums(acc[(ns - 1) & 1], part);
+#pragma unroll
+                    for (int t = 0; t < KSTEPS; ++t) {
+                        __builtin_amdgcn_sched_group_barrier(0x100, FP8 ? 3 : 1, 0);   // LDS reads
+#pragma unroll
+                        for (int jj = 0; jj < QPW; ++jj) {
+                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
+                            __builtin_amdgcn_sched_group_barrier(0x002, FP8 ? 16 : 4, 0);  // VALU
+                        }
+                    }
+                    finish(ns - 1, part);
+                }
+                {
+                    float part[QPW];
+                    head_sums(acc[(NSUB - 1) & 1], part);
+                    finish(NSUB - 1, part);
+                }
+                continue;
+            }
+#pragma unroll
+            for (int ns = 0; ns < NSUB; ++ns) {
+                const int nt = sub0 + ns;
+                const int64_t s0 = t0 + nt * 32;
+                bool any = false;
+#pragma unroll
+                for (int jj = 0; jj < QPW; ++jj) any = any || (active && inrun[jj] && s0 <= apos[jj]);
+                if (any) {                                        // wave-uniform
+                    f32x16 acc[QPW];
+#pragma unroll
+                    for (int t = 0; t < KSTEPS; ++t) {
+                        if constexpr (FP8) {
+                            const lds_u8* base = (const lds_u8*)(uintptr_t)(tile_addr + nt * 32 * T::kRowBytes);
+                            const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(base + lds_off[2 * t]);
+                            const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(base + lds_off[2 * t + 1]);
+                            const i32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                            const int ke = e8m0_of(*(const __attribute__((address_space(3))) float*)(
+                                (const lds_u8*)(uintptr_t)(tile_addr + T::kBytes + nt * 128) + 4 * n));
+#pragma unroll
+                            for (int jj = 0; jj < QPW; ++jj)
+                                acc[jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                                    a[jj][t], b, t == 0 ? f32x16{} : acc[jj], 0, 0, 0, a_e8[jj], 0, ke);
+                        } else {
+                            const lds_u8* base = (const lds_u8*)(uintptr_t)(tile_addr + nt * 32 * T::kRowBytes);
+                            const bf16x8 b = *(const __attribute__((address_space(3))) bf16x8*)(base + lds_off[t]);
+#pragma unroll
+                            for (int jj = 0; jj < QPW; ++jj)
+                                acc[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    a[jj][t], b, t == 0 ? f32x16{} : acc[jj], 0, 0, 0);
+                        }
+                    }
+#pragma unroll
+                    for (int jj = 0; jj < QPW; ++jj) {
+                        if (!inrun[jj]) continue;                 // wave-uniform
+                        // keys s0 + n with n <= lim are causal for this query
+                        const int lim = (int)min((int64_t)apos[jj] - s0, (int64_t)64);
+                        float part = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 16; ++i)              // relu on the bit pattern: exact
+                            part = fmaf(wr[jj][i], __int_as_float(max(__float_as_int(acc[jj][i]), 0)), part);
+                        part = sum_x32(part);
+                        const float res = (active && n <= lim) ? part : neg_inf();
+                        float* row = scores + (int64_t)(qb0 + jw0 + jj) * ld + s0;
+                        if (g == 0 && s0 + n < c1) row[n] = res;
+                    }
+                } else {
+#pragma unroll
+                    for (int jj = 0; jj < QPW; ++jj) {
+                        if (!inrun[jj]) continue;
+                        float* row = scores + (int64_t)(qb0 + jw0 + jj) * ld + s0;
+                        if (g == 0 && s0 + n < c1) row[n] = neg_inf();
+                    }
+                }
+            }
+        }
+        ring_barrier();
+        j0 = j1;
+    }
+}
+
+template <int QB>
+hipError_t launch_mq(bool fp8, dim3 grid, hipStream_t st, const void* q, const float* qs,
+                     const float* w, const void* k, const float* ks, const int32_t* q_seq,
+                     const int32_t* q_pos, int n_q, int64_t n_cap, float* scores, int64_t ld,
+                     int chunk) {
+    if (fp8)
+        hipLaunchKernelGGL((indexer_score_mq<QB, true>), grid, dim3(kMqThreads), 0, st,
+                           (const uint8_t*)q, qs, w, (const uint8_t*)k, ks, q_seq, q_pos, n_q,
+                           n_cap, scores, ld, chunk);
+    else
+        hipLaunchKernelGGL((indexer_score_mq<QB, false>), grid, dim3(kMqThreads), 0, st,
+                           (const uint8_t*)q, qs, w, (const uint8_t*)k, ks, q_seq, q_pos, n_q,
+                           n_cap, scores, ld, chunk);
+    return hipGetLastError();
 }
 
 template <int QB>
@@ -242,15 +533,16 @@ hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, c
                                 float* scores, int64_t ld, hipStream_t stream) {
     // Queries per work-group: the typical number of queries per sequence.
     const int per_seq = n_q / (batch > 0 ? batch : 1);
-    const int qb = per_seq >= 8 ? 8 : per_seq >= 4 ? 4 : per_seq >= 2 ? 2 : 1;
+    const int qb = per_seq >= 16 ? 16 : per_seq >= 8 ? 8 : per_seq >= 4 ? 4 : per_seq >= 2 ? 2 : 1;
     const int64_t n_qblk = (n_q + qb - 1) / qb;
     // Key chunk per work-group: aim for >= 2048 work-groups, chunks of 1K..16K keys.
     int64_t chunk = 16384;
     while (chunk > 1024 && n_qblk * ((n_cap + chunk - 1) / chunk) < 2048) chunk >>= 1;
     const dim3 grid((unsigned)((n_cap + chunk - 1) / chunk), (unsigned)n_qblk);
     switch (qb) {
-        case 8: return launch_qb<8>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
-        case 4: return launch_qb<4>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
+        case 16: return launch_mq<16>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
+        case 8: return launch_mq<8>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
+        case 4: return launch_mq<4>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
         case 2: return launch_qb<2>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
         default: return launch_qb<1>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
     }

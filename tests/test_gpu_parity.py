@@ -68,22 +68,26 @@ def test_score_tiny_group(dtype):
     _score_case(W.WORKLOADS["group_b1_n4096_q4"], 0, dtype=dtype)
 
 
-@pytest.mark.parametrize("q_per_seq", [1, 2, 3, 4, 8, 11])
+@pytest.mark.parametrize("q_per_seq", [1, 2, 3, 4, 8, 11, 16, 19, 37])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
 def test_score_ragged_and_query_blocks(q_per_seq, dtype):
+    # 1-2 per sequence: one query per wave pair; 4-15: 4 or 8 queries per work-group;
+    # 16+: 16 per work-group, with blocks that straddle two sequences (19, 37)
     # n_cap not a multiple of the 128-key tile; several sequences; ld padded
     wl = W.Workload("ragged", 3, 1000 + 37 * q_per_seq, q_per_seq, 1, dtype)
     _score_case(wl, q_per_seq, ld=(wl.n_ctx + 12 + 3) // 4 * 4, dtype=dtype)
 
 
-def test_score_unsorted_sequences_and_positions():
-    wl = W.Workload("mixed", 4, 700, 5, 1, "bf16")
+@pytest.mark.parametrize("n_per", [5, 10, 20])
+def test_score_unsorted_sequences_and_positions(n_per):
+    # random sequence per query: every query block holds several short runs
+    wl = W.Workload("mixed", 4, 700, n_per, 1, "bf16")
     perm = torch.randperm(wl.n_q, generator=torch.Generator().manual_seed(3))
     q, w = W.indexer_queries(wl, 5, 0)
     k = W.indexer_keys(wl, 5, 0)
     q_seq = torch.randint(0, 4, (wl.n_q,), generator=torch.Generator().manual_seed(4), dtype=torch.int32)
-    q_pos = torch.tensor([0, 1, 127, 128, 129, 699, 300, 5, 64, 255, 256, 511, 512, 2, 3, 698, 640,
-                          641, 10, 600][: wl.n_q], dtype=torch.int32)
+    q_pos = torch.tensor(([0, 1, 127, 128, 129, 699, 300, 5, 64, 255, 256, 511, 512, 2, 3, 698, 640,
+                           641, 10, 600] * 4)[: wl.n_q], dtype=torch.int32)
     d = dev()
     s = gsa.indexer_score(q.to(d), w.to(d), k.to(d), q_seq.to(d), q_pos.to(d))
     torch.cuda.synchronize()
