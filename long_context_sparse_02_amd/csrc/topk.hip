@@ -43,6 +43,7 @@ constexpr int kBins = 256;                     // 8-bit radix digit
 struct Scratch {
     uint32_t hist[2][kWaves][kBins];            // per-wave digit histograms, double-buffered
     uint32_t wsum[kWaves];
+    uint32_t weq[kWaves];
     uint32_t wmin[kWaves];
     uint32_t wmax[kWaves];
     uint32_t wtot[4];
@@ -57,6 +58,20 @@ __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
+    return v;
+}
+// The fp32 value of an order-preserving key (inverse of score_key).
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+// A value every lane of the wave holds (read from LDS after a barrier, or a
+// wave reduction), moved to a scalar register so that branches on it are
+// scalar branches.
+__device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
+
+__device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
     return v;
 }
 // number of set bits of `mask` in lanes below this one
@@ -129,20 +144,24 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
     __syncthreads();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) { mn = min(mn, sc.wmin[w]); mx = max(mx, sc.wmax[w]); }
+    mn = uni(mn);
+    mx = uni(mx);
 
-    // ---- radix passes: candidates are keys in [base, base + 2^nb)
-    uint32_t base = mn, need = kK, in_bin = 0;
-    int nb = mx == mn ? 0 : 32 - __builtin_clz(mx - mn);
-    bool whole = false;                                        // the last bin was taken whole
+    // ---- Search for the k-th key. Candidates are the keys in [lo, hi], the exact
+    // key range of the bin chosen last (at first: all keys). Each pass
+    // histograms the candidates into 256 bins and keeps the bin where the count
+    // of candidates in it and above first reaches `need`. Bins are linear in the
+    // score value while the range is wide (keys crowd into a few exponents, so
+    // bins of key bits would put most lanes of a wave on two or three
+    // counters); once the range is narrow they are the top bits of key - lo.
+    // Both are monotone in the key, lo lands in bin 0 and hi in the last used
+    // bin, so each pass shrinks the range.
+    uint32_t lo = mn, hi = mx, need = kK, in_bin = 0;
+    uint32_t sel_w = 0, in_bin_w = 0;      // this wave: keys above the current bin, keys in it
+    bool whole = false;                    // the last bin was taken whole: keys >= lo are the set
     int buf = 0;
-    while (nb > 0) {                                           // uniform over the block
-        const int db = min(8, nb), sh = nb - db;
-        uint32_t* h = sc.hist[buf][wave];
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const uint32_t d = (v[r] - base) >> sh;
-            if (valid(r) && d < (1u << db)) atomicAdd(&h[d], 1u);
-        }
+    auto pick_bin = [&](uint32_t& b, uint32_t& above, uint32_t& tot_b) {
+        // after the histogram of sc.hist[buf] is complete (uniform over the block)
         __syncthreads();
         clear_hist(sc, buf ^ 1);
         uint32_t tot = 0, sfx = 0;
@@ -161,7 +180,6 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
         if (threadIdx.x < kBins) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) sfx += w > wave ? sc.wtot[w] : 0u;
-            // count(key in bins >= t) = sfx; the chosen bin is the one where it reaches need
             if (sfx >= need && sfx - tot < need) {
                 sc.pick[0] = threadIdx.x;
                 sc.pick[1] = sfx - tot;
@@ -169,27 +187,97 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
             }
         }
         __syncthreads();
-        const uint32_t b = sc.pick[0];
-        need -= sc.pick[1];
-        in_bin = sc.pick[2];
-        base += b << sh;
-        nb = sh;
+        b = uni(sc.pick[0]);
+        above = uni(sc.pick[1]);
+        tot_b = uni(sc.pick[2]);
+        // this wave's share: its keys in bins above b (selected for good) and in b
+        const uint4 hv = ((const uint4*)sc.hist[buf][wave])[lane];
+        const uint32_t d0 = 4 * lane;
+        uint32_t mine = (d0 > b ? hv.x : 0u) + (d0 + 1 > b ? hv.y : 0u) + (d0 + 2 > b ? hv.z : 0u) +
+                        (d0 + 3 > b ? hv.w : 0u);
+        sel_w += uni(wave_sum(mine));
+        in_bin_w = uni(sc.hist[buf][wave][b]);
         buf ^= 1;
+    };
+    while (lo != hi) {                                         // uniform over the block
+        const float flo = key_value(lo), fspan = key_value(hi) - flo;
+        const bool by_value = hi - lo > 4096u && fspan > 1e-30f && fspan < 3.0e38f;
+        const float inv = by_value ? 256.f / fspan : 0.f;
+        const int nb = 32 - __builtin_clz(hi - lo);
+        const int sh = nb > 8 ? nb - 8 : 0;
+        auto bin_of = [&](uint32_t key) {
+            return by_value ? min((int)((key_value(key) - flo) * inv), kBins - 1) : (int)((key - lo) >> sh);
+        };
+        uint32_t* h = sc.hist[buf][wave];
+        // the empty asm keeps the compiler from hoisting 32 converted keys out of
+        // the loop (registers that would cost a work-group of occupancy)
+        if (by_value) {
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) {
+                uint32_t key = v[r];
+                asm volatile("" : "+v"(key));
+                if (valid(r) && key >= lo && key <= hi)
+                    atomicAdd(&h[min((int)((key_value(key) - flo) * inv), kBins - 1)], 1u);
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < kPer; ++r) {
+                const uint32_t d = v[r] - lo;
+                if (valid(r) && v[r] >= lo && d <= hi - lo) atomicAdd(&h[d >> sh], 1u);
+            }
+        }
+        uint32_t b, above, tot_b;
+        pick_bin(b, above, tot_b);
+        need -= above;
+        in_bin = tot_b;
+        // exact key range of the chosen bin
+        uint32_t nlo = 0xffffffffu, nhi = 0u;
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            uint32_t key = v[r];
+            asm volatile("" : "+v"(key));     // recompute the bin: keeping 32 values live costs occupancy
+            if (valid(r) && key >= lo && key <= hi && bin_of(key) == (int)b) {
+                nlo = min(nlo, key);
+                nhi = max(nhi, key);
+            }
+        }
+        nlo = wave_min(nlo);
+        nhi = wave_max(nhi);
+        if (lane == 0) { sc.wmin[wave] = nlo; sc.wmax[wave] = nhi; }
+        __syncthreads();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) { nlo = min(nlo, sc.wmin[w]); nhi = max(nhi, sc.wmax[w]); }
+        __syncthreads();
+        lo = uni(nlo);
+        hi = uni(nhi);
         if (in_bin == need) { whole = true; break; }
     }
-    // Selection. whole: every key >= base (exactly k of them). Otherwise the
-    // search ended on one key value T = base with `in_bin` copies: keys > T,
+    const uint32_t base = lo;
+    // Selection. whole: every key >= lo (exactly k of them). Otherwise the
+    // search ended on one key value T = lo with `in_bin` copies: keys > T,
     // plus the first `need` copies of T by position (all of them if need = in_bin).
-    uint32_t T = base;
-    if (!whole && mx == mn) in_bin = kFull ? (uint32_t)kMaxItems : (uint32_t)n;
-    const bool partial = !whole && need != in_bin;
-    uint32_t eq_before = 0;
-    if (partial) {
+    const uint32_t T = base;
+    if (mx == mn) {                                            // no pass ran: every key is T
+        in_bin = kFull ? (uint32_t)kMaxItems : (uint32_t)n;
         uint32_t c = 0;
 #pragma unroll
-        for (int r = 0; r < kPer; ++r)
-            c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid(r) && v[r] == T));
-        block_sum(c, sc, &eq_before);
+        for (int r = 0; r < kPer; ++r) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid(r)));
+        in_bin_w = c;
+    }
+    const bool partial = !whole && need != in_bin;
+    if (!partial) { sel_w += in_bin_w; in_bin_w = 0; }
+    // every wave's count of keys above T and of copies of T, from the histograms
+    if (lane == 0) { sc.wsum[wave] = sel_w; sc.weq[wave] = in_bin_w; }
+    __syncthreads();
+    uint32_t slot = 0, eq_before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) {
+            const uint32_t eq = sc.weq[w];
+            const uint32_t taken = partial ? min(eq, need > eq_before ? need - eq_before : 0u) : 0u;
+            slot += sc.wsum[w] + taken;
+            eq_before += eq;
+        }
     }
     auto take = [&](int r, uint32_t& eq_run) {                 // wave-uniform call
         if (!partial) return valid(r) && v[r] >= T;
@@ -199,14 +287,6 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
         eq_run += __builtin_popcountll(eqm);
         return s;
     };
-    uint32_t n_sel = 0;
-    {
-        uint32_t eq_run = eq_before;
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) n_sel += __builtin_popcountll(__builtin_amdgcn_ballot_w64(take(r, eq_run)));
-    }
-    uint32_t slot;
-    const uint32_t n_out = block_sum(n_sel, sc, &slot);
     {
         uint32_t eq_run = eq_before;
 #pragma unroll
@@ -218,7 +298,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
             slot += __builtin_popcountll(sm);
         }
     }
-    return (int)min(n_out, (uint32_t)kK);
+    return kK;
 }
 
 __device__ __forceinline__ void write_final_pad(int32_t* out, int count) {
