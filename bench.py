@@ -139,18 +139,25 @@ def build_inputs(wl, seed, dev):
 
 def make_step(wl, inp, dev):
     """The measured unit as the sequence of library calls gsa_indexshare_group /
-    gsa_layer_stack make (same kernels, order and stream), so that events can
-    be recorded between the calls. Returns (step, buffers, kinds): step(evs)
-    records evs[i] before call i and evs[-1] after the last."""
+    gsa_layer_stack make (same kernels, order and stream): per group the full
+    layer's score and top-k, then one attention launch over the group's layers.
+    Events can be recorded between the calls. Returns (step, buffers, calls):
+    step(evs) records evs[i] before call i and evs[-1] after the last; calls is
+    [(kind, algorithmic bytes)] per call."""
     ld = (wl.n_ctx + 3) // 4 * 4
     n_full = len(inp["full_layers"])
+    n_att = len(inp["layers"])
+    if is_stack(wl):
+        ws_bytes = gsa.stack_workspace_bytes(wl.n_q, ld, n_att)
+    else:
+        ws_bytes = gsa.group_workspace_bytes(wl.n_q, ld, max(n_att, 1))
     bufs = dict(
         scores=torch.empty((wl.n_q, ld), dtype=torch.float32, device=dev),
         idx=torch.empty((n_full, wl.n_q, 2048), dtype=torch.int32, device=dev),
-        ws=torch.empty(max(gsa.group_workspace_bytes(wl.n_q, ld), 16), dtype=torch.uint8, device=dev),
+        ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev),
         outs=[(torch.empty((wl.n_q, 64, 512), dtype=torch.float32, device=dev),
                torch.empty((wl.n_q, 64), dtype=torch.float32, device=dev)) for _ in inp["layers"]])
-    calls = []                                  # (kind, fn)
+    calls = []                                  # (kind, bytes, fn)
     q_seq, q_pos = inp["q_seq"], inp["q_pos"]
 
     def score_call(j):
@@ -161,30 +168,29 @@ def make_step(wl, inp, dev):
     def topk_call(j):
         return lambda: gsa.topk(bufs["scores"], q_pos, idx=bufs["idx"][j], workspace=bufs["ws"])
 
-    def mla_call(l):
-        (ql, qr, kv), (o, s) = inp["layers"][l], bufs["outs"][l]
-        j = inp["src"][l]
-        return lambda: gsa.sparse_mla_attn(ql, qr, kv, q_seq, bufs["idx"][j], SCALE, out=o, lse=s,
-                                           workspace=bufs["ws"])
+    def mla_call(j, layers):
+        lay = [inp["layers"][l] for l in layers]
+        outs = [bufs["outs"][l] for l in layers]
+        return lambda: gsa.sparse_mla_attn_layers(lay, q_seq, bufs["idx"][j], SCALE, outs=outs,
+                                                  workspace=bufs["ws"])
 
-    n_units = max(len(inp["layers"]), 1)
-    for l in range(n_units):
-        j = inp["src"][l]
-        if inp["full_layers"][j] == l:
-            calls += [("indexer_score", score_call(j)), ("topk", topk_call(j))]
-        if inp["layers"]:
-            calls.append(("sparse_mla", mla_call(l)))
-    kinds = [k for k, _ in calls]
+    fp8 = inp["fp8"]
+    for j, f in enumerate(inp["full_layers"]):
+        calls.append(("indexer_score", launch_bytes("indexer_score", wl, fp8), score_call(j)))
+        calls.append(("topk", launch_bytes("topk", wl, fp8), topk_call(j)))
+        group = [l for l in range(n_att) if inp["src"][l] == j]
+        if group:
+            calls.append(("sparse_mla", launch_bytes("sparse_mla", wl, fp8) * len(group), mla_call(j, group)))
 
     def step(evs=None):
-        for i, (_, fn) in enumerate(calls):
+        for i, (_, _, fn) in enumerate(calls):
             if evs is not None:
                 evs[i].record()
             fn()
         if evs is not None:
             evs[-1].record()
 
-    return step, bufs, kinds
+    return step, bufs, [(k, b) for k, b, _ in calls]
 
 
 def run_bench(args):
@@ -192,11 +198,11 @@ def run_bench(args):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = build_inputs(wl, args.seed, dev)
-    step, bufs, kinds = make_step(wl, inp, dev)
+    step, bufs, calls = make_step(wl, inp, dev)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(kinds) + 1)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
@@ -208,19 +214,19 @@ def run_bench(args):
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    per_kind = {}                              # kind -> list of launch durations (ms)
-    for e in evs:
-        for i, k in enumerate(kinds):
-            per_kind.setdefault(k, []).append(e[i].elapsed_time(e[i + 1]))
-    launches = {k: kinds.count(k) for k in per_kind}
-    step_share = {k: float(np.mean(v)) * launches[k] for k, v in per_kind.items()}
-    dom = max(step_share, key=step_share.get)
-    avg_ms = float(np.mean(per_kind[dom]))
-    nbytes = launch_bytes(dom, wl, inp["fp8"])
-    achieved = nbytes / (avg_ms / 1e3) / 1e9
+    kinds = sorted({k for k, _ in calls}, key=[k for k, _ in calls].index)
+    ms_kind = {k: 0.0 for k in kinds}           # per step
+    bytes_kind = {k: 0 for k in kinds}          # per step
+    launches = {k: 0 for k in kinds}            # per step
+    for i, (k, b) in enumerate(calls):
+        ms_kind[k] += float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
+        bytes_kind[k] += b
+        launches[k] += 1
+    dom = max(ms_kind, key=ms_kind.get)
+    achieved = bytes_kind[dom] / (ms_kind[dom] / 1e3) / 1e9
     value = wl.n_q / (ms_step / 1e3)
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); " +
-        ", ".join(f"{k} {launches[k]}x {np.mean(v) * 1e3:.1f} us" for k, v in per_kind.items()))
+        ", ".join(f"{k} {launches[k]}x {ms_kind[k] / launches[k] * 1e3:.1f} us" for k in kinds))
     result = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -238,15 +244,15 @@ def run_bench(args):
                    "queries": wl.n_q, "full_layers": len(inp["full_layers"]),
                    "attention_layers": len(inp["layers"]), "indexer": wl.indexer_dtype,
                    "topk": 2048, "mla_heads": 64, "seed": args.seed},
-        "breakdown_ms_per_step": {k: round(v, 4) for k, v in step_share.items()},
-        "avg_launch_us": {k: round(float(np.mean(v)) * 1e3, 2) for k, v in per_kind.items()},
-        "achieved_GBs": {k: round(launch_bytes(k, wl, inp["fp8"]) / (float(np.mean(v)) / 1e3) / 1e9, 1)
-                         for k, v in per_kind.items()},
+        "breakdown_ms_per_step": {k: round(v, 4) for k, v in ms_kind.items()},
+        "avg_launch_us": {k: round(ms_kind[k] / launches[k] * 1e3, 2) for k in kinds},
+        "achieved_GBs": {k: round(bytes_kind[k] / (ms_kind[k] / 1e3) / 1e9, 1) for k in kinds},
         "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(dom, wl),
                      "traffic_unit": "HBM bytes per launch (rocprofv3 counters)",
-                     "bytes_per_launch": nbytes, "avg_launch_ms": round(avg_ms, 4)},
+                     "bytes_per_launch": bytes_kind[dom] // launches[dom],
+                     "avg_launch_ms": round(ms_kind[dom] / launches[dom], 4)},
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args)

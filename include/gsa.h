@@ -172,7 +172,8 @@ gsa_status gsa_sparse_mla_attn(const void* q_lat_dev, const void* q_rope_dev, co
  * index_buf_dev int32 [n_q, k], owned by the caller, who keeps it consistent
  *                    with the prefix and positions it was computed for.
  * scores_dev   fp32 [n_q, ld_scores] scratch for the F layer's scores.
- * workspace    at least gsa_group_workspace_bytes(n_q, ld_scores, k, n_heads).
+ * workspace    at least gsa_group_workspace_bytes(n_q, ld_scores, k, n_heads, n_layers).
+ * Attention for all n_layers layers runs as gsa_sparse_mla_attn_layers.
  */
 typedef struct gsa_mla_layer {
     const void* q_lat_dev;     /* bf16 [n_q, n_heads, 512] */
@@ -196,8 +197,29 @@ typedef struct gsa_group_desc {
     void* workspace_dev; size_t workspace_bytes;
 } gsa_group_desc;
 
-size_t gsa_group_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads);
+/* workspace of a group with n_layers attention layers (the full layer included) */
+size_t gsa_group_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads, int n_layers);
 gsa_status gsa_indexshare_group(const gsa_group_desc* desc, void* stream);
+
+/*
+ * gsa_sparse_mla_attn_layers — gsa_sparse_mla_attn for n_layers layers that
+ * attend over the same index buffer, the layers of one IndexShare group
+ * ([Serving] §10: the indexer runs once per group, then every layer gathers
+ * from its own cache and attends; [Arch] §2.2: the same index set serves the
+ * full layer and its shared layers). The layers are independent given the
+ * indices, so they run in one launch (per 8 layers), which lets a small batch
+ * fill the chip with fewer row splits per query.
+ *
+ * layers        host array of n_layers gsa_mla_layer (each layer's own q, cache, out, lse).
+ * The other arguments mean what they mean in gsa_sparse_mla_attn.
+ * workspace_dev at least gsa_mla_layers_workspace_bytes(n_q, n_heads, k, n_layers) bytes.
+ * Errors as gsa_sparse_mla_attn, checked for every layer before anything is enqueued.
+ */
+size_t gsa_mla_layers_workspace_bytes(int n_q, int n_heads, int k, int n_layers);
+gsa_status gsa_sparse_mla_attn_layers(const gsa_mla_layer* layers, int n_layers,
+                                      const int32_t* q_seq_dev, const int32_t* idx_dev, int k,
+                                      int n_q, int n_heads, int batch, int64_t n_cap, float scale,
+                                      void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
  * gsa_layer_pattern — which layers run the indexer in GLM-5.2's layer stack
@@ -229,7 +251,8 @@ int gsa_layer_pattern(int n_layers, int32_t* src);
  *               index_stride = 0 reuses one buffer (enough for the stack
  *               itself, since each group reads only its own full layer's
  *               indices); otherwise index_stride >= n_q * k, a multiple of 4.
- * workspace     at least gsa_group_workspace_bytes(n_q, ld_scores, k, n_heads).
+ * workspace     at least gsa_stack_workspace_bytes(n_q, ld_scores, k, n_heads, n_layers)
+ *               (the largest need of its groups).
  * The other fields mean what they mean in gsa_group_desc.
  */
 typedef struct gsa_indexer_layer {
@@ -250,6 +273,7 @@ typedef struct gsa_stack_desc {
     void* workspace_dev; size_t workspace_bytes;
 } gsa_stack_desc;
 
+size_t gsa_stack_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads, int n_layers);
 gsa_status gsa_layer_stack(const gsa_stack_desc* desc, void* stream);
 
 #ifdef __cplusplus

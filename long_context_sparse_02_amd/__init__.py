@@ -78,7 +78,10 @@ def _declare(lib):
         "gsa_topk": (I, [P, I64, P, I, I, P, P, SZ, P]),
         "gsa_mla_workspace_bytes": (SZ, [I, I, I]),
         "gsa_sparse_mla_attn": (I, [P, P, P, P, P, I, I, I, I, I64, F, P, P, P, SZ, P]),
-        "gsa_group_workspace_bytes": (SZ, [I, I64, I, I]),
+        "gsa_group_workspace_bytes": (SZ, [I, I64, I, I, I]),
+        "gsa_stack_workspace_bytes": (SZ, [I, I64, I, I, I]),
+        "gsa_mla_layers_workspace_bytes": (SZ, [I, I, I, I]),
+        "gsa_sparse_mla_attn_layers": (I, [ctypes.POINTER(_MlaLayer), I, P, P, I, I, I, I, I64, F, P, SZ, P]),
         "gsa_indexshare_group": (I, [ctypes.POINTER(_GroupDesc), P]),
         "gsa_layer_pattern": (I, [I, P]),
         "gsa_layer_stack": (I, [ctypes.POINTER(_StackDesc), P]),
@@ -171,8 +174,16 @@ def mla_workspace_bytes(n_q, n_heads=MLA_HEADS, k=TOPK):
     return int(lib().gsa_mla_workspace_bytes(n_q, n_heads, k))
 
 
-def group_workspace_bytes(n_q, ld, k=TOPK, n_heads=MLA_HEADS):
-    return int(lib().gsa_group_workspace_bytes(n_q, ld, k, n_heads))
+def mla_layers_workspace_bytes(n_q, n_layers, n_heads=MLA_HEADS, k=TOPK):
+    return int(lib().gsa_mla_layers_workspace_bytes(n_q, n_heads, k, n_layers))
+
+
+def group_workspace_bytes(n_q, ld, n_layers=4, k=TOPK, n_heads=MLA_HEADS):
+    return int(lib().gsa_group_workspace_bytes(n_q, ld, k, n_heads, n_layers))
+
+
+def stack_workspace_bytes(n_q, ld, n_layers=78, k=TOPK, n_heads=MLA_HEADS):
+    return int(lib().gsa_stack_workspace_bytes(n_q, ld, k, n_heads, n_layers))
 
 
 def _workspace(nbytes, device, ws):
@@ -218,6 +229,35 @@ def sparse_mla_attn(q_lat, q_rope, kv, q_seq, idx, scale=1.0 / 16.0, out=None, l
     return out, lse
 
 
+def sparse_mla_attn_layers(layers, q_seq, idx, scale=1.0 / 16.0, outs=None, workspace=None):
+    """Attention for several layers over one index buffer (the layers of an
+    IndexShare group) in one launch: layers = [(q_lat, q_rope, kv), ...].
+    Returns [(out, lse)] per layer."""
+    n_q = q_seq.shape[0]
+    kv0 = layers[0][2]
+    batch, n_cap = kv0.shape[0], kv0.shape[1]
+    _need(q_seq, "q_seq", torch.int32, (n_q,))
+    _need(idx, "idx", torch.int32)
+    k = idx.shape[1]
+    dev = q_seq.device
+    for ql, qr, kv in layers:
+        _need(ql, "q_lat", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
+        _need(qr, "q_rope", torch.bfloat16, (n_q, MLA_HEADS, ROPE_DIM))
+        _need(kv, "kv", torch.bfloat16, (batch, n_cap, KV_ROW))
+    if outs is None:
+        outs = [(torch.empty((n_q, MLA_HEADS, LATENT_DIM), dtype=torch.float32, device=dev),
+                 torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)) for _ in layers]
+    arr = (_MlaLayer * len(layers))()
+    for i, ((ql, qr, kv), (o, s)) in enumerate(zip(layers, outs)):
+        arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
+                           None if s is None else s.data_ptr())
+    ws = _workspace(mla_layers_workspace_bytes(n_q, len(layers), MLA_HEADS, k), dev, workspace)
+    _check(lib().gsa_sparse_mla_attn_layers(ctypes.cast(arr, ctypes.POINTER(_MlaLayer)), len(layers),
+                                            _p(q_seq), _p(idx), k, n_q, MLA_HEADS, batch, n_cap, scale,
+                                            _p(ws), ws.numel(), _stream(dev)))
+    return outs
+
+
 def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_idx=None,
                      q_scale=None, k_scale=None, scores=None, compute_index=True,
                      scale=1.0 / 16.0, workspace=None, outs=None):
@@ -244,7 +284,8 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     for i, ((ql, qr, kv), (o, s)) in enumerate(zip(layers, outs)):
         arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
                            None if s is None else s.data_ptr())
-    nbytes = group_workspace_bytes(n_q, ld, k) if compute_index else mla_workspace_bytes(n_q, MLA_HEADS, k)
+    nbytes = (group_workspace_bytes(n_q, ld, len(layers), k) if compute_index
+              else mla_layers_workspace_bytes(n_q, len(layers), MLA_HEADS, k))
     ws = _workspace(nbytes, dev, workspace)
     d = _GroupDesc()
     d.compute_index = 1 if compute_index else 0
@@ -310,7 +351,7 @@ def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_st
     for i, ((ql, qr, kv), (o, s)) in enumerate(zip(layers, outs)):
         arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
                            None if s is None else s.data_ptr())
-    ws = _workspace(group_workspace_bytes(n_q, ld, k), dev, workspace)
+    ws = _workspace(stack_workspace_bytes(n_q, ld, len(layers), k), dev, workspace)
     d = _StackDesc()
     d.n_layers, d.dt = len(layers), FP8_E4M3 if fp8 else BF16
     d.indexers = ctypes.cast(xs, ctypes.POINTER(_IndexerLayer))

@@ -67,9 +67,11 @@ gsa_status check_topk(const float* scores, int64_t ld, const int32_t* q_pos, int
     return GSA_OK;
 }
 
+// One attention layer's checks; the workspace must serve n_layers layers launched together.
 gsa_status check_mla(const void* q_lat, const void* q_rope, const void* kv, const int32_t* q_seq,
                      const int32_t* idx, int k, int n_q, int n_heads, int batch, int64_t n_cap,
-                     float scale, const float* out, const float* lse, const void* ws, size_t ws_bytes) {
+                     float scale, const float* out, const float* lse, const void* ws, size_t ws_bytes,
+                     int n_layers) {
     REQUIRE_PTR(q_lat); REQUIRE_PTR(q_rope); REQUIRE_PTR(kv); REQUIRE_PTR(q_seq); REQUIRE_PTR(idx);
     REQUIRE_PTR(out);
     if (lse != nullptr) REQUIRE(aligned16(lse), "lse is not 16-byte aligned");
@@ -80,10 +82,29 @@ gsa_status check_mla(const void* q_lat, const void* q_rope, const void* kv, cons
     if (n_heads != 64) return fail(GSA_ERR_UNSUPPORTED, "n_heads must be 64 (got %d)", n_heads);
     if (k != GSA_TOPK) return fail(GSA_ERR_UNSUPPORTED, "k must be %d (got %d)", GSA_TOPK, k);
     REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
-    const size_t need = gsa::mla_workspace_bytes(n_q, n_heads, k);
+    const size_t need = gsa::mla_workspace_bytes(n_q, n_heads, k, n_layers);
     if (need > 0 && (ws == nullptr || ws_bytes < need))
         return fail(GSA_ERR_WORKSPACE, "attention workspace needs %zu bytes (got %zu)", need, ws_bytes);
     if (need > 0) REQUIRE(aligned16(ws), "workspace is not 16-byte aligned");
+    return GSA_OK;
+}
+
+// Attention for layers that share one index buffer, in one launch per 8 layers.
+gsa_status enqueue_attention(const gsa_mla_layer* layers, int n_layers, const int32_t* q_seq,
+                             const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
+                             float scale, void* ws, hipStream_t s) {
+    gsa::MlaLayerPtrs ptrs[8];
+    for (int l0 = 0; l0 < n_layers; l0 += 8) {
+        const int nl = n_layers - l0 < 8 ? n_layers - l0 : 8;
+        for (int i = 0; i < nl; ++i)
+            ptrs[i] = {layers[l0 + i].q_lat_dev, layers[l0 + i].q_rope_dev, layers[l0 + i].kv_dev,
+                       layers[l0 + i].out_dev, layers[l0 + i].lse_dev};
+        // the workspace was sized for n_layers; a later launch of fewer layers needs no more
+        const hipError_t e = gsa::launch_sparse_mla_layers(ptrs, nl, q_seq, idx, k, n_q, n_heads, n_cap,
+                                                           scale, ws, s);
+        if (e != hipSuccess) return hip_result(e, "sparse_mla_attn");
+    }
+    g_err[0] = 0;
     return GSA_OK;
 }
 
@@ -138,26 +159,62 @@ gsa_status gsa_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n
 }
 
 size_t gsa_mla_workspace_bytes(int n_q, int n_heads, int k) {
-    if (n_q < 1 || n_heads != 64 || k != GSA_TOPK) return 0;
-    return gsa::mla_workspace_bytes(n_q, n_heads, k);
+    return gsa_mla_layers_workspace_bytes(n_q, n_heads, k, 1);
+}
+
+size_t gsa_mla_layers_workspace_bytes(int n_q, int n_heads, int k, int n_layers) {
+    if (n_q < 1 || n_heads != 64 || k != GSA_TOPK || n_layers < 1) return 0;
+    return gsa::mla_workspace_bytes(n_q, n_heads, k, n_layers);
 }
 
 gsa_status gsa_sparse_mla_attn(const void* q_lat, const void* q_rope, const void* kv,
                                const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
                                int batch, int64_t n_cap, float scale, float* out, float* lse,
                                void* ws, size_t ws_bytes, void* stream) {
-    gsa_status st = check_mla(q_lat, q_rope, kv, q_seq, idx, k, n_q, n_heads, batch, n_cap, scale,
-                              out, lse, ws, ws_bytes);
-    if (st != GSA_OK) return st;
-    return hip_result(gsa::launch_sparse_mla(q_lat, q_rope, kv, q_seq, idx, k, n_q, n_heads, n_cap,
-                                             scale, out, lse, ws, (hipStream_t)stream),
-                      "sparse_mla_attn");
+    const gsa_mla_layer layer = {q_lat, q_rope, kv, out, lse};
+    return gsa_sparse_mla_attn_layers(&layer, 1, q_seq, idx, k, n_q, n_heads, batch, n_cap, scale, ws,
+                                      ws_bytes, stream);
 }
 
-size_t gsa_group_workspace_bytes(int n_q, int64_t ld, int k, int n_heads) {
+gsa_status gsa_sparse_mla_attn_layers(const gsa_mla_layer* layers, int n_layers, const int32_t* q_seq,
+                                      const int32_t* idx, int k, int n_q, int n_heads, int batch,
+                                      int64_t n_cap, float scale, void* ws, size_t ws_bytes,
+                                      void* stream) {
+    REQUIRE(n_layers >= 1, "n_layers must be >= 1 (got %d)", n_layers);
+    REQUIRE(layers != nullptr, "layers is NULL");
+    for (int l = 0; l < n_layers; ++l) {
+        const gsa_status st = check_mla(layers[l].q_lat_dev, layers[l].q_rope_dev, layers[l].kv_dev, q_seq,
+                                        idx, k, n_q, n_heads, batch, n_cap, scale, layers[l].out_dev,
+                                        layers[l].lse_dev, ws, ws_bytes, n_layers);
+        if (st != GSA_OK) {
+            if (n_layers > 1) {
+                char tmp[512];
+                snprintf(tmp, sizeof(tmp), "layer %d: %s", l, g_err);
+                snprintf(g_err, sizeof(g_err), "%s", tmp);
+            }
+            return st;
+        }
+    }
+    return enqueue_attention(layers, n_layers, q_seq, idx, k, n_q, n_heads, n_cap, scale, ws,
+                             (hipStream_t)stream);
+}
+
+size_t gsa_group_workspace_bytes(int n_q, int64_t ld, int k, int n_heads, int n_layers) {
     const size_t a = gsa_topk_workspace_bytes(n_q, ld, k);
-    const size_t b = gsa_mla_workspace_bytes(n_q, n_heads, k);
+    const size_t b = gsa_mla_layers_workspace_bytes(n_q, n_heads, k, n_layers);
     return a > b ? a : b;     // top-k finishes (stream order) before attention reuses the space
+}
+
+size_t gsa_stack_workspace_bytes(int n_q, int64_t ld, int k, int n_heads, int n_layers) {
+    size_t need = 0;
+    for (int i = 0; i < n_layers; ++i) {                   // every group: a full layer + the shared after it
+        if (!(i < 3 || i % 4 == 2)) continue;
+        int len = 1;
+        while (i + len < n_layers && !(i + len < 3 || (i + len) % 4 == 2)) ++len;
+        const size_t g = gsa_group_workspace_bytes(n_q, ld, k, n_heads, len);
+        need = g > need ? g : need;
+    }
+    return need;
 }
 
 }  // extern "C"
@@ -184,7 +241,7 @@ gsa_status validate_group(const gsa_group_desc* d) {
         const gsa_mla_layer& L = d->layers[l];
         gsa_status st = check_mla(L.q_lat_dev, L.q_rope_dev, L.kv_dev, d->q_seq_dev, d->index_buf_dev,
                                   d->k, d->n_q, d->n_heads, d->batch, d->n_cap, d->scale, L.out_dev,
-                                  L.lse_dev, d->workspace_dev, d->workspace_bytes);
+                                  L.lse_dev, d->workspace_dev, d->workspace_bytes, d->n_layers);
         if (st != GSA_OK) {
             char tmp[512];
             snprintf(tmp, sizeof(tmp), "layer %d: %s", l, g_err);
@@ -207,13 +264,9 @@ gsa_status enqueue_group(const gsa_group_desc* d, hipStream_t s) {
                              d->workspace_dev, s);
         if (e != hipSuccess) return hip_result(e, "group: topk");
     }
-    for (int l = 0; l < d->n_layers; ++l) {
-        const gsa_mla_layer& L = d->layers[l];
-        hipError_t e = gsa::launch_sparse_mla(L.q_lat_dev, L.q_rope_dev, L.kv_dev, d->q_seq_dev,
-                                              d->index_buf_dev, d->k, d->n_q, d->n_heads, d->n_cap,
-                                              d->scale, L.out_dev, L.lse_dev, d->workspace_dev, s);
-        if (e != hipSuccess) return hip_result(e, "group: sparse_mla_attn");
-    }
+    if (d->n_layers > 0)
+        return enqueue_attention(d->layers, d->n_layers, d->q_seq_dev, d->index_buf_dev, d->k, d->n_q,
+                                 d->n_heads, d->n_cap, d->scale, d->workspace_dev, s);
     return GSA_OK;
 }
 

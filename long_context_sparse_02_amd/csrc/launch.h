@@ -20,10 +20,19 @@ size_t topk_workspace_bytes(int n_q, int64_t ld, int k);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
                        int32_t* idx, void* ws, hipStream_t stream);
 
-size_t mla_workspace_bytes(int n_q, int n_heads, int k);
-hipError_t launch_sparse_mla(const void* q_lat, const void* q_rope, const void* kv,
-                             const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
-                             int64_t n_cap, float scale, float* out, float* lse, void* ws,
-                             hipStream_t stream);
+// One attention layer's operands (a layer of an IndexShare group).
+struct MlaLayerPtrs {
+    const void* q_lat;
+    const void* q_rope;
+    const void* kv;
+    float* out;
+    float* lse;
+};
+
+// Workspace for attention over n_layers layers that share one index buffer.
+size_t mla_workspace_bytes(int n_q, int n_heads, int k, int n_layers);
+hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, const int32_t* q_seq,
+                                    const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
+                                    float scale, void* ws, hipStream_t stream);
 
 }  // namespace gsa

@@ -63,6 +63,7 @@ constexpr int kDmaHi = kDmaLo + 1;              // 5
 constexpr int kRing = 3;                        // LDS blocks in the ring
 constexpr int kMaxRows = 2048;
 constexpr float kRescale = 8.0f;                // lazy-rescale threshold (log2 units)
+constexpr int kMaxLayersPerLaunch = 8;
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -72,6 +73,17 @@ __shared__ int32_t g_rows[kMaxRows];
 __shared__ f32x4 g_xs[kWaves][2][64];           // partial S^T of each wave (2 KiB per wave)
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Per-layer operands of one launch (kernel argument, indexed by blockIdx.z):
+// the layers of an IndexShare group share the index buffer and are independent
+// otherwise, so one launch covers all of them.
+struct LayerArgs {
+    const uint8_t* q_lat[kMaxLayersPerLaunch];
+    const uint8_t* q_rope[kMaxLayersPerLaunch];
+    const uint8_t* kv[kMaxLayersPerLaunch];
+    float* out[kMaxLayersPerLaunch];
+    float* lse[kMaxLayersPerLaunch];
+};
 
 // s_waitcnt lgkmcnt(0) alone: this wave's LDS writes have landed
 __device__ __forceinline__ void wait_lgkm0() { __builtin_amdgcn_s_waitcnt(0xC07F); }
@@ -99,11 +111,18 @@ __device__ __forceinline__ void wait_block(int later) {
 }
 
 __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
-    const uint8_t* __restrict__ q_lat, const uint8_t* __restrict__ q_rope,
-    const uint8_t* __restrict__ kv, const int32_t* __restrict__ q_seq,
-    const int32_t* __restrict__ idx, int k, int64_t n_cap, float scale_log2, int rows_per_split,
-    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ part_o,
-    float* __restrict__ part_ml) {
+    LayerArgs L, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ idx, int k,
+    int n_q, int64_t n_cap, float scale_log2, int rows_per_split, float* __restrict__ part_o_all,
+    float* __restrict__ part_ml_all) {
+    // this work-group's layer (uniform): its operands and its part of the workspace
+    const int layer = blockIdx.z;
+    const uint8_t* __restrict__ q_lat = L.q_lat[layer];
+    const uint8_t* __restrict__ q_rope = L.q_rope[layer];
+    const uint8_t* __restrict__ kv = L.kv[layer];
+    float* __restrict__ out = L.out[layer];
+    float* __restrict__ lse = L.lse[layer];
+    float* __restrict__ part_o = part_o_all + (size_t)layer * n_q * gridDim.x * kHeads * kLat;
+    float* __restrict__ part_ml = part_ml_all + (size_t)layer * n_q * gridDim.x * kHeads * 2;
     int32_t* rows_s = g_rows;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
@@ -284,10 +303,15 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 
 // Combine the per-split partial results with their log-sum-exp. Grid
 // (n_q, 16): a work-group merges 4 heads x 512 dims of one query.
-__global__ __launch_bounds__(256) void sparse_mla_merge(const float* __restrict__ part_o,
-                                                             const float* __restrict__ part_ml,
-                                                             int n_split, float* __restrict__ out,
-                                                             float* __restrict__ lse) {
+__global__ __launch_bounds__(256) void sparse_mla_merge(LayerArgs L, int n_q,
+                                                             const float* __restrict__ part_o_all,
+                                                             const float* __restrict__ part_ml_all,
+                                                             int n_split) {
+    const int layer = blockIdx.z;
+    float* __restrict__ out = L.out[layer];
+    float* __restrict__ lse = L.lse[layer];
+    const float* __restrict__ part_o = part_o_all + (size_t)layer * n_q * n_split * kHeads * kLat;
+    const float* __restrict__ part_ml = part_ml_all + (size_t)layer * n_q * n_split * kHeads * 2;
     const int q = blockIdx.x;
     const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
     const int c = threadIdx.x & 63;              // float4 columns c and c + 64
@@ -313,37 +337,54 @@ __global__ __launch_bounds__(256) void sparse_mla_merge(const float* __restrict_
         lse[(int64_t)q * kHeads + h] = lsum > 0.f ? (mx + log2f(lsum)) * 0.69314718055994531f : neg_inf();
 }
 
-int choose_split(int n_q, int k) {
+// Splits per (layer, query) so that about 256 work-groups run.
+int choose_split(int units, int k) {
     int s = 1;
-    while (s < 32 && n_q * s < 256 && (k / (2 * s)) % kBlk == 0 && k / (2 * s) >= kBlk) s *= 2;
+    while (s < 32 && units * s < 256 && (k / (2 * s)) % kBlk == 0 && k / (2 * s) >= kBlk) s *= 2;
     return s;
 }
 
 }  // namespace
 
-size_t mla_workspace_bytes(int n_q, int n_heads, int k) {
-    const int s = choose_split(n_q, k);
+size_t mla_workspace_bytes(int n_q, int n_heads, int k, int n_layers) {
+    (void)n_heads;
+    if (n_layers < 1) return 0;
+    const int per = n_layers < kMaxLayersPerLaunch ? n_layers : kMaxLayersPerLaunch;
+    const int s = choose_split(n_q * per, k);
     if (s == 1) return 0;
-    return (size_t)n_q * s * n_heads * (kLat + 2) * sizeof(float);
+    return (size_t)per * n_q * s * kHeads * (kLat + 2) * sizeof(float);
 }
 
-hipError_t launch_sparse_mla(const void* q_lat, const void* q_rope, const void* kv,
-                             const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
-                             int64_t n_cap, float scale, float* out, float* lse, void* ws,
-                             hipStream_t st) {
+hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, const int32_t* q_seq,
+                                    const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
+                                    float scale, void* ws, hipStream_t st) {
     (void)n_heads;
-    const int s = choose_split(n_q, k);
-    const int rows = k / s;
-    float* part_o = (float*)ws;
-    float* part_ml = s > 1 ? part_o + (size_t)n_q * s * kHeads * kLat : nullptr;
     const float scale_log2 = scale * 1.4426950408889634f;
-    hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, n_q), dim3(kThreads), 0, st,
-                       (const uint8_t*)q_lat, (const uint8_t*)q_rope, (const uint8_t*)kv, q_seq, idx,
-                       k, n_cap, scale_log2, rows, out, lse, part_o, part_ml);
-    if (s > 1)
-        hipLaunchKernelGGL(sparse_mla_merge, dim3(n_q, kHeads / 4), dim3(256), 0, st, part_o,
-                           part_ml, s, out, lse);
-    return hipGetLastError();
+    for (int l0 = 0; l0 < n_layers; l0 += kMaxLayersPerLaunch) {
+        const int nl = n_layers - l0 < kMaxLayersPerLaunch ? n_layers - l0 : kMaxLayersPerLaunch;
+        LayerArgs L{};
+        for (int i = 0; i < nl; ++i) {
+            L.q_lat[i] = (const uint8_t*)layers[l0 + i].q_lat;
+            L.q_rope[i] = (const uint8_t*)layers[l0 + i].q_rope;
+            L.kv[i] = (const uint8_t*)layers[l0 + i].kv;
+            L.out[i] = layers[l0 + i].out;
+            L.lse[i] = layers[l0 + i].lse;
+        }
+        // the split is chosen for a full launch, so every launch fits the workspace
+        const int per = n_layers < kMaxLayersPerLaunch ? n_layers : kMaxLayersPerLaunch;
+        const int s = choose_split(n_q * per, k);
+        const int rows = k / s;
+        float* part_o = (float*)ws;
+        float* part_ml = s > 1 ? part_o + (size_t)per * n_q * s * kHeads * kLat : nullptr;
+        hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq, idx, k,
+                           n_q, n_cap, scale_log2, rows, part_o, part_ml);
+        if (s > 1)
+            hipLaunchKernelGGL(sparse_mla_merge, dim3(n_q, kHeads / 4, nl), dim3(256), 0, st, L, n_q,
+                               part_o, part_ml, s);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
 }
 
 }  // namespace gsa

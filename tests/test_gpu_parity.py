@@ -228,12 +228,45 @@ def test_group_tiny(dtype):
 
 
 def test_group_s_only_call_reuses_buffer_and_is_deterministic():
+    # an S-only call over the F layer's buffer reproduces the group's S layers (to the
+    # attention tolerance: a call over fewer layers may split rows differently), and
+    # repeating the same call gives the same bits
     wl = W.WORKLOADS["group_b1_n4096_q4"]
     idx, outs = _group_case(wl, 1)
     g = W.group_inputs(wl, 1, n_layers=4)
     d = dev()
     layers = [tuple(t.to(d) for t in L) for L in g.layers[1:]]
     outs2 = gsa.indexshare_group(layers, g.q_seq.to(d), idx, compute_index=False)
+    outs3 = gsa.indexshare_group(layers, g.q_seq.to(d), idx, compute_index=False)
     torch.cuda.synchronize()
-    for (o1, s1), (o2, s2) in zip(outs[1:], outs2):
-        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    for (o1, s1), (o2, s2), (o3, s3) in zip(outs[1:], outs2, outs3):
+        assert max_abs(np32(o1), np32(o2)) <= ATOL_OUT and max_abs(np32(s1), np32(s2)) <= ATOL_LSE
+        assert torch.equal(o2, o3) and torch.equal(s2, s3)
+
+
+@pytest.mark.parametrize("n_layers,n_q,batch", [(3, 2, 1), (4, 8, 8), (9, 5, 2)])
+def test_sparse_mla_layers_launch_matches_oracle(n_layers, n_q, batch):
+    # one launch over several layers sharing the index buffer (9 layers: two launches);
+    # the split per query depends on layers x queries, so every case splits differently
+    wl = W.Workload("mla_layers", batch, 3000, n_q // batch if n_q % batch == 0 else 1, n_layers, "bf16")
+    q_seq = torch.arange(n_q, dtype=torch.int32) % batch
+    q_pos = torch.full((n_q,), 2999, dtype=torch.int32)
+    g = torch.Generator().manual_seed(40 + n_layers)
+    idx = torch.stack([torch.sort(torch.randperm(3000, generator=g)[:2048])[0] for _ in range(n_q)]).to(torch.int32)
+    idx[0, 2000:] = -1                                      # a ragged row
+    d = dev()
+    layers_cpu = []
+    for l in range(n_layers):
+        ql, qr = W.mla_queries(W.Workload("x", batch, 3000, 1, 1, "bf16"), 7, l)
+        ql, qr = ql[:1].repeat(n_q, 1, 1), qr[:1].repeat(n_q, 1, 1)
+        ql = ql + 0.25 * torch.randn(ql.shape, generator=g).to(torch.bfloat16)
+        layers_cpu.append((ql, qr, W.mla_cache(W.Workload("x", batch, 3000, 1, 1, "bf16"), 7, l)))
+    layers = [tuple(t.to(d) for t in L) for L in layers_cpu]
+    outs = gsa.sparse_mla_attn_layers(layers, q_seq.to(d), idx.to(d), 1 / 16)
+    torch.cuda.synchronize()
+    for l, ((o, s), (ql, qr, kv)) in enumerate(zip(outs, layers_cpu)):
+        wo, ws = oracle.sparse_mla(np32(ql), np32(qr), np32(kv), np32(q_seq), np32(idx), 1 / 16)
+        eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
+        say(f"layers launch {n_layers}x{n_q}: layer {l} out err {eo:.2e} lse err {el:.2e}")
+        assert eo <= ATOL_OUT and el <= ATOL_LSE
+    del q_pos
