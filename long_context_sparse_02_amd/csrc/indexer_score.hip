@@ -16,7 +16,7 @@
 // heads) stays in registers: each lane holds 16 heads of one key and one
 // cross-lane add finishes the sum, so only the final fp32 score reaches HBM.
 //
-// Keys stream through LDS in 128-key tiles with LDS-DMA (global_load_lds:
+// Keys stream through LDS in 32 KiB tiles (128 bf16 or 256 fp8 keys) with LDS-DMA (global_load_lds:
 // whole 1 KiB key blocks per wave instruction, no staging registers) into a
 // ring of kRing slots, so kRing - 1 tiles are in flight per work-group. The
 // DMA source chunk of each lane is chosen so that 16-byte chunks land XOR-
@@ -37,15 +37,17 @@ constexpr int kTile = 128;      // keys per LDS tile
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kRing = 4;        // LDS tile slots
 
-template <bool FP8>
+template <bool FP8, int KEYS = kTile>
 struct KeyTile {
+    static constexpr int kKeys = KEYS;                          // keys per tile
     static constexpr int kRowBytes = FP8 ? kDim : kDim * 2;
     static constexpr int kChunks = kRowBytes / 16;              // 16-byte chunks per key row
-    static constexpr int kBytes = kTile * kRowBytes;
+    static constexpr int kBytes = KEYS * kRowBytes;
     static constexpr int kRowsPerDma = 1024 / kRowBytes;        // key rows per 1 KiB DMA
-    static constexpr int kDma = kBytes / 1024;                  // 32 (bf16) or 16 (fp8)
+    static constexpr int kDma = kBytes / 1024;
     static constexpr int kDmaPerWave = kDma / 4;
-    static constexpr int kScaleBytes = FP8 ? 512 : 0;           // fp32 scale per key (2 x 256 B DMA)
+    static constexpr int kScaleDma = FP8 ? KEYS / 64 : 0;       // 256-byte DMAs of fp32 scales
+    static constexpr int kScaleBytes = 256 * kScaleDma;
     static constexpr int kSlot = kBytes + kScaleBytes;
     // byte offset of logical chunk c of tile row r (XOR swizzle over the row's chunks)
     __device__ static __forceinline__ int off(int r, int c) {
@@ -60,8 +62,13 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int n_q, int64_t n_cap,
     float* __restrict__ scores, int64_t ld, int chunk) {
-    using T = KeyTile<FP8>;
-    constexpr int QPW = QB >= 4 ? QB / 4 : 1;   // queries per wave
+    // fp8 tiles hold 256 keys, so every tile moves 32 KiB like a bf16 tile and the
+    // per-tile barrier and waits are paid per 32 KiB either way
+    using T = KeyTile<FP8, FP8 ? 256 : 128>;
+    static_assert(QB <= 2, "one or two queries per work-group");
+    constexpr int NSUBT = T::kKeys / 32;         // 32-key subtiles per tile
+    constexpr int PPW = QB * NSUBT / 4;          // (query, subtile) pairs per wave
+    constexpr int QPW = 1;                       // queries per wave
     constexpr int KSTEPS = FP8 ? 2 : 8;         // MFMA steps over 128 dims
     using AVec = std::conditional_t<FP8, i32x8, bf16x8>;
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -113,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     wait_vmcnt<0>();   // operands are in registers before any ring load is counted
 
     // DMA instructions per tile issued by this wave (wave 0 also moves the fp8 scales)
-    const int per = T::kDmaPerWave + ((FP8 && wave == 0) ? 2 : 0);
+    const int per = T::kDmaPerWave + ((FP8 && wave == 0) ? T::kScaleDma : 0);
     const uint32_t ring_base = (uint32_t)(uintptr_t)(lds_u8*)ring;
 
     // Queries of the block are processed in runs that share a sequence.
@@ -130,18 +137,18 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
         const float* ksb = FP8 ? k_scale + (int64_t)seq * n_cap : nullptr;
         // tiles [0, na) hold keys at or before the run's last position; later ones are masked
         const int64_t t_end = min(c1, (int64_t)maxpos + 1);
-        const int na = t_end > c0 ? (int)((t_end - c0 + kTile - 1) / kTile) : 0;
-        const int nt_all = (int)((c1 - c0 + kTile - 1) / kTile);
+        const int na = t_end > c0 ? (int)((t_end - c0 + T::kKeys - 1) / T::kKeys) : 0;
+        const int nt_all = (int)((c1 - c0 + T::kKeys - 1) / T::kKeys);
         // score stores this wave issues per tile in this run (one per owned pair in the run)
         int stores = 0;
 #pragma unroll
-        for (int p = 0; p < QB; ++p) {
-            const int j = (wave * QB + p) >> 2;
+        for (int p = 0; p < PPW; ++p) {
+            const int j = (wave * PPW + p) / NSUBT;
             stores += (j >= j0 && j < j1) ? 1 : 0;
         }
 
         auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
-            const int64_t t0 = c0 + (int64_t)ti * kTile;
+            const int64_t t0 = c0 + (int64_t)ti * T::kKeys;
             const uint32_t dst = ring_base + slot * T::kSlot;
 #pragma unroll
             for (int jd = 0; jd < T::kDmaPerWave; ++jd) {
@@ -155,7 +162,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
             if constexpr (FP8) {
                 if (wave == 0) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < T::kScaleDma; ++h) {
                         const int64_t krow = min(t0 + 64 * h + lane, c1 - 1);
                         lds_dma4(ksb + krow, dst + T::kBytes + 256 * h);
                     }
@@ -166,7 +173,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
         for (int p = 0; p < kRing - 1; ++p)
             if (p < na) issue(p, p);
         for (int ti = 0; ti < nt_all; ++ti) {
-            const int64_t t0 = c0 + (int64_t)ti * kTile;
+            const int64_t t0 = c0 + (int64_t)ti * T::kKeys;
             const bool active = ti < na;                 // uniform over the work-group
             const lds_u8* tile = (const lds_u8*)ring + (ti % kRing) * T::kSlot;
             if (active) {
@@ -174,14 +181,14 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
                 // DMAs of tiles ti+1 .. min(na, ti+kRing-1)-1 and the score stores of
                 // the iterations since tile ti was issued
                 const int later = min(na, ti + kRing - 1) - ti - 1;
-                wait_vmcnt_le<2 * 8 + 3 * 8>(later * per + stores * min(ti, kRing - 1));
+                wait_vmcnt_le<63>(later * per + stores * min(ti, kRing - 1));
                 ring_barrier();   // every wave's part of tile ti landed; tile ti-1's readers are done
                 if (ti + kRing - 1 < na) issue(ti + kRing - 1, (ti + kRing - 1) % kRing);
             }
 #pragma unroll
-            for (int p = 0; p < QB; ++p) {
-                const int pp = wave * QB + p;
-                const int j = pp >> 2, nt = pp & 3;
+            for (int p = 0; p < PPW; ++p) {
+                const int pp = wave * PPW + p;
+                const int j = pp / NSUBT, nt = pp % NSUBT;
                 const int jj = j - jw0;
                 if (j < j0 || j >= j1) continue;         // other run (wave-uniform)
                 const int64_t s0 = t0 + nt * 32;
@@ -294,7 +301,7 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
     }
     wait_vmcnt<0>();
 
-    const int per = kDmaPerWave + ((FP8 && wave == 0) ? 2 : 0);
+    const int per = kDmaPerWave + ((FP8 && wave == 0) ? T::kScaleDma : 0);
     const uint32_t ring_base = (uint32_t)(uintptr_t)(lds_u8*)ring;
 
     int j0 = 0;
@@ -335,7 +342,7 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
             if constexpr (FP8) {
                 if (wave == 0) {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
+                    for (int h = 0; h < T::kScaleDma; ++h) {
                         const int64_t krow = min(t0 + 64 * h + lane, c1 - 1);
                         lds_dma4(ksb + krow, dst + T::kBytes + 256 * h);
                     }
@@ -535,9 +542,13 @@ hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, c
     const int per_seq = n_q / (batch > 0 ? batch : 1);
     const int qb = per_seq >= 16 ? 16 : per_seq >= 8 ? 8 : per_seq >= 4 ? 4 : per_seq >= 2 ? 2 : 1;
     const int64_t n_qblk = (n_q + qb - 1) / qb;
-    // Key chunk per work-group: aim for >= 2048 work-groups, chunks of 1K..16K keys.
+    // Key chunk per work-group, 1K..16K keys. One query per work-group streams
+    // from HBM and wants many work-groups in flight (>= 2048); several queries
+    // per work-group are compute bound, and fewer, longer chunks (>= 512
+    // work-groups) save the ring refill each work-group start costs.
+    const int64_t min_wg = qb >= 4 ? 512 : 2048;
     int64_t chunk = 16384;
-    while (chunk > 1024 && n_qblk * ((n_cap + chunk - 1) / chunk) < 2048) chunk >>= 1;
+    while (chunk > 1024 && n_qblk * ((n_cap + chunk - 1) / chunk) < min_wg) chunk >>= 1;
     const dim3 grid((unsigned)((n_cap + chunk - 1) / chunk), (unsigned)n_qblk);
     switch (qb) {
         case 16: return launch_mq<16>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
