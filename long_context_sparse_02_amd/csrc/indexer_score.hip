@@ -242,17 +242,22 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int n_q, int64_t n_cap,
     float* __restrict__ scores, int64_t ld, int chunk) {
-    using T = KeyTile<FP8>;
+    // 64 KiB tiles (256 bf16 / 512 fp8 keys) in a 2-slot ring: the keys come from
+    // L2 (every work-group of a chunk reads the same ones), so one tile in flight
+    // covers the latency, and the barrier and DMA issue are paid per 64 KiB
+    using T = KeyTile<FP8, FP8 ? 512 : 256>;
+    constexpr int kRingMq = 2;
     constexpr int QPW = 2;                       // queries per wave
     constexpr int NQP = QB / QPW;                // query pairs per work-group
-    constexpr int NSUB = 4 * NQP / kMqWaves;     // subtiles per wave per tile
+    constexpr int NT = T::kKeys / 32;            // 32-key subtiles per tile
+    constexpr int NSUB = NT * NQP / kMqWaves;    // subtiles per wave per tile
     static_assert(QB == 4 || QB == 8 || QB == 16, "QB");
     constexpr int KSTEPS = FP8 ? 2 : 8;
     constexpr int kDmaPerWave = T::kDma / kMqWaves;
     using AVec = std::conditional_t<FP8, i32x8, bf16x8>;
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
-    __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * T::kSlot];
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRingMq * T::kSlot];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -316,8 +321,8 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
         const uint8_t* kb = k + (int64_t)seq * n_cap * T::kRowBytes;
         const float* ksb = FP8 ? k_scale + (int64_t)seq * n_cap : nullptr;
         const int64_t t_end = min(c1, (int64_t)maxpos + 1);
-        const int na = t_end > c0 ? (int)((t_end - c0 + kTile - 1) / kTile) : 0;
-        const int nt_all = (int)((c1 - c0 + kTile - 1) / kTile);
+        const int na = t_end > c0 ? (int)((t_end - c0 + T::kKeys - 1) / T::kKeys) : 0;
+        const int nt_all = (int)((c1 - c0 + T::kKeys - 1) / T::kKeys);
         bool inrun[QPW];
         int nin = 0;
 #pragma unroll
@@ -328,7 +333,7 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
         const int stores = nin * NSUB;           // score stores of this wave per tile
 
         auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
-            const int64_t t0 = c0 + (int64_t)ti * kTile;
+            const int64_t t0 = c0 + (int64_t)ti * T::kKeys;
             const uint32_t dst = ring_base + slot * T::kSlot;
 #pragma unroll
             for (int jd = 0; jd < kDmaPerWave; ++jd) {
@@ -350,20 +355,19 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
             }
         };
 
-        for (int p = 0; p < kRing - 1; ++p)
+        for (int p = 0; p < kRingMq - 1; ++p)
             if (p < na) issue(p, p);
         for (int ti = 0; ti < nt_all; ++ti) {
-            const int64_t t0 = c0 + (int64_t)ti * kTile;
+            const int64_t t0 = c0 + (int64_t)ti * T::kKeys;
             const bool active = ti < na;
-            const lds_u8* tile = (const lds_u8*)ring + (ti % kRing) * T::kSlot;
             if (active) {
-                const int later = min(na, ti + kRing - 1) - ti - 1;
-                wait_vmcnt_le<63>(later * per + stores * min(ti, kRing - 1));
+                const int later = min(na, ti + kRingMq - 1) - ti - 1;
+                wait_vmcnt_le<63>(later * per + stores * min(ti, kRingMq - 1));
                 ring_barrier();
-                if (ti + kRing - 1 < na) issue(ti + kRing - 1, (ti + kRing - 1) % kRing);
+                if (ti + kRingMq - 1 < na) issue(ti + kRingMq - 1, (ti + kRingMq - 1) % kRingMq);
             }
             if (nin == 0) continue;                       // wave-uniform
-            const uint32_t tile_addr = ring_base + (ti % kRing) * T::kSlot;
+            const uint32_t tile_addr = ring_base + (ti % kRingMq) * T::kSlot;
             // Fast path: both queries in the run and every key of this wave's
             // subtiles causal for both. Straight-line code in which the epilogue of
             // subtile ns - 1 is interleaved with the MFMAs of subtile ns, so the VALU
@@ -416,12 +420,7 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                     for (int jj = 0; jj < QPW; ++jj)            // both half-waves hold the sum
                         scores[(int64_t)(qb0 + jw0 + jj) * ld + s0 + n] = sum_x32(part[jj]);
                 };
-                mfmas(0, acc[0]);
-#pragma unroll
-                for (int ns = 1; ns < NSUB; ++ns) {
-                    float part[QPW];
-                    mfmas(ns, acc[ns & 1]);
-                    head_sums(acc[(ns - 1) & 1], part);
+                auto interleave = [&]() __attribute__((always_inline)) {
 #pragma unroll
                     for (int t = 0; t < KSTEPS; ++t) {
                         __builtin_amdgcn_sched_group_barrier(0x100, FP8 ? 3 : 1, 0);   // LDS reads
@@ -431,16 +430,30 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                             __builtin_amdgcn_sched_group_barrier(0x002, FP8 ? 16 : 4, 0);  // VALU
                         }
                     }
-                    finish(ns - 1, part);
-                }
-                {
+                };
+                // subtiles in pairs (acc[0]: even, acc[1]: odd), not unrolled: the
+                // registers of one pair are all that is live
+                mfmas(0, acc[0]);
+#pragma unroll 1
+                for (int ns = 0; ns < NSUB; ns += 2) {
                     float part[QPW];
-                    head_sums(acc[(NSUB - 1) & 1], part);
-                    finish(NSUB - 1, part);
+                    mfmas(ns + 1, acc[1]);
+                    head_sums(acc[0], part);
+                    interleave();
+                    finish(ns, part);
+                    if (ns + 2 < NSUB) {                      // uniform
+                        mfmas(ns + 2, acc[0]);
+                        head_sums(acc[1], part);
+                        interleave();
+                        finish(ns + 1, part);
+                    } else {
+                        head_sums(acc[1], part);
+                        finish(ns + 1, part);
+                    }
                 }
                 continue;
             }
-#pragma unroll
+#pragma unroll 1
             for (int ns = 0; ns < NSUB; ++ns) {
                 const int nt = sub0 + ns;
                 const int64_t s0 = t0 + nt * 32;
