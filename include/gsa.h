@@ -183,6 +183,25 @@ typedef struct gsa_mla_layer {
     float* lse_dev;            /* fp32 [n_q, n_heads] or NULL */
 } gsa_mla_layer;
 
+/*
+ * gsa_paged_kv — a latent cache kept in pages, as a serving system allocates it
+ * (the serving-side form of the gather in [Serving] §10: each layer gathers its
+ * own cache rows at the selected positions). Each layer's kv_dev is then a
+ * pool of n_pages pages of page_size rows ([n_pages * page_size, 576] bf16),
+ * and position s of sequence b is pool row
+ *     block_table_dev[b * max_pages + s / page_size] * page_size + s % page_size.
+ * The table (int32 [batch, max_pages], device) is shared by the layers; the
+ * caller keeps it consistent with the indices, and its entries must be page
+ * numbers < n_pages for every page a selected position falls in (not checked
+ * on the device). A sequence holds max_pages * page_size positions.
+ */
+typedef struct gsa_paged_kv {
+    const int32_t* block_table_dev;
+    int page_size;
+    int max_pages;
+    int64_t n_pages;
+} gsa_paged_kv;
+
 typedef struct gsa_group_desc {
     int compute_index;
     gsa_dtype dt;
@@ -195,6 +214,9 @@ typedef struct gsa_group_desc {
     int n_layers; const gsa_mla_layer* layers;   /* host array of n_layers */
     int n_heads; float scale;
     void* workspace_dev; size_t workspace_bytes;
+    const gsa_paged_kv* paged_kv;   /* NULL: contiguous caches [batch, n_cap, 576]; else each
+                                       layer's kv_dev is a page pool and n_cap still sizes the
+                                       indexer keys and scores (max_pages * page_size >= n_cap) */
 } gsa_group_desc;
 
 /* workspace of a group with n_layers attention layers (the full layer included) */
@@ -216,6 +238,19 @@ gsa_status gsa_indexshare_group(const gsa_group_desc* desc, void* stream);
  * Errors as gsa_sparse_mla_attn, checked for every layer before anything is enqueued.
  */
 size_t gsa_mla_layers_workspace_bytes(int n_q, int n_heads, int k, int n_layers);
+
+/*
+ * gsa_sparse_mla_attn_paged — gsa_sparse_mla_attn_layers over paged caches
+ * (gsa_paged_kv above): each layers[l].kv_dev is that layer's page pool.
+ * Indices are sequence positions, < max_pages * page_size. Same workspace as
+ * gsa_sparse_mla_attn_layers; errors as there, plus GSA_ERR_INVALID_ARG for a
+ * NULL or malformed paged_kv.
+ */
+gsa_status gsa_sparse_mla_attn_paged(const gsa_mla_layer* layers, int n_layers,
+                                     const gsa_paged_kv* paged_kv, const int32_t* q_seq_dev,
+                                     const int32_t* idx_dev, int k, int n_q, int n_heads, int batch,
+                                     float scale, void* workspace_dev, size_t workspace_bytes,
+                                     void* stream);
 gsa_status gsa_sparse_mla_attn_layers(const gsa_mla_layer* layers, int n_layers,
                                       const int32_t* q_seq_dev, const int32_t* idx_dev, int k,
                                       int n_q, int n_heads, int batch, int64_t n_cap, float scale,
@@ -271,6 +306,7 @@ typedef struct gsa_stack_desc {
     int32_t* index_buf_dev; int64_t index_stride;
     int n_heads; float scale;
     void* workspace_dev; size_t workspace_bytes;
+    const gsa_paged_kv* paged_kv;   /* as in gsa_group_desc */
 } gsa_stack_desc;
 
 size_t gsa_stack_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads, int n_layers);

@@ -36,6 +36,11 @@ class _MlaLayer(ctypes.Structure):
                 ("lse_dev", ctypes.c_void_p)]
 
 
+class _PagedKV(ctypes.Structure):
+    _fields_ = [("block_table_dev", ctypes.c_void_p), ("page_size", ctypes.c_int),
+                ("max_pages", ctypes.c_int), ("n_pages", ctypes.c_int64)]
+
+
 class _GroupDesc(ctypes.Structure):
     _fields_ = [("compute_index", ctypes.c_int), ("dt", ctypes.c_int),
                 ("q_idx_dev", ctypes.c_void_p), ("q_scale_dev", ctypes.c_void_p),
@@ -46,7 +51,8 @@ class _GroupDesc(ctypes.Structure):
                 ("n_cap", ctypes.c_int64), ("k", ctypes.c_int), ("index_buf_dev", ctypes.c_void_p),
                 ("n_layers", ctypes.c_int), ("layers", ctypes.POINTER(_MlaLayer)),
                 ("n_heads", ctypes.c_int), ("scale", ctypes.c_float),
-                ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("paged_kv", ctypes.POINTER(_PagedKV))]
 
 
 class _IndexerLayer(ctypes.Structure):
@@ -63,7 +69,8 @@ class _StackDesc(ctypes.Structure):
                 ("n_q", ctypes.c_int), ("batch", ctypes.c_int), ("n_cap", ctypes.c_int64),
                 ("k", ctypes.c_int), ("index_buf_dev", ctypes.c_void_p),
                 ("index_stride", ctypes.c_int64), ("n_heads", ctypes.c_int), ("scale", ctypes.c_float),
-                ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
+                ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
+                ("paged_kv", ctypes.POINTER(_PagedKV))]
 
 
 def _declare(lib):
@@ -82,6 +89,8 @@ def _declare(lib):
         "gsa_stack_workspace_bytes": (SZ, [I, I64, I, I, I]),
         "gsa_mla_layers_workspace_bytes": (SZ, [I, I, I, I]),
         "gsa_sparse_mla_attn_layers": (I, [ctypes.POINTER(_MlaLayer), I, P, P, I, I, I, I, I64, F, P, SZ, P]),
+        "gsa_sparse_mla_attn_paged": (I, [ctypes.POINTER(_MlaLayer), I, ctypes.POINTER(_PagedKV), P, P,
+                                          I, I, I, I, F, P, SZ, P]),
         "gsa_indexshare_group": (I, [ctypes.POINTER(_GroupDesc), P]),
         "gsa_layer_pattern": (I, [I, P]),
         "gsa_layer_stack": (I, [ctypes.POINTER(_StackDesc), P]),
@@ -229,6 +238,54 @@ def sparse_mla_attn(q_lat, q_rope, kv, q_seq, idx, scale=1.0 / 16.0, out=None, l
     return out, lse
 
 
+def _paged(block_table, kv0):
+    """_PagedKV for pools kv [n_pages, page_size, 576] and block_table int32 [batch, max_pages]."""
+    _need(block_table, "block_table", torch.int32)
+    if block_table.dim() != 2:
+        raise GsaError("block_table must be [batch, max_pages]")
+    if kv0.dim() != 3 or kv0.shape[2] != KV_ROW:
+        raise GsaError("a paged kv must be a pool [n_pages, page_size, 576]")
+    return _PagedKV(block_table.data_ptr(), kv0.shape[1], block_table.shape[1], kv0.shape[0])
+
+
+def _layer_array(layers, outs):
+    arr = (_MlaLayer * len(layers))()
+    for i, ((ql, qr, kv), (o, s)) in enumerate(zip(layers, outs)):
+        arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
+                           None if s is None else s.data_ptr())
+    return arr
+
+
+def _new_outs(n_q, n_layers, dev):
+    return [(torch.empty((n_q, MLA_HEADS, LATENT_DIM), dtype=torch.float32, device=dev),
+             torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)) for _ in range(n_layers)]
+
+
+def sparse_mla_attn_paged(layers, block_table, q_seq, idx, scale=1.0 / 16.0, outs=None, workspace=None):
+    """sparse_mla_attn_layers over paged caches: each layer's kv is a page pool
+    [n_pages, page_size, 576] bf16 and block_table int32 [batch, max_pages] maps
+    sequence b's page j to a pool page. Returns [(out, lse)] per layer."""
+    n_q = q_seq.shape[0]
+    kv0 = layers[0][2]
+    pg = _paged(block_table, kv0)
+    _need(q_seq, "q_seq", torch.int32, (n_q,))
+    _need(idx, "idx", torch.int32)
+    k = idx.shape[1]
+    dev = q_seq.device
+    for ql, qr, kv in layers:
+        _need(ql, "q_lat", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
+        _need(qr, "q_rope", torch.bfloat16, (n_q, MLA_HEADS, ROPE_DIM))
+        _need(kv, "kv", torch.bfloat16, tuple(kv0.shape))
+    if outs is None:
+        outs = _new_outs(n_q, len(layers), dev)
+    arr = _layer_array(layers, outs)
+    ws = _workspace(mla_layers_workspace_bytes(n_q, len(layers), MLA_HEADS, k), dev, workspace)
+    _check(lib().gsa_sparse_mla_attn_paged(ctypes.cast(arr, ctypes.POINTER(_MlaLayer)), len(layers),
+                                           ctypes.byref(pg), _p(q_seq), _p(idx), k, n_q, MLA_HEADS,
+                                           block_table.shape[0], scale, _p(ws), ws.numel(), _stream(dev)))
+    return outs
+
+
 def sparse_mla_attn_layers(layers, q_seq, idx, scale=1.0 / 16.0, outs=None, workspace=None):
     """Attention for several layers over one index buffer (the layers of an
     IndexShare group) in one launch: layers = [(q_lat, q_rope, kv), ...].
@@ -260,14 +317,21 @@ def sparse_mla_attn_layers(layers, q_seq, idx, scale=1.0 / 16.0, outs=None, work
 
 def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_idx=None,
                      q_scale=None, k_scale=None, scores=None, compute_index=True,
-                     scale=1.0 / 16.0, workspace=None, outs=None):
+                     scale=1.0 / 16.0, workspace=None, outs=None, block_table=None):
     """One IndexShare group: layers = [(q_lat, q_rope, kv), ...], F layer first.
     With compute_index the F layer's indexer + top-k write index_buf, then every
-    layer attends over it. Returns [(out, lse)] per layer."""
+    layer attends over it. With block_table (int32 [batch, max_pages]) each kv is
+    a page pool [n_pages, page_size, 576]. Returns [(out, lse)] per layer."""
     L = lib()
     n_q = q_seq.shape[0]
     kv0 = layers[0][2]
-    batch, n_cap = kv0.shape[0], kv0.shape[1]
+    pg = None
+    if block_table is None:
+        batch, n_cap = kv0.shape[0], kv0.shape[1]
+    else:
+        pg = _paged(block_table, kv0)
+        batch = block_table.shape[0]
+        n_cap = k_idx.shape[1] if compute_index else pg.max_pages * pg.page_size
     k = index_buf.shape[1]
     dev = q_seq.device
     fp8 = compute_index and q_idx.dtype == torch.uint8
@@ -302,6 +366,8 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     d.n_layers, d.layers = len(layers), ctypes.cast(arr, ctypes.POINTER(_MlaLayer))
     d.n_heads, d.scale = MLA_HEADS, scale
     d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
+    if pg is not None:
+        d.paged_kv = ctypes.pointer(pg)
     _check(L.gsa_indexshare_group(ctypes.byref(d), _stream(dev)))
     return outs
 
@@ -316,15 +382,21 @@ def layer_pattern(n_layers=78):
 
 
 def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_stride=None,
-                scale=1.0 / 16.0, workspace=None, outs=None):
+                scale=1.0 / 16.0, workspace=None, outs=None, block_table=None):
     """The attention stack: indexers = [(q_idx, w, k_idx, q_scale, k_scale)] per full
     layer in layer order (scales None for bf16); layers = [(q_lat, q_rope, kv)] per
     layer. index_buf: int32 [n_full, n_q, k] (each full layer's indices kept) or
-    [n_q, k] (one buffer reused). Returns [(out, lse)] per layer."""
+    [n_q, k] (one buffer reused). With block_table (int32 [batch, max_pages]) each
+    kv is a page pool [n_pages, page_size, 576]. Returns [(out, lse)] per layer."""
     L = lib()
     n_q = q_seq.shape[0]
     kv0 = layers[0][2]
-    batch, n_cap = kv0.shape[0], kv0.shape[1]
+    pg = None
+    if block_table is None:
+        batch, n_cap = kv0.shape[0], kv0.shape[1]
+    else:
+        pg = _paged(block_table, kv0)
+        batch, n_cap = block_table.shape[0], indexers[0][2].shape[1]
     k = index_buf.shape[-1]
     dev = q_seq.device
     if not index_buf.is_contiguous():
@@ -362,5 +434,7 @@ def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_st
     d.index_buf_dev, d.index_stride = index_buf.data_ptr(), index_stride
     d.n_heads, d.scale = MLA_HEADS, scale
     d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
+    if pg is not None:
+        d.paged_kv = ctypes.pointer(pg)
     _check(L.gsa_layer_stack(ctypes.byref(d), _stream(dev)))
     return outs

@@ -89,10 +89,23 @@ gsa_status check_mla(const void* q_lat, const void* q_rope, const void* kv, cons
     return GSA_OK;
 }
 
+// Host checks of a paged-cache description; *n_cap = positions a sequence can hold.
+gsa_status check_paged(const gsa_paged_kv* pg, int64_t* n_cap) {
+    REQUIRE(pg != nullptr, "paged_kv is NULL");
+    REQUIRE_PTR(pg->block_table_dev);
+    REQUIRE(pg->page_size >= 1, "page_size must be >= 1 (got %d)", pg->page_size);
+    REQUIRE(pg->max_pages >= 1, "max_pages must be >= 1 (got %d)", pg->max_pages);
+    REQUIRE(pg->n_pages >= 1, "n_pages must be >= 1");
+    REQUIRE(pg->n_pages * (int64_t)pg->page_size <= 0x7fffffff, "a pool must hold < 2^31 rows");
+    REQUIRE((int64_t)pg->max_pages * pg->page_size <= 0x7fffffff, "a sequence must hold < 2^31 positions");
+    *n_cap = (int64_t)pg->max_pages * pg->page_size;
+    return GSA_OK;
+}
+
 // Attention for layers that share one index buffer, in one launch per 8 layers.
 gsa_status enqueue_attention(const gsa_mla_layer* layers, int n_layers, const int32_t* q_seq,
                              const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
-                             float scale, void* ws, hipStream_t s) {
+                             const gsa_paged_kv* paged, float scale, void* ws, hipStream_t s) {
     gsa::MlaLayerPtrs ptrs[8];
     for (int l0 = 0; l0 < n_layers; l0 += 8) {
         const int nl = n_layers - l0 < 8 ? n_layers - l0 : 8;
@@ -100,8 +113,9 @@ gsa_status enqueue_attention(const gsa_mla_layer* layers, int n_layers, const in
             ptrs[i] = {layers[l0 + i].q_lat_dev, layers[l0 + i].q_rope_dev, layers[l0 + i].kv_dev,
                        layers[l0 + i].out_dev, layers[l0 + i].lse_dev};
         // the workspace was sized for n_layers; a later launch of fewer layers needs no more
-        const hipError_t e = gsa::launch_sparse_mla_layers(ptrs, nl, q_seq, idx, k, n_q, n_heads, n_cap,
-                                                           scale, ws, s);
+        const hipError_t e = gsa::launch_sparse_mla_layers(
+            ptrs, nl, q_seq, idx, k, n_q, n_heads, n_cap, paged ? paged->block_table_dev : nullptr,
+            paged ? paged->page_size : 0, paged ? paged->max_pages : 0, scale, ws, s);
         if (e != hipSuccess) return hip_result(e, "sparse_mla_attn");
     }
     g_err[0] = 0;
@@ -195,7 +209,25 @@ gsa_status gsa_sparse_mla_attn_layers(const gsa_mla_layer* layers, int n_layers,
             return st;
         }
     }
-    return enqueue_attention(layers, n_layers, q_seq, idx, k, n_q, n_heads, n_cap, scale, ws,
+    return enqueue_attention(layers, n_layers, q_seq, idx, k, n_q, n_heads, n_cap, nullptr, scale, ws,
+                             (hipStream_t)stream);
+}
+
+gsa_status gsa_sparse_mla_attn_paged(const gsa_mla_layer* layers, int n_layers, const gsa_paged_kv* paged_kv,
+                                     const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
+                                     int batch, float scale, void* ws, size_t ws_bytes, void* stream) {
+    int64_t n_cap = 0;
+    gsa_status st = check_paged(paged_kv, &n_cap);
+    if (st != GSA_OK) return st;
+    REQUIRE(n_layers >= 1, "n_layers must be >= 1 (got %d)", n_layers);
+    REQUIRE(layers != nullptr, "layers is NULL");
+    for (int l = 0; l < n_layers; ++l) {
+        st = check_mla(layers[l].q_lat_dev, layers[l].q_rope_dev, layers[l].kv_dev, q_seq, idx, k, n_q,
+                       n_heads, batch, n_cap, scale, layers[l].out_dev, layers[l].lse_dev, ws, ws_bytes,
+                       n_layers);
+        if (st != GSA_OK) return st;
+    }
+    return enqueue_attention(layers, n_layers, q_seq, idx, k, n_q, n_heads, n_cap, paged_kv, scale, ws,
                              (hipStream_t)stream);
 }
 
@@ -228,6 +260,13 @@ gsa_status validate_group(const gsa_group_desc* d) {
     REQUIRE(d->n_layers >= 0, "n_layers must be >= 0");
     REQUIRE(d->n_layers == 0 || d->layers != nullptr, "layers is NULL");
     REQUIRE(d->compute_index == 0 || d->compute_index == 1, "compute_index must be 0 or 1");
+    if (d->paged_kv != nullptr) {
+        int64_t n_cap_pg = 0;
+        const gsa_status st = check_paged(d->paged_kv, &n_cap_pg);
+        if (st != GSA_OK) return st;
+        REQUIRE(n_cap_pg >= d->n_cap, "paged_kv holds %lld positions per sequence, fewer than n_cap %lld",
+                (long long)n_cap_pg, (long long)d->n_cap);
+    }
     if (d->compute_index) {
         gsa_status st = check_score(d->dt, d->q_idx_dev, d->q_scale_dev, d->w_dev, d->k_idx_dev,
                                     d->k_scale_dev, d->q_seq_dev, d->q_pos_dev, d->n_q, d->batch,
@@ -266,7 +305,7 @@ gsa_status enqueue_group(const gsa_group_desc* d, hipStream_t s) {
     }
     if (d->n_layers > 0)
         return enqueue_attention(d->layers, d->n_layers, d->q_seq_dev, d->index_buf_dev, d->k, d->n_q,
-                                 d->n_heads, d->n_cap, d->scale, d->workspace_dev, s);
+                                 d->n_heads, d->n_cap, d->paged_kv, d->scale, d->workspace_dev, s);
     return GSA_OK;
 }
 
@@ -320,6 +359,7 @@ gsa_status gsa_layer_stack(const gsa_stack_desc* d, void* stream) {
         g.layers = d->layers + i;
         g.n_heads = d->n_heads; g.scale = d->scale;
         g.workspace_dev = d->workspace_dev; g.workspace_bytes = d->workspace_bytes;
+        g.paged_kv = d->paged_kv;
         return g;
     };
     for (int i = 0, f = 0; i < d->n_layers; ++i) {      // validate all before enqueuing any

@@ -31,8 +31,11 @@ struct MlaLayerPtrs {
 
 // Workspace for attention over n_layers layers that share one index buffer.
 size_t mla_workspace_bytes(int n_q, int n_heads, int k, int n_layers);
+// block_table NULL: each layer's cache is [batch, n_cap, 576]; otherwise a pool
+// of page_size-row pages addressed through block_table [batch, max_pages].
 hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, const int32_t* q_seq,
                                     const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
+                                    const int32_t* block_table, int page_size, int max_pages,
                                     float scale, void* ws, hipStream_t stream);
 
 }  // namespace gsa

@@ -112,7 +112,8 @@ __device__ __forceinline__ void wait_block(int later) {
 
 __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     LayerArgs L, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ idx, int k,
-    int n_q, int64_t n_cap, float scale_log2, int rows_per_split, float* __restrict__ part_o_all,
+    int n_q, int64_t n_cap, const int32_t* __restrict__ block_table, int page_size, int max_pages,
+    float scale_log2, int rows_per_split, float* __restrict__ part_o_all,
     float* __restrict__ part_ml_all) {
     // this work-group's layer (uniform): its operands and its part of the workspace
     const int layer = blockIdx.z;
@@ -131,9 +132,22 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     const int r0 = split * rows_per_split;
     const int nrows = rows_per_split;
     const int seq = q_seq[q];
-    const uint8_t* kvs = kv + (int64_t)seq * n_cap * kRowBytes;
-
-    for (int i = tid; i < nrows; i += kThreads) rows_s[i] = idx[(int64_t)q * k + r0 + i];
+    // Contiguous cache: the sequence's rows start at seq * n_cap. Paged cache
+    // (block_table != NULL): the layer's cache is a pool of page_size-row pages
+    // and position s of the sequence is row table[seq][s / page_size] *
+    // page_size + s % page_size of the pool; indices become pool rows here, once.
+    const uint8_t* kvs;
+    if (block_table == nullptr) {
+        kvs = kv + (int64_t)seq * n_cap * kRowBytes;
+        for (int i = tid; i < nrows; i += kThreads) rows_s[i] = idx[(int64_t)q * k + r0 + i];
+    } else {
+        kvs = kv;
+        const int32_t* bt = block_table + (int64_t)seq * max_pages;
+        for (int i = tid; i < nrows; i += kThreads) {
+            const int s = idx[(int64_t)q * k + r0 + i];
+            rows_s[i] = s < 0 ? -1 : bt[s / page_size] * page_size + s % page_size;
+        }
+    }
 
     // Q as the B operand: head 16*hg + l16, K-steps t = 9*hf .. 9*hf+8 of the
     // 576 dims (dims 32t + 8g .. +8; steps 16 and 17 are the RoPE dims)
@@ -357,6 +371,7 @@ size_t mla_workspace_bytes(int n_q, int n_heads, int k, int n_layers) {
 
 hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, const int32_t* q_seq,
                                     const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
+                                    const int32_t* block_table, int page_size, int max_pages,
                                     float scale, void* ws, hipStream_t st) {
     (void)n_heads;
     const float scale_log2 = scale * 1.4426950408889634f;
@@ -377,7 +392,8 @@ hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, co
         float* part_o = (float*)ws;
         float* part_ml = s > 1 ? part_o + (size_t)per * n_q * s * kHeads * kLat : nullptr;
         hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq, idx, k,
-                           n_q, n_cap, scale_log2, rows, part_o, part_ml);
+                           n_q, n_cap, block_table, page_size, max_pages, scale_log2, rows, part_o,
+                           part_ml);
         if (s > 1)
             hipLaunchKernelGGL(sparse_mla_merge, dim3(n_q, kHeads / 4, nl), dim3(256), 0, st, L, n_q,
                                part_o, part_ml, s);

@@ -49,3 +49,29 @@ def sparse_mla(q_lat, q_rope, kv, q_seq, idx, scale: float, d_latent: int = 512)
         out[i] = (e @ c) / denom
         lse[i] = (m + np.log(denom))[:, 0]
     return out, lse
+
+
+def paged_cache_view(pool, block_table, page_size: int):
+    """The per-sequence cache [B, max_pages * page_size, D] that a paged pool
+    stands for: position s of sequence b lives in pool row
+    block_table[b, s // page_size] * page_size + s % page_size.
+
+    pool [n_pages * page_size, D] (or [n_pages, page_size, D]); block_table
+    int [B, max_pages]. Pages whose table entry is not a pool page (e.g. -1 for
+    a page not yet allocated) read as NaN, so that attending to them shows.
+
+    Pages: "GLM-5→5.1→5.2…" §10 (each layer gathers the selected positions'
+    rows from its own cache); the paged layout is the serving-side reading of
+    where those rows live: fixed-size pages named by a per-sequence table."""
+    pool = np.asarray(pool, dtype=np.float64)
+    pool = pool.reshape(-1, pool.shape[-1])
+    bt = np.asarray(block_table, dtype=np.int64)
+    n_pages = pool.shape[0] // page_size
+    B, max_pages = bt.shape
+    view = np.full((B, max_pages * page_size, pool.shape[1]), np.nan)
+    for b in range(B):
+        for j in range(max_pages):
+            p = int(bt[b, j])
+            if 0 <= p < n_pages:
+                view[b, j * page_size:(j + 1) * page_size] = pool[p * page_size:(p + 1) * page_size]
+    return view

@@ -79,6 +79,35 @@ def test_sparse_mla_rejects():
     assert L.gsa_sparse_mla_attn(*bad) == INVALID
 
 
+def test_paged_attention_rejects():
+    L = gsa.lib()
+    need = L.gsa_mla_layers_workspace_bytes(8, 64, 2048, 1)
+    layers = (gsa._MlaLayer * 1)()
+    layers[0] = gsa._MlaLayer(FAKE, FAKE, FAKE, FAKE, None)
+    arr = ctypes.cast(layers, ctypes.POINTER(gsa._MlaLayer))
+
+    def call(pg):
+        return L.gsa_sparse_mla_attn_paged(arr, 1, pg, FAKE, FAKE, 2048, 8, 64, 2, 1 / 16, FAKE, need, None)
+    assert call(None) == INVALID
+    for bad in (dict(block_table_dev=None), dict(page_size=0), dict(max_pages=0), dict(n_pages=0),
+                dict(n_pages=1 << 31, page_size=64)):
+        kw = dict(block_table_dev=FAKE, page_size=64, max_pages=16, n_pages=100)
+        kw.update(bad)
+        assert call(ctypes.byref(gsa._PagedKV(**kw))) == INVALID, bad
+    # a group's pages must cover the indexer's n_cap positions
+    d = gsa._GroupDesc()
+    d.compute_index = 0
+    d.q_seq_dev = d.index_buf_dev = FAKE
+    d.n_q, d.batch, d.n_cap, d.k = 8, 2, 4096, 2048
+    d.n_layers, d.layers = 1, arr
+    d.n_heads, d.scale = 64, 1 / 16
+    d.workspace_dev, d.workspace_bytes = FAKE, need
+    pg = gsa._PagedKV(block_table_dev=FAKE, page_size=64, max_pages=63, n_pages=200)
+    d.paged_kv = ctypes.pointer(pg)
+    assert L.gsa_indexshare_group(ctypes.byref(d), None) == INVALID
+    assert b"fewer than n_cap" in L.gsa_last_error()
+
+
 def test_group_validates_every_layer_before_launching():
     L = gsa.lib()
     layers = (gsa._MlaLayer * 2)()

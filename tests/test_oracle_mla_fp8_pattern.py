@@ -96,6 +96,56 @@ def test_mla_no_valid_index():
     assert np.all(out == 0) and np.all(lse == -np.inf)
 
 
+# ---------------------------------------------------------------- paged cache
+def _scatter_to_pages(cache, page_size, n_pages, rng):
+    """Place each sequence's pages of a contiguous cache [B, N, D] at random
+    distinct pages of a pool; unused pool pages hold noise."""
+    B, N, D = cache.shape
+    mp = N // page_size
+    perm = rng.permutation(n_pages)[:B * mp].reshape(B, mp)
+    pool = rng.standard_normal((n_pages, page_size, D))
+    for b in range(B):
+        for j in range(mp):
+            pool[perm[b, j]] = cache[b, j * page_size:(j + 1) * page_size]
+    return pool, perm
+
+
+@pytest.mark.parametrize("page_size", [1, 3, 64])
+def test_paged_view_restores_the_scattered_cache(page_size):
+    rng = np.random.default_rng(page_size)
+    cache = rng.standard_normal((3, page_size * 5, 7))
+    pool, bt = _scatter_to_pages(cache, page_size, 20, rng)
+    view = oracle.paged_cache_view(pool, bt, page_size)
+    assert np.array_equal(view, cache)
+    # the flat pool form reads the same
+    assert np.array_equal(oracle.paged_cache_view(pool.reshape(-1, 7), bt, page_size), cache)
+
+
+def test_paged_view_page_size_one_is_a_row_table_and_unbacked_pages_are_nan():
+    pool = np.arange(12.0).reshape(6, 2)
+    bt = np.array([[4, 0, -1], [5, 9, 2]])
+    view = oracle.paged_cache_view(pool, bt, 1)
+    assert np.array_equal(view[0, :2], pool[[4, 0]]) and np.isnan(view[0, 2]).all()
+    assert np.array_equal(view[1, [0, 2]], pool[[5, 2]]) and np.isnan(view[1, 1]).all()
+
+
+def test_mla_over_paged_cache_equals_contiguous():
+    rng = np.random.default_rng(8)
+    ps, B, N, H = 16, 2, 160, 4
+    cache = rng.standard_normal((B, N, 576))
+    pool, bt = _scatter_to_pages(cache, ps, 40, rng)
+    q_lat = rng.standard_normal((3, H, 512))
+    q_rope = rng.standard_normal((3, H, 64))
+    q_seq = np.array([0, 1, 1])
+    idx = np.full((3, 2048), -1)
+    idx[0, :50] = np.sort(rng.choice(N, 50, replace=False))
+    idx[1, :N] = np.arange(N)
+    idx[2, :1] = [N - 1]
+    a = oracle.sparse_mla(q_lat, q_rope, cache, q_seq, idx, 1 / 16)
+    b = oracle.sparse_mla(q_lat, q_rope, oracle.paged_cache_view(pool, bt, ps), q_seq, idx, 1 / 16)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
 # ---------------------------------------------------------------- E4M3
 def test_e4m3_decode_all_codes_match_torch():
     codes = np.arange(256, dtype=np.uint8)
