@@ -39,6 +39,7 @@ import workloads as W
 
 METRIC = "query-tokens/s via indexer+top-2048+sparse MLA at 128K/1M; % of roofline"
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "fp8": 5000.0}   # MI355X dense matrix peaks
 SCALE = 1.0 / 16.0           # 1/sqrt(QK dim 256)
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = "long_context_sparse_02_amd/csrc/"
@@ -68,14 +69,24 @@ def score_bytes(wl, fp8):
 
 def topk_bytes(wl):
     """One top-k launch: each query's causal scores read once + its indices written."""
-    first = wl.n_ctx - wl.q_per_seq + 1                     # causal length of the first query
-    causal = wl.batch * sum(first + j for j in range(wl.q_per_seq))
-    return causal * 4 + wl.n_q * 2048 * 4
+    return causal_pairs(wl) * 4 + wl.n_q * 2048 * 4
 
 
 def mla_bytes(wl):
     """One sparse-MLA launch: gathered rows + indices + q_lat/q_rope + fp32 output."""
     return wl.n_q * (2048 * 1152 + 2048 * 4 + 64 * 576 * 2 + 64 * 512 * 4)
+
+
+def score_flops(wl):
+    """One indexer-score launch: 32 heads x 128-dim dot products (2 flops per
+    multiply-add) for every causal (query, key) pair; the ReLU and the weighted
+    head sum are not matrix work and are left out."""
+    return causal_pairs(wl) * 32 * 128 * 2
+
+
+def causal_pairs(wl):
+    first = wl.n_ctx - wl.q_per_seq + 1                     # causal length of the first query
+    return wl.batch * sum(first + j for j in range(wl.q_per_seq))
 
 
 def launch_bytes(kind, wl, fp8):
@@ -223,7 +234,7 @@ def run_bench(args):
         bytes_kind[k] += b
         launches[k] += 1
     dom = max(ms_kind, key=ms_kind.get)
-    achieved = bytes_kind[dom] / (ms_kind[dom] / 1e3) / 1e9
+    roof = roofline(dom, wl, inp["fp8"], bytes_kind[dom], ms_kind[dom], launches[dom])
     value = wl.n_q / (ms_step / 1e3)
     log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); " +
         ", ".join(f"{k} {launches[k]}x {ms_kind[k] / launches[k] * 1e3:.1f} us" for k in kinds))
@@ -247,35 +258,61 @@ def run_bench(args):
         "breakdown_ms_per_step": {k: round(v, 4) for k, v in ms_kind.items()},
         "avg_launch_us": {k: round(ms_kind[k] / launches[k] * 1e3, 2) for k in kinds},
         "achieved_GBs": {k: round(bytes_kind[k] / (ms_kind[k] / 1e3) / 1e9, 1) for k in kinds},
-        "roofline": {"kernel": dom, "bound": "hbm", "achieved": round(achieved, 1),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(dom, wl),
-                     "traffic_unit": "HBM bytes per launch (rocprofv3 counters)",
-                     "bytes_per_launch": bytes_kind[dom] // launches[dom],
-                     "avg_launch_ms": round(ms_kind[dom] / launches[dom], 4)},
+        "roofline": roof,
     }
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(wl, inp, args)
     return result
 
 
+def roofline(kind, wl, fp8, nbytes, ms, launches):
+    """The bound of the dominant kernel: HBM unless its matrix work at the MFMA
+    peak of its input type takes longer than its bytes at the HBM peak (the
+    indexer score with thousands of queries per sequence)."""
+    sec = ms / 1e3
+    out = {"kernel": kind}
+    flops = score_flops(wl) * launches if kind == "indexer_score" else 0
+    peak_tf = MFMA_PEAK_TFLOPS["fp8" if fp8 else "bf16"]
+    if flops / (peak_tf * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
+        achieved = flops / sec / 1e12
+        out.update({"bound": "mfma", "achieved": round(achieved, 1), "peak": peak_tf, "unit": "TFLOP/s",
+                    "frac": round(achieved / peak_tf, 4), "flops_per_launch": flops // launches})
+    else:
+        achieved = nbytes / sec / 1e9
+        out.update({"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                    "frac": round(achieved / HBM_PEAK_GBS, 4)})
+    out.update({"traffic": measured_traffic(kind, wl),
+                "traffic_unit": "HBM bytes per launch (rocprofv3 counters)",
+                "bytes_per_launch": nbytes // launches, "avg_launch_ms": round(ms / launches, 4)})
+    return out
+
+
 # ---- the oracle on the host ---------------------------------------------------------
-def host_indexer_inputs(wl, inp, j, qi, seed):
+def host_indexer_inputs(wl, inp, j, qi, seed, keys=None):
     """Host copies of full layer j's indexer inputs for query qi: (q [1,32,128],
     w [1,32], keys [N,128]) as the oracle reads them. For the fp8 workload the
     original integer values are redrawn on the device (same generator, same
-    values) and the oracle applies its own e4m3 block quantisation."""
+    values) and the oracle applies its own e4m3 block quantisation. `keys`, a
+    dict, keeps each (layer, sequence)'s host keys for later queries."""
     import oracle
     b = int(inp["q_seq"][qi])
     q, w, k, _, _ = inp["indexers"][j]
+    kh = None if keys is None else keys.get((j, b))
     if inp["fp8"]:
         f = inp["full_layers"][j]
         qv, wv = W.indexer_queries(wl, seed, f, q.device)
-        qh = qv[qi:qi + 1].float().cpu().numpy()
-        kh = W.indexer_keys_seq(wl, seed, f, b, q.device).float().cpu().numpy()
-        qh, kh = oracle.indexer_inputs_fp8(qh, kh)
-        return qh, wv[qi:qi + 1].cpu().numpy(), kh
-    return q[qi:qi + 1].float().cpu().numpy(), w[qi:qi + 1].cpu().numpy(), k[b].float().cpu().numpy()
+        qh = oracle.dequantize_blocks(*oracle.quantize_blocks(qv[qi:qi + 1].float().cpu().numpy()))
+        if kh is None:
+            kh = W.indexer_keys_seq(wl, seed, f, b, q.device).float().cpu().numpy()
+            kh = oracle.dequantize_blocks(*oracle.quantize_blocks(kh))
+        wh = wv[qi:qi + 1].cpu().numpy()
+    else:
+        qh, wh = q[qi:qi + 1].float().cpu().numpy(), w[qi:qi + 1].cpu().numpy()
+        if kh is None:
+            kh = k[b].float().cpu().numpy()
+    if keys is not None:
+        keys[(j, b)] = kh
+    return qh, wh, kh
 
 
 def host_rows(kv, b, sel):
@@ -293,16 +330,20 @@ def cpu_baseline(wl, inp, args):
     layer's score over all causal keys and top-2048, then every attention
     layer over the oracle's own selection). Host copies are made untimed."""
     import oracle                                  # test infrastructure: baseline leg only
-    n = min(args.cpu_queries, wl.n_q)
     threads = len(os.sched_getaffinity(0))
     torch.set_num_threads(threads)
     secs = 0.0
-    for qi in range(n):
+    n = 0
+    keys = {}
+    for qi in range(min(args.cpu_queries, wl.n_q)):
+        if secs >= args.cpu_seconds:
+            break
+        n += 1
         b = int(inp["q_seq"][qi])
         pos = np.array([int(inp["q_pos"][qi])], np.int32)
         sels = []
         for j in range(len(inp["full_layers"])):
-            qh, wh, kh = host_indexer_inputs(wl, inp, j, qi, args.seed)
+            qh, wh, kh = host_indexer_inputs(wl, inp, j, qi, args.seed, keys)
             t0 = time.perf_counter()
             sc = oracle.indexer_score(qh, wh, kh[None], np.zeros(1, np.int32), pos)
             sels.append(oracle.topk_select(sc, pos, 2048)[0])
@@ -342,7 +383,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--workload", default="decode_b64_n131072", choices=sorted(W.WORKLOADS))
-    ap.add_argument("--cpu-queries", type=int, default=64)
+    ap.add_argument("--cpu-queries", type=int, default=1 << 30, help="most queries in the CPU sample")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="the CPU sample stops at the first query that starts past this much oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
     args = ap.parse_args()

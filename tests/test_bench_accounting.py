@@ -1,0 +1,37 @@
+"""The benchmark's algorithmic work per launch (CPU only): the byte and flop
+counts that its roofline divides by, against sizes worked out by hand from the
+workload shapes."""
+import bench
+import workloads as W
+
+
+def test_prefill_causal_pairs_and_flops():
+    wl = W.WORKLOADS["prefill_q4096_n131072"]
+    # queries at positions 126976 .. 131071 (one sequence): sum of (pos + 1)
+    assert bench.causal_pairs(wl) == sum(range(126977, 131073)) == 528_484_352
+    assert bench.score_flops(wl) == 528_484_352 * 32 * 128 * 2
+
+
+def test_decode_bytes():
+    wl = W.WORKLOADS["decode_b64_n131072"]
+    assert bench.score_bytes(wl, False) == 64 * 131072 * 256 + 64 * (32 * 128 * 2 + 32 * 4)
+    wl8 = W.WORKLOADS["decode_b8_n1048576_fp8"]
+    assert bench.score_bytes(wl8, True) == 8 * (1 << 20) * 132 + 8 * (32 * 128 + 32 * 4 + 32 * 4)
+    assert bench.topk_bytes(wl) == 64 * 131072 * 4 + 64 * 2048 * 4
+    assert bench.mla_bytes(wl) == 64 * (2048 * 1152 + 2048 * 4 + 64 * 576 * 2 + 64 * 512 * 4)
+
+
+def test_roofline_bound_follows_arithmetic_intensity():
+    pre = W.WORKLOADS["prefill_q4096_n131072"]
+    r = bench.roofline("indexer_score", pre, False, bench.score_bytes(pre, False), 3.5, 1)
+    assert r["bound"] == "mfma" and r["unit"] == "TFLOP/s" and r["peak"] == 2500.0
+    assert abs(r["achieved"] - bench.score_flops(pre) / 3.5e-3 / 1e12) < 0.1
+    pre8 = W.WORKLOADS["prefill_q4096_n131072_fp8"]
+    assert bench.roofline("indexer_score", pre8, True, bench.score_bytes(pre8, True), 2.0, 1)["peak"] == 5000.0
+    dec = W.WORKLOADS["decode_b64_n131072"]
+    r = bench.roofline("indexer_score", dec, False, 2 * bench.score_bytes(dec, False), 0.8, 2)
+    assert r["bound"] == "hbm" and r["unit"] == "GB/s"
+    assert abs(r["achieved"] - 2 * bench.score_bytes(dec, False) / 0.8e-3 / 1e9) < 0.1
+    assert r["bytes_per_launch"] == bench.score_bytes(dec, False)
+    r = bench.roofline("topk", pre, False, bench.topk_bytes(pre), 1.8, 1)
+    assert r["bound"] == "hbm"
