@@ -252,6 +252,7 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
     constexpr int NT = T::kKeys / 32;            // 32-key subtiles per tile
     constexpr int NSUB = NT * NQP / kMqWaves;    // subtiles per wave per tile
     static_assert(QB == 4 || QB == 8 || QB == 16, "QB");
+    static_assert(NSUB >= 2 && NSUB % 2 == 0, "the fast path pairs subtiles");
     constexpr int KSTEPS = FP8 ? 2 : 8;
     constexpr int kDmaPerWave = T::kDma / kMqWaves;
     using AVec = std::conditional_t<FP8, i32x8, bf16x8>;
@@ -378,32 +379,8 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
             for (int jj = 0; jj < QPW; ++jj) fast = fast && s_last <= apos[jj];
             if (fast) {
                 f32x16 acc[2][QPW];
-                auto mfmas = [&](int ns, f32x16 (&c)[QPW]) __attribute__((always_inline)) {
-                    const int nt = sub0 + ns;
-                    const lds_u8* base = (const lds_u8*)(uintptr_t)(tile_addr + nt * 32 * T::kRowBytes);
-#pragma unroll
-                    for (int t = 0; t < KSTEPS; ++t) {
-                        if constexpr (FP8) {
-                            const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(base + lds_off[2 * t]);
-                            const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(base + lds_off[2 * t + 1]);
-                            const i32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                            const int ke = e8m0_of(*(const __attribute__((address_space(3))) float*)(
-                                (const lds_u8*)(uintptr_t)(tile_addr + T::kBytes + nt * 128) + 4 * n));
-#pragma unroll
-                            for (int jj = 0; jj < QPW; ++jj)
-                                c[jj] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                    a[jj][t], b, t == 0 ? f32x16{} : c[jj], 0, 0, 0, a_e8[jj], 0, ke);
-                        } else {
-                            const bf16x8 b = *(const __attribute__((address_space(3))) bf16x8*)(base + lds_off[t]);
-#pragma unroll
-                            for (int jj = 0; jj < QPW; ++jj)
-                                c[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                                    a[jj][t], b, t == 0 ? f32x16{} : c[jj], 0, 0, 0);
-                        }
-                    }
-                };
                 // epilogue in two parts: the per-lane head sums (VALU only, scheduled
-                // between the MFMAs) and the cross-half add + store after them
+                // between the MFMAs of the next subtile) and the cross-half add + store
                 auto head_sums = [&](const f32x16 (&c)[QPW], float (&part)[QPW]) __attribute__((always_inline)) {
 #pragma unroll
                     for (int jj = 0; jj < QPW; ++jj) {
@@ -420,37 +397,98 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                     for (int jj = 0; jj < QPW; ++jj)            // both half-waves hold the sum
                         scores[(int64_t)(qb0 + jw0 + jj) * ld + s0 + n] = sum_x32(part[jj]);
                 };
-                auto interleave = [&]() __attribute__((always_inline)) {
+                // One step of the software pipeline: the LDS reads and MFMAs of subtile
+                // ns into cm and, when EPI, the head sums of the previous subtile (ce) cut
+                // into pieces that sit between those MFMAs, so that the VALU work issues
+                // while the matrix core is busy. The order is fixed in the source:
+                // scheduling fences between the pieces keep the compiler from regrouping
+                // them (it otherwise clusters all MFMAs and all VALU work).
+                auto fence = []() __attribute__((always_inline)) { __builtin_amdgcn_sched_barrier(0); };
+                auto piece = [&](const f32x16 (&ce)[QPW], float (&part)[QPW], int jj, int i0, int cnt)
+                    __attribute__((always_inline)) {
 #pragma unroll
-                    for (int t = 0; t < KSTEPS; ++t) {
-                        __builtin_amdgcn_sched_group_barrier(0x100, FP8 ? 3 : 1, 0);   // LDS reads
+                    for (int i = i0; i < i0 + cnt; ++i)
+                        part[jj] = fmaf(wr[jj][i], __int_as_float(max(__float_as_int(ce[jj][i]), 0)),
+                                        i == 0 ? 0.f : part[jj]);
+                };
+                auto step = [&](auto epi_c, int ns, f32x16 (&cm)[QPW], const f32x16 (&ce)[QPW],
+                                float (&part)[QPW]) __attribute__((always_inline)) {
+                    constexpr bool EPI = decltype(epi_c)::value;
+                    const int nt = sub0 + ns;
+                    const uint32_t sub_addr = tile_addr + nt * 32 * T::kRowBytes;
+                    fence();
+                    if constexpr (FP8) {
+                        // 4 x 16 bytes of key codes and the key scale, then 4 MFMAs with a
+                        // quarter of the head sums after the reads and after each MFMA
+                        i32x4 ch[4];
 #pragma unroll
-                        for (int jj = 0; jj < QPW; ++jj) {
-                            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);         // one MFMA
-                            __builtin_amdgcn_sched_group_barrier(0x002, FP8 ? 16 : 4, 0);  // VALU
+                        for (int t = 0; t < 4; ++t)
+                            ch[t] = *(const __attribute__((address_space(3))) i32x4*)(
+                                (const lds_u8*)(uintptr_t)(sub_addr + lds_off[t]));
+                        const float ksf = *(const __attribute__((address_space(3))) float*)(
+                            (const lds_u8*)(uintptr_t)(tile_addr + T::kBytes + nt * 128) + 4 * n);
+                        fence();
+                        if constexpr (EPI) piece(ce, part, 0, 0, 8);
+                        fence();
+                        const int ke = e8m0_of(ksf);
+                        const i32x8 b0 = {ch[0][0], ch[0][1], ch[0][2], ch[0][3], ch[1][0], ch[1][1], ch[1][2], ch[1][3]};
+                        const i32x8 b1 = {ch[2][0], ch[2][1], ch[2][2], ch[2][3], ch[3][0], ch[3][1], ch[3][2], ch[3][3]};
+                        cm[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][0], b0, f32x16{}, 0, 0, 0, a_e8[0], 0, ke);
+                        fence();
+                        if constexpr (EPI) piece(ce, part, 0, 8, 8);
+                        fence();
+                        cm[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][0], b0, f32x16{}, 0, 0, 0, a_e8[1], 0, ke);
+                        fence();
+                        if constexpr (EPI) piece(ce, part, 1, 0, 8);
+                        fence();
+                        cm[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][1], b1, cm[0], 0, 0, 0, a_e8[0], 0, ke);
+                        fence();
+                        if constexpr (EPI) piece(ce, part, 1, 8, 8);
+                        fence();
+                        cm[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][1], b1, cm[1], 0, 0, 0, a_e8[1], 0, ke);
+                    } else {
+                        // the B operand of k-step t is read two k-steps ahead; one eighth
+                        // of a query's head sums (2 values) after each MFMA
+                        bf16x8 b[KSTEPS];
+                        auto rd = [&](int t) __attribute__((always_inline)) {
+                            b[t] = *(const __attribute__((address_space(3))) bf16x8*)(
+                                (const lds_u8*)(uintptr_t)(sub_addr + lds_off[t]));
+                        };
+                        rd(0);
+                        rd(1);
+#pragma unroll
+                        for (int t = 0; t < KSTEPS; ++t) {
+                            if (t + 2 < KSTEPS) rd(t + 2);
+                            fence();
+#pragma unroll
+                            for (int jj = 0; jj < QPW; ++jj) {
+                                cm[jj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                                    a[jj][t], b[t], t == 0 ? f32x16{} : cm[jj], 0, 0, 0);
+                                fence();
+                                if constexpr (EPI) piece(ce, part, jj, 2 * t, 2);
+                                fence();
+                            }
                         }
                     }
+                    fence();
                 };
-                // subtiles in pairs (acc[0]: even, acc[1]: odd), not unrolled: the
-                // registers of one pair are all that is live
-                mfmas(0, acc[0]);
+                using Yes = std::integral_constant<bool, true>;
+                using No = std::integral_constant<bool, false>;
+                float part[QPW];
+                // subtiles in pairs (acc[0]: even, acc[1]: odd); the last pair is peeled
+                // so that no branch splits a step
+                step(No{}, 0, acc[0], acc[1], part);
 #pragma unroll 1
-                for (int ns = 0; ns < NSUB; ns += 2) {
-                    float part[QPW];
-                    mfmas(ns + 1, acc[1]);
-                    head_sums(acc[0], part);
-                    interleave();
+                for (int ns = 0; ns + 2 < NSUB; ns += 2) {
+                    step(Yes{}, ns + 1, acc[1], acc[0], part);
                     finish(ns, part);
-                    if (ns + 2 < NSUB) {                      // uniform
-                        mfmas(ns + 2, acc[0]);
-                        head_sums(acc[1], part);
-                        interleave();
-                        finish(ns + 1, part);
-                    } else {
-                        head_sums(acc[1], part);
-                        finish(ns + 1, part);
-                    }
+                    step(Yes{}, ns + 2, acc[0], acc[1], part);
+                    finish(ns + 1, part);
                 }
+                step(Yes{}, NSUB - 1, acc[1], acc[0], part);
+                finish(NSUB - 2, part);
+                head_sums(acc[1], part);
+                finish(NSUB - 1, part);
                 continue;
             }
 #pragma unroll 1
