@@ -164,6 +164,7 @@ def make_step(wl, inp, dev):
         ws_bytes = gsa.group_workspace_bytes(wl.n_q, ld, max(n_att, 1))
     bufs = dict(
         scores=torch.empty((wl.n_q, ld), dtype=torch.float32, device=dev),
+        gmax=torch.empty((wl.n_q, gsa.group_max_ld(ld)), dtype=torch.float32, device=dev),
         idx=torch.empty((n_full, wl.n_q, 2048), dtype=torch.int32, device=dev),
         ws=torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev),
         outs=[(torch.empty((wl.n_q, 64, 512), dtype=torch.float32, device=dev),
@@ -174,10 +175,11 @@ def make_step(wl, inp, dev):
     def score_call(j):
         q, w, k, qs, ks = inp["indexers"][j]
         return lambda: gsa.indexer_score(q, w, k, q_seq, q_pos, q_scale=qs, k_scale=ks,
-                                         scores=bufs["scores"])
+                                         scores=bufs["scores"], group_max=bufs["gmax"])
 
     def topk_call(j):
-        return lambda: gsa.topk(bufs["scores"], q_pos, idx=bufs["idx"][j], workspace=bufs["ws"])
+        return lambda: gsa.topk(bufs["scores"], q_pos, idx=bufs["idx"][j], workspace=bufs["ws"],
+                                group_max=bufs["gmax"])
 
     def mla_call(j, layers):
         lay = [inp["layers"][l] for l in layers]

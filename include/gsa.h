@@ -100,6 +100,10 @@ gsa_status gsa_quantize_e4m3(const void* x_dev, int64_t n_blocks,
  *            [0, n_cap). Queries of one sequence should be adjacent (any order
  *            is correct; adjacency lets them share key reads).
  * scores_dev fp32 [n_q, ld_scores], ld_scores >= n_cap, ld_scores % 4 == 0.
+ * group_max_dev fp32 [n_q, gsa_group_max_ld(ld_scores)] out, or NULL (not
+ *            written): group_max[i, g] = the largest of scores[i, 32g .. 32g+31]
+ *            over columns < n_cap, -0.0 given as +0.0. gsa_topk uses them to
+ *            pass over scores that cannot be selected.
  * Errors: null pointers, n_q < 1, batch < 1, n_cap < 1, bad ld, bad dtype,
  *         missing scales for FP8, n_cap > 2^31 - 1.
  */
@@ -108,7 +112,11 @@ gsa_status gsa_indexer_score(gsa_dtype dt,
                              const void* k_dev, const float* k_scale_dev,
                              const int32_t* q_seq_dev, const int32_t* q_pos_dev,
                              int n_q, int batch, int64_t n_cap,
-                             float* scores_dev, int64_t ld_scores, void* stream);
+                             float* scores_dev, int64_t ld_scores, float* group_max_dev,
+                             void* stream);
+
+/* Row stride of the group maxima of score rows of stride ld_scores: ceil(ld / 32). */
+int64_t gsa_group_max_ld(int64_t ld_scores);
 
 /*
  * gsa_topk — causal top-k over each score row ([Arch] §2.2 and §1.1:
@@ -118,14 +126,22 @@ gsa_status gsa_indexer_score(gsa_dtype dt,
  * largest scores; ties go to the lower position; -0.0 ties with +0.0.
  * idx_dev int32 [n_q, k] out: the kept positions in ascending order, then -1.
  * NaN scores are not supported.
- * scores_dev fp32 [n_q, ld_scores] (ld_scores % 4 == 0, >= max q_pos + 1).
+ * scores_dev fp32 [n_q, ld_scores] (ld_scores % 4 == 0, >= max q_pos + 1,
+ *            <= 2^23).
+ * group_max_dev the group maxima of these scores as gsa_indexer_score writes
+ *            them, or NULL (then computed in the workspace, at the cost of one
+ *            more read of the rows). Rows of at least 2048 full groups
+ *            (q_pos + 1 >= 65536) select only among scores >= the 2048th
+ *            largest group maximum, which holds the selection exactly when the
+ *            maxima are those of the scores (the caller's duty when passing them).
  * workspace_dev: at least gsa_topk_workspace_bytes(n_q, ld_scores, k) bytes,
  *            16-byte aligned; its contents on entry do not matter.
- * Errors: k != 2048 (GSA_ERR_UNSUPPORTED), null pointers, small workspace.
+ * Errors: k != 2048 or ld_scores > 2^23 (GSA_ERR_UNSUPPORTED), null pointers,
+ *         small workspace.
  */
 size_t gsa_topk_workspace_bytes(int n_q, int64_t ld_scores, int k);
 gsa_status gsa_topk(const float* scores_dev, int64_t ld_scores, const int32_t* q_pos_dev,
-                    int n_q, int k, int32_t* idx_dev,
+                    int n_q, int k, const float* group_max_dev, int32_t* idx_dev,
                     void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*

@@ -80,9 +80,10 @@ def _declare(lib):
         "gsa_last_error": (ctypes.c_char_p, []),
         "gsa_version": (ctypes.c_char_p, []),
         "gsa_quantize_e4m3": (I, [P, I64, P, P, P]),
-        "gsa_indexer_score": (I, [I, P, P, P, P, P, P, P, I, I, I64, P, I64, P]),
+        "gsa_indexer_score": (I, [I, P, P, P, P, P, P, P, I, I, I64, P, I64, P, P]),
+        "gsa_group_max_ld": (I64, [I64]),
         "gsa_topk_workspace_bytes": (SZ, [I, I64, I]),
-        "gsa_topk": (I, [P, I64, P, I, I, P, P, SZ, P]),
+        "gsa_topk": (I, [P, I64, P, I, I, P, P, P, SZ, P]),
         "gsa_mla_workspace_bytes": (SZ, [I, I, I]),
         "gsa_sparse_mla_attn": (I, [P, P, P, P, P, I, I, I, I, I64, F, P, P, P, SZ, P]),
         "gsa_group_workspace_bytes": (SZ, [I, I64, I, I, I]),
@@ -151,9 +152,17 @@ def quantize_e4m3(x):
     return codes, scales
 
 
-def indexer_score(q, w, k, q_seq, q_pos, q_scale=None, k_scale=None, scores=None, ld=None):
+def group_max_ld(ld):
+    """Row stride of the group maxima of score rows of stride ld."""
+    return int(lib().gsa_group_max_ld(ld))
+
+
+def indexer_score(q, w, k, q_seq, q_pos, q_scale=None, k_scale=None, scores=None, ld=None,
+                  group_max=None):
     """q [n_q,32,128], k [B,N,128] (bf16, or uint8 E4M3 codes with scales);
-    w fp32 [n_q,32]; q_seq/q_pos int32 [n_q]. Returns fp32 scores [n_q, ld]."""
+    w fp32 [n_q,32]; q_seq/q_pos int32 [n_q]. Returns fp32 scores [n_q, ld].
+    group_max: fp32 [n_q, group_max_ld(ld)] to receive the maxima of each 32
+    scores (for topk), or None."""
     fp8 = q.dtype == torch.uint8
     n_q, batch, n_cap = q.shape[0], k.shape[0], k.shape[1]
     _need(q, "q", torch.uint8 if fp8 else torch.bfloat16, (n_q, INDEX_HEADS, INDEX_DIM))
@@ -169,9 +178,11 @@ def indexer_score(q, w, k, q_seq, q_pos, q_scale=None, k_scale=None, scores=None
     if scores is None:
         scores = torch.empty((n_q, ld), dtype=torch.float32, device=q.device)
     _need(scores, "scores", torch.float32)
+    if group_max is not None:
+        _need(group_max, "group_max", torch.float32, (n_q, group_max_ld(scores.shape[1])))
     _check(lib().gsa_indexer_score(FP8_E4M3 if fp8 else BF16, _p(q), _p(q_scale), _p(w), _p(k),
                                    _p(k_scale), _p(q_seq), _p(q_pos), n_q, batch, n_cap,
-                                   _p(scores), scores.shape[1], _stream(q.device)))
+                                   _p(scores), scores.shape[1], _p(group_max), _stream(q.device)))
     return scores
 
 
@@ -201,16 +212,19 @@ def _workspace(nbytes, device, ws):
     return ws
 
 
-def topk(scores, q_pos, k=TOPK, idx=None, workspace=None):
-    """scores fp32 [n_q, ld]; q_pos int32 [n_q] -> idx int32 [n_q, k]."""
+def topk(scores, q_pos, k=TOPK, idx=None, workspace=None, group_max=None):
+    """scores fp32 [n_q, ld]; q_pos int32 [n_q] -> idx int32 [n_q, k].
+    group_max: the scores' group maxima from indexer_score, or None."""
     n_q, ld = scores.shape
     _need(scores, "scores", torch.float32)
     _need(q_pos, "q_pos", torch.int32, (n_q,))
+    if group_max is not None:
+        _need(group_max, "group_max", torch.float32, (n_q, group_max_ld(ld)))
     if idx is None:
         idx = torch.empty((n_q, k), dtype=torch.int32, device=scores.device)
     _need(idx, "idx", torch.int32, (n_q, k))
     ws = _workspace(topk_workspace_bytes(n_q, ld, k), scores.device, workspace)
-    _check(lib().gsa_topk(_p(scores), ld, _p(q_pos), n_q, k, _p(idx), _p(ws), ws.numel(),
+    _check(lib().gsa_topk(_p(scores), ld, _p(q_pos), n_q, k, _p(group_max), _p(idx), _p(ws), ws.numel(),
                           _stream(scores.device)))
     return idx
 

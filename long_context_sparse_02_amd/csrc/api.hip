@@ -58,7 +58,8 @@ gsa_status check_topk(const float* scores, int64_t ld, const int32_t* q_pos, int
     if (n_q > kMaxGridY) return fail(GSA_ERR_UNSUPPORTED, "n_q must be <= %d (got %d)", kMaxGridY, n_q);
     if (k != GSA_TOPK) return fail(GSA_ERR_UNSUPPORTED, "k must be %d (got %d)", GSA_TOPK, k);
     REQUIRE(ld >= 1 && ld % 4 == 0, "ld_scores must be a positive multiple of 4 (got %lld)", (long long)ld);
-    REQUIRE(ld <= 0x7fffffff, "ld_scores must be < 2^31");
+    if (ld > ((int64_t)1 << 23))
+        return fail(GSA_ERR_UNSUPPORTED, "ld_scores must be <= 2^23 (got %lld)", (long long)ld);
     const size_t need = gsa::topk_workspace_bytes(n_q, ld, k);
     if (ws == nullptr || ws_bytes < need)
         return fail(GSA_ERR_WORKSPACE, "top-k workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
@@ -152,13 +153,16 @@ gsa_status gsa_quantize_e4m3(const void* x, int64_t n_blocks, uint8_t* codes, fl
 gsa_status gsa_indexer_score(gsa_dtype dt, const void* q, const float* q_scale, const float* w,
                              const void* k, const float* k_scale, const int32_t* q_seq,
                              const int32_t* q_pos, int n_q, int batch, int64_t n_cap,
-                             float* scores, int64_t ld, void* stream) {
+                             float* scores, int64_t ld, float* group_max, void* stream) {
     gsa_status st = check_score(dt, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, batch, n_cap, scores, ld);
     if (st != GSA_OK) return st;
     return hip_result(gsa::launch_indexer_score(dt == GSA_FP8_E4M3, q, q_scale, w, k, k_scale, q_seq,
-                                                q_pos, n_q, batch, n_cap, scores, ld, (hipStream_t)stream),
+                                                q_pos, n_q, batch, n_cap, scores, ld, group_max,
+                                                (hipStream_t)stream),
                       "indexer_score");
 }
+
+int64_t gsa_group_max_ld(int64_t ld) { return ld < 1 ? 0 : gsa::group_max_ld(ld); }
 
 size_t gsa_topk_workspace_bytes(int n_q, int64_t ld, int k) {
     if (n_q < 1 || ld < 1) return 0;
@@ -166,10 +170,11 @@ size_t gsa_topk_workspace_bytes(int n_q, int64_t ld, int k) {
 }
 
 gsa_status gsa_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
-                    int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+                    const float* group_max, int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
     gsa_status st = check_topk(scores, ld, q_pos, n_q, k, idx, ws, ws_bytes);
     if (st != GSA_OK) return st;
-    return hip_result(gsa::launch_topk(scores, ld, q_pos, n_q, k, idx, ws, (hipStream_t)stream), "topk");
+    return hip_result(gsa::launch_topk(scores, ld, q_pos, n_q, k, group_max, idx, ws, (hipStream_t)stream),
+                      "topk");
 }
 
 size_t gsa_mla_workspace_bytes(int n_q, int n_heads, int k) {
@@ -294,12 +299,14 @@ gsa_status validate_group(const gsa_group_desc* d) {
 // Enqueues a validated group: score -> top-k (F layer) -> attention per layer.
 gsa_status enqueue_group(const gsa_group_desc* d, hipStream_t s) {
     if (d->compute_index) {
+        // the score kernel writes the group maxima where the top-k keeps them
+        float* gm = gsa::topk_group_max_area(d->workspace_dev, d->n_q, d->ld_scores);
         hipError_t e = gsa::launch_indexer_score(d->dt == GSA_FP8_E4M3, d->q_idx_dev, d->q_scale_dev,
                                                  d->w_dev, d->k_idx_dev, d->k_scale_dev, d->q_seq_dev,
                                                  d->q_pos_dev, d->n_q, d->batch, d->n_cap,
-                                                 d->scores_dev, d->ld_scores, s);
+                                                 d->scores_dev, d->ld_scores, gm, s);
         if (e != hipSuccess) return hip_result(e, "group: indexer_score");
-        e = gsa::launch_topk(d->scores_dev, d->ld_scores, d->q_pos_dev, d->n_q, d->k, d->index_buf_dev,
+        e = gsa::launch_topk(d->scores_dev, d->ld_scores, d->q_pos_dev, d->n_q, d->k, gm, d->index_buf_dev,
                              d->workspace_dev, s);
         if (e != hipSuccess) return hip_result(e, "group: topk");
     }

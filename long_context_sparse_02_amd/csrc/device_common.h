@@ -25,6 +25,35 @@ __device__ __forceinline__ uint32_t score_key(float f) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The fp32 value of an order-preserving key (inverse of score_key; +0 for the
+// folded zero).
+__device__ __forceinline__ float key_value(uint32_t key) {
+    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
+// The largest key over the 32 lanes of each half-wave, in every lane: two
+// quad permutations, the half-row and row mirrors (DPP) and a permlane16 swap
+// between the two rows of the half-wave. VALU only.
+__device__ __forceinline__ uint32_t max_x32(uint32_t v) {
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // lane ^ 1
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // lane ^ 2
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // 7 - lane in 8
+    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // 15 - lane in 16
+    const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);                   // other row
+    return max((uint32_t)r[0], (uint32_t)r[1]);
+}
+
+// The same over fp32 values (v_max_f32 with DPP operands): the result is one of
+// the 32 values (a NaN counts as missing), and a zero maximum may be -0.0.
+__device__ __forceinline__ float max_x32f(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 // E8M0 exponent byte of a power-of-two fp32 scale (its biased exponent field).
 __device__ __forceinline__ int e8m0_of(float s) {
     return (int)((__float_as_uint(s) >> 23) & 0xffu);

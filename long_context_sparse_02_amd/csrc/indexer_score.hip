@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int n_q, int64_t n_cap,
-    float* __restrict__ scores, int64_t ld, int chunk) {
+    float* __restrict__ scores, int64_t ld, float* __restrict__ gmax, int64_t ldg, int chunk) {
     // fp8 tiles hold 256 keys, so every tile moves 32 KiB like a bf16 tile and the
     // per-tile barrier and waits are paid per 32 KiB either way
     using T = KeyTile<FP8, FP8 ? 256 : 128>;
@@ -218,6 +218,10 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
                     res = (s <= apos[jj]) ? part : neg_inf();
                 }
                 if (g == 0 && s < c1) scores[(int64_t)(qb0 + j) * ld + s] = res;
+                if (gmax != nullptr && s0 < c1) {                       // uniform
+                    const uint32_t m = max_x32(score_key(s < c1 ? res : neg_inf()));
+                    if (lane == 0) gmax[(int64_t)(qb0 + j) * ldg + (s0 >> 5)] = key_value(m);
+                }
             }
         }
         ring_barrier();     // the next run refills slots this run's last tiles were read from
@@ -241,7 +245,7 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
     const float* __restrict__ w, const uint8_t* __restrict__ k,
     const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
     const int32_t* __restrict__ q_pos, int n_q, int64_t n_cap,
-    float* __restrict__ scores, int64_t ld, int chunk) {
+    float* __restrict__ scores, int64_t ld, float* __restrict__ gmax, int64_t ldg, int chunk) {
     // 64 KiB tiles (256 bf16 / 512 fp8 keys) in a 2-slot ring: the keys come from
     // L2 (every work-group of a chunk reads the same ones), so one tile in flight
     // covers the latency, and the barrier and DMA issue are paid per 64 KiB
@@ -391,11 +395,46 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                         part[jj] = acc_s;
                     }
                 };
+                // One permlane32 swap of the two queries' partial sums leaves query
+                // jw0 + g's score of key s0 + n in lane 32g + n: one add and one store
+                // serve both queries, and one 32-lane max gives both group maxima
+                // (+0.0f turns a -0.0 maximum into +0.0). Split in four parts that
+                // the fp8 step places between its (64-cycle) MFMAs.
+                static_assert(QPW == 2, "the finish pairs two queries");
+                struct Fin { float sc; float m; int64_t s0; };
+                auto fin_a = [&](int ns, const float (&part)[QPW], Fin& f) __attribute__((always_inline)) {
+                    f.s0 = t0 + (sub0 + ns) * 32;
+                    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
+                                                                    __float_as_uint(part[1]), false, false);
+                    f.sc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
+                    scores[(int64_t)(qb0 + jw0 + g) * ld + f.s0 + n] = f.sc;
+                };
+                auto fin_b = [&](Fin& f) __attribute__((always_inline)) {
+                    if (gmax == nullptr) return;               // uniform
+                    float v = f.sc;
+                    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));
+                    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+                    f.m = v;
+                };
+                auto fin_c = [&](Fin& f) __attribute__((always_inline)) {
+                    if (gmax == nullptr) return;
+                    float v = f.m;
+                    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+                    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+                    f.m = v;
+                };
+                auto fin_d = [&](Fin& f) __attribute__((always_inline)) {
+                    if (gmax == nullptr) return;
+                    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(f.m), __float_as_uint(f.m), false, false);
+                    const float m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) + 0.0f;
+                    if (n == 0) gmax[(int64_t)(qb0 + jw0 + g) * ldg + (f.s0 >> 5)] = m;
+                };
                 auto finish = [&](int ns, const float (&part)[QPW]) __attribute__((always_inline)) {
-                    const int64_t s0 = t0 + (sub0 + ns) * 32;
-#pragma unroll
-                    for (int jj = 0; jj < QPW; ++jj)            // both half-waves hold the sum
-                        scores[(int64_t)(qb0 + jw0 + jj) * ld + s0 + n] = sum_x32(part[jj]);
+                    Fin f;
+                    fin_a(ns, part, f);
+                    fin_b(f);
+                    fin_c(f);
+                    fin_d(f);
                 };
                 // One step of the software pipeline: the LDS reads and MFMAs of subtile
                 // ns into cm and, when EPI, the head sums of the previous subtile (ce) cut
@@ -411,9 +450,11 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                         part[jj] = fmaf(wr[jj][i], __int_as_float(max(__float_as_int(ce[jj][i]), 0)),
                                         i == 0 ? 0.f : part[jj]);
                 };
-                auto step = [&](auto epi_c, int ns, f32x16 (&cm)[QPW], const f32x16 (&ce)[QPW],
-                                float (&part)[QPW]) __attribute__((always_inline)) {
+                auto step = [&](auto epi_c, auto fin_c_, int ns, f32x16 (&cm)[QPW], const f32x16 (&ce)[QPW],
+                                float (&part)[QPW], int ns_fin, const float (&pf)[QPW]) __attribute__((always_inline)) {
                     constexpr bool EPI = decltype(epi_c)::value;
+                    constexpr bool FIN = decltype(fin_c_)::value;   // finish subtile ns_fin (sums in pf)
+                    Fin f;
                     const int nt = sub0 + ns;
                     const uint32_t sub_addr = tile_addr + nt * 32 * T::kRowBytes;
                     fence();
@@ -437,15 +478,21 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                         fence();
                         if constexpr (EPI) piece(ce, part, 0, 8, 8);
                         fence();
+                        if constexpr (FIN) fin_a(ns_fin, pf, f);
+                        fence();
                         cm[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][0], b0, f32x16{}, 0, 0, 0, a_e8[1], 0, ke);
                         fence();
                         if constexpr (EPI) piece(ce, part, 1, 0, 8);
+                        if constexpr (FIN) fin_b(f);
                         fence();
                         cm[0] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[0][1], b1, cm[0], 0, 0, 0, a_e8[0], 0, ke);
                         fence();
                         if constexpr (EPI) piece(ce, part, 1, 8, 8);
+                        if constexpr (FIN) fin_c(f);
                         fence();
                         cm[1] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[1][1], b1, cm[1], 0, 0, 0, a_e8[1], 0, ke);
+                        fence();
+                        if constexpr (FIN) fin_d(f);
                     } else {
                         // the B operand of k-step t is read two k-steps ahead; one eighth
                         // of a query's head sums (2 values) after each MFMA
@@ -469,26 +516,46 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                                 fence();
                             }
                         }
+                        static_assert(!FIN || FP8, "bf16 steps finish outside");
                     }
                     fence();
                 };
                 using Yes = std::integral_constant<bool, true>;
                 using No = std::integral_constant<bool, false>;
-                float part[QPW];
-                // subtiles in pairs (acc[0]: even, acc[1]: odd); the last pair is peeled
-                // so that no branch splits a step
-                step(No{}, 0, acc[0], acc[1], part);
+                // Subtiles in pairs (acc[0]: even, acc[1]: odd). Step ns runs the MFMAs
+                // of subtile ns, the head sums of subtile ns - 1 and the finish of
+                // subtile ns - 2 (head sums alternate between pa and pb); the first
+                // two steps and the last two finishes are peeled, so that no branch
+                // splits a step.
+                float pa[QPW], pb[QPW];
+                if constexpr (FP8) {
+                    step(No{}, No{}, 0, acc[0], acc[1], pa, 0, pb);
+                    step(Yes{}, No{}, 1, acc[1], acc[0], pa, 0, pb);             // pa: subtile 0
 #pragma unroll 1
-                for (int ns = 0; ns + 2 < NSUB; ns += 2) {
-                    step(Yes{}, ns + 1, acc[1], acc[0], part);
-                    finish(ns, part);
-                    step(Yes{}, ns + 2, acc[0], acc[1], part);
-                    finish(ns + 1, part);
+                    for (int ns = 2; ns + 1 < NSUB; ns += 2) {
+                        step(Yes{}, Yes{}, ns, acc[0], acc[1], pb, ns - 2, pa);  // pb: ns - 1
+                        step(Yes{}, Yes{}, ns + 1, acc[1], acc[0], pa, ns - 1, pb);  // pa: ns
+                    }
+                    head_sums(acc[1], pb);                                       // subtile NSUB - 1
+                    finish(NSUB - 2, pa);
+                    finish(NSUB - 1, pb);
+                } else {
+                    // bf16 MFMAs are short (32 cycles): each subtile's finish runs as
+                    // one block right after the next step (measured faster than
+                    // spreading it over the MFMAs)
+                    step(No{}, No{}, 0, acc[0], acc[1], pa, 0, pb);
+#pragma unroll 1
+                    for (int ns = 0; ns + 2 < NSUB; ns += 2) {
+                        step(Yes{}, No{}, ns + 1, acc[1], acc[0], pa, 0, pb);
+                        finish(ns, pa);
+                        step(Yes{}, No{}, ns + 2, acc[0], acc[1], pa, 0, pb);
+                        finish(ns + 1, pa);
+                    }
+                    step(Yes{}, No{}, NSUB - 1, acc[1], acc[0], pa, 0, pb);
+                    finish(NSUB - 2, pa);
+                    head_sums(acc[1], pa);
+                    finish(NSUB - 1, pa);
                 }
-                step(Yes{}, NSUB - 1, acc[1], acc[0], part);
-                finish(NSUB - 2, part);
-                head_sums(acc[1], part);
-                finish(NSUB - 1, part);
                 continue;
             }
 #pragma unroll 1
@@ -535,6 +602,10 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                         const float res = (active && n <= lim) ? part : neg_inf();
                         float* row = scores + (int64_t)(qb0 + jw0 + jj) * ld + s0;
                         if (g == 0 && s0 + n < c1) row[n] = res;
+                        if (gmax != nullptr && s0 < c1) {              // uniform
+                            const uint32_t m = max_x32(score_key(s0 + n < c1 ? res : neg_inf()));
+                            if (lane == 0) gmax[(int64_t)(qb0 + jw0 + jj) * ldg + (s0 >> 5)] = key_value(m);
+                        }
                     }
                 } else {
 #pragma unroll
@@ -542,6 +613,8 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                         if (!inrun[jj]) continue;
                         float* row = scores + (int64_t)(qb0 + jw0 + jj) * ld + s0;
                         if (g == 0 && s0 + n < c1) row[n] = neg_inf();
+                        if (gmax != nullptr && s0 < c1 && lane == 0)
+                            gmax[(int64_t)(qb0 + jw0 + jj) * ldg + (s0 >> 5)] = neg_inf();
                     }
                 }
             }
@@ -555,15 +628,16 @@ template <int QB>
 hipError_t launch_mq(bool fp8, dim3 grid, hipStream_t st, const void* q, const float* qs,
                      const float* w, const void* k, const float* ks, const int32_t* q_seq,
                      const int32_t* q_pos, int n_q, int64_t n_cap, float* scores, int64_t ld,
-                     int chunk) {
+                     float* gmax, int chunk) {
+    const int64_t ldg = (ld + 31) / 32;
     if (fp8)
         hipLaunchKernelGGL((indexer_score_mq<QB, true>), grid, dim3(kMqThreads), 0, st,
                            (const uint8_t*)q, qs, w, (const uint8_t*)k, ks, q_seq, q_pos, n_q,
-                           n_cap, scores, ld, chunk);
+                           n_cap, scores, ld, gmax, ldg, chunk);
     else
         hipLaunchKernelGGL((indexer_score_mq<QB, false>), grid, dim3(kMqThreads), 0, st,
                            (const uint8_t*)q, qs, w, (const uint8_t*)k, ks, q_seq, q_pos, n_q,
-                           n_cap, scores, ld, chunk);
+                           n_cap, scores, ld, gmax, ldg, chunk);
     return hipGetLastError();
 }
 
@@ -571,15 +645,16 @@ template <int QB>
 hipError_t launch_qb(bool fp8, dim3 grid, hipStream_t st, const void* q, const float* qs,
                      const float* w, const void* k, const float* ks, const int32_t* q_seq,
                      const int32_t* q_pos, int n_q, int64_t n_cap, float* scores, int64_t ld,
-                     int chunk) {
+                     float* gmax, int chunk) {
+    const int64_t ldg = (ld + 31) / 32;
     if (fp8)
         hipLaunchKernelGGL((indexer_score_kernel<QB, true>), grid, dim3(kThreads), 0, st,
                            (const uint8_t*)q, qs, w, (const uint8_t*)k, ks, q_seq, q_pos, n_q,
-                           n_cap, scores, ld, chunk);
+                           n_cap, scores, ld, gmax, ldg, chunk);
     else
         hipLaunchKernelGGL((indexer_score_kernel<QB, false>), grid, dim3(kThreads), 0, st,
                            (const uint8_t*)q, qs, w, (const uint8_t*)k, ks, q_seq, q_pos, n_q,
-                           n_cap, scores, ld, chunk);
+                           n_cap, scores, ld, gmax, ldg, chunk);
     return hipGetLastError();
 }
 
@@ -588,7 +663,7 @@ hipError_t launch_qb(bool fp8, dim3 grid, hipStream_t st, const void* q, const f
 hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, const float* w,
                                 const void* k, const float* k_scale, const int32_t* q_seq,
                                 const int32_t* q_pos, int n_q, int batch, int64_t n_cap,
-                                float* scores, int64_t ld, hipStream_t stream) {
+                                float* scores, int64_t ld, float* gmax, hipStream_t stream) {
     // Queries per work-group: the typical number of queries per sequence.
     const int per_seq = n_q / (batch > 0 ? batch : 1);
     const int qb = per_seq >= 16 ? 16 : per_seq >= 8 ? 8 : per_seq >= 4 ? 4 : per_seq >= 2 ? 2 : 1;
@@ -602,11 +677,11 @@ hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, c
     while (chunk > 1024 && n_qblk * ((n_cap + chunk - 1) / chunk) < min_wg) chunk >>= 1;
     const dim3 grid((unsigned)((n_cap + chunk - 1) / chunk), (unsigned)n_qblk);
     switch (qb) {
-        case 16: return launch_mq<16>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
-        case 8: return launch_mq<8>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
-        case 4: return launch_mq<4>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
-        case 2: return launch_qb<2>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
-        default: return launch_qb<1>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, (int)chunk);
+        case 16: return launch_mq<16>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, (int)chunk);
+        case 8: return launch_mq<8>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, (int)chunk);
+        case 4: return launch_mq<4>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, (int)chunk);
+        case 2: return launch_qb<2>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, (int)chunk);
+        default: return launch_qb<1>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, (int)chunk);
     }
 }
 

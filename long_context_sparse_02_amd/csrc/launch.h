@@ -14,11 +14,22 @@ hipError_t launch_quantize_e4m3(const void* x, int64_t n_blocks, uint8_t* codes,
 hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, const float* w,
                                 const void* k, const float* k_scale, const int32_t* q_seq,
                                 const int32_t* q_pos, int n_q, int batch, int64_t n_cap,
-                                float* scores, int64_t ld, hipStream_t stream);
+                                float* scores, int64_t ld, float* group_max, hipStream_t stream);
+
+// Group maxima: group_max[q * ((ld + 31) / 32) + g] = the largest score of
+// positions [32g, 32g + 32) of row q (by the order-preserving key).
+constexpr int kGroup = 32;
+inline int64_t group_max_ld(int64_t ld) { return (ld + kGroup - 1) / kGroup; }
 
 size_t topk_workspace_bytes(int n_q, int64_t ld, int k);
+// Where, inside a top-k workspace, the group maxima of these scores are kept
+// (NULL when rows this short need none): a score launch that writes them there
+// saves the top-k their computation.
+float* topk_group_max_area(void* ws, int n_q, int64_t ld);
+// group_max: the score kernel's group maxima of these scores, or NULL (the
+// top-k then computes them in its workspace).
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
-                       int32_t* idx, void* ws, hipStream_t stream);
+                       const float* group_max, int32_t* idx, void* ws, hipStream_t stream);
 
 // One attention layer's operands (a layer of an IndexShare group).
 struct MlaLayerPtrs {

@@ -33,7 +33,8 @@ constexpr int kFan = 8;                        // lists per merge work-group
 constexpr int kMaxItems = kFan * kK;           // = kChunk
 constexpr int kThreads = 512;
 constexpr int kWaves = kThreads / 64;
-constexpr size_t kListBytes = 16 + (size_t)kK * 8; // count (16-byte slot) + (key, position) pairs
+// count (16-byte slot) + (key, position) pairs, rounded to whole 128-byte lines
+constexpr size_t kListBytes = (16 + (size_t)kK * 8 + 127) / 128 * 128;
 
 constexpr int kPer = kMaxItems / kThreads;      // items per lane (32)
 constexpr int kSeg = 64 * kPer;                 // items per wave (2048)
@@ -59,10 +60,6 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 #pragma unroll
     for (int o = 1; o < 64; o <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
     return v;
-}
-// The fp32 value of an order-preserving key (inverse of score_key).
-__device__ __forceinline__ float key_value(uint32_t key) {
-    return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 // A value every lane of the wave holds (read from LDS after a barrier, or a
 // wave reduction), moved to a scalar register so that branches on it are
@@ -101,10 +98,13 @@ __device__ __forceinline__ void clear_hist(Scratch& sc, int b) {
     h[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
 }
 
-// Item i = kSeg*wave + 64*r + lane of the block is v[r] of that lane (valid for
-// i < n; kFull: n = kMaxItems). The items are in position order. Selects the
-// min(k, n) largest by (key desc, position asc) and emits them in position
-// order through emit(slot, i, r). Returns the number emitted.
+// Item i = 64*PER*wave + 64*r + lane of the block is v[r] of that lane; key 0 (the
+// key of no score but a NaN with every bit set) marks an item that is not there
+// (kFull: every item is). The items are in position order. Selects the min(k, #valid) largest valid items by (key desc,
+// position asc) and emits them in position order through emit(slot, i, r).
+// Returns the number emitted. With t_out (and at least k valid items) only the
+// k-th largest key is found, stored to *t_out by every thread, and nothing is
+// emitted.
 //
 // Threshold: the k-th largest key T is found by radix selection on keys
 // relative to the block minimum: each pass histograms the next 8 bits of the
@@ -113,29 +113,34 @@ __device__ __forceinline__ void clear_hist(Scratch& sc, int b) {
 // search early when its bin is taken whole; otherwise the last pass leaves a
 // single key value T and the number `need` of its copies to keep, which are
 // the lowest positions among them.
-template <bool kFull, typename Emit>
-__device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scratch& sc, Emit emit) {
+template <int PER, bool kFull, typename Emit>
+__device__ __forceinline__ int select_regs(const uint32_t (&v)[PER], Scratch& sc, Emit emit,
+                                           uint32_t* t_out = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int seg0 = kSeg * wave;
-    auto valid = [&](int r) { return kFull || seg0 + 64 * r + lane < n; };
-    if (!kFull && n <= kK) {                                  // everything is kept
+    constexpr int SEG = 64 * PER;                          // items per wave
+    const int seg0 = SEG * wave;
+    auto valid = [&](int r) { return kFull || v[r] != 0u; };
+    uint32_t n_valid = kThreads * PER;
+    if (!kFull) {
         uint32_t c = 0;
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid(r)));
+        for (int r = 0; r < PER; ++r) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid(r)));
         uint32_t slot;
-        block_sum(c, sc, &slot);
+        n_valid = uni(block_sum(uni(c), sc, &slot));
+        if (n_valid <= (uint32_t)kK && t_out == nullptr) {    // everything is kept
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const uint64_t m = __builtin_amdgcn_ballot_w64(valid(r));
-            if (valid(r)) emit(slot + lanes_below(m), seg0 + 64 * r + lane, r);
-            slot += __builtin_popcountll(m);
+            for (int r = 0; r < PER; ++r) {
+                const uint64_t m = __builtin_amdgcn_ballot_w64(valid(r));
+                if (valid(r)) emit(slot + lanes_below(m), seg0 + 64 * r + lane, r);
+                slot += __builtin_popcountll(m);
+            }
+            return (int)n_valid;
         }
-        return n < 0 ? 0 : n;
     }
     // ---- min / max of the valid keys
     uint32_t mn = 0xffffffffu, mx = 0u;
 #pragma unroll
-    for (int r = 0; r < kPer; ++r)
+    for (int r = 0; r < PER; ++r)
         if (valid(r)) { mn = min(mn, v[r]); mx = max(mx, v[r]); }
     mn = wave_min(mn);
     mx = wave_max(mx);
@@ -213,7 +218,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
         // the loop (registers that would cost a work-group of occupancy)
         if (by_value) {
 #pragma unroll
-            for (int r = 0; r < kPer; ++r) {
+            for (int r = 0; r < PER; ++r) {
                 uint32_t key = v[r];
                 asm volatile("" : "+v"(key));
                 if (valid(r) && key >= lo && key <= hi)
@@ -221,7 +226,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
             }
         } else {
 #pragma unroll
-            for (int r = 0; r < kPer; ++r) {
+            for (int r = 0; r < PER; ++r) {
                 const uint32_t d = v[r] - lo;
                 if (valid(r) && v[r] >= lo && d <= hi - lo) atomicAdd(&h[d >> sh], 1u);
             }
@@ -233,7 +238,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
         // exact key range of the chosen bin
         uint32_t nlo = 0xffffffffu, nhi = 0u;
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
+        for (int r = 0; r < PER; ++r) {
             uint32_t key = v[r];
             asm volatile("" : "+v"(key));     // recompute the bin: keeping 32 values live costs occupancy
             if (valid(r) && key >= lo && key <= hi && bin_of(key) == (int)b) {
@@ -257,11 +262,15 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
     // search ended on one key value T = lo with `in_bin` copies: keys > T,
     // plus the first `need` copies of T by position (all of them if need = in_bin).
     const uint32_t T = base;
+    if (t_out != nullptr) {                                    // the k-th largest key only
+        *t_out = T;
+        return 0;
+    }
     if (mx == mn) {                                            // no pass ran: every key is T
-        in_bin = kFull ? (uint32_t)kMaxItems : (uint32_t)n;
+        in_bin = n_valid;
         uint32_t c = 0;
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid(r)));
+        for (int r = 0; r < PER; ++r) c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(valid(r)));
         in_bin_w = c;
     }
     const bool partial = !whole && need != in_bin;
@@ -290,7 +299,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[kPer], int n, Scr
     {
         uint32_t eq_run = eq_before;
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
+        for (int r = 0; r < PER; ++r) {
             const bool s = take(r, eq_run);
             const uint64_t sm = __builtin_amdgcn_ballot_w64(s);
             const uint32_t my = slot + lanes_below(sm);
@@ -305,102 +314,268 @@ __device__ __forceinline__ void write_final_pad(int32_t* out, int count) {
     for (int j = count + threadIdx.x; j < kK; j += kThreads) out[j] = -1;
 }
 
-// Level 1: chunk c of row q.
+// Row q's causal length (never past the row: positions must be < ld).
+__device__ __forceinline__ int64_t row_len(const int32_t* q_pos, int q, int64_t ld) {
+    return min((int64_t)q_pos[q] + 1, ld);
+}
+
+// Group maxima of rows whose scores came without them: work-group (c, q) covers
+// positions [16K c, 16K c + 16K) of row q; positions past q's own are -inf.
+__global__ __launch_bounds__(kThreads) void topk_group_max(const float* __restrict__ scores, int64_t ld,
+                                                           const int32_t* __restrict__ q_pos,
+                                                           float* __restrict__ gmax, int64_t ldg) {
+    const int q = blockIdx.y, c = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t len = row_len(q_pos, q, ld);
+    const int64_t s0 = (int64_t)c * kChunk + kSeg * wave;
+    const float* row = scores + (int64_t)q * ld;
+    float x[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) x[r] = row[min(s0 + 64 * r + lane, ld - 1)];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r) {
+        const int64_t s = s0 + 64 * r + lane;               // groups: lanes 0-31 and 32-63
+        const uint32_t m = max_x32(score_key(s < len && s < ld ? x[r] : neg_inf()));
+        const int64_t grp = (s0 + 64 * r) / kGroup + (lane >> 5);
+        if ((lane & 31) == 0 && grp < ldg) gmax[(int64_t)q * ldg + grp] = key_value(m);
+    }
+}
+
+// Bound: L(q) = the k-th largest maximum over the full 32-position groups of row
+// q, or 0 (no bound) with fewer than k full groups. At most kSmall items take
+// part: beyond that, runs of rg adjacent groups count as one (the maximum of
+// the run), which keeps the bound valid and only loosens it.
+constexpr int kPerSmall = 8;                   // items per lane of the small selections
+constexpr int kSmall = kThreads * kPerSmall;   // 4096 items
+
+__global__ __launch_bounds__(kThreads) void topk_bound(const float* __restrict__ gmax, int64_t ldg,
+                                                       const int32_t* __restrict__ q_pos,
+                                                       uint32_t* __restrict__ bound) {
+    __shared__ Scratch sc;
+    const int q = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int64_t n_full = row_len(q_pos, q, ldg * kGroup) / kGroup;
+    if (n_full < kK) {
+        if (threadIdx.x == 0) bound[q] = 0u;
+        return;
+    }
+    const int64_t rg = (n_full + kSmall - 1) / kSmall;       // groups per item
+    const int n_items = (int)((n_full + rg - 1) / rg);
+    const float* gm = gmax + (int64_t)q * ldg;
+    uint32_t v[kPerSmall];                                    // 0: no item
+#pragma unroll
+    for (int r = 0; r < kPerSmall; ++r) v[r] = 0u;
+    // item i is the maximum of groups i, i + n_items, i + 2 n_items, ... (< n_full):
+    // consecutive lanes read consecutive groups; 4 group runs per load batch
+    auto take = [&](int64_t j, const float (&x)[kPerSmall]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < kPerSmall; ++r) {
+            const int i = 64 * kPerSmall * wave + 64 * r + lane;
+            if (i < n_items && j * n_items + i < n_full) v[r] = max(v[r], score_key(x[r]));
+        }
+    };
+    auto load = [&](int64_t j, float (&x)[kPerSmall]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < kPerSmall; ++r)
+            x[r] = gm[min(j * n_items + 64 * kPerSmall * wave + 64 * r + lane, n_full - 1)];
+    };
+    int64_t j = 0;
+    for (; j + 4 <= rg; j += 4) {                            // uniform
+        float x0[kPerSmall], x1[kPerSmall], x2[kPerSmall], x3[kPerSmall];
+        load(j, x0); load(j + 1, x1); load(j + 2, x2); load(j + 3, x3);
+        take(j, x0); take(j + 1, x1); take(j + 2, x2); take(j + 3, x3);
+    }
+    for (; j < rg; ++j) {
+        float x0[kPerSmall];
+        load(j, x0);
+        take(j, x0);
+    }
+    uint32_t T = 0;
+    select_regs<kPerSmall, false>(v, sc, [](uint32_t, int, int) {}, &T);
+    if (threadIdx.x == 0) bound[q] = T;
+}
+
+// Chunk c of row q: its keys >= the row's bound (all keys without one), cut to
+// their top k. One list per chunk, or the final indices when the row has one chunk.
 __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__ scores, int64_t ld,
                                                        const int32_t* __restrict__ q_pos, int n_chunks,
+                                                       const uint32_t* __restrict__ bound,
                                                        uint8_t* __restrict__ lists, int32_t* __restrict__ idx) {
     __shared__ Scratch sc;
     const int q = blockIdx.y, c = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t len = (int64_t)q_pos[q] + 1;
+    const int64_t len = row_len(q_pos, q, ld);
     const int64_t s0 = (int64_t)c * kChunk;
     const int n = (int)max((int64_t)0, min(s0 + kChunk, len) - s0);
+    const uint32_t L = bound != nullptr ? uni(bound[q]) : 0u;
     const float* row = scores + (int64_t)q * ld + s0;
     // lane holds items kSeg*wave + 64r + lane: each wave load reads 256 contiguous bytes.
     // Loads are unconditional (clamped address) so all 32 are in flight together; a
     // branch around each would make the compiler wait for each one at the join.
-    uint32_t v[kPer];
+    uint32_t v[kPer];                                         // 0: not a candidate
     if (n > 0) {
         float x[kPer];
 #pragma unroll
         for (int r = 0; r < kPer; ++r) x[r] = row[min(kSeg * wave + 64 * r + lane, n - 1)];
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) v[r] = kSeg * wave + 64 * r + lane < n ? score_key(x[r]) : 0u;
+        for (int r = 0; r < kPer; ++r) {
+            const uint32_t key = score_key(x[r]);
+            v[r] = (kSeg * wave + 64 * r + lane < n && key >= L) ? key : 0u;
+        }
     } else {
 #pragma unroll
         for (int r = 0; r < kPer; ++r) v[r] = 0u;
     }
+    const bool full = n == kMaxItems && L == 0u;                // uniform
     if (n_chunks == 1) {
         int32_t* out = idx + (int64_t)q * kK;
         auto em = [&](uint32_t slot, int i, int) { out[slot] = (int32_t)(s0 + i); };
-        const int cnt = n == kMaxItems ? select_regs<true>(v, n, sc, em) : select_regs<false>(v, n, sc, em);
+        const int cnt = full ? select_regs<kPer, true>(v, sc, em) : select_regs<kPer, false>(v, sc, em);
         write_final_pad(out, cnt);
     } else {
-        uint8_t* L = lists + ((size_t)q * n_chunks + c) * kListBytes;
-        uint2* items = (uint2*)(L + 16);
+        uint8_t* Lst = lists + ((size_t)q * n_chunks + c) * kListBytes;
+        uint2* items = (uint2*)(Lst + 16);
         auto em = [&](uint32_t slot, int i, int r) { items[slot] = make_uint2(v[r], (uint32_t)(s0 + i)); };
-        const int cnt = n == kMaxItems ? select_regs<true>(v, n, sc, em) : select_regs<false>(v, n, sc, em);
-        if (threadIdx.x == 0) *(uint32_t*)L = (uint32_t)cnt;
+        const int cnt = full ? select_regs<kPer, true>(v, sc, em) : select_regs<kPer, false>(v, sc, em);
+        if (threadIdx.x == 0) *(uint32_t*)Lst = (uint32_t)cnt;
     }
 }
 
-// Level 2+: lists [kFan*g, kFan*g + kFan) of row q (n_in lists per row) into one.
-__global__ __launch_bounds__(kThreads) void topk_merge(const uint8_t* __restrict__ in, int n_in,
-                                                       uint8_t* __restrict__ out_lists, int n_out,
-                                                       int32_t* __restrict__ idx) {
-    __shared__ Scratch sc;
-    __shared__ uint32_t base[kFan + 1];
-    const int q = blockIdx.y, g = blockIdx.x;
+// Number of list levels the merge may write: rounds of 8 until one list is left.
+__host__ __device__ inline int64_t level_lists(int64_t n_lists) { return (n_lists + kFan - 1) / kFan; }
+
+struct MergeLds {
+    Scratch sc;
+    uint32_t base[kThreads + 1];                // item offset of each list in the concatenation
+};
+
+// Lists [l0, l0 + nl) of a row (each at most k items, in position order), at
+// most kMaxItems items in all, concatenated into registers: item i of the
+// concatenation sits in list l with base[l] <= i < base[l + 1] (a binary search
+// over the offsets in LDS) and is read from HBM / L2 directly. Returns the
+// number of items.
+template <int PER>
+__device__ __forceinline__ int gather_lists(const uint8_t* lists0, int l0, int nl, MergeLds& m,
+                                            uint32_t (&v)[PER], uint32_t (&p)[PER]) {
+    constexpr int SEG = 64 * PER;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int l0 = g * kFan;
-    const int nl = min(kFan, n_in - l0);
-    if (threadIdx.x == 0) {
-        uint32_t b = 0;
-        for (int l = 0; l < nl; ++l) {
-            base[l] = b;
-            b += min(*(const uint32_t*)(in + ((size_t)q * n_in + l0 + l) * kListBytes), (uint32_t)kK);
-        }
-        base[nl] = b;
+    __syncthreads();                                          // earlier readers of sc and base are done
+    uint32_t cnt = 0;
+    if (threadIdx.x < nl)
+        cnt = min(*(const uint32_t*)(lists0 + (size_t)(l0 + threadIdx.x) * kListBytes), (uint32_t)kK);
+    // exclusive prefix over the lists (nl <= kThreads)
+    uint32_t incl = cnt;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t t = (uint32_t)__shfl_up((int)incl, o, 64);
+        if (lane >= o) incl += t;
     }
+    if (lane == 63) m.sc.wsum[wave] = incl;
     __syncthreads();
-    const int n = (int)base[nl];
-    // item i of the concatenation (lists in order) is item i - base[l] of list l
-    uint32_t v[kPer], p[kPer];
-    uint32_t bl[kFan];
+    uint32_t before = 0, total = 0;
 #pragma unroll
-    for (int j = 0; j < kFan; ++j) bl[j] = j < nl ? base[j] : 0xffffffffu;
-    {
-        uint2 it[kPer];
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t t = m.sc.wsum[w];
+        before += w < wave ? t : 0u;
+        total += t;
+    }
+    total = uni(total);
+    if (threadIdx.x < nl) m.base[threadIdx.x] = before + incl - cnt;
+    if (threadIdx.x == 0) m.base[nl] = total;
+    __syncthreads();
+    const int steps = 32 - __builtin_clz((uint32_t)nl);         // ceil(log2(nl + 1))
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {        // unconditional loads: all in flight together
-            const int i = min(kSeg * wave + 64 * r + lane, max(n - 1, 0));
-            int l = 0;
+    for (int r = 0; r < PER; ++r) { v[r] = 0u; p[r] = 0u; }
+    if ((uint32_t)(SEG * wave) < total) {                    // uniform: this wave holds items
+        uint32_t li[PER];
 #pragma unroll
-            for (int j = 1; j < kFan; ++j) l += (uint32_t)i >= bl[j] ? 1 : 0;
-            it[r] = ((const uint2*)(in + ((size_t)q * n_in + l0 + l) * kListBytes + 16))[i - bl[l]];
+        for (int r = 0; r < PER; ++r) {
+            const uint32_t i = min((uint32_t)(SEG * wave + 64 * r + lane), total - 1);
+            uint32_t lo = 0, span = 1u << steps;              // largest l with base[l] <= i
+            for (int t = 0; t < steps; ++t) {
+                span >>= 1;
+                const uint32_t mid = lo + span;
+                if (mid < (uint32_t)nl && m.base[min(mid, (uint32_t)nl)] <= i) lo = mid;
+            }
+            li[r] = lo;
+        }
+        uint2 it[PER];
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const uint32_t i = min((uint32_t)(SEG * wave + 64 * r + lane), total - 1);
+            it[r] = ((const uint2*)(lists0 + (size_t)(l0 + li[r]) * kListBytes + 16))[i - m.base[li[r]]];
         }
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const bool ok = kSeg * wave + 64 * r + lane < n;
+        for (int r = 0; r < PER; ++r) {
+            const bool ok = (uint32_t)(SEG * wave + 64 * r + lane) < total;
             v[r] = ok ? it[r].x : 0u;
             p[r] = ok ? it[r].y : 0u;
         }
     }
-    if (n_out == 1) {
-        int32_t* out = idx + (int64_t)q * kK;
-        auto em = [&](uint32_t slot, int, int r) { out[slot] = (int32_t)p[r]; };
-        const int cnt = n == kMaxItems ? select_regs<true>(v, n, sc, em) : select_regs<false>(v, n, sc, em);
-        write_final_pad(out, cnt);
-    } else {
-        uint8_t* L = out_lists + ((size_t)q * n_out + g) * kListBytes;
-        uint2* items = (uint2*)(L + 16);
-        auto em = [&](uint32_t slot, int, int r) { items[slot] = make_uint2(v[r], p[r]); };
-        const int cnt = n == kMaxItems ? select_regs<true>(v, n, sc, em) : select_regs<false>(v, n, sc, em);
-        if (threadIdx.x == 0) *(uint32_t*)L = (uint32_t)cnt;
+    return (int)total;
+}
+
+// Row q: its n_lists chunk lists into the final indices. levels: workspace for
+// the rounds of the fallback (level_lists(n_lists) lists per row, then
+// level_lists of that, ...), used only when the lists hold more than 16K items.
+__global__ __launch_bounds__(kThreads) void topk_merge(const uint8_t* __restrict__ lists, int n_lists,
+                                                       uint8_t* __restrict__ levels, int32_t* __restrict__ idx) {
+    __shared__ MergeLds m;
+    const int q = blockIdx.x;
+    int32_t* out = idx + (int64_t)q * kK;
+    const uint8_t* in = lists + (size_t)q * n_lists * kListBytes;
+    int nl = n_lists;
+    // items of this row's lists (each count read once per list)
+    uint32_t tot_local = 0;
+    for (int l = threadIdx.x; l < nl; l += kThreads)
+        tot_local += min(*(const uint32_t*)(in + (size_t)l * kListBytes), (uint32_t)kK);
+    uint32_t total = uni(block_sum(uni(wave_sum(tot_local)), m.sc));
+    // fallback: rounds of 8 lists until the rest fits in one selection
+    uint8_t* lvl = levels;
+    int64_t lvl_rows = level_lists(n_lists);
+    while (total > (uint32_t)kMaxItems) {                     // uniform
+        const int ng = (nl + kFan - 1) / kFan;
+        uint8_t* outl = lvl + (size_t)q * lvl_rows * kListBytes;
+        uint32_t new_total = 0;
+        for (int gi = 0; gi < ng; ++gi) {
+            uint32_t v[kPer], p[kPer];
+            gather_lists<kPer>(in, gi * kFan, min(kFan, nl - gi * kFan), m, v, p);
+            uint8_t* Lst = outl + (size_t)gi * kListBytes;
+            uint2* items = (uint2*)(Lst + 16);
+            auto em = [&](uint32_t slot, int, int r) { items[slot] = make_uint2(v[r], p[r]); };
+            const int cnt = select_regs<kPer, false>(v, m.sc, em);
+            if (threadIdx.x == 0) *(uint32_t*)Lst = (uint32_t)cnt;
+            new_total += (uint32_t)cnt;
+            __threadfence();
+            __syncthreads();
+        }
+        in = outl;
+        nl = ng;
+        total = new_total;
+        lvl += (size_t)gridDim.x * lvl_rows * kListBytes;
+        lvl_rows = level_lists(lvl_rows);
     }
+    int cnt;
+    if (total <= (uint32_t)kSmall) {                          // the usual case with a bound
+        uint32_t v[kPerSmall], p[kPerSmall];
+        gather_lists<kPerSmall>(in, 0, nl, m, v, p);
+        auto em = [&](uint32_t slot, int, int r) { out[slot] = (int32_t)p[r]; };
+        cnt = select_regs<kPerSmall, false>(v, m.sc, em);
+    } else {
+        uint32_t v[kPer], p[kPer];
+        gather_lists<kPer>(in, 0, nl, m, v, p);
+        auto em = [&](uint32_t slot, int, int r) { out[slot] = (int32_t)p[r]; };
+        cnt = select_regs<kPer, false>(v, m.sc, em);
+    }
+    write_final_pad(out, cnt);
 }
 
 int n_chunks_of(int64_t ld) { return (int)((ld + kChunk - 1) / kChunk); }
+
+// Rows of at least kK full groups exist only when ld >= kK * kGroup.
+bool bounded(int64_t ld) { return ld >= (int64_t)kK * kGroup; }
+
+size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 }  // namespace
 
@@ -408,28 +583,52 @@ size_t topk_workspace_bytes(int n_q, int64_t ld, int k) {
     (void)k;
     const int nc = n_chunks_of(ld);
     if (nc <= 1) return 16;
-    const int n2 = (nc + kFan - 1) / kFan;
-    return (size_t)n_q * (nc + n2) * kListBytes;
+    size_t b = 0;
+    if (bounded(ld)) {
+        b += align256((size_t)n_q * 4);                              // bounds
+        b += align256((size_t)n_q * group_max_ld(ld) * 4);           // group maxima (when not given)
+    }
+    b += (size_t)n_q * nc * kListBytes;                             // chunk lists
+    for (int64_t n = level_lists(nc); ; n = level_lists(n)) {       // merge fallback rounds
+        b += (size_t)n_q * n * kListBytes;
+        if (n <= 1) break;
+    }
+    return b;
+}
+
+float* topk_group_max_area(void* ws, int n_q, int64_t ld) {
+    if (n_chunks_of(ld) <= 1 || !bounded(ld)) return nullptr;
+    return (float*)((uint8_t*)ws + align256((size_t)n_q * 4));
 }
 
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
-                       int32_t* idx, void* ws, hipStream_t st) {
+                       const float* group_max, int32_t* idx, void* ws, hipStream_t st) {
     (void)k;
     const int nc = n_chunks_of(ld);
-    uint8_t* a = (uint8_t*)ws;                                  // level-1 lists (n_q x nc)
-    uint8_t* b = a + (size_t)n_q * nc * kListBytes;            // level-2 lists (n_q x nc/8)
-    hipLaunchKernelGGL(topk_chunk, dim3(nc, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, nc, a, idx);
-    int n = nc;
-    uint8_t* in = a;
-    uint8_t* out = b;
-    while (n > 1) {
-        const int ng = (n + kFan - 1) / kFan;
-        hipLaunchKernelGGL(topk_merge, dim3(ng, n_q), dim3(kThreads), 0, st, in, n, out, ng, idx);
-        n = ng;
-        uint8_t* t = in;
-        in = out;
-        out = t;
+    if (nc == 1) {
+        hipLaunchKernelGGL(topk_chunk, dim3(1, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, 1,
+                           (const uint32_t*)nullptr, (uint8_t*)nullptr, idx);
+        return hipGetLastError();
     }
+    uint8_t* p = (uint8_t*)ws;
+    const uint32_t* bound = nullptr;
+    if (bounded(ld)) {
+        uint32_t* b = (uint32_t*)p;
+        p += align256((size_t)n_q * 4);
+        float* gm = (float*)p;
+        p += align256((size_t)n_q * group_max_ld(ld) * 4);
+        const int64_t ldg = group_max_ld(ld);
+        if (group_max == nullptr) {
+            hipLaunchKernelGGL(topk_group_max, dim3(nc, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, gm, ldg);
+            group_max = gm;
+        }
+        hipLaunchKernelGGL(topk_bound, dim3(n_q), dim3(kThreads), 0, st, group_max, ldg, q_pos, b);
+        bound = b;
+    }
+    uint8_t* lists = p;
+    uint8_t* levels = lists + (size_t)n_q * nc * kListBytes;
+    hipLaunchKernelGGL(topk_chunk, dim3(nc, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, nc, bound, lists, idx);
+    hipLaunchKernelGGL(topk_merge, dim3(n_q), dim3(kThreads), 0, st, (const uint8_t*)lists, nc, levels, idx);
     return hipGetLastError();
 }
 

@@ -27,7 +27,7 @@ unpinned".
 """
 from .e4m3 import e4m3_decode, e4m3_encode, quantize_blocks, dequantize_blocks
 from .indexer import indexer_score
-from .topk import topk_select
+from .topk import group_max, topk_select
 from .mla import paged_cache_view, sparse_mla
 from .pattern import layer_pattern, shared_source
 from .group import indexer_inputs_fp8, indexshare_group, layer_stack
@@ -36,5 +36,5 @@ __all__ = [
     "e4m3_decode", "e4m3_encode", "quantize_blocks", "dequantize_blocks",
     "indexer_score", "topk_select", "sparse_mla", "layer_pattern",
     "shared_source", "indexshare_group", "layer_stack", "indexer_inputs_fp8",
-    "paged_cache_view",
+    "paged_cache_view", "group_max",
 ]

@@ -31,3 +31,21 @@ def topk_select(scores, q_pos, k: int = 2048) -> np.ndarray:
         kept = np.sort(order[: min(k, length)])
         out[i, : kept.size] = kept
     return out
+
+
+def group_max(scores, n_cols=None, group: int = 32) -> np.ndarray:
+    """The largest score of every run of `group` consecutive columns of each row
+    (columns [group*g, group*g + group) below n_cols; the last run may be
+    shorter), with -0.0 reported as +0.0.
+
+    Not a quantity of the pages: the library's score call can also return these
+    maxima, which its top-k uses to pass over scores that cannot be selected.
+    The oracle states them so that this output can be checked."""
+    scores = np.asarray(scores, dtype=np.float64)
+    n_q, n = scores.shape
+    n_cols = n if n_cols is None else int(n_cols)
+    n_groups = -(-n_cols // group)
+    out = np.empty((n_q, n_groups), dtype=np.float64)
+    for g in range(n_groups):
+        out[:, g] = scores[:, group * g: min(group * g + group, n_cols)].max(axis=1)
+    return out + 0.0                                   # -0.0 + 0.0 = +0.0

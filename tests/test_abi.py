@@ -36,7 +36,7 @@ def _score(**kw):
     a.update(kw)
     return gsa.lib().gsa_indexer_score(a["dt"], a["q"], a["qs"], a["w"], a["k"], a["ks"], a["q_seq"],
                                        a["q_pos"], a["n_q"], a["batch"], a["n_cap"], a["scores"],
-                                       a["ld"], None)
+                                       a["ld"], None, None)
 
 
 @pytest.mark.parametrize("kw,code", [
@@ -55,11 +55,23 @@ def test_topk_rejects():
     L = gsa.lib()
     need = L.gsa_topk_workspace_bytes(4, 4096, 2048)
     assert need > 0
-    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 1024, FAKE, FAKE, need, None) == UNSUPPORTED
-    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 2048, FAKE, FAKE, need - 1, None) == WORKSPACE
-    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 2048, FAKE, None, need, None) == WORKSPACE
-    assert L.gsa_topk(None, 4096, FAKE, 4, 2048, FAKE, FAKE, need, None) == INVALID
-    assert L.gsa_topk(FAKE, 4094, FAKE, 4, 2048, FAKE, FAKE, need, None) == INVALID
+    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 1024, None, FAKE, FAKE, need, None) == UNSUPPORTED
+    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 2048, None, FAKE, FAKE, need - 1, None) == WORKSPACE
+    assert L.gsa_topk(FAKE, 4096, FAKE, 4, 2048, None, FAKE, None, need, None) == WORKSPACE
+    assert L.gsa_topk(None, 4096, FAKE, 4, 2048, None, FAKE, FAKE, need, None) == INVALID
+    assert L.gsa_topk(FAKE, 4094, FAKE, 4, 2048, None, FAKE, FAKE, need, None) == INVALID
+    big = (1 << 23) + 4
+    assert L.gsa_topk(FAKE, big, FAKE, 4, 2048, None, FAKE, FAKE, 1 << 40, None) == UNSUPPORTED
+
+
+def test_topk_workspace_and_group_max_layout():
+    L = gsa.lib()
+    assert L.gsa_group_max_ld(4096) == 128 and L.gsa_group_max_ld(4100) == 129
+    # rows that cannot have 2048 full groups need no bound; longer ones keep one
+    # bound word and one group maximum per 32 scores per row besides the lists
+    short = L.gsa_topk_workspace_bytes(8, 65504, 2048)
+    long_ = L.gsa_topk_workspace_bytes(8, 65536, 2048)
+    assert long_ - short >= 8 * (4 + 4 * 2048)
 
 
 def test_sparse_mla_rejects():

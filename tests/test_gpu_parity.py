@@ -48,18 +48,28 @@ def _score_case(wl, seed, ld=None, dtype="bf16", perm=None):
     d = dev()
     ld = ld or (wl.n_ctx + 3) // 4 * 4
     scores = torch.full((wl.n_q, ld), 12345.0, device=d)
+    gmax = torch.full((wl.n_q, gsa.group_max_ld(ld)), 777.0, device=d)
     if dtype == "fp8":
         qc, qs = gsa.quantize_e4m3(q.to(d))
         kc, ks = gsa.quantize_e4m3(k.to(d))
-        gsa.indexer_score(qc, w.to(d), kc, q_seq.to(d), q_pos.to(d), q_scale=qs, k_scale=ks, scores=scores)
+        gsa.indexer_score(qc, w.to(d), kc, q_seq.to(d), q_pos.to(d), q_scale=qs, k_scale=ks, scores=scores,
+                          group_max=gmax)
     else:
-        gsa.indexer_score(q.to(d), w.to(d), k.to(d), q_seq.to(d), q_pos.to(d), scores=scores)
+        gsa.indexer_score(q.to(d), w.to(d), k.to(d), q_seq.to(d), q_pos.to(d), scores=scores, group_max=gmax)
     torch.cuda.synchronize()
     want = oracle.indexer_score(np32(q), np32(w), np32(k), np32(q_seq), np32(q_pos))
     got = np32(scores)
     for i in range(wl.n_q):
         assert_scores_equal(got[i, : wl.n_ctx], want[i], f"query {i}")
     assert np.all(got[:, wl.n_ctx:] == 12345.0), "columns past n_cap were written"
+    # group maxima: bit-exact (integer inputs), +0.0 for a zero maximum, untouched past n_cap
+    ng = -(-wl.n_ctx // 32)
+    gm_want = oracle.group_max(want, n_cols=wl.n_ctx)
+    gm = np32(gmax)
+    for i in range(wl.n_q):
+        assert_scores_equal(gm[i, :ng], gm_want[i], f"query {i} group maxima")
+    assert not np.any(np.signbit(gm[:, :ng]) & (gm[:, :ng] == 0)), "-0.0 group maximum"
+    assert np.all(gm[:, ng:] == 777.0), "group maxima past n_cap were written"
     return got
 
 
@@ -127,6 +137,46 @@ def test_topk_matches_oracle(kind):
     got = np32(idx)
     for i in range(pos.numel()):
         assert np.array_equal(got[i], want[i]), f"{kind} row {i} (pos {int(pos[i])})"
+
+
+def _topk_case(s, pos, label, with_max=True):
+    """gsa.topk with the group maxima computed inside, and (with_max) with the
+    oracle's maxima passed in; both against the oracle."""
+    d = dev()
+    want = oracle.topk_select(np32(s), np32(pos), 2048)
+    runs = [("inside", None)]
+    if with_max:
+        ld = s.shape[1]
+        gm = np.full((s.shape[0], gsa.group_max_ld(ld)), -np.inf, np.float32)
+        gm[:, : -(-ld // 32)] = oracle.group_max(np32(s)).astype(np.float32)
+        runs.append(("given", torch.from_numpy(gm).to(d)))
+    for how, gm in runs:
+        got = np32(gsa.topk(s.to(d), pos.to(d), group_max=gm))
+        for i in range(pos.numel()):
+            assert np.array_equal(got[i], want[i]), f"{label} ({how} maxima) row {i} (pos {int(pos[i])})"
+    say(f"top-k {label}: {pos.numel()} rows match the oracle")
+
+
+@pytest.mark.parametrize("kind", W.SCORE_KINDS)
+def test_topk_bounded_rows_match_oracle(kind):
+    # rows long enough for the group-maximum bound (>= 2048 full groups of 32)
+    # and rows just short of it, in one call; 13 chunks with a ragged tail
+    n = 200_004
+    pos = torch.tensor([n - 1, 65535, 65534, 65536 + 31, 65536 + 32, 150_000, 16383, 2047, 0, 99_999],
+                       dtype=torch.int32)
+    s = W.score_matrix(kind, pos.numel(), n, seed=17)
+    _topk_case(s, pos, f"{kind} n={n}")
+
+
+def test_topk_bound_with_one_huge_value_per_group():
+    # every 32-group holds one large value: the bound is the k-th of them and
+    # many equal scores sit exactly at it
+    n = 131_072
+    s = torch.zeros((3, n))
+    s[:, ::32] = torch.arange(n // 32, dtype=torch.float32).remainder(50)[None] + 100
+    s[1, 5::32] = 149.0
+    pos = torch.tensor([n - 1, n - 1, 70_000], dtype=torch.int32)
+    _topk_case(s, pos, "one large value per group")
 
 
 def test_topk_one_million_row():

@@ -168,3 +168,38 @@ def test_score_on_tiny_group_is_integer_and_fp32_exact():
     fin = sc[np.isfinite(sc)]
     assert np.all(fin == np.round(fin)) and np.abs(fin).max() < 2 ** 24
     assert np.array_equal(fin.astype(np.float32).astype(np.float64), fin)
+
+
+# ---------------------------------------------------------------- group maxima
+def test_group_max_worked_example():
+    row = np.array([[1.0, -0.0, 3.0, 2.0, -np.inf, -np.inf, -5.0, 7.0, -0.0, -1.0]])
+    got = oracle.group_max(row, group=4)
+    assert got.tolist() == [[3.0, 7.0, 0.0]]                    # last run: 2 columns
+    assert not np.signbit(got[0, 2])                            # -0.0 reported as +0.0
+    assert oracle.group_max(row, n_cols=5, group=4).tolist() == [[3.0, -np.inf]]
+
+
+@pytest.mark.parametrize("n", [1, 31, 32, 33, 1000])
+def test_group_max_is_attained_and_bounds_its_group(n):
+    rng = np.random.default_rng(n)
+    s = rng.integers(-50, 50, size=(3, n)).astype(np.float64)
+    gm = oracle.group_max(s)
+    assert gm.shape == (3, -(-n // 32))
+    for i in range(3):
+        for g in range(gm.shape[1]):
+            blk = s[i, 32 * g: 32 * g + 32]
+            assert gm[i, g] in blk and np.all(blk <= gm[i, g])
+        assert gm[i].max() == s[i].max()
+
+
+def test_kth_group_max_bounds_the_kth_score():
+    # the fact the GPU top-k relies on: the k-th largest group maximum is <= the
+    # k-th largest score, so no selected score is below it
+    rng = np.random.default_rng(3)
+    for _ in range(20):
+        n, k = int(rng.integers(64, 3000)), int(rng.integers(1, 60))
+        s = rng.integers(0, 40, size=(1, n)).astype(np.float64)
+        gm = oracle.group_max(s, group=int(rng.integers(1, 40)))
+        if gm.shape[1] < k:
+            continue
+        assert np.sort(gm[0])[::-1][k - 1] <= np.sort(s[0])[::-1][k - 1]
