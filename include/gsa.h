@@ -200,9 +200,9 @@ typedef struct gsa_mla_layer {
 } gsa_mla_layer;
 
 /*
- * gsa_paged_kv — a latent cache kept in pages, as a serving system allocates it
- * (the serving-side form of the gather in [Serving] §10: each layer gathers its
- * own cache rows at the selected positions). Each layer's kv_dev is then a
+ * gsa_paged_kv — a latent cache kept in pages ([Arch] §4.4 names PagedAttention
+ * as the paging used with the 512-d latent cache), for the gather of [Serving]
+ * §10 (each layer gathers its own cache rows at the selected positions). Each layer's kv_dev is then a
  * pool of n_pages pages of page_size rows ([n_pages * page_size, 576] bf16),
  * and position s of sequence b is pool row
  *     block_table_dev[b * max_pages + s / page_size] * page_size + s % page_size.

@@ -669,10 +669,12 @@ hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, c
     const int qb = per_seq >= 16 ? 16 : per_seq >= 8 ? 8 : per_seq >= 4 ? 4 : per_seq >= 2 ? 2 : 1;
     const int64_t n_qblk = (n_q + qb - 1) / qb;
     // Key chunk per work-group, 1K..16K keys. One query per work-group streams
-    // from HBM and wants many work-groups in flight (>= 2048); several queries
+    // from HBM: bf16 rows run best with >= 2048 work-groups (~1 MiB each), fp8
+    // rows with >= 512 (~2 MiB each: half the bytes per key, so the ring fill
+    // each work-group start costs is spread over more keys). Several queries
     // per work-group are compute bound, and fewer, longer chunks (>= 512
-    // work-groups) save the ring refill each work-group start costs.
-    const int64_t min_wg = qb >= 4 ? 512 : 2048;
+    // work-groups) save that refill too.
+    const int64_t min_wg = (qb >= 4 || fp8) ? 512 : 2048;
     int64_t chunk = 16384;
     while (chunk > 1024 && n_qblk * ((n_cap + chunk - 1) / chunk) < min_wg) chunk >>= 1;
     const dim3 grid((unsigned)((n_cap + chunk - 1) / chunk), (unsigned)n_qblk);

@@ -61,8 +61,9 @@ def paged_cache_view(pool, block_table, page_size: int):
     a page not yet allocated) read as NaN, so that attending to them shows.
 
     Pages: "GLM-5→5.1→5.2…" §10 (each layer gathers the selected positions'
-    rows from its own cache); the paged layout is the serving-side reading of
-    where those rows live: fixed-size pages named by a per-sequence table."""
+    rows from its own cache); "GLM-5.2 架构深度拆解" CH4 §4.4 (PagedAttention as
+    the paging used with the 512-d latent cache). The layout is a reading (the
+    pages give none): fixed-size pages named by a per-sequence table."""
     pool = np.asarray(pool, dtype=np.float64)
     pool = pool.reshape(-1, pool.shape[-1])
     bt = np.asarray(block_table, dtype=np.int64)
