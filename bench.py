@@ -73,8 +73,10 @@ def topk_bytes(wl):
 
 
 def mla_bytes(wl):
-    """One sparse-MLA launch: gathered rows + indices + q_lat/q_rope + fp32 output."""
-    return wl.n_q * (2048 * 1152 + 2048 * 4 + 64 * 576 * 2 + 64 * 512 * 4)
+    """One sparse-MLA layer: gathered rows (1152 B bf16, 656 B FP8) + indices +
+    q_lat/q_rope + fp32 output."""
+    row = 656 if wl.kv_dtype == "fp8" else 1152
+    return wl.n_q * (2048 * row + 2048 * 4 + 64 * 576 * 2 + 64 * 512 * 4)
 
 
 def score_flops(wl):
@@ -139,7 +141,12 @@ def build_inputs(wl, seed, dev):
     if wl.mla:
         for l in range(wl.n_layers):
             q_lat, q_rope = W.mla_queries(wl, seed, l, dev)
-            layers.append((q_lat, q_rope, W.mla_cache(wl, seed, l, dev)))
+            kv = W.mla_cache(wl, seed, l, dev)
+            if wl.kv_dtype == "fp8":                   # the cache is kept quantised
+                kv8 = gsa.quantize_latent_fp8(kv)
+                del kv
+                kv = kv8
+            layers.append((q_lat, q_rope, kv))
     torch.cuda.synchronize()
     log(f"[bench] inputs for {wl.name} generated in {time.time() - t0:.1f}s "
         f"({len(full_layers)} full layers, {len(layers)} attention layers)")
@@ -256,6 +263,7 @@ def run_bench(args):
         "config": {"workload": wl.name, "batch": wl.batch, "context": wl.n_ctx,
                    "queries": wl.n_q, "full_layers": len(inp["full_layers"]),
                    "attention_layers": len(inp["layers"]), "indexer": wl.indexer_dtype,
+                   "latent_cache": wl.kv_dtype,
                    "topk": 2048, "mla_heads": 64, "seed": args.seed},
         "breakdown_ms_per_step": {k: round(v, 4) for k, v in ms_kind.items()},
         "avg_launch_us": {k: round(ms_kind[k] / launches[k] * 1e3, 2) for k in kinds},
@@ -319,10 +327,16 @@ def host_indexer_inputs(wl, inp, j, qi, seed, keys=None):
 
 def host_rows(kv, b, sel):
     """The latent rows `sel` (valid entries) of sequence b, fetched by torch's
-    index_select on the device, and the local indices that address them."""
+    index_select on the device (FP8 rows dequantised by the oracle), and the
+    local indices that address them. For the oracle-side callers only."""
     v = sel >= 0
-    rows = np.zeros((len(sel), 576), np.float32)
-    rows[v] = kv[b].index_select(0, torch.from_numpy(sel[v]).to(kv.device).long()).float().cpu().numpy()
+    rows = np.zeros((len(sel), 576), np.float64)
+    got = kv[b].index_select(0, torch.from_numpy(sel[v]).to(kv.device).long()).cpu()
+    if kv.dtype == torch.uint8:
+        import oracle                                  # test infrastructure: oracle-side helper
+        rows[v] = oracle.dequantize_latent(got.numpy())
+    else:
+        rows[v] = got.float().numpy()
     return rows[None], np.where(v, np.arange(len(sel)), -1)[None]
 
 

@@ -218,6 +218,33 @@ typedef struct gsa_paged_kv {
     int64_t n_pages;
 } gsa_paged_kv;
 
+/*
+ * gsa_quantize_latent_fp8 — the FP8 latent cache row ([Overview]
+ * tbl-glm52-config: about 656 bytes per token and layer with per-group scales;
+ * glossary: KV FP8 is E4M3 on the 512-dim latent):
+ *   out[r] = [512 E4M3 codes | 4 fp32 scales | 64 bf16 RoPE dims] (656 bytes)
+ * The latent is quantised in four 128-dim groups with the rule of
+ * gsa_quantize_e4m3 (power-of-two scale, nearest even, saturating at 448); the
+ * RoPE dims are copied. rows_dev bf16 [n_rows, 576]; out_dev uint8 [n_rows,
+ * 656]; both 16-byte aligned. Errors: null or misaligned pointers, n_rows < 0.
+ */
+gsa_status gsa_quantize_latent_fp8(const void* rows_dev, int64_t n_rows, uint8_t* out_dev, void* stream);
+
+/*
+ * gsa_sparse_mla_attn_fp8kv — gsa_sparse_mla_attn_layers over FP8 latent
+ * caches: each layers[l].kv_dev holds 656-byte rows (gsa_quantize_latent_fp8),
+ * [batch, n_cap, 656] contiguous, or page pools [n_pages * page_size, 656] when
+ * paged_kv is not NULL (n_cap is then ignored). Attention is computed on the
+ * dequantised rows (code x group scale, exact in bf16) with the same
+ * arithmetic as the bf16 cache. Same workspace and errors as
+ * gsa_sparse_mla_attn_layers / gsa_sparse_mla_attn_paged.
+ */
+gsa_status gsa_sparse_mla_attn_fp8kv(const gsa_mla_layer* layers, int n_layers,
+                                     const gsa_paged_kv* paged_kv, const int32_t* q_seq_dev,
+                                     const int32_t* idx_dev, int k, int n_q, int n_heads, int batch,
+                                     int64_t n_cap, float scale, void* workspace_dev,
+                                     size_t workspace_bytes, void* stream);
+
 typedef struct gsa_group_desc {
     int compute_index;
     gsa_dtype dt;
@@ -230,9 +257,11 @@ typedef struct gsa_group_desc {
     int n_layers; const gsa_mla_layer* layers;   /* host array of n_layers */
     int n_heads; float scale;
     void* workspace_dev; size_t workspace_bytes;
-    const gsa_paged_kv* paged_kv;   /* NULL: contiguous caches [batch, n_cap, 576]; else each
+    const gsa_paged_kv* paged_kv;   /* NULL: contiguous caches [batch, n_cap, row]; else each
                                        layer's kv_dev is a page pool and n_cap still sizes the
                                        indexer keys and scores (max_pages * page_size >= n_cap) */
+    gsa_dtype kv_dt;                 /* GSA_BF16 (0): 1152-byte bf16 rows; GSA_FP8_E4M3: 656-byte
+                                       FP8 latent rows (gsa_sparse_mla_attn_fp8kv) */
 } gsa_group_desc;
 
 /* workspace of a group with n_layers attention layers (the full layer included) */
@@ -323,6 +352,7 @@ typedef struct gsa_stack_desc {
     int n_heads; float scale;
     void* workspace_dev; size_t workspace_bytes;
     const gsa_paged_kv* paged_kv;   /* as in gsa_group_desc */
+    gsa_dtype kv_dt;                 /* as in gsa_group_desc */
 } gsa_stack_desc;
 
 size_t gsa_stack_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads, int n_layers);

@@ -21,6 +21,7 @@ HEADER = os.path.join(_HERE, "..", "include", "gsa.h")
 
 INDEX_HEADS, INDEX_DIM, TOPK = 32, 128, 2048
 MLA_HEADS, LATENT_DIM, ROPE_DIM, KV_ROW = 64, 512, 64, 576
+KV_ROW_FP8 = 656            # [512 E4M3 | 4 fp32 scales | 64 bf16 RoPE] bytes
 BF16, FP8_E4M3 = 0, 1
 
 _lib = None
@@ -52,7 +53,7 @@ class _GroupDesc(ctypes.Structure):
                 ("n_layers", ctypes.c_int), ("layers", ctypes.POINTER(_MlaLayer)),
                 ("n_heads", ctypes.c_int), ("scale", ctypes.c_float),
                 ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("paged_kv", ctypes.POINTER(_PagedKV))]
+                ("paged_kv", ctypes.POINTER(_PagedKV)), ("kv_dt", ctypes.c_int)]
 
 
 class _IndexerLayer(ctypes.Structure):
@@ -70,7 +71,7 @@ class _StackDesc(ctypes.Structure):
                 ("k", ctypes.c_int), ("index_buf_dev", ctypes.c_void_p),
                 ("index_stride", ctypes.c_int64), ("n_heads", ctypes.c_int), ("scale", ctypes.c_float),
                 ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("paged_kv", ctypes.POINTER(_PagedKV))]
+                ("paged_kv", ctypes.POINTER(_PagedKV)), ("kv_dt", ctypes.c_int)]
 
 
 def _declare(lib):
@@ -92,6 +93,9 @@ def _declare(lib):
         "gsa_sparse_mla_attn_layers": (I, [ctypes.POINTER(_MlaLayer), I, P, P, I, I, I, I, I64, F, P, SZ, P]),
         "gsa_sparse_mla_attn_paged": (I, [ctypes.POINTER(_MlaLayer), I, ctypes.POINTER(_PagedKV), P, P,
                                           I, I, I, I, F, P, SZ, P]),
+        "gsa_sparse_mla_attn_fp8kv": (I, [ctypes.POINTER(_MlaLayer), I, ctypes.POINTER(_PagedKV), P, P,
+                                          I, I, I, I, I64, F, P, SZ, P]),
+        "gsa_quantize_latent_fp8": (I, [P, I64, P, P]),
         "gsa_indexshare_group": (I, [ctypes.POINTER(_GroupDesc), P]),
         "gsa_layer_pattern": (I, [I, P]),
         "gsa_layer_stack": (I, [ctypes.POINTER(_StackDesc), P]),
@@ -150,6 +154,25 @@ def quantize_e4m3(x):
     scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
     _check(lib().gsa_quantize_e4m3(_p(x), n, _p(codes), _p(scales), _stream(x.device)))
     return codes, scales
+
+
+def quantize_latent_fp8(rows):
+    """Latent cache rows bf16 [..., 576] -> FP8 latent rows uint8 [..., 656]."""
+    _need(rows, "rows", torch.bfloat16)
+    if rows.shape[-1] != KV_ROW:
+        raise GsaError("rows must end in 576 (512 latent + 64 RoPE)")
+    out = torch.empty(rows.shape[:-1] + (KV_ROW_FP8,), dtype=torch.uint8, device=rows.device)
+    _check(lib().gsa_quantize_latent_fp8(_p(rows), rows.numel() // KV_ROW, _p(out), _stream(rows.device)))
+    return out
+
+
+def _kv_fp8(kv):
+    """True for FP8 latent rows (uint8 [..., 656]), False for bf16 [..., 576]."""
+    if kv.dtype == torch.uint8:
+        if kv.shape[-1] != KV_ROW_FP8:
+            raise GsaError("an FP8 latent cache has 656-byte rows")
+        return True
+    return False
 
 
 def group_max_ld(ld):
@@ -257,8 +280,8 @@ def _paged(block_table, kv0):
     _need(block_table, "block_table", torch.int32)
     if block_table.dim() != 2:
         raise GsaError("block_table must be [batch, max_pages]")
-    if kv0.dim() != 3 or kv0.shape[2] != KV_ROW:
-        raise GsaError("a paged kv must be a pool [n_pages, page_size, 576]")
+    if kv0.dim() != 3 or kv0.shape[2] != (KV_ROW_FP8 if _kv_fp8(kv0) else KV_ROW):
+        raise GsaError("a paged kv must be a pool [n_pages, page_size, 576] (bf16) or [.., 656] (FP8)")
     return _PagedKV(block_table.data_ptr(), kv0.shape[1], block_table.shape[1], kv0.shape[0])
 
 
@@ -286,17 +309,24 @@ def sparse_mla_attn_paged(layers, block_table, q_seq, idx, scale=1.0 / 16.0, out
     _need(idx, "idx", torch.int32)
     k = idx.shape[1]
     dev = q_seq.device
+    fp8 = _kv_fp8(kv0)
     for ql, qr, kv in layers:
         _need(ql, "q_lat", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
         _need(qr, "q_rope", torch.bfloat16, (n_q, MLA_HEADS, ROPE_DIM))
-        _need(kv, "kv", torch.bfloat16, tuple(kv0.shape))
+        _need(kv, "kv", kv0.dtype, tuple(kv0.shape))
     if outs is None:
         outs = _new_outs(n_q, len(layers), dev)
     arr = _layer_array(layers, outs)
     ws = _workspace(mla_layers_workspace_bytes(n_q, len(layers), MLA_HEADS, k), dev, workspace)
-    _check(lib().gsa_sparse_mla_attn_paged(ctypes.cast(arr, ctypes.POINTER(_MlaLayer)), len(layers),
-                                           ctypes.byref(pg), _p(q_seq), _p(idx), k, n_q, MLA_HEADS,
-                                           block_table.shape[0], scale, _p(ws), ws.numel(), _stream(dev)))
+    la = ctypes.cast(arr, ctypes.POINTER(_MlaLayer))
+    if fp8:
+        _check(lib().gsa_sparse_mla_attn_fp8kv(la, len(layers), ctypes.byref(pg), _p(q_seq), _p(idx), k, n_q,
+                                               MLA_HEADS, block_table.shape[0], 0, scale, _p(ws), ws.numel(),
+                                               _stream(dev)))
+    else:
+        _check(lib().gsa_sparse_mla_attn_paged(la, len(layers), ctypes.byref(pg), _p(q_seq), _p(idx), k, n_q,
+                                               MLA_HEADS, block_table.shape[0], scale, _p(ws), ws.numel(),
+                                               _stream(dev)))
     return outs
 
 
@@ -311,10 +341,11 @@ def sparse_mla_attn_layers(layers, q_seq, idx, scale=1.0 / 16.0, outs=None, work
     _need(idx, "idx", torch.int32)
     k = idx.shape[1]
     dev = q_seq.device
+    fp8 = _kv_fp8(kv0)
     for ql, qr, kv in layers:
         _need(ql, "q_lat", torch.bfloat16, (n_q, MLA_HEADS, LATENT_DIM))
         _need(qr, "q_rope", torch.bfloat16, (n_q, MLA_HEADS, ROPE_DIM))
-        _need(kv, "kv", torch.bfloat16, (batch, n_cap, KV_ROW))
+        _need(kv, "kv", kv0.dtype, (batch, n_cap, KV_ROW_FP8 if fp8 else KV_ROW))
     if outs is None:
         outs = [(torch.empty((n_q, MLA_HEADS, LATENT_DIM), dtype=torch.float32, device=dev),
                  torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)) for _ in layers]
@@ -323,6 +354,11 @@ def sparse_mla_attn_layers(layers, q_seq, idx, scale=1.0 / 16.0, outs=None, work
         arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
                            None if s is None else s.data_ptr())
     ws = _workspace(mla_layers_workspace_bytes(n_q, len(layers), MLA_HEADS, k), dev, workspace)
+    if fp8:
+        _check(lib().gsa_sparse_mla_attn_fp8kv(ctypes.cast(arr, ctypes.POINTER(_MlaLayer)), len(layers), None,
+                                               _p(q_seq), _p(idx), k, n_q, MLA_HEADS, batch, n_cap, scale,
+                                               _p(ws), ws.numel(), _stream(dev)))
+        return outs
     _check(lib().gsa_sparse_mla_attn_layers(ctypes.cast(arr, ctypes.POINTER(_MlaLayer)), len(layers),
                                             _p(q_seq), _p(idx), k, n_q, MLA_HEADS, batch, n_cap, scale,
                                             _p(ws), ws.numel(), _stream(dev)))
@@ -382,6 +418,7 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
     if pg is not None:
         d.paged_kv = ctypes.pointer(pg)
+    d.kv_dt = FP8_E4M3 if _kv_fp8(kv0) else BF16
     _check(L.gsa_indexshare_group(ctypes.byref(d), _stream(dev)))
     return outs
 
@@ -450,5 +487,6 @@ def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_st
     d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
     if pg is not None:
         d.paged_kv = ctypes.pointer(pg)
+    d.kv_dt = FP8_E4M3 if _kv_fp8(kv0) else BF16
     _check(L.gsa_layer_stack(ctypes.byref(d), _stream(dev)))
     return outs

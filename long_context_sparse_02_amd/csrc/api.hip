@@ -106,7 +106,8 @@ gsa_status check_paged(const gsa_paged_kv* pg, int64_t* n_cap) {
 // Attention for layers that share one index buffer, in one launch per 8 layers.
 gsa_status enqueue_attention(const gsa_mla_layer* layers, int n_layers, const int32_t* q_seq,
                              const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
-                             const gsa_paged_kv* paged, float scale, void* ws, hipStream_t s) {
+                             const gsa_paged_kv* paged, bool fp8_kv, float scale, void* ws,
+                             hipStream_t s) {
     gsa::MlaLayerPtrs ptrs[8];
     for (int l0 = 0; l0 < n_layers; l0 += 8) {
         const int nl = n_layers - l0 < 8 ? n_layers - l0 : 8;
@@ -116,7 +117,7 @@ gsa_status enqueue_attention(const gsa_mla_layer* layers, int n_layers, const in
         // the workspace was sized for n_layers; a later launch of fewer layers needs no more
         const hipError_t e = gsa::launch_sparse_mla_layers(
             ptrs, nl, q_seq, idx, k, n_q, n_heads, n_cap, paged ? paged->block_table_dev : nullptr,
-            paged ? paged->page_size : 0, paged ? paged->max_pages : 0, scale, ws, s);
+            paged ? paged->page_size : 0, paged ? paged->max_pages : 0, fp8_kv, scale, ws, s);
         if (e != hipSuccess) return hip_result(e, "sparse_mla_attn");
     }
     g_err[0] = 0;
@@ -214,16 +215,25 @@ gsa_status gsa_sparse_mla_attn_layers(const gsa_mla_layer* layers, int n_layers,
             return st;
         }
     }
-    return enqueue_attention(layers, n_layers, q_seq, idx, k, n_q, n_heads, n_cap, nullptr, scale, ws,
+    return enqueue_attention(layers, n_layers, q_seq, idx, k, n_q, n_heads, n_cap, nullptr, false, scale, ws,
                              (hipStream_t)stream);
 }
 
-gsa_status gsa_sparse_mla_attn_paged(const gsa_mla_layer* layers, int n_layers, const gsa_paged_kv* paged_kv,
-                                     const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
-                                     int batch, float scale, void* ws, size_t ws_bytes, void* stream) {
-    int64_t n_cap = 0;
-    gsa_status st = check_paged(paged_kv, &n_cap);
-    if (st != GSA_OK) return st;
+}  // extern "C"
+
+namespace {
+
+// Checks and enqueues attention over paged (paged_kv) or contiguous (n_cap)
+// caches of bf16 or FP8 latent rows.
+gsa_status attention_call(const gsa_mla_layer* layers, int n_layers, const gsa_paged_kv* paged_kv,
+                          bool fp8_kv, const int32_t* q_seq, const int32_t* idx, int k, int n_q,
+                          int n_heads, int batch, int64_t n_cap, float scale, void* ws, size_t ws_bytes,
+                          void* stream) {
+    gsa_status st;
+    if (paged_kv != nullptr) {
+        st = check_paged(paged_kv, &n_cap);
+        if (st != GSA_OK) return st;
+    }
     REQUIRE(n_layers >= 1, "n_layers must be >= 1 (got %d)", n_layers);
     REQUIRE(layers != nullptr, "layers is NULL");
     for (int l = 0; l < n_layers; ++l) {
@@ -232,8 +242,34 @@ gsa_status gsa_sparse_mla_attn_paged(const gsa_mla_layer* layers, int n_layers, 
                        n_layers);
         if (st != GSA_OK) return st;
     }
-    return enqueue_attention(layers, n_layers, q_seq, idx, k, n_q, n_heads, n_cap, paged_kv, scale, ws,
+    return enqueue_attention(layers, n_layers, q_seq, idx, k, n_q, n_heads, n_cap, paged_kv, fp8_kv, scale, ws,
                              (hipStream_t)stream);
+}
+
+}  // namespace
+
+extern "C" {
+
+gsa_status gsa_sparse_mla_attn_paged(const gsa_mla_layer* layers, int n_layers, const gsa_paged_kv* paged_kv,
+                                     const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
+                                     int batch, float scale, void* ws, size_t ws_bytes, void* stream) {
+    if (paged_kv == nullptr) return fail(GSA_ERR_INVALID_ARG, "paged_kv is NULL");
+    return attention_call(layers, n_layers, paged_kv, false, q_seq, idx, k, n_q, n_heads, batch, 0, scale, ws,
+                          ws_bytes, stream);
+}
+
+gsa_status gsa_sparse_mla_attn_fp8kv(const gsa_mla_layer* layers, int n_layers, const gsa_paged_kv* paged_kv,
+                                     const int32_t* q_seq, const int32_t* idx, int k, int n_q, int n_heads,
+                                     int batch, int64_t n_cap, float scale, void* ws, size_t ws_bytes,
+                                     void* stream) {
+    return attention_call(layers, n_layers, paged_kv, true, q_seq, idx, k, n_q, n_heads, batch,
+                          paged_kv != nullptr ? 0 : n_cap, scale, ws, ws_bytes, stream);
+}
+
+gsa_status gsa_quantize_latent_fp8(const void* rows, int64_t n_rows, uint8_t* out, void* stream) {
+    REQUIRE_PTR(rows); REQUIRE_PTR(out);
+    REQUIRE(n_rows >= 0, "n_rows must be >= 0");
+    return hip_result(gsa::launch_quantize_latent(rows, n_rows, out, (hipStream_t)stream), "quantize_latent_fp8");
 }
 
 size_t gsa_group_workspace_bytes(int n_q, int64_t ld, int k, int n_heads, int n_layers) {
@@ -265,6 +301,7 @@ gsa_status validate_group(const gsa_group_desc* d) {
     REQUIRE(d->n_layers >= 0, "n_layers must be >= 0");
     REQUIRE(d->n_layers == 0 || d->layers != nullptr, "layers is NULL");
     REQUIRE(d->compute_index == 0 || d->compute_index == 1, "compute_index must be 0 or 1");
+    REQUIRE(d->kv_dt == GSA_BF16 || d->kv_dt == GSA_FP8_E4M3, "kv_dt must be GSA_BF16 or GSA_FP8_E4M3");
     if (d->paged_kv != nullptr) {
         int64_t n_cap_pg = 0;
         const gsa_status st = check_paged(d->paged_kv, &n_cap_pg);
@@ -312,7 +349,8 @@ gsa_status enqueue_group(const gsa_group_desc* d, hipStream_t s) {
     }
     if (d->n_layers > 0)
         return enqueue_attention(d->layers, d->n_layers, d->q_seq_dev, d->index_buf_dev, d->k, d->n_q,
-                                 d->n_heads, d->n_cap, d->paged_kv, d->scale, d->workspace_dev, s);
+                                 d->n_heads, d->n_cap, d->paged_kv, d->kv_dt == GSA_FP8_E4M3, d->scale,
+                                 d->workspace_dev, s);
     return GSA_OK;
 }
 
@@ -367,6 +405,7 @@ gsa_status gsa_layer_stack(const gsa_stack_desc* d, void* stream) {
         g.n_heads = d->n_heads; g.scale = d->scale;
         g.workspace_dev = d->workspace_dev; g.workspace_bytes = d->workspace_bytes;
         g.paged_kv = d->paged_kv;
+        g.kv_dt = d->kv_dt;
         return g;
     };
     for (int i = 0, f = 0; i < d->n_layers; ++i) {      // validate all before enqueuing any

@@ -42,11 +42,15 @@ struct MlaLayerPtrs {
 
 // Workspace for attention over n_layers layers that share one index buffer.
 size_t mla_workspace_bytes(int n_q, int n_heads, int k, int n_layers);
-// block_table NULL: each layer's cache is [batch, n_cap, 576]; otherwise a pool
+// block_table NULL: each layer's cache is [batch, n_cap, row]; otherwise a pool
 // of page_size-row pages addressed through block_table [batch, max_pages].
+// Rows are 576 bf16 (1152 bytes) or, with fp8_kv, 656-byte FP8 latent rows.
 hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, const int32_t* q_seq,
                                     const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
                                     const int32_t* block_table, int page_size, int max_pages,
-                                    float scale, void* ws, hipStream_t stream);
+                                    bool fp8_kv, float scale, void* ws, hipStream_t stream);
+
+// FP8 latent cache rows [512 E4M3 | 4 fp32 scales | 64 bf16 RoPE] from bf16 rows [n, 576].
+hipError_t launch_quantize_latent(const void* rows, int64_t n_rows, uint8_t* out, hipStream_t stream);
 
 }  // namespace gsa

@@ -74,7 +74,57 @@ __global__ __launch_bounds__(kThreads) void quantize_e4m3_kernel(const uint16_t*
     if (part == 0) scales[row] = __uint_as_float((uint32_t)(e + 127) << 23);
 }
 
+// The FP8 latent cache row: [512 E4M3 codes | 4 fp32 scales | 64 bf16 RoPE]
+// (656 bytes). The latent is quantised in four 128-dim groups with the block
+// rule above; the RoPE key is kept in bf16. One wave per row: 16 lanes per
+// group, lanes 0-7 also move the RoPE bytes.
+__global__ __launch_bounds__(kThreads) void quantize_latent_kernel(const uint16_t* __restrict__ x,
+                                                                   int64_t n_rows,
+                                                                   uint8_t* __restrict__ out) {
+    const int64_t row = (int64_t)blockIdx.x * (kThreads / 64) + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    const int grp = lane >> 4, part = lane & 15;
+    if (row >= n_rows) return;                            // uniform per wave
+    const uint16_t* xr = x + row * 576;
+    uint8_t* o = out + row * 656;
+    float v[8];
+    float amax = 0.f;
+    const i32x4 raw = *(const i32x4*)(xr + grp * 128 + part * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t w = (uint32_t)raw[e];
+        v[2 * e] = __uint_as_float(w << 16);
+        v[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
+    }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) amax = fmaxf(amax, __shfl_xor(amax, m, 64));
+    int e = 0;
+    if (amax > 0.f) {
+        const uint32_t b = __float_as_uint(amax);
+        const int ea = (int)(b >> 23) - 127;
+        if ((b >> 23) == 0) e = -126;
+        else e = ((b & 0x7fffffu) <= 0x600000u) ? ea - 8 : ea - 7;
+        e = e < -126 ? -126 : (e > 127 ? 127 : e);
+    }
+    const float inv = __uint_as_float((uint32_t)(127 - e) << 23);
+    uint32_t packed[2] = {0u, 0u};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) packed[i >> 2] |= encode_e4m3(v[i] * inv) << (8 * (i & 3));
+    *(uint2*)(o + grp * 128 + part * 8) = make_uint2(packed[0], packed[1]);
+    if (part == 0) *(float*)(o + 512 + 4 * grp) = __uint_as_float((uint32_t)(e + 127) << 23);
+    if (lane < 8) *(i32x4*)(o + 528 + 16 * lane) = *(const i32x4*)(xr + 512 + 8 * lane);
+}
+
 }  // namespace
+
+hipError_t launch_quantize_latent(const void* rows, int64_t n_rows, uint8_t* out, hipStream_t st) {
+    if (n_rows == 0) return hipSuccess;
+    hipLaunchKernelGGL(quantize_latent_kernel, dim3((unsigned)((n_rows + 3) / 4)), dim3(kThreads), 0, st,
+                       (const uint16_t*)rows, n_rows, out);
+    return hipGetLastError();
+}
 
 hipError_t launch_quantize_e4m3(const void* x, int64_t n_rows, uint8_t* codes, float* scales,
                                 hipStream_t st) {

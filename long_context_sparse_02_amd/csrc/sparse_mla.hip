@@ -19,6 +19,11 @@
 // of Q and 64 of O, which leaves room for two waves per SIMD; the LDS reads
 // per 32-row block (each head group reads the block once for Q.K and once
 // for P.V) are what bounds this kernel.
+// FP8 latent cache ("GLM-5.2 总览" tbl-glm52-config: ~656 bytes per token and
+// layer with per-group scales; glossary: E4M3 on the 512-dim latent): rows of
+// [512 E4M3 | 4 fp32 scales | 64 bf16 RoPE] are gathered into a staging ring
+// and widened to the bf16 block layout (one scaled conversion per two codes)
+// before the same compute.
 // Per 32-row block:
 //   gather  global_load_lds_dwordx4 copies the block's 32 x 1152 bytes straight
 //           into LDS (no staging registers); each wave instruction moves 1 KiB
@@ -68,7 +73,21 @@ constexpr int kMaxLayersPerLaunch = 8;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
+// FP8 latent rows ([512 E4M3 | 4 fp32 scales | 64 bf16 RoPE], 656 bytes): the
+// gather lands them unpadded in a staging ring, and every block is widened to
+// the bf16 layout above (exact: code x power-of-two scale) before the same
+// compute runs on it.
+constexpr int kRowBytesF8 = 656;
+constexpr int kChunksF8 = kRowBytesF8 / 16;     // 41
+constexpr int kDmaF8 = (kBlk * kRowBytesF8 + 1023) / 1024;   // 21
+constexpr int kStageBuf = kDmaF8 * 1024;
+constexpr int kDmaLoF8 = kDmaF8 / kWaves;       // 2
+constexpr int kDmaHiF8 = kDmaLoF8 + 1;          // 3
+constexpr int kDmaBigF8 = kDmaF8 - kWaves * kDmaLoF8;       // 5
+
 __shared__ __attribute__((aligned(16))) uint8_t g_ring[kRing * kBuf];
+__shared__ __attribute__((aligned(16))) uint8_t g_stage[kRing * kStageBuf];
+__shared__ __attribute__((aligned(16))) uint8_t g_blk[kBuf];
 __shared__ int32_t g_rows[kMaxRows];
 __shared__ f32x4 g_xs[kWaves][2][64];           // partial S^T of each wave (2 KiB per wave)
 
@@ -110,6 +129,7 @@ __device__ __forceinline__ void wait_block(int later) {
     else wait_vmcnt<0>();
 }
 
+template <bool FP8KV>
 __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     LayerArgs L, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ idx, int k,
     int n_q, int64_t n_cap, const int32_t* __restrict__ block_table, int page_size, int max_pages,
@@ -136,9 +156,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     // (block_table != NULL): the layer's cache is a pool of page_size-row pages
     // and position s of the sequence is row table[seq][s / page_size] *
     // page_size + s % page_size of the pool; indices become pool rows here, once.
+    constexpr int RB = FP8KV ? kRowBytesF8 : kRowBytes;   // bytes per cache row
     const uint8_t* kvs;
     if (block_table == nullptr) {
-        kvs = kv + (int64_t)seq * n_cap * kRowBytes;
+        kvs = kv + (int64_t)seq * n_cap * RB;
         for (int i = tid; i < nrows; i += kThreads) rows_s[i] = idx[(int64_t)q * k + r0 + i];
     } else {
         kvs = kv;
@@ -166,29 +187,69 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     wait_vmcnt<0>();     // Q is in registers before any ring load is counted
     __syncthreads();
 
-    // 16-byte LDS position s = 64*i + lane of a block holds row s / 73, chunk s % 73
-    // (chunk 72 and positions past row 31 are padding, filled from the zero row)
-    const bool big = wave < kDmaBig;
-    const int i0 = big ? kDmaHi * wave : kDmaHi * kDmaBig + kDmaLo * (wave - kDmaBig);
+    // bf16: 16-byte LDS position s = 64*i + lane of a block holds row s / 73,
+    // chunk s % 73 (chunk 72 and positions past row 31 are padding, filled from
+    // the zero row). FP8: row s / 41, chunk s % 41 of the staging slot, unpadded.
+    constexpr int DMA_BIG = FP8KV ? kDmaBigF8 : kDmaBig;
+    constexpr int DMA_HI = FP8KV ? kDmaHiF8 : kDmaHi;
+    constexpr int DMA_LO = FP8KV ? kDmaLoF8 : kDmaLo;
+    constexpr int UNIT = FP8KV ? kChunksF8 : kChunksPerPitch;    // 16-byte units per LDS row
+    constexpr int ROW_CHUNKS = FP8KV ? kChunksF8 : kChunksPerRow;
+    constexpr int SLOT = FP8KV ? kStageBuf : kBuf;
+    uint8_t* const ring = FP8KV ? g_stage : g_ring;
+    const bool big = wave < DMA_BIG;
+    const int i0 = big ? DMA_HI * wave : DMA_HI * DMA_BIG + DMA_LO * (wave - DMA_BIG);
     auto issue = [&](int b, int slot) __attribute__((always_inline)) {
-        const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)g_ring + slot * kBuf;
-        const int nload = big ? kDmaHi : kDmaLo;
-        int srow[kDmaHi];
+        const uint32_t dst = (uint32_t)(uintptr_t)(lds_u8*)ring + slot * SLOT;
+        const int nload = big ? DMA_HI : DMA_LO;
+        int srow[DMA_HI];
 #pragma unroll
-        for (int j = 0; j < kDmaHi; ++j) {              // every index read first, one wait
+        for (int j = 0; j < DMA_HI; ++j) {              // every index read first, one wait
             const int pos = 64 * (i0 + j) + lane;
-            const int row = pos / kChunksPerPitch;
-            const int c = pos - row * kChunksPerPitch;
-            srow[j] = (j < nload && row < kBlk && c < kChunksPerRow) ? rows_s[b * kBlk + row] : -1;
+            const int row = pos / UNIT;
+            const int c = pos - row * UNIT;
+            srow[j] = (j < nload && row < kBlk && c < ROW_CHUNKS) ? rows_s[b * kBlk + row] : -1;
         }
 #pragma unroll
-        for (int j = 0; j < kDmaHi; ++j) {
-            if (j == kDmaHi - 1 && !big) break;
+        for (int j = 0; j < DMA_HI; ++j) {
+            if (j == DMA_HI - 1 && !big) break;
             const int pos = 64 * (i0 + j) + lane;
-            const int row = pos / kChunksPerPitch;
-            const int c = pos - row * kChunksPerPitch;
-            const uint8_t* src = srow[j] >= 0 ? kvs + (int64_t)srow[j] * kRowBytes + 16 * c : g_zero_row;
+            const int row = pos / UNIT;
+            const int c = pos - row * UNIT;
+            const uint8_t* src = srow[j] >= 0 ? kvs + (int64_t)srow[j] * RB + 16 * c : g_zero_row;
             lds_dma16(src, dst + 1024 * (i0 + j));
+        }
+    };
+    // FP8: widen staging slot `slot` into g_blk in the bf16 row layout. Thread t
+    // converts codes 32*(t%16) .. +31 of row t/16 with that group's scale (the
+    // scaled conversion is exact for a power-of-two scale); threads 0-255 move
+    // the RoPE dims (16 bytes each).
+    auto widen = [&](int slot) __attribute__((always_inline)) {
+        const lds_u8* st = (const lds_u8*)g_stage + slot * kStageBuf;
+        const int r = tid >> 4, j = tid & 15;
+        const lds_u8* sr = st + r * kRowBytesF8;
+        const i32x4 c0 = *(const __attribute__((address_space(3))) i32x4*)(sr + 32 * j);
+        const i32x4 c1 = *(const __attribute__((address_space(3))) i32x4*)(sr + 32 * j + 16);
+        const float sc = *(const __attribute__((address_space(3))) float*)(sr + 512 + 4 * (j >> 2));
+        i32x4 w[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const auto lo0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c0[e], sc, false);
+            const auto hi0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c0[e], sc, true);
+            const auto lo1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c1[e], sc, false);
+            const auto hi1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c1[e], sc, true);
+            w[e >> 1][2 * (e & 1)] = __builtin_bit_cast(int, lo0);
+            w[e >> 1][2 * (e & 1) + 1] = __builtin_bit_cast(int, hi0);
+            w[2 + (e >> 1)][2 * (e & 1)] = __builtin_bit_cast(int, lo1);
+            w[2 + (e >> 1)][2 * (e & 1) + 1] = __builtin_bit_cast(int, hi1);
+        }
+        lds_u8* dr = (lds_u8*)g_blk + r * kPitch + 64 * j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) *(__attribute__((address_space(3))) i32x4*)(dr + 16 * e) = w[e];
+        if (tid < 256) {
+            const int r2 = tid >> 3, c = tid & 7;
+            *(__attribute__((address_space(3))) i32x4*)((lds_u8*)g_blk + r2 * kPitch + 1024 + 16 * c) =
+                *(const __attribute__((address_space(3))) i32x4*)(st + r2 * kRowBytesF8 + 528 + 16 * c);
         }
     };
 
@@ -277,11 +338,18 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         // this wave's loads of block b are done once at most the later issued
         // blocks (b+1 .. min(nblk, b+kRing-1) - 1) remain outstanding
         const int later = min(nblk, b + kRing - 1) - b - 1;
-        if (big) wait_block<kDmaHi>(later);
-        else wait_block<kDmaLo>(later);
+        if (big) wait_block<DMA_HI>(later);
+        else wait_block<DMA_LO>(later);
         ring_barrier();    // every wave's part of block b is in; block b-1's readers are done
         if (b + kRing - 1 < nblk) issue(b + kRing - 1, (b + kRing - 1) % kRing);
-        compute(b, (const lds_u8*)g_ring + (b % kRing) * kBuf);
+        if constexpr (FP8KV) {
+            widen(b % kRing);
+            wait_lgkm0();
+            ring_barrier();    // the widened block is complete
+            compute(b, (const lds_u8*)g_blk);
+        } else {
+            compute(b, (const lds_u8*)g_ring + (b % kRing) * kBuf);
+        }
     }
 
     const float l_tot = sum_x32(sum_x16(l_part));
@@ -372,7 +440,7 @@ size_t mla_workspace_bytes(int n_q, int n_heads, int k, int n_layers) {
 hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, const int32_t* q_seq,
                                     const int32_t* idx, int k, int n_q, int n_heads, int64_t n_cap,
                                     const int32_t* block_table, int page_size, int max_pages,
-                                    float scale, void* ws, hipStream_t st) {
+                                    bool fp8_kv, float scale, void* ws, hipStream_t st) {
     (void)n_heads;
     const float scale_log2 = scale * 1.4426950408889634f;
     for (int l0 = 0; l0 < n_layers; l0 += kMaxLayersPerLaunch) {
@@ -391,9 +459,14 @@ hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, co
         const int rows = k / s;
         float* part_o = (float*)ws;
         float* part_ml = s > 1 ? part_o + (size_t)per * n_q * s * kHeads * kLat : nullptr;
-        hipLaunchKernelGGL(sparse_mla_kernel, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq, idx, k,
-                           n_q, n_cap, block_table, page_size, max_pages, scale_log2, rows, part_o,
-                           part_ml);
+        if (fp8_kv)
+            hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq,
+                               idx, k, n_q, n_cap, block_table, page_size, max_pages, scale_log2, rows,
+                               part_o, part_ml);
+        else
+            hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq,
+                               idx, k, n_q, n_cap, block_table, page_size, max_pages, scale_log2, rows,
+                               part_o, part_ml);
         if (s > 1)
             hipLaunchKernelGGL(sparse_mla_merge, dim3(n_q, kHeads / 4, nl), dim3(256), 0, st, L, n_q,
                                part_o, part_ml, s);

@@ -35,3 +35,8 @@ def test_roofline_bound_follows_arithmetic_intensity():
     assert r["bytes_per_launch"] == bench.score_bytes(dec, False)
     r = bench.roofline("topk", pre, False, bench.topk_bytes(pre), 1.8, 1)
     assert r["bound"] == "hbm"
+
+
+def test_fp8_latent_bytes():
+    wl = W.WORKLOADS["decode_b64_n131072_kv8"]
+    assert bench.mla_bytes(wl) == 64 * (2048 * 656 + 2048 * 4 + 64 * 576 * 2 + 64 * 512 * 4)

@@ -298,3 +298,36 @@ def test_stack_uses_latest_full_layer():
         o, _ = oracle.sparse_mla(*mla[l], _np(q_seq), idx_of[src[l]], 1 / 16)
         assert np.array_equal(outs[l][0], o)
     assert src[3:6] == [2, 2, 2] and src[7:10] == [6, 6, 6] and src[11] == 10
+
+
+# ---------------------------------------------------------------- FP8 latent cache row
+def test_latent_row_layout_worked_example():
+    row = np.zeros((1, 576))
+    row[0, 0], row[0, 1], row[0, 127] = 448.0, -3.0, 0.5       # group 0: amax 448 -> scale 1
+    row[0, 128] = 7.0                                          # group 1: amax 7 -> scale 2^-6
+    row[0, 512], row[0, 575] = 1.5, -2.0                       # RoPE dims kept in bf16
+    p = oracle.quantize_latent(row)
+    assert p.shape == (1, 656) and p.dtype == np.uint8
+    assert p[0, 0] == 0x7E and p[0, 1] == 0xC4 and p[0, 127] == 0x30      # 448, -3 = -1.5*2^1, 0.5
+    assert p[0, 128] == 0x7E                                               # 7 / 2^-6 = 448
+    scales = p[0, 512:528].view("<f4")
+    assert scales.tolist() == [1.0, 2.0 ** -6, 1.0, 1.0]                   # zero groups: 2^0
+    rope = p[0, 528:].view("<u2")
+    assert rope[0] == 0x3FC0 and rope[63] == 0xC000                         # bf16 1.5, -2.0
+    assert np.array_equal(oracle.dequantize_latent(p), row)
+
+
+def test_latent_codes_match_torch_fp8_cast():
+    g = torch.Generator().manual_seed(4)
+    rows = (torch.randn((64, 576), generator=g) * torch.rand((64, 1), generator=g) * 50).to(torch.bfloat16)
+    p = oracle.quantize_latent(rows.float().numpy())
+    lat = rows.float()[:, :512].reshape(64, 4, 128).double()
+    scales = torch.from_numpy(p[:, 512:528].copy().view("<f4").astype(np.float64)).reshape(64, 4, 1)
+    want = (lat / scales).to(torch.float8_e4m3fn).view(torch.uint8).reshape(64, 512).numpy()
+    assert np.array_equal(p[:, :512], want)
+    # power-of-two scales, each the smallest with amax <= 448 * scale
+    amax = lat.abs().amax(-1, keepdim=True)
+    s = scales
+    assert torch.all(torch.log2(s) == torch.round(torch.log2(s)))
+    assert torch.all(amax <= 448 * s) and torch.all(amax > 224 * s)
+    assert np.array_equal(p[:, 528:].view("<u2"), rows[:, 512:].view(torch.int16).numpy().astype(np.uint16))

@@ -44,6 +44,7 @@ class Workload:
     indexer_dtype: str      # "bf16" or "fp8"
     mla: bool = True        # False: indexer + top-k only (chunked prefill F layer)
     note: str = ""
+    kv_dtype: str = "bf16"  # latent cache rows: "bf16" (1152 B) or "fp8" (656 B E4M3 + scales)
 
     @property
     def n_q(self) -> int:
@@ -65,6 +66,10 @@ WORKLOADS = {
                  note="1M-context decode batch 8, fp8 indexer keys, one group"),
         Workload("stack78_b8_q8_n262144", 8, 1 << 18, 8, 78, "bf16",
                  note="78-layer stack (21F+57S), MTP verify shape 8 queries/seq"),
+        Workload("decode_b64_n131072_kv8", 64, 131072, 1, 4, "bf16", kv_dtype="fp8",
+                 note="decode_b64_n131072 with the FP8 latent cache (656-byte rows)"),
+        Workload("decode_b8_n1048576_fp8_kv8", 8, 1 << 20, 1, 4, "fp8", kv_dtype="fp8",
+                 note="1M decode with fp8 indexer keys and the FP8 latent cache"),
     ]
 }
 
