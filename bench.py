@@ -47,6 +47,7 @@ KERNEL_SOURCES = {
     "indexer_score": (CSRC + "indexer_score.hip", CSRC + "device_common.h"),
     "topk": (CSRC + "topk.hip", CSRC + "device_common.h"),
     "sparse_mla": (CSRC + "sparse_mla.hip", CSRC + "device_common.h"),
+    "quantize_q": (CSRC + "quantize_e4m3.hip", CSRC + "device_common.h"),
 }
 
 
@@ -120,23 +121,28 @@ def build_inputs(wl, seed, dev):
     """Device inputs of the workload, drawn by the seeded generators in `workloads`."""
     t0 = time.time()
     q_seq, q_pos = W.query_layout(wl, dev)
-    fp8 = wl.indexer_dtype == "fp8"
+    fp8 = wl.indexer_dtype in ("fp8", "fp8h")
+    rot = wl.indexer_dtype == "fp8h"           # Hadamard-rotated fp8: the step quantises q
     if is_stack(wl):
         src = gsa.layer_pattern(wl.n_layers)
     else:                                      # one group: layer 0 full, the rest shared
         src = [0] * (wl.n_layers if wl.mla else 1)
     full_layers = [l for l, s in enumerate(src) if s == l]
     indexers = []
+    q_src = []                                 # bf16 indexer queries the step quantises (fp8h)
     for f in full_layers:
         q_idx, w = W.indexer_queries(wl, seed, f, dev)
         k_idx = W.indexer_keys(wl, seed, f, dev)
         q_scale = k_scale = None
+        q_bf16 = q_idx
         if fp8:
-            q_idx, q_scale = gsa.quantize_e4m3(q_idx)
-            k8, k_scale = gsa.quantize_e4m3(k_idx)
+            q_idx, q_scale = gsa.quantize_e4m3(q_idx, hadamard=rot)
+            k8, k_scale = gsa.quantize_e4m3(k_idx, hadamard=rot)
             del k_idx
             k_idx = k8
         indexers.append((q_idx, w, k_idx, q_scale, k_scale))
+        if rot:
+            q_src.append(q_bf16)
     layers = []
     if wl.mla:
         for l in range(wl.n_layers):
@@ -152,7 +158,7 @@ def build_inputs(wl, seed, dev):
         f"({len(full_layers)} full layers, {len(layers)} attention layers)")
     ordinal = {f: j for j, f in enumerate(full_layers)}
     return dict(q_seq=q_seq, q_pos=q_pos, indexers=indexers, full_layers=full_layers,
-                src=[ordinal[s] for s in src], layers=layers, fp8=fp8)
+                src=[ordinal[s] for s in src], layers=layers, fp8=fp8, rot=rot, q_src=q_src)
 
 
 def make_step(wl, inp, dev):
@@ -194,8 +200,14 @@ def make_step(wl, inp, dev):
         return lambda: gsa.sparse_mla_attn_layers(lay, q_seq, bufs["idx"][j], SCALE, outs=outs,
                                                   workspace=bufs["ws"])
 
+    def quant_call(j):
+        q, _, _, qs, _ = inp["indexers"][j]
+        return lambda: gsa.quantize_e4m3(inp["q_src"][j], hadamard=True, out=(q, qs))
+
     fp8 = inp["fp8"]
     for j, f in enumerate(inp["full_layers"]):
+        if inp["rot"]:                          # rotate + quantise this step's indexer queries
+            calls.append(("quantize_q", wl.n_q * 32 * (256 + 128 + 4), quant_call(j)))
         calls.append(("indexer_score", launch_bytes("indexer_score", wl, fp8), score_call(j)))
         calls.append(("topk", launch_bytes("topk", wl, fp8), topk_call(j)))
         group = [l for l in range(n_att) if inp["src"][l] == j]
@@ -310,11 +322,12 @@ def host_indexer_inputs(wl, inp, j, qi, seed, keys=None):
     kh = None if keys is None else keys.get((j, b))
     if inp["fp8"]:
         f = inp["full_layers"][j]
+        quant = oracle.quantize_blocks_hadamard if inp["rot"] else oracle.quantize_blocks
         qv, wv = W.indexer_queries(wl, seed, f, q.device)
-        qh = oracle.dequantize_blocks(*oracle.quantize_blocks(qv[qi:qi + 1].float().cpu().numpy()))
+        qh = oracle.dequantize_blocks(*quant(qv[qi:qi + 1].float().cpu().numpy()))
         if kh is None:
             kh = W.indexer_keys_seq(wl, seed, f, b, q.device).float().cpu().numpy()
-            kh = oracle.dequantize_blocks(*oracle.quantize_blocks(kh))
+            kh = oracle.dequantize_blocks(*quant(kh))
         wh = wv[qi:qi + 1].cpu().numpy()
     else:
         qh, wh = q[qi:qi + 1].float().cpu().numpy(), w[qi:qi + 1].cpu().numpy()

@@ -79,6 +79,20 @@ gsa_status gsa_quantize_e4m3(const void* x_dev, int64_t n_blocks,
                              uint8_t* codes_dev, float* scales_dev, void* stream);
 
 /*
+ * gsa_quantize_e4m3_hadamard — the same after a Hadamard rotation of each block
+ * ([Overview] sub-document index row 02 names FP8 per-block quantisation with a
+ * Hadamard rotation for the indexer):
+ *   y = H x / sqrt(128), H the Sylvester-ordered 128 x 128 Hadamard matrix
+ *   (H[i][j] = (-1)^popcount(i & j)), computed as the exact +-1 sums in fp32
+ *   times the fp32 value of 1/sqrt(128); then codes and scale of y as above.
+ * Rotating both q and k leaves q . k unchanged in exact arithmetic (H is
+ * orthogonal up to the factor 128), so gsa_indexer_score takes the rotated
+ * codes as they are. Same arguments and errors as gsa_quantize_e4m3.
+ */
+gsa_status gsa_quantize_e4m3_hadamard(const void* x_dev, int64_t n_blocks,
+                                      uint8_t* codes_dev, float* scales_dev, void* stream);
+
+/*
  * gsa_indexer_score — the full (F) layer's lightning-indexer score
  * ([Arch] §2.2: an F layer scores each query against every history token
  * with 32 heads x 128 dims; [Overview] sub-document index: ReLU).

@@ -81,6 +81,7 @@ def _declare(lib):
         "gsa_last_error": (ctypes.c_char_p, []),
         "gsa_version": (ctypes.c_char_p, []),
         "gsa_quantize_e4m3": (I, [P, I64, P, P, P]),
+        "gsa_quantize_e4m3_hadamard": (I, [P, I64, P, P, P]),
         "gsa_indexer_score": (I, [I, P, P, P, P, P, P, P, I, I, I64, P, I64, P, P]),
         "gsa_group_max_ld": (I64, [I64]),
         "gsa_topk_workspace_bytes": (SZ, [I, I64, I]),
@@ -146,13 +147,23 @@ def _need(t, name, dtype, shape=None):
 
 
 # ---------------------------------------------------------------- entry points
-def quantize_e4m3(x):
-    """x bf16 [..., 128] -> (codes uint8 same shape, scales fp32 [...])."""
+def quantize_e4m3(x, hadamard=False, out=None):
+    """x bf16 [..., 128] -> (codes uint8 same shape, scales fp32 [...]); with
+    hadamard, each block is rotated by the orthonormal Hadamard matrix first.
+    out: optional (codes, scales) to write into."""
     _need(x, "x", torch.bfloat16)
+    if x.shape[-1] != 128:
+        raise GsaError("x must end in 128")
     n = x.numel() // 128
-    codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
-    scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
-    _check(lib().gsa_quantize_e4m3(_p(x), n, _p(codes), _p(scales), _stream(x.device)))
+    if out is None:
+        codes = torch.empty(x.shape, dtype=torch.uint8, device=x.device)
+        scales = torch.empty(x.shape[:-1], dtype=torch.float32, device=x.device)
+    else:
+        codes, scales = out
+        _need(codes, "codes", torch.uint8, tuple(x.shape))
+        _need(scales, "scales", torch.float32, tuple(x.shape[:-1]))
+    fn = lib().gsa_quantize_e4m3_hadamard if hadamard else lib().gsa_quantize_e4m3
+    _check(fn(_p(x), n, _p(codes), _p(scales), _stream(x.device)))
     return codes, scales
 
 

@@ -147,8 +147,16 @@ gsa_status gsa_quantize_e4m3(const void* x, int64_t n_blocks, uint8_t* codes, fl
                              void* stream) {
     REQUIRE_PTR(x); REQUIRE_PTR(codes); REQUIRE_PTR(scales);
     REQUIRE(n_blocks >= 0, "n_blocks must be >= 0");
-    return hip_result(gsa::launch_quantize_e4m3(x, n_blocks, codes, scales, (hipStream_t)stream),
+    return hip_result(gsa::launch_quantize_e4m3(x, n_blocks, codes, scales, false, (hipStream_t)stream),
                       "quantize_e4m3");
+}
+
+gsa_status gsa_quantize_e4m3_hadamard(const void* x, int64_t n_blocks, uint8_t* codes, float* scales,
+                                      void* stream) {
+    REQUIRE_PTR(x); REQUIRE_PTR(codes); REQUIRE_PTR(scales);
+    REQUIRE(n_blocks >= 0, "n_blocks must be >= 0");
+    return hip_result(gsa::launch_quantize_e4m3(x, n_blocks, codes, scales, true, (hipStream_t)stream),
+                      "quantize_e4m3_hadamard");
 }
 
 gsa_status gsa_indexer_score(gsa_dtype dt, const void* q, const float* q_scale, const float* w,

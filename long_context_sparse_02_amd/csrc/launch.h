@@ -8,8 +8,9 @@
 
 namespace gsa {
 
+// rotate: multiply each 128-element block by the orthonormal Hadamard matrix first.
 hipError_t launch_quantize_e4m3(const void* x, int64_t n_blocks, uint8_t* codes, float* scales,
-                                hipStream_t stream);
+                                bool rotate, hipStream_t stream);
 
 hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, const float* w,
                                 const void* k, const float* k_scale, const int32_t* q_seq,

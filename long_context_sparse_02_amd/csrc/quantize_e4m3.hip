@@ -1,7 +1,9 @@
 // Per-block FP8 E4M3 quantisation of indexer q/k rows on gfx950.
 //
 // "GLM-5.2 总览" sub-document index (row 02): the lightning indexer quantises
-// q and k to FP8 per block; glossary: the FP8 format is E4M3.
+// q and k to FP8 per block, with a Hadamard rotation; glossary: the FP8 format
+// is E4M3. The rotated variant multiplies each block by the orthonormal
+// Hadamard matrix first (dot products are unchanged in exact arithmetic).
 // Block = one 128-element row. Scale = 2^e, e the smallest integer with
 // max|x| <= 448 * 2^e (clamped to [-126, 127]; e = 0 for a zero row). Codes are
 // x / scale rounded to nearest even in E4M3FN (bias 7, max 448, no inf),
@@ -35,6 +37,37 @@ __device__ __forceinline__ uint32_t encode_e4m3(float v) {
     return sign | code;
 }
 
+// y = H x / sqrt(128) over one 128-element block held by 16 lanes (8
+// consecutive elements each), H the Sylvester-ordered Hadamard matrix
+// (H[i][j] = (-1)^popcount(i & j)): the in-place butterflies (a, b) -> (a + b,
+// a - b) at distances 1, 2, 4 inside a lane and 8 .. 64 across lanes give the
+// exact +-1 sums (integer inputs stay exact in fp32), then one multiply by the
+// fp32 value of 1/sqrt(128).
+__device__ __forceinline__ void hadamard128(float (&v)[8], int part) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            if ((e & h) == 0) {
+                const float a = v[e], b = v[e + h];
+                v[e] = a + b;
+                v[e + h] = a - b;
+            }
+#pragma unroll
+    for (int m = 1; m < 16; m <<= 1) {
+        const bool upper = (part & m) != 0;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+            const float o = __shfl_xor(v[e], m, 64);
+            v[e] = upper ? o - v[e] : v[e] + o;
+        }
+    }
+    constexpr float kInvSqrt128 = 0.08838834764831844055f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) v[e] *= kInvSqrt128;
+}
+
+template <bool kRotate>
 __global__ __launch_bounds__(kThreads) void quantize_e4m3_kernel(const uint16_t* __restrict__ x,
                                                                  int64_t n_rows,
                                                                  uint8_t* __restrict__ codes,
@@ -44,14 +77,15 @@ __global__ __launch_bounds__(kThreads) void quantize_e4m3_kernel(const uint16_t*
     const bool ok = row < n_rows;
     float v[8];
     float amax = 0.f;
-    if (ok) {
-        const i32x4 raw = *(const i32x4*)(x + row * 128 + part * 8);
+    {
+        const i32x4 raw = ok ? *(const i32x4*)(x + row * 128 + part * 8) : i32x4{0, 0, 0, 0};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const uint32_t w = (uint32_t)raw[e];
             v[2 * e] = __uint_as_float(w << 16);             // bf16 -> fp32 is exact
             v[2 * e + 1] = __uint_as_float(w & 0xffff0000u);
         }
+        if constexpr (kRotate) hadamard128(v, part);       // every lane takes part in the shuffles
 #pragma unroll
         for (int e = 0; e < 8; ++e) amax = fmaxf(amax, fabsf(v[e]));
     }
@@ -127,10 +161,14 @@ hipError_t launch_quantize_latent(const void* rows, int64_t n_rows, uint8_t* out
 }
 
 hipError_t launch_quantize_e4m3(const void* x, int64_t n_rows, uint8_t* codes, float* scales,
-                                hipStream_t st) {
+                                bool rotate, hipStream_t st) {
     if (n_rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(quantize_e4m3_kernel, dim3((unsigned)((n_rows + 15) / 16)), dim3(kThreads), 0,
-                       st, (const uint16_t*)x, n_rows, codes, scales);
+    if (rotate)
+        hipLaunchKernelGGL(quantize_e4m3_kernel<true>, dim3((unsigned)((n_rows + 15) / 16)), dim3(kThreads),
+                           0, st, (const uint16_t*)x, n_rows, codes, scales);
+    else
+        hipLaunchKernelGGL(quantize_e4m3_kernel<false>, dim3((unsigned)((n_rows + 15) / 16)), dim3(kThreads),
+                           0, st, (const uint16_t*)x, n_rows, codes, scales);
     return hipGetLastError();
 }
 

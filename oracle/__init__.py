@@ -31,6 +31,7 @@ from .indexer import indexer_score
 from .topk import group_max, topk_select
 from .mla import paged_cache_view, sparse_mla
 from .latent_fp8 import dequantize_latent, quantize_latent
+from .hadamard import hadamard, indexer_inputs_fp8_hadamard, quantize_blocks_hadamard, rotate_blocks
 from .pattern import layer_pattern, shared_source
 from .group import indexer_inputs_fp8, indexshare_group, layer_stack
 
@@ -39,4 +40,5 @@ __all__ = [
     "indexer_score", "topk_select", "sparse_mla", "layer_pattern",
     "shared_source", "indexshare_group", "layer_stack", "indexer_inputs_fp8",
     "paged_cache_view", "group_max", "quantize_latent", "dequantize_latent",
+    "hadamard", "rotate_blocks", "quantize_blocks_hadamard", "indexer_inputs_fp8_hadamard",
 ]

@@ -134,3 +134,24 @@ def test_stack78_full_size():
         assert bool((ix >= 0).all()) and bool((ix[:, 1:] > ix[:, :-1]).all())
     check_sampled_queries(wl, inp, bufs, [0, wl.n_q - 1], [0, 1, 2, 3, 5, 6, 9, 41, 74, 77],
                           list(range(n_full)))
+
+
+def test_prefill_rotated_fp8_full_size():
+    # Hadamard-rotated fp8 indexer: the selection is exact for the scores the
+    # kernel produced (all properties above), and the sampled queries' scores and
+    # sets track the oracle's rotated-fp8 scores (not bit-exact: rotated values
+    # are not integers, so fp32 accumulation rounds)
+    wl, inp, bufs = run_unit("prefill_q4096_n131072_fp8h")
+    check_selection_properties(bufs["scores"], bufs["idx"][0], inp["q_pos"], wl.n_ctx)
+    for qi in [0, 2047, 4095]:
+        pos = np.array([int(inp["q_pos"][qi])], np.int32)
+        qh, wh, kh = bench.host_indexer_inputs(wl, inp, 0, qi, SEED)
+        row = oracle.indexer_score(qh, wh, kh[None], np.zeros(1, np.int32), pos)[0]
+        got = np32(bufs["scores"][qi, :wl.n_ctx]).astype(np.float64)
+        fin = np.isfinite(row)
+        assert np.array_equal(np.isfinite(got), fin)
+        assert np.all(np.abs(got[fin] - row[fin]) <= 1e-4 * (1 + np.abs(row[fin])))
+        want = set(oracle.topk_select(row[None], pos, 2048)[0]) - {-1}
+        have = set(np32(bufs["idx"][0, qi])) - {-1}
+        assert len(want & have) >= 0.995 * len(want)
+        say(f"{wl.name}: query {qi} tracks the oracle ({len(want & have)} of {len(want)} shared)")

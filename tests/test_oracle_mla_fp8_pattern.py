@@ -331,3 +331,32 @@ def test_latent_codes_match_torch_fp8_cast():
     assert torch.all(torch.log2(s) == torch.round(torch.log2(s)))
     assert torch.all(amax <= 448 * s) and torch.all(amax > 224 * s)
     assert np.array_equal(p[:, 528:].view("<u2"), rows[:, 512:].view(torch.int16).numpy().astype(np.uint16))
+
+
+# ---------------------------------------------------------------- Hadamard rotation
+def test_hadamard_matches_scipy_and_is_orthogonal():
+    import scipy.linalg
+    h = oracle.hadamard(128)
+    assert np.array_equal(h, scipy.linalg.hadamard(128))
+    assert np.array_equal(h @ h.T, 128 * np.eye(128, dtype=np.int64))
+
+
+def test_rotation_closed_forms():
+    # a scaled one-hot block becomes a scaled column of H / sqrt(128), rounded once to float32
+    x = np.zeros((1, 128))
+    x[0, 37] = 3.0
+    want = (3.0 * oracle.hadamard(128)[:, 37]).astype(np.float32) * np.float32(1 / np.sqrt(128))
+    assert np.array_equal(oracle.rotate_blocks(x)[0], want)
+    # two blocks per row rotate independently
+    x2 = np.zeros((1, 256))
+    x2[0, 128 + 37] = 3.0
+    assert np.array_equal(oracle.rotate_blocks(x2)[0, 128:], want) and not oracle.rotate_blocks(x2)[0, :128].any()
+
+
+def test_rotation_keeps_dot_products_and_inverts_itself():
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal((50, 128))
+    k = rng.standard_normal((50, 128))
+    rq, rk = oracle.rotate_blocks(q).astype(np.float64), oracle.rotate_blocks(k).astype(np.float64)
+    assert np.allclose(np.sum(rq * rk, axis=1), np.sum(q * k, axis=1), rtol=1e-5, atol=1e-5)
+    assert np.allclose(oracle.rotate_blocks(rq), q, atol=1e-5)

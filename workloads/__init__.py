@@ -41,7 +41,7 @@ class Workload:
     n_ctx: int
     q_per_seq: int
     n_layers: int           # layers the measured unit covers (4 = one F + 3 S group)
-    indexer_dtype: str      # "bf16" or "fp8"
+    indexer_dtype: str      # "bf16", "fp8", or "fp8h" (fp8 after a Hadamard rotation)
     mla: bool = True        # False: indexer + top-k only (chunked prefill F layer)
     note: str = ""
     kv_dtype: str = "bf16"  # latent cache rows: "bf16" (1152 B) or "fp8" (656 B E4M3 + scales)
@@ -66,6 +66,8 @@ WORKLOADS = {
                  note="1M-context decode batch 8, fp8 indexer keys, one group"),
         Workload("stack78_b8_q8_n262144", 8, 1 << 18, 8, 78, "bf16",
                  note="78-layer stack (21F+57S), MTP verify shape 8 queries/seq"),
+        Workload("prefill_q4096_n131072_fp8h", 1, 131072, 4096, 1, "fp8h", mla=False,
+                 note="prefill F layer, Hadamard-rotated e4m3 indexer; the step rotates and quantises q"),
         Workload("decode_b64_n131072_kv8", 64, 131072, 1, 4, "bf16", kv_dtype="fp8",
                  note="decode_b64_n131072 with the FP8 latent cache (656-byte rows)"),
         Workload("decode_b8_n1048576_fp8_kv8", 8, 1 << 20, 1, 4, "fp8", kv_dtype="fp8",
