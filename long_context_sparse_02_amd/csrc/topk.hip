@@ -518,9 +518,8 @@ __device__ __forceinline__ int gather_lists(const uint8_t* lists0, int l0, int n
 // Row q: its n_lists chunk lists into the final indices. levels: workspace for
 // the rounds of the fallback (level_lists(n_lists) lists per row, then
 // level_lists of that, ...), used only when the lists hold more than 16K items.
-__global__ __launch_bounds__(kThreads) void topk_merge(const uint8_t* __restrict__ lists, int n_lists,
-                                                       uint8_t* __restrict__ levels, int32_t* __restrict__ idx) {
-    __shared__ MergeLds m;
+__device__ __forceinline__ void merge_row(const uint8_t* __restrict__ lists, int n_lists,
+                                          uint8_t* __restrict__ levels, int32_t* __restrict__ idx, MergeLds& m) {
     const int q = blockIdx.x;
     int32_t* out = idx + (int64_t)q * kK;
     const uint8_t* in = lists + (size_t)q * n_lists * kListBytes;
@@ -569,6 +568,22 @@ __global__ __launch_bounds__(kThreads) void topk_merge(const uint8_t* __restrict
     }
     write_final_pad(out, cnt);
 }
+
+// Two builds of the merge: few rows want each work-group's latency low (no cap
+// on registers); many rows (prefill) want two work-groups per CU, i.e. at most
+// 128 registers, at the cost of spills in the rare paths (measured: 4096 rows
+// 746 -> 665 us; 8 to 64 rows about 1.5 us slower).
+__global__ __launch_bounds__(kThreads) void topk_merge(const uint8_t* __restrict__ lists, int n_lists,
+                                                       uint8_t* __restrict__ levels, int32_t* __restrict__ idx) {
+    __shared__ MergeLds m;
+    merge_row(lists, n_lists, levels, idx, m);
+}
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_merge_wide(
+    const uint8_t* __restrict__ lists, int n_lists, uint8_t* __restrict__ levels, int32_t* __restrict__ idx) {
+    __shared__ MergeLds m;
+    merge_row(lists, n_lists, levels, idx, m);
+}
+constexpr int kWideRows = 512;                  // rows from which the capped build is used
 
 int n_chunks_of(int64_t ld) { return (int)((ld + kChunk - 1) / kChunk); }
 
@@ -628,7 +643,10 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, in
     uint8_t* lists = p;
     uint8_t* levels = lists + (size_t)n_q * nc * kListBytes;
     hipLaunchKernelGGL(topk_chunk, dim3(nc, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, nc, bound, lists, idx);
-    hipLaunchKernelGGL(topk_merge, dim3(n_q), dim3(kThreads), 0, st, (const uint8_t*)lists, nc, levels, idx);
+    if (n_q >= kWideRows)
+        hipLaunchKernelGGL(topk_merge_wide, dim3(n_q), dim3(kThreads), 0, st, (const uint8_t*)lists, nc, levels, idx);
+    else
+        hipLaunchKernelGGL(topk_merge, dim3(n_q), dim3(kThreads), 0, st, (const uint8_t*)lists, nc, levels, idx);
     return hipGetLastError();
 }
 

@@ -168,6 +168,18 @@ def test_topk_bounded_rows_match_oracle(kind):
     _topk_case(s, pos, f"{kind} n={n}")
 
 
+def test_topk_many_rows_mixed_kinds():
+    # >= 512 rows take the register-capped merge build; constant rows take its
+    # round-based fallback (every score passes the bound, 5 lists of 2048)
+    n, rows = 66_000, 520
+    parts = [W.score_matrix(kind, rows, n, seed=31) for kind in ("all_equal", "int_ties", "few_values")]
+    s = torch.stack([parts[i % 3][i] for i in range(rows)])
+    g = torch.Generator().manual_seed(32)
+    pos = torch.randint(60_000, n, (rows,), generator=g, dtype=torch.int32)
+    pos[::7] = 65_535
+    _topk_case(s, pos, f"{rows} mixed rows", with_max=False)
+
+
 def test_topk_bound_with_one_huge_value_per_group():
     # every 32-group holds one large value: the bound is the k-th of them and
     # many equal scores sit exactly at it
