@@ -117,13 +117,17 @@ def measured_traffic(kind, wl):
 
 
 # ---- inputs and the step ----------------------------------------------------------
-def build_inputs(wl, seed, dev):
-    """Device inputs of the workload, drawn by the seeded generators in `workloads`."""
+def build_inputs(wl, seed, dev, per_layer_dsa=False):
+    """Device inputs of the workload, drawn by the seeded generators in `workloads`.
+    per_layer_dsa: every layer is full (its own indexer and top-k), the schedule
+    IndexShare replaces."""
     t0 = time.time()
     q_seq, q_pos = W.query_layout(wl, dev)
     fp8 = wl.indexer_dtype in ("fp8", "fp8h")
     rot = wl.indexer_dtype == "fp8h"           # Hadamard-rotated fp8: the step quantises q
-    if is_stack(wl):
+    if per_layer_dsa:
+        src = list(range(wl.n_layers if wl.mla else 1))
+    elif is_stack(wl):
         src = gsa.layer_pattern(wl.n_layers)
     else:                                      # one group: layer 0 full, the rest shared
         src = [0] * (wl.n_layers if wl.mla else 1)
@@ -171,10 +175,10 @@ def make_step(wl, inp, dev):
     ld = (wl.n_ctx + 3) // 4 * 4
     n_full = len(inp["full_layers"])
     n_att = len(inp["layers"])
-    if is_stack(wl):
-        ws_bytes = gsa.stack_workspace_bytes(wl.n_q, ld, n_att)
-    else:
-        ws_bytes = gsa.group_workspace_bytes(wl.n_q, ld, max(n_att, 1))
+    # the largest group this step runs decides the workspace (a group of fewer
+    # layers may split its queries further and need more attention partials)
+    sizes = {sum(1 for l in range(n_att) if inp["src"][l] == j) for j in range(n_full)} or {1}
+    ws_bytes = max(gsa.group_workspace_bytes(wl.n_q, ld, max(g, 1)) for g in sizes)
     bufs = dict(
         scores=torch.empty((wl.n_q, ld), dtype=torch.float32, device=dev),
         gmax=torch.empty((wl.n_q, gsa.group_max_ld(ld)), dtype=torch.float32, device=dev),
@@ -229,7 +233,7 @@ def run_bench(args):
     wl = W.WORKLOADS[args.workload]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    inp = build_inputs(wl, args.seed, dev)
+    inp = build_inputs(wl, args.seed, dev, per_layer_dsa=args.per_layer_dsa)
     step, bufs, calls = make_step(wl, inp, dev)
     for _ in range(args.warmup):
         step()
@@ -276,7 +280,8 @@ def run_bench(args):
                    "queries": wl.n_q, "full_layers": len(inp["full_layers"]),
                    "attention_layers": len(inp["layers"]), "indexer": wl.indexer_dtype,
                    "latent_cache": wl.kv_dtype,
-                   "topk": 2048, "mla_heads": 64, "seed": args.seed},
+                   "topk": 2048, "mla_heads": 64, "seed": args.seed,
+                   "schedule": "per-layer DSA" if args.per_layer_dsa else "IndexShare"},
         "breakdown_ms_per_step": {k: round(v, 4) for k, v in ms_kind.items()},
         "avg_launch_us": {k: round(ms_kind[k] / launches[k] * 1e3, 2) for k in kinds},
         "achieved_GBs": {k: round(bytes_kind[k] / (ms_kind[k] / 1e3) / 1e9, 1) for k in kinds},
@@ -417,6 +422,8 @@ def main():
                     help="the CPU sample stops at the first query that starts past this much oracle time")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
+    ap.add_argument("--per-layer-dsa", action="store_true",
+                    help="every layer full (own indexer + top-k): the schedule IndexShare replaces")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path is measured on a single MI355X); "
