@@ -335,7 +335,13 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
             inrun[jj] = jw0 + jj >= j0 && jw0 + jj < j1;
             nin += inrun[jj] ? 1 : 0;
         }
-        const int stores = nin * NSUB;           // score stores of this wave per tile
+        // vector-memory stores this wave issues per tile, as a lower bound (the wait
+        // below lets that many stores stay outstanding besides the later tiles'
+        // DMAs; counting more than are issued would let it pass before this tile's
+        // DMAs land). The fast path issues one store per subtile for both queries
+        // (two with group maxima); the general path one per run query and subtile
+        // (two with group maxima) below the chunk end.
+        const int stores = nin > 0 ? NSUB : 0;
 
         auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
             const int64_t t0 = c0 + (int64_t)ti * T::kKeys;
