@@ -39,7 +39,7 @@ def test_quantize_e4m3_matches_oracle():
 
 
 # ------------------------------------------------------------------ indexer score
-def _score_case(wl, seed, ld=None, dtype="bf16", perm=None):
+def _score_case(wl, seed, ld=None, dtype="bf16", perm=None, with_max=True):
     q, w = W.indexer_queries(wl, seed, 0)
     k = W.indexer_keys(wl, seed, 0)
     q_seq, q_pos = W.query_layout(wl)
@@ -48,7 +48,7 @@ def _score_case(wl, seed, ld=None, dtype="bf16", perm=None):
     d = dev()
     ld = ld or (wl.n_ctx + 3) // 4 * 4
     scores = torch.full((wl.n_q, ld), 12345.0, device=d)
-    gmax = torch.full((wl.n_q, gsa.group_max_ld(ld)), 777.0, device=d)
+    gmax = torch.full((wl.n_q, gsa.group_max_ld(ld)), 777.0, device=d) if with_max else None
     if dtype == "fp8":
         qc, qs = gsa.quantize_e4m3(q.to(d))
         kc, ks = gsa.quantize_e4m3(k.to(d))
@@ -62,6 +62,8 @@ def _score_case(wl, seed, ld=None, dtype="bf16", perm=None):
     for i in range(wl.n_q):
         assert_scores_equal(got[i, : wl.n_ctx], want[i], f"query {i}")
     assert np.all(got[:, wl.n_ctx:] == 12345.0), "columns past n_cap were written"
+    if gmax is None:
+        return got
     # group maxima: bit-exact (integer inputs), +0.0 for a zero maximum, untouched past n_cap
     ng = -(-wl.n_ctx // 32)
     gm_want = oracle.group_max(want, n_cols=wl.n_ctx)
@@ -78,14 +80,24 @@ def test_score_tiny_group(dtype):
     _score_case(W.WORKLOADS["group_b1_n4096_q4"], 0, dtype=dtype)
 
 
+@pytest.mark.parametrize("with_max", [True, False])
 @pytest.mark.parametrize("q_per_seq", [1, 2, 3, 4, 8, 11, 16, 19, 37])
 @pytest.mark.parametrize("dtype", ["bf16", "fp8"])
-def test_score_ragged_and_query_blocks(q_per_seq, dtype):
+def test_score_ragged_and_query_blocks(q_per_seq, dtype, with_max):
     # 1-2 per sequence: one query per wave pair; 4-15: 4 or 8 queries per work-group;
     # 16+: 16 per work-group, with blocks that straddle two sequences (19, 37)
-    # n_cap not a multiple of the 128-key tile; several sequences; ld padded
+    # n_cap not a multiple of the 128-key tile; several sequences; ld padded;
+    # with and without group maxima (the kernels issue different stores)
     wl = W.Workload("ragged", 3, 1000 + 37 * q_per_seq, q_per_seq, 1, dtype)
-    _score_case(wl, q_per_seq, ld=(wl.n_ctx + 12 + 3) // 4 * 4, dtype=dtype)
+    _score_case(wl, q_per_seq, ld=(wl.n_ctx + 12 + 3) // 4 * 4, dtype=dtype, with_max=with_max)
+
+
+@pytest.mark.parametrize("q_per_seq", [4, 8, 16])
+def test_score_many_tiles_without_group_max(q_per_seq):
+    # long rows through the multi-query kernel's two-query fast path with no group
+    # maxima written: many tiles per work-group, so the ring waits see every case
+    wl = W.Workload("long_mq", 2, 20_000 + 7, q_per_seq, 1, "bf16")
+    _score_case(wl, 50 + q_per_seq, with_max=False)
 
 
 @pytest.mark.parametrize("n_per", [5, 10, 20])
