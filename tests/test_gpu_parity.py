@@ -92,17 +92,22 @@ def test_score_ragged_and_query_blocks(q_per_seq, dtype, with_max):
     _score_case(wl, q_per_seq, ld=(wl.n_ctx + 12 + 3) // 4 * 4, dtype=dtype, with_max=with_max)
 
 
-@pytest.mark.parametrize("q_per_seq", [4, 8, 16])
-def test_score_many_tiles_without_group_max(q_per_seq):
-    # long rows through the multi-query kernel's two-query fast path with no group
-    # maxima written: many tiles per work-group, so the ring waits see every case
-    wl = W.Workload("long_mq", 2, 20_000 + 7, q_per_seq, 1, "bf16")
-    _score_case(wl, 50 + q_per_seq, with_max=False)
+@pytest.mark.parametrize("with_max", [False, True])
+@pytest.mark.parametrize("dtype", ["bf16", "fp8"])
+@pytest.mark.parametrize("q_per_seq", [1, 4, 8, 16])
+def test_score_many_tiles(q_per_seq, dtype, with_max):
+    # long rows (many tiles per work-group, so the ring waits see every case)
+    # through the one-query kernel and the multi-query kernel's two-query fast path,
+    # with and without group maxima (each wait counts the stores issued since);
+    # 8 or 16 queries per sequence stream their keys through the deeper ring
+    wl = W.Workload("long_mq", 2, 20_000 + 7, q_per_seq, 1, dtype)
+    _score_case(wl, 50 + q_per_seq, dtype=dtype, with_max=with_max)
 
 
-@pytest.mark.parametrize("n_per", [5, 10, 20])
+@pytest.mark.parametrize("n_per", [5, 8, 10, 16, 20])
 def test_score_unsorted_sequences_and_positions(n_per):
     # random sequence per query: every query block holds several short runs
+    # (8 and 16 per sequence take the streaming multi-query kernel)
     wl = W.Workload("mixed", 4, 700, n_per, 1, "bf16")
     perm = torch.randperm(wl.n_q, generator=torch.Generator().manual_seed(3))
     q, w = W.indexer_queries(wl, 5, 0)
