@@ -377,7 +377,7 @@ __global__ __launch_bounds__(kThreads) void topk_bound(const float* __restrict__
     auto load = [&](int64_t j, float (&x)[kPerSmall]) __attribute__((always_inline)) {
 #pragma unroll
         for (int r = 0; r < kPerSmall; ++r)
-            x[r] = gm[min(j * n_items + 64 * kPerSmall * wave + 64 * r + lane, n_full - 1)];
+            x[r] = __builtin_nontemporal_load(gm + min(j * n_items + 64 * kPerSmall * wave + 64 * r + lane, n_full - 1));
     };
     int64_t j = 0;
     for (; j + 4 <= rg; j += 4) {                            // uniform
@@ -412,11 +412,12 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__
     // lane holds items kSeg*wave + 64r + lane: each wave load reads 256 contiguous bytes.
     // Loads are unconditional (clamped address) so all 32 are in flight together; a
     // branch around each would make the compiler wait for each one at the join.
+    // Each score is read once: non-temporal loads (prefill top-k 1.7-3.4% faster).
     uint32_t v[kPer];                                         // 0: not a candidate
     if (n > 0) {
         float x[kPer];
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) x[r] = row[min(kSeg * wave + 64 * r + lane, n - 1)];
+        for (int r = 0; r < kPer; ++r) x[r] = __builtin_nontemporal_load(row + min(kSeg * wave + 64 * r + lane, n - 1));
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
             const uint32_t key = score_key(x[r]);
