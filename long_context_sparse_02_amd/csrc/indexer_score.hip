@@ -690,14 +690,20 @@ hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, c
     const int per_seq = n_q / (batch > 0 ? batch : 1);
     const int qb = per_seq >= 16 ? 16 : per_seq >= 8 ? 8 : per_seq >= 4 ? 4 : per_seq >= 2 ? 2 : 1;
     const int64_t n_qblk = (n_q + qb - 1) / qb;
-    // Key chunk per work-group, 1K..16K keys. One query per work-group streams
+    // Key chunk per work-group, 1K..16K keys (64K with several queries per
+    // work-group). One query per work-group streams
     // from HBM: bf16 rows run best with >= 2048 work-groups (~1 MiB each), fp8
     // rows with >= 512 (~2 MiB each: half the bytes per key, so the ring fill
     // each work-group start costs is spread over more keys). Several queries
-    // per work-group are compute bound, and fewer, longer chunks (>= 512
-    // work-groups) save that refill too.
-    const int64_t min_wg = (qb >= 4 || fp8) ? 512 : 2048;
-    int64_t chunk = 16384;
+    // per work-group are compute bound, and fewer, longer chunks save that
+    // refill too: >= 256 work-groups, one per CU (8 x 256K keys with 8 queries
+    // per sequence: 142 us against 149 / 171 / 208 us at 512 / 1024 / 2048;
+    // prefill has 256 query blocks, so its chunks stay at the cap). The
+    // multi-query cap is 64K keys: each work-group first loads the A operands
+    // of its 16 queries (128 KiB), and 4096 x 128K-key prefill measured 1.3-2.1%
+    // faster than with 16K (32K: 1%; 128K: mixed).
+    const int64_t min_wg = qb >= 4 ? 256 : fp8 ? 512 : 2048;
+    int64_t chunk = qb >= 4 ? 65536 : 16384;
     while (chunk > 1024 && n_qblk * ((n_cap + chunk - 1) / chunk) < min_wg) chunk >>= 1;
     const dim3 grid((unsigned)((n_cap + chunk - 1) / chunk), (unsigned)n_qblk);
     // One query block per sequence (decode): every key is read by one
