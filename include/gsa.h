@@ -159,6 +159,37 @@ gsa_status gsa_topk(const float* scores_dev, int64_t ld_scores, const int32_t* q
                     void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /*
+ * gsa_indexer_topk — the full layer's score and top-k without a score buffer
+ * ([Serving] §10: the candidate scoring and top-k a sparse layer adds perform
+ * according to how far they are fused; here no [n_q, n_cap] score matrix
+ * reaches memory).
+ *
+ * Selects exactly what gsa_indexer_score followed by gsa_topk selects (same
+ * positions, same order, -1 padded), from the same inputs (arguments as in
+ * gsa_indexer_score, without scores_dev / ld_scores / group_max_dev). Rows of at
+ * least 2048 full 32-position groups run the score kernel writing only group
+ * maxima, take the 2048th largest of them as a lower bound of every selected
+ * score, and recompute the scores of the groups whose maximum reaches it with
+ * the score kernel's own arithmetic (bit-identical scores); shorter rows
+ * recompute every group. It saves the score buffer's memory (4 * n_q * n_cap
+ * bytes: 2 GiB for 4096 queries over 2^17 positions) and its traffic; on
+ * MI355X it is not faster than the buffered pair at 2^17 to 2^20 positions
+ * (the key rows of the ~6% of groups that reach the bound at 2^20 are re-read
+ * one row per lane, and the score pass without a buffer measured no faster).
+ * k must be 2048; n_cap <= 2^23.
+ * workspace_dev: at least gsa_indexer_topk_workspace_bytes(n_q, n_cap, k)
+ *            bytes, 16-byte aligned; its contents on entry do not matter.
+ * Errors: as gsa_indexer_score and gsa_topk.
+ */
+size_t gsa_indexer_topk_workspace_bytes(int n_q, int64_t n_cap, int k);
+gsa_status gsa_indexer_topk(gsa_dtype dt,
+                            const void* q_dev, const float* q_scale_dev, const float* w_dev,
+                            const void* k_dev, const float* k_scale_dev,
+                            const int32_t* q_seq_dev, const int32_t* q_pos_dev,
+                            int n_q, int batch, int64_t n_cap, int k, int32_t* idx_dev,
+                            void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/*
  * gsa_sparse_mla_attn — absorbed MLA over the selected positions of one layer
  * ([Overview] tbl-glm52-config: 64 heads, QK dim 256 = 192 + 64, latent 512,
  * cache row 512 + 64 in BF16 = 1152 B; sub-document index: decode in latent
@@ -201,7 +232,10 @@ gsa_status gsa_sparse_mla_attn(const void* q_lat_dev, const void* q_rope_dev, co
  *                    the indexer fields are ignored.
  * index_buf_dev int32 [n_q, k], owned by the caller, who keeps it consistent
  *                    with the prefix and positions it was computed for.
- * scores_dev   fp32 [n_q, ld_scores] scratch for the F layer's scores.
+ * scores_dev   fp32 [n_q, ld_scores] scratch for the F layer's scores, or NULL:
+ *              then the F layer selects as gsa_indexer_topk does (no score
+ *              buffer; ld_scores is ignored) and the workspace is sized with
+ *              ld_scores = n_cap rounded up to a multiple of 4.
  * workspace    at least gsa_group_workspace_bytes(n_q, ld_scores, k, n_heads, n_layers).
  * Attention for all n_layers layers runs as gsa_sparse_mla_attn_layers.
  */

@@ -84,6 +84,8 @@ def _declare(lib):
         "gsa_quantize_e4m3_hadamard": (I, [P, I64, P, P, P]),
         "gsa_indexer_score": (I, [I, P, P, P, P, P, P, P, I, I, I64, P, I64, P, P]),
         "gsa_group_max_ld": (I64, [I64]),
+        "gsa_indexer_topk_workspace_bytes": (SZ, [I, I64, I]),
+        "gsa_indexer_topk": (I, [I, P, P, P, P, P, P, P, I, I, I64, I, P, P, SZ, P]),
         "gsa_topk_workspace_bytes": (SZ, [I, I64, I]),
         "gsa_topk": (I, [P, I64, P, I, I, P, P, P, SZ, P]),
         "gsa_mla_workspace_bytes": (SZ, [I, I, I]),
@@ -218,6 +220,33 @@ def indexer_score(q, w, k, q_seq, q_pos, q_scale=None, k_scale=None, scores=None
                                    _p(k_scale), _p(q_seq), _p(q_pos), n_q, batch, n_cap,
                                    _p(scores), scores.shape[1], _p(group_max), _stream(q.device)))
     return scores
+
+
+def indexer_topk_workspace_bytes(n_q, n_cap, k=TOPK):
+    return int(lib().gsa_indexer_topk_workspace_bytes(n_q, n_cap, k))
+
+
+def indexer_topk(q, w, k, q_seq, q_pos, q_scale=None, k_scale=None, topk=TOPK, idx=None, workspace=None):
+    """Score + top-k without a score buffer (the indices indexer_score + topk
+    give). Same inputs as indexer_score; returns idx int32 [n_q, topk]."""
+    fp8 = q.dtype == torch.uint8
+    n_q, batch, n_cap = q.shape[0], k.shape[0], k.shape[1]
+    _need(q, "q", torch.uint8 if fp8 else torch.bfloat16, (n_q, INDEX_HEADS, INDEX_DIM))
+    _need(k, "k", q.dtype, (batch, n_cap, INDEX_DIM))
+    _need(w, "w", torch.float32, (n_q, INDEX_HEADS))
+    _need(q_seq, "q_seq", torch.int32, (n_q,))
+    _need(q_pos, "q_pos", torch.int32, (n_q,))
+    if fp8:
+        _need(q_scale, "q_scale", torch.float32, (n_q, INDEX_HEADS))
+        _need(k_scale, "k_scale", torch.float32, (batch, n_cap))
+    if idx is None:
+        idx = torch.empty((n_q, topk), dtype=torch.int32, device=q.device)
+    _need(idx, "idx", torch.int32, (n_q, topk))
+    ws = _workspace(indexer_topk_workspace_bytes(n_q, n_cap, topk), q.device, workspace)
+    _check(lib().gsa_indexer_topk(FP8_E4M3 if fp8 else BF16, _p(q), _p(q_scale), _p(w), _p(k), _p(k_scale),
+                                  _p(q_seq), _p(q_pos), n_q, batch, n_cap, topk, _p(idx), _p(ws), ws.numel(),
+                                  _stream(q.device)))
+    return idx
 
 
 def topk_workspace_bytes(n_q, ld, k=TOPK):
@@ -378,11 +407,12 @@ def sparse_mla_attn_layers(layers, q_seq, idx, scale=1.0 / 16.0, outs=None, work
 
 def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_idx=None,
                      q_scale=None, k_scale=None, scores=None, compute_index=True,
-                     scale=1.0 / 16.0, workspace=None, outs=None, block_table=None):
+                     scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True):
     """One IndexShare group: layers = [(q_lat, q_rope, kv), ...], F layer first.
     With compute_index the F layer's indexer + top-k write index_buf, then every
     layer attends over it. With block_table (int32 [batch, max_pages]) each kv is
-    a page pool [n_pages, page_size, 576]. Returns [(out, lse)] per layer."""
+    a page pool [n_pages, page_size, 576]. score_buffer=False selects without a
+    score buffer (as indexer_topk). Returns [(out, lse)] per layer."""
     L = lib()
     n_q = q_seq.shape[0]
     kv0 = layers[0][2]
@@ -396,10 +426,12 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     k = index_buf.shape[1]
     dev = q_seq.device
     fp8 = compute_index and q_idx.dtype == torch.uint8
-    if compute_index:
+    if compute_index and score_buffer:
         if scores is None:
             scores = torch.empty((n_q, (n_cap + 3) // 4 * 4), dtype=torch.float32, device=dev)
         ld = scores.shape[1]
+    elif compute_index:
+        scores, ld = None, (n_cap + 3) // 4 * 4
     else:
         ld = 4
     if outs is None:
@@ -419,7 +451,7 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
         d.q_idx_dev, d.w_dev, d.k_idx_dev = q_idx.data_ptr(), w.data_ptr(), k_idx.data_ptr()
         d.q_scale_dev = q_scale.data_ptr() if fp8 else None
         d.k_scale_dev = k_scale.data_ptr() if fp8 else None
-        d.scores_dev, d.q_pos_dev = scores.data_ptr(), q_pos.data_ptr()
+        d.scores_dev, d.q_pos_dev = (None if scores is None else scores.data_ptr()), q_pos.data_ptr()
     d.ld_scores = ld
     d.q_seq_dev = q_seq.data_ptr()
     d.n_q, d.batch, d.n_cap, d.k = n_q, batch, n_cap, k

@@ -35,18 +35,21 @@ bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
 constexpr int kMaxGridY = 65535;
 
+// with_scores = false: the indexer inputs only (the path without a score buffer)
 gsa_status check_score(gsa_dtype dt, const void* q, const float* qs, const float* w, const void* k,
                        const float* ks, const int32_t* q_seq, const int32_t* q_pos, int n_q,
-                       int batch, int64_t n_cap, const float* scores, int64_t ld) {
+                       int batch, int64_t n_cap, const float* scores, int64_t ld, bool with_scores = true) {
     if (dt != GSA_BF16 && dt != GSA_FP8_E4M3) return fail(GSA_ERR_INVALID_ARG, "unknown dtype %d", (int)dt);
     REQUIRE_PTR(q); REQUIRE_PTR(w); REQUIRE_PTR(k); REQUIRE_PTR(q_seq); REQUIRE_PTR(q_pos);
-    REQUIRE_PTR(scores);
+    if (with_scores) REQUIRE_PTR(scores);
     if (dt == GSA_FP8_E4M3) { REQUIRE_PTR(qs); REQUIRE_PTR(ks); }
     REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
     REQUIRE(batch >= 1, "batch must be >= 1 (got %d)", batch);
     REQUIRE(n_cap >= 1 && n_cap <= 0x7fffffff, "n_cap must be in [1, 2^31-1] (got %lld)", (long long)n_cap);
-    REQUIRE(ld >= n_cap, "ld_scores (%lld) must be >= n_cap (%lld)", (long long)ld, (long long)n_cap);
-    REQUIRE(ld % 4 == 0, "ld_scores must be a multiple of 4 (got %lld)", (long long)ld);
+    if (with_scores) {
+        REQUIRE(ld >= n_cap, "ld_scores (%lld) must be >= n_cap (%lld)", (long long)ld, (long long)n_cap);
+        REQUIRE(ld % 4 == 0, "ld_scores must be a multiple of 4 (got %lld)", (long long)ld);
+    }
     if (n_q > kMaxGridY) return fail(GSA_ERR_UNSUPPORTED, "n_q must be <= %d (got %d)", kMaxGridY, n_q);
     return GSA_OK;
 }
@@ -63,6 +66,22 @@ gsa_status check_topk(const float* scores, int64_t ld, const int32_t* q_pos, int
     const size_t need = gsa::topk_workspace_bytes(n_q, ld, k);
     if (ws == nullptr || ws_bytes < need)
         return fail(GSA_ERR_WORKSPACE, "top-k workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
+                    ws == nullptr ? ", NULL" : "");
+    REQUIRE(aligned16(ws), "workspace is not 16-byte aligned");
+    return GSA_OK;
+}
+
+// The selection without a score buffer (after check_score without scores).
+gsa_status check_indexer_topk(int n_q, int64_t n_cap, int k, const int32_t* idx, const void* ws,
+                              size_t ws_bytes) {
+    REQUIRE_PTR(idx);
+    if (k != GSA_TOPK) return fail(GSA_ERR_UNSUPPORTED, "k must be %d (got %d)", GSA_TOPK, k);
+    const int64_t ld = gsa::indexer_topk_ld(n_cap);
+    if (ld > ((int64_t)1 << 23))
+        return fail(GSA_ERR_UNSUPPORTED, "n_cap must be <= 2^23 (got %lld)", (long long)n_cap);
+    const size_t need = gsa::topk_workspace_bytes(n_q, ld, k);
+    if (ws == nullptr || ws_bytes < need)
+        return fail(GSA_ERR_WORKSPACE, "indexer top-k workspace needs %zu bytes (got %zu%s)", need, ws_bytes,
                     ws == nullptr ? ", NULL" : "");
     REQUIRE(aligned16(ws), "workspace is not 16-byte aligned");
     return GSA_OK;
@@ -169,6 +188,25 @@ gsa_status gsa_indexer_score(gsa_dtype dt, const void* q, const float* q_scale, 
                                                 q_pos, n_q, batch, n_cap, scores, ld, group_max,
                                                 (hipStream_t)stream),
                       "indexer_score");
+}
+
+size_t gsa_indexer_topk_workspace_bytes(int n_q, int64_t n_cap, int k) {
+    if (n_q < 1 || n_cap < 1) return 0;
+    return gsa::topk_workspace_bytes(n_q, gsa::indexer_topk_ld(n_cap), k);
+}
+
+gsa_status gsa_indexer_topk(gsa_dtype dt, const void* q, const float* q_scale, const float* w,
+                            const void* k, const float* k_scale, const int32_t* q_seq,
+                            const int32_t* q_pos, int n_q, int batch, int64_t n_cap, int k_sel,
+                            int32_t* idx, void* ws, size_t ws_bytes, void* stream) {
+    gsa_status st = check_score(dt, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, batch, n_cap, nullptr, 0,
+                                false);
+    if (st != GSA_OK) return st;
+    st = check_indexer_topk(n_q, n_cap, k_sel, idx, ws, ws_bytes);
+    if (st != GSA_OK) return st;
+    return hip_result(gsa::launch_indexer_topk(dt == GSA_FP8_E4M3, q, q_scale, w, k, k_scale, q_seq, q_pos,
+                                               n_q, batch, n_cap, k_sel, idx, ws, (hipStream_t)stream),
+                      "indexer_topk");
 }
 
 int64_t gsa_group_max_ld(int64_t ld) { return ld < 1 ? 0 : gsa::group_max_ld(ld); }
@@ -318,12 +356,15 @@ gsa_status validate_group(const gsa_group_desc* d) {
                 (long long)n_cap_pg, (long long)d->n_cap);
     }
     if (d->compute_index) {
+        const bool buffered = d->scores_dev != nullptr;        // else: selection without a score buffer
         gsa_status st = check_score(d->dt, d->q_idx_dev, d->q_scale_dev, d->w_dev, d->k_idx_dev,
                                     d->k_scale_dev, d->q_seq_dev, d->q_pos_dev, d->n_q, d->batch,
-                                    d->n_cap, d->scores_dev, d->ld_scores);
+                                    d->n_cap, d->scores_dev, d->ld_scores, buffered);
         if (st != GSA_OK) return st;
-        st = check_topk(d->scores_dev, d->ld_scores, d->q_pos_dev, d->n_q, d->k, d->index_buf_dev,
-                        d->workspace_dev, d->workspace_bytes);
+        st = buffered ? check_topk(d->scores_dev, d->ld_scores, d->q_pos_dev, d->n_q, d->k, d->index_buf_dev,
+                                   d->workspace_dev, d->workspace_bytes)
+                      : check_indexer_topk(d->n_q, d->n_cap, d->k, d->index_buf_dev, d->workspace_dev,
+                                           d->workspace_bytes);
         if (st != GSA_OK) return st;
     }
     for (int l = 0; l < d->n_layers; ++l) {
@@ -343,7 +384,13 @@ gsa_status validate_group(const gsa_group_desc* d) {
 
 // Enqueues a validated group: score -> top-k (F layer) -> attention per layer.
 gsa_status enqueue_group(const gsa_group_desc* d, hipStream_t s) {
-    if (d->compute_index) {
+    if (d->compute_index && d->scores_dev == nullptr) {
+        const hipError_t e = gsa::launch_indexer_topk(d->dt == GSA_FP8_E4M3, d->q_idx_dev, d->q_scale_dev,
+                                                      d->w_dev, d->k_idx_dev, d->k_scale_dev, d->q_seq_dev,
+                                                      d->q_pos_dev, d->n_q, d->batch, d->n_cap, d->k,
+                                                      d->index_buf_dev, d->workspace_dev, s);
+        if (e != hipSuccess) return hip_result(e, "group: indexer_topk");
+    } else if (d->compute_index) {
         // the score kernel writes the group maxima where the top-k keeps them
         float* gm = gsa::topk_group_max_area(d->workspace_dev, d->n_q, d->ld_scores);
         hipError_t e = gsa::launch_indexer_score(d->dt == GSA_FP8_E4M3, d->q_idx_dev, d->q_scale_dev,

@@ -153,11 +153,13 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
         const int na = t_end > c0 ? (int)((t_end - c0 + T::kKeys - 1) / T::kKeys) : 0;
         const int nt_all = (int)((c1 - c0 + T::kKeys - 1) / T::kKeys);
         // score stores this wave issues per tile in this run (one per owned pair in the run)
+        // (none without a score buffer: the group-maximum stores then go uncounted,
+        // which only makes the waits stricter)
         int stores = 0;
 #pragma unroll
         for (int p = 0; p < PPW; ++p) {
             const int j = (wave * PPW + p) / NSUBT;
-            stores += (j >= j0 && j < j1) ? 1 : 0;
+            stores += (j >= j0 && j < j1 && scores != nullptr) ? 1 : 0;
         }
 
         auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
@@ -230,7 +232,8 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
                     part = sum_x32(part);
                     res = (s <= apos[jj]) ? part : neg_inf();
                 }
-                if (g == 0 && s < c1) store_score<FP8>(scores + (int64_t)(qb0 + j) * ld + s, res);
+                if (scores != nullptr && g == 0 && s < c1)   // uniform pointer test
+                    store_score<FP8>(scores + (int64_t)(qb0 + j) * ld + s, res);
                 if (gmax != nullptr && s0 < c1) {                       // uniform
                     const uint32_t m = max_x32(score_key(s < c1 ? res : neg_inf()));
                     if (lane == 0) gmax[(int64_t)(qb0 + j) * ldg + (s0 >> 5)] = key_value(m);
@@ -354,7 +357,8 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
         // DMAs land). The fast path issues one store per subtile for both queries
         // (two with group maxima); the general path one per run query and subtile
         // (two with group maxima) below the chunk end.
-        const int stores = nin > 0 ? NSUB : 0;
+        // Without a score buffer only group maxima are stored; they go uncounted.
+        const int stores = nin > 0 && scores != nullptr ? NSUB : 0;
 
         auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
             const int64_t t0 = c0 + (int64_t)ti * T::kKeys;
@@ -426,7 +430,8 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
                                                                     __float_as_uint(part[1]), false, false);
                     f.sc = __uint_as_float(r[0]) + __uint_as_float(r[1]);
-                    store_score<FP8>(scores + (int64_t)(qb0 + jw0 + g) * ld + f.s0 + n, f.sc);
+                    if (scores != nullptr)                     // uniform
+                        store_score<FP8>(scores + (int64_t)(qb0 + jw0 + g) * ld + f.s0 + n, f.sc);
                 };
                 auto fin_b = [&](Fin& f) __attribute__((always_inline)) {
                     if (gmax == nullptr) return;               // uniform
@@ -619,8 +624,8 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                             part = fmaf(wr[jj][i], __int_as_float(max(__float_as_int(acc[jj][i]), 0)), part);
                         part = sum_x32(part);
                         const float res = (active && n <= lim) ? part : neg_inf();
-                        float* row = scores + (int64_t)(qb0 + jw0 + jj) * ld + s0;
-                        if (g == 0 && s0 + n < c1) row[n] = res;
+                        if (scores != nullptr && g == 0 && s0 + n < c1)
+                            scores[(int64_t)(qb0 + jw0 + jj) * ld + s0 + n] = res;
                         if (gmax != nullptr && s0 < c1) {              // uniform
                             const uint32_t m = max_x32(score_key(s0 + n < c1 ? res : neg_inf()));
                             if (lane == 0) gmax[(int64_t)(qb0 + jw0 + jj) * ldg + (s0 >> 5)] = key_value(m);
@@ -630,8 +635,8 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
 #pragma unroll
                     for (int jj = 0; jj < QPW; ++jj) {
                         if (!inrun[jj]) continue;
-                        float* row = scores + (int64_t)(qb0 + jw0 + jj) * ld + s0;
-                        if (g == 0 && s0 + n < c1) row[n] = neg_inf();
+                        if (scores != nullptr && g == 0 && s0 + n < c1)
+                            scores[(int64_t)(qb0 + jw0 + jj) * ld + s0 + n] = neg_inf();
                         if (gmax != nullptr && s0 < c1 && lane == 0)
                             gmax[(int64_t)(qb0 + jw0 + jj) * ldg + (s0 >> 5)] = neg_inf();
                     }

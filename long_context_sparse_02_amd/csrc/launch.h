@@ -32,6 +32,14 @@ float* topk_group_max_area(void* ws, int n_q, int64_t ld);
 hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, int n_q, int k,
                        const float* group_max, int32_t* idx, void* ws, hipStream_t stream);
 
+// Score and top-k without a score buffer: group maxima from the score kernel,
+// their bound, then a rescoring of the 32-position groups that reach it. The
+// workspace is topk_workspace_bytes(n_q, indexer_topk_ld(n_cap), k) bytes.
+inline int64_t indexer_topk_ld(int64_t n_cap) { return (n_cap + 3) / 4 * 4; }
+hipError_t launch_indexer_topk(bool fp8, const void* q, const float* q_scale, const float* w, const void* k,
+                               const float* k_scale, const int32_t* q_seq, const int32_t* q_pos, int n_q,
+                               int batch, int64_t n_cap, int k_sel, int32_t* idx, void* ws, hipStream_t stream);
+
 // One attention layer's operands (a layer of an IndexShare group).
 struct MlaLayerPtrs {
     const void* q_lat;

@@ -21,6 +21,8 @@
 // The last level writes the positions (ascending) and pads with -1. The row is
 // read from HBM once; no counter or histogram is shared between work-groups,
 // so the result is the same on every run.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launch.h"
 
@@ -442,6 +444,136 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__
     }
 }
 
+// ---- Selection without a score buffer ----------------------------------------
+// The score kernel wrote only the group maxima (the largest score of every 32
+// positions) and topk_bound turned them into the bound L of each row. A
+// selected position scores >= L, so it lies in a group whose maximum reaches L;
+// this kernel recomputes the scores of exactly those groups and selects among
+// them as topk_chunk does among stored scores (same lists, same merge). The
+// recomputation is the score kernels' own arithmetic: the same MFMA, the same
+// split of the 128 dims (lane group g owns dims [64g, 64g + 64) of query and
+// key) and the same ReLU, weight and head-sum order, so every score, and with
+// it the selection, is bit-identical to the path through a score buffer.
+// Rows without a bound (too short) recompute every group.
+template <bool FP8>
+__global__ __launch_bounds__(kThreads) void topk_rescore(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale, const float* __restrict__ w,
+    const uint8_t* __restrict__ k, const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int64_t n_cap, const float* __restrict__ gmax, int64_t ldg,
+    const uint32_t* __restrict__ bound, int n_chunks, uint8_t* __restrict__ lists, int32_t* __restrict__ idx) {
+    constexpr int kHeadsIx = 32, kDimIx = 128;
+    constexpr int kRowBytes = FP8 ? kDimIx : 2 * kDimIx;
+    constexpr int KSTEPS = FP8 ? 2 : 8;              // MFMA steps over the 128 dims
+    constexpr int NLD = FP8 ? 4 : 8;                 // 16-byte key loads per lane per group
+    using AVec = std::conditional_t<FP8, i32x8, bf16x8>;
+    // the chunk's candidate keys, each written and read back by the wave that
+    // owns it; the selection scratch reuses the space once they are in registers
+    __shared__ union { uint32_t keys[kChunk]; Scratch sc; } lds;
+    const int qi = blockIdx.y, c = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 31, g = lane >> 5;
+    const int64_t len = min((int64_t)q_pos[qi] + 1, n_cap);          // positions 0..len-1 are causal
+    const int64_t s0 = (int64_t)c * kChunk;
+    const int nvalid = (int)max((int64_t)0, min(s0 + kChunk, len) - s0);
+    const uint32_t L = bound != nullptr ? uni(bound[qi]) : 0u;
+    // this wave: positions w0 + [0, kSeg), 64 groups of 32; group j passes when
+    // it holds a causal position and (with a bound) its maximum reaches L
+    const int64_t w0 = s0 + (int64_t)kSeg * wave;
+    const int nw = max(0, min(kSeg, nvalid - kSeg * wave));
+    bool ok = 32 * lane < nw;
+    if (ok && bound != nullptr) ok = score_key(gmax[(int64_t)qi * ldg + (w0 >> 5) + lane]) >= L;
+    const uint64_t pass = __builtin_amdgcn_ballot_w64(ok);
+
+    if (pass != 0) {                                                  // uniform
+        // A operand: row = head n, this lane group's 64 dims; weights in accumulator order
+        AVec a[KSTEPS];
+        float wr[16];
+        const uint8_t* qh = q + ((int64_t)qi * kHeadsIx + n) * kRowBytes;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            if constexpr (FP8) {
+                const i32x4* pq = (const i32x4*)(qh + 64 * g + 32 * t);
+                const i32x4 lo = pq[0], hi = pq[1];
+                a[t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            } else {
+                a[t] = *(const bf16x8*)(qh + 2 * (64 * g + 8 * t));
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wr[i] = w[(int64_t)qi * kHeadsIx + 8 * (i >> 2) + 4 * g + (i & 3)];
+        const int a_e8 = FP8 ? e8m0_of(q_scale[(int64_t)qi * kHeadsIx + n]) : 127;
+        const int seq = q_seq[qi];
+        const uint8_t* kb = k + (int64_t)seq * n_cap * kRowBytes;
+        const float* ksb = FP8 ? k_scale + (int64_t)seq * n_cap : nullptr;
+        uint32_t* kw = lds.keys + kSeg * wave;
+        // lane (n, g) of group j: key w0 + 32j + n, its dims [64g, 64g + 64)
+        // (a row past n_cap in a ragged last group reads row n_cap - 1: not a candidate)
+        auto load = [&](int j, i32x4 (&kr)[NLD], float& ks) __attribute__((always_inline)) {
+            const int64_t p = min(w0 + 32 * j + n, n_cap - 1);
+            const i32x4* src = (const i32x4*)(kb + p * kRowBytes + (kRowBytes / 2) * g);
+#pragma unroll
+            for (int i = 0; i < NLD; ++i) kr[i] = src[i];
+            ks = FP8 ? ksb[p] : 1.f;
+        };
+        // the passing groups in batches whose key loads are all in flight together
+        constexpr int NB = FP8 ? 4 : 2;
+        uint64_t todo = pass;
+        while (todo != 0) {                                           // uniform: todo is a ballot
+            int js[NB];
+            i32x4 kr[NB][NLD];
+            float ks[NB];
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                js[b] = todo != 0 ? (int)__builtin_ctzll(todo) : -1;
+                todo &= todo - 1;
+                if (js[b] >= 0) load(js[b], kr[b], ks[b]);
+            }
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                if (js[b] < 0) break;
+                f32x16 acc = {};
+#pragma unroll
+                for (int t = 0; t < KSTEPS; ++t) {
+                    if constexpr (FP8) {
+                        const i32x4 lo = kr[b][2 * t], hi = kr[b][2 * t + 1];
+                        const i32x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[t], bv, acc, 0, 0, 0, a_e8, 0,
+                                                                              e8m0_of(ks[b]));
+                    } else {
+                        acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[t], __builtin_bit_cast(bf16x8, kr[b][t]),
+                                                                      acc, 0, 0, 0);
+                    }
+                }
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i) part = fmaf(wr[i], fmaxf(acc[i], 0.f), part);
+                part = sum_x32(part);
+                const int64_t s = w0 + 32 * js[b] + n;
+                const uint32_t key = score_key(part);
+                if (g == 0) kw[32 * js[b] + n] = (s < len && key >= L) ? key : 0u;
+            }
+        }
+    }
+    // items as topk_chunk holds them: lane item r = position kSeg*wave + 64r + lane,
+    // group 2r + g of the wave; groups that did not pass hold no candidate
+    uint32_t v[kPer];
+#pragma unroll
+    for (int r = 0; r < kPer; ++r)
+        v[r] = ((pass >> (2 * r + g)) & 1u) ? lds.keys[kSeg * wave + 64 * r + lane] : 0u;
+    __syncthreads();                                                  // keys read: the scratch may reuse them
+    if (n_chunks == 1) {
+        int32_t* out = idx + (int64_t)qi * kK;
+        auto em = [&](uint32_t slot, int i, int) { out[slot] = (int32_t)(s0 + i); };
+        write_final_pad(out, select_regs<kPer, false>(v, lds.sc, em));
+    } else {
+        uint8_t* Lst = lists + ((size_t)qi * n_chunks + c) * kListBytes;
+        uint2* items = (uint2*)(Lst + 16);
+        auto em = [&](uint32_t slot, int i, int r) { items[slot] = make_uint2(v[r], (uint32_t)(s0 + i)); };
+        const int cnt = select_regs<kPer, false>(v, lds.sc, em);
+        if (threadIdx.x == 0) *(uint32_t*)Lst = (uint32_t)cnt;
+    }
+}
+
 // Number of list levels the merge may write: rounds of 8 until one list is left.
 __host__ __device__ inline int64_t level_lists(int64_t n_lists) { return (n_lists + kFan - 1) / kFan; }
 
@@ -648,6 +780,47 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, in
         hipLaunchKernelGGL(topk_merge_wide, dim3(n_q), dim3(kThreads), 0, st, (const uint8_t*)lists, nc, levels, idx);
     else
         hipLaunchKernelGGL(topk_merge, dim3(n_q), dim3(kThreads), 0, st, (const uint8_t*)lists, nc, levels, idx);
+    return hipGetLastError();
+}
+
+
+hipError_t launch_indexer_topk(bool fp8, const void* q, const float* q_scale, const float* w, const void* k,
+                               const float* k_scale, const int32_t* q_seq, const int32_t* q_pos, int n_q,
+                               int batch, int64_t n_cap, int k_sel, int32_t* idx, void* ws, hipStream_t st) {
+    (void)k_sel;
+    const int64_t ld = indexer_topk_ld(n_cap);
+    const int nc = n_chunks_of(ld);
+    const int64_t ldg = group_max_ld(ld);
+    uint8_t* p = (uint8_t*)ws;
+    const uint32_t* bound = nullptr;
+    const float* gm = nullptr;
+    if (nc > 1 && bounded(ld)) {
+        // the workspace layout of launch_topk: bounds, group maxima, lists, merge levels
+        uint32_t* b = (uint32_t*)p;
+        p += align256((size_t)n_q * 4);
+        float* g = (float*)p;
+        p += align256((size_t)n_q * ldg * 4);
+        hipError_t e = launch_indexer_score(fp8, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, batch, n_cap,
+                                            nullptr, ld, g, st);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(topk_bound, dim3(n_q), dim3(kThreads), 0, st, (const float*)g, ldg, q_pos, b);
+        bound = b;
+        gm = g;
+    }
+    uint8_t* lists = nc > 1 ? p : nullptr;
+    uint8_t* levels = nc > 1 ? lists + (size_t)n_q * nc * kListBytes : nullptr;
+    if (fp8)
+        hipLaunchKernelGGL(topk_rescore<true>, dim3(nc, n_q), dim3(kThreads), 0, st, (const uint8_t*)q, q_scale,
+                           w, (const uint8_t*)k, k_scale, q_seq, q_pos, n_cap, gm, ldg, bound, nc, lists, idx);
+    else
+        hipLaunchKernelGGL(topk_rescore<false>, dim3(nc, n_q), dim3(kThreads), 0, st, (const uint8_t*)q, q_scale,
+                           w, (const uint8_t*)k, k_scale, q_seq, q_pos, n_cap, gm, ldg, bound, nc, lists, idx);
+    if (nc > 1) {
+        if (n_q >= kWideRows)
+            hipLaunchKernelGGL(topk_merge_wide, dim3(n_q), dim3(kThreads), 0, st, (const uint8_t*)lists, nc, levels, idx);
+        else
+            hipLaunchKernelGGL(topk_merge, dim3(n_q), dim3(kThreads), 0, st, (const uint8_t*)lists, nc, levels, idx);
+    }
     return hipGetLastError();
 }
 

@@ -51,6 +51,33 @@ def test_indexer_score_rejects(kw, code):
     assert gsa.lib().gsa_last_error() != b""
 
 
+def test_indexer_topk_rejects():
+    # the selection without a score buffer: indexer checks, k, n_cap bound, workspace
+    L = gsa.lib()
+    need = L.gsa_indexer_topk_workspace_bytes(4, 200_001, 2048)
+    # as large as the buffered top-k's workspace for rows of n_cap rounded up to 4
+    assert need == L.gsa_topk_workspace_bytes(4, 200_004, 2048) > 0
+
+    def call(**kw):
+        a = dict(dt=0, q=FAKE, qs=None, w=FAKE, k=FAKE, ks=None, q_seq=FAKE, q_pos=FAKE, n_q=4, batch=1,
+                 n_cap=200_001, topk=2048, idx=FAKE, ws=FAKE, ws_bytes=need)
+        a.update(kw)
+        return L.gsa_indexer_topk(a["dt"], a["q"], a["qs"], a["w"], a["k"], a["ks"], a["q_seq"], a["q_pos"],
+                                  a["n_q"], a["batch"], a["n_cap"], a["topk"], a["idx"], a["ws"], a["ws_bytes"],
+                                  None)
+
+    assert call(topk=1024) == UNSUPPORTED
+    assert call(ws_bytes=need - 1) == WORKSPACE
+    assert call(ws=None) == WORKSPACE
+    assert call(ws=MISALIGNED, ws_bytes=need) == INVALID
+    assert call(idx=None) == INVALID
+    assert call(q=None) == INVALID
+    assert call(dt=1) == INVALID                                # fp8 without scales
+    assert call(n_q=0) == INVALID
+    assert call(n_cap=(1 << 23) + 1, ws_bytes=1 << 40) == UNSUPPORTED
+    assert gsa.lib().gsa_last_error() != b""
+
+
 def test_topk_rejects():
     L = gsa.lib()
     need = L.gsa_topk_workspace_bytes(4, 4096, 2048)
