@@ -92,8 +92,14 @@ def causal_pairs(wl):
     return wl.batch * sum(first + j for j in range(wl.q_per_seq))
 
 
+def indexer_topk_bytes(wl, fp8):
+    """Score and top-k without a score buffer: the score's inputs + the indices written."""
+    return score_bytes(wl, fp8) + wl.n_q * 2048 * 4
+
+
 def launch_bytes(kind, wl, fp8):
     return {"indexer_score": lambda: score_bytes(wl, fp8), "topk": lambda: topk_bytes(wl),
+            "indexer_topk": lambda: indexer_topk_bytes(wl, fp8),
             "sparse_mla": lambda: mla_bytes(wl)}[kind]()
 
 
@@ -165,11 +171,12 @@ def build_inputs(wl, seed, dev, per_layer_dsa=False):
                 src=[ordinal[s] for s in src], layers=layers, fp8=fp8, rot=rot, q_src=q_src)
 
 
-def make_step(wl, inp, dev):
+def make_step(wl, inp, dev, score_buffer=True):
     """The measured unit as the sequence of library calls gsa_indexshare_group /
     gsa_layer_stack make (same kernels, order and stream): per group the full
-    layer's score and top-k, then one attention launch over the group's layers.
-    Events can be recorded between the calls. Returns (step, buffers, calls):
+    layer's score and top-k (score_buffer=False: one gsa_indexer_topk call, the
+    selection without a score buffer), then one attention launch over the
+    group's layers. Events can be recorded between the calls. Returns (step, buffers, calls):
     step(evs) records evs[i] before call i and evs[-1] after the last; calls is
     [(kind, algorithmic bytes)] per call."""
     ld = (wl.n_ctx + 3) // 4 * 4
@@ -194,6 +201,11 @@ def make_step(wl, inp, dev):
         return lambda: gsa.indexer_score(q, w, k, q_seq, q_pos, q_scale=qs, k_scale=ks,
                                          scores=bufs["scores"], group_max=bufs["gmax"])
 
+    def indexer_topk_call(j):
+        q, w, k, qs, ks = inp["indexers"][j]
+        return lambda: gsa.indexer_topk(q, w, k, q_seq, q_pos, q_scale=qs, k_scale=ks, idx=bufs["idx"][j],
+                                        workspace=bufs["ws"])
+
     def topk_call(j):
         return lambda: gsa.topk(bufs["scores"], q_pos, idx=bufs["idx"][j], workspace=bufs["ws"],
                                 group_max=bufs["gmax"])
@@ -212,8 +224,11 @@ def make_step(wl, inp, dev):
     for j, f in enumerate(inp["full_layers"]):
         if inp["rot"]:                          # rotate + quantise this step's indexer queries
             calls.append(("quantize_q", wl.n_q * 32 * (256 + 128 + 4), quant_call(j)))
-        calls.append(("indexer_score", launch_bytes("indexer_score", wl, fp8), score_call(j)))
-        calls.append(("topk", launch_bytes("topk", wl, fp8), topk_call(j)))
+        if score_buffer:
+            calls.append(("indexer_score", launch_bytes("indexer_score", wl, fp8), score_call(j)))
+            calls.append(("topk", launch_bytes("topk", wl, fp8), topk_call(j)))
+        else:
+            calls.append(("indexer_topk", launch_bytes("indexer_topk", wl, fp8), indexer_topk_call(j)))
         group = [l for l in range(n_att) if inp["src"][l] == j]
         if group:
             calls.append(("sparse_mla", launch_bytes("sparse_mla", wl, fp8) * len(group), mla_call(j, group)))
@@ -234,7 +249,7 @@ def run_bench(args):
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
     inp = build_inputs(wl, args.seed, dev, per_layer_dsa=args.per_layer_dsa)
-    step, bufs, calls = make_step(wl, inp, dev)
+    step, bufs, calls = make_step(wl, inp, dev, score_buffer=not args.no_score_buffer)
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
@@ -281,7 +296,8 @@ def run_bench(args):
                    "attention_layers": len(inp["layers"]), "indexer": wl.indexer_dtype,
                    "latent_cache": wl.kv_dtype,
                    "topk": 2048, "mla_heads": 64, "seed": args.seed,
-                   "schedule": "per-layer DSA" if args.per_layer_dsa else "IndexShare"},
+                   "schedule": "per-layer DSA" if args.per_layer_dsa else "IndexShare",
+                   "score_buffer": not args.no_score_buffer},
         "breakdown_ms_per_step": {k: round(v, 4) for k, v in ms_kind.items()},
         "avg_launch_us": {k: round(ms_kind[k] / launches[k] * 1e3, 2) for k in kinds},
         "achieved_GBs": {k: round(bytes_kind[k] / (ms_kind[k] / 1e3) / 1e9, 1) for k in kinds},
@@ -298,7 +314,7 @@ def roofline(kind, wl, fp8, nbytes, ms, launches):
     indexer score with thousands of queries per sequence)."""
     sec = ms / 1e3
     out = {"kernel": kind}
-    flops = score_flops(wl) * launches if kind == "indexer_score" else 0
+    flops = score_flops(wl) * launches if kind in ("indexer_score", "indexer_topk") else 0
     peak_tf = MFMA_PEAK_TFLOPS["fp8" if fp8 else "bf16"]
     if flops / (peak_tf * 1e12) > nbytes / (HBM_PEAK_GBS * 1e9):
         achieved = flops / sec / 1e12
@@ -424,6 +440,8 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true")
     ap.add_argument("--per-layer-dsa", action="store_true",
                     help="every layer full (own indexer + top-k): the schedule IndexShare replaces")
+    ap.add_argument("--no-score-buffer", action="store_true",
+                    help="score + top-k as one gsa_indexer_topk call (no [n_q, n_ctx] score buffer)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path is measured on a single MI355X); "
