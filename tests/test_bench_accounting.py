@@ -40,3 +40,13 @@ def test_roofline_bound_follows_arithmetic_intensity():
 def test_fp8_latent_bytes():
     wl = W.WORKLOADS["decode_b64_n131072_kv8"]
     assert bench.mla_bytes(wl) == 64 * (2048 * 656 + 2048 * 4 + 64 * 576 * 2 + 64 * 512 * 4)
+
+
+def test_score_and_topk_without_a_buffer():
+    # one gsa_indexer_topk call moves the score's inputs and writes the indices;
+    # at prefill its matrix work decides the bound as for the score alone
+    dec = W.WORKLOADS["decode_b8_n1048576_fp8"]
+    assert bench.launch_bytes("indexer_topk", dec, True) == bench.score_bytes(dec, True) + 8 * 2048 * 4
+    pre = W.WORKLOADS["prefill_q4096_n131072"]
+    r = bench.roofline("indexer_topk", pre, False, bench.launch_bytes("indexer_topk", pre, False), 6.0, 1)
+    assert r["bound"] == "mfma" and r["kernel"] == "indexer_topk"
