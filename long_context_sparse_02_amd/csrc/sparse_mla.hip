@@ -152,26 +152,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     const int r0 = split * rows_per_split;
     const int nrows = rows_per_split;
     const int seq = q_seq[q];
-    // Contiguous cache: the sequence's rows start at seq * n_cap. Paged cache
-    // (block_table != NULL): the layer's cache is a pool of page_size-row pages
-    // and position s of the sequence is row table[seq][s / page_size] *
-    // page_size + s % page_size of the pool; indices become pool rows here, once.
-    constexpr int RB = FP8KV ? kRowBytesF8 : kRowBytes;   // bytes per cache row
-    const uint8_t* kvs;
-    if (block_table == nullptr) {
-        kvs = kv + (int64_t)seq * n_cap * RB;
-        for (int i = tid; i < nrows; i += kThreads) rows_s[i] = idx[(int64_t)q * k + r0 + i];
-    } else {
-        kvs = kv;
-        const int32_t* bt = block_table + (int64_t)seq * max_pages;
-        for (int i = tid; i < nrows; i += kThreads) {
-            const int s = idx[(int64_t)q * k + r0 + i];
-            rows_s[i] = s < 0 ? -1 : bt[s / page_size] * page_size + s % page_size;
-        }
-    }
-
     // Q as the B operand: head 16*hg + l16, K-steps t = 9*hf .. 9*hf+8 of the
-    // 576 dims (dims 32t + 8g .. +8; steps 16 and 17 are the RoPE dims)
+    // 576 dims (dims 32t + 8g .. +8; steps 16 and 17 are the RoPE dims). Issued
+    // before the index loads, so that the two latencies overlap (the index
+    // stores to LDS wait for every earlier load); the fence keeps that order.
     const int head = 16 * hg + l16;
     bf16x8 qr[9];
     {
@@ -184,7 +168,39 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
                            : *(const bf16x8*)(qp + 2 * (32 * (t - 16) + 8 * g));
         }
     }
-    wait_vmcnt<0>();     // Q is in registers before any ring load is counted
+    asm volatile("" ::: "memory");
+    // Contiguous cache: the sequence's rows start at seq * n_cap. Paged cache
+    // (block_table != NULL): the layer's cache is a pool of page_size-row pages
+    // and position s of the sequence is row table[seq][s / page_size] *
+    // page_size + s % page_size of the pool; indices become pool rows here, once.
+    constexpr int RB = FP8KV ? kRowBytesF8 : kRowBytes;   // bytes per cache row
+    const uint8_t* kvs;
+    // (all of a thread's index loads, and then its block-table loads, are in
+    // flight together: a loop that stores each to LDS before the next load
+    // waits out one memory latency per row batch)
+    constexpr int kIdxPer = kMaxRows / kThreads;          // rows per thread at most
+    int32_t iv[kIdxPer];
+#pragma unroll
+    for (int u = 0; u < kIdxPer; ++u) {
+        const int i = tid + u * kThreads;
+        iv[u] = i < nrows ? idx[(int64_t)q * k + r0 + i] : -1;
+    }
+    if (block_table == nullptr) {
+        kvs = kv + (int64_t)seq * n_cap * RB;
+    } else {
+        kvs = kv;
+        const int32_t* bt = block_table + (int64_t)seq * max_pages;
+        int32_t pg[kIdxPer];
+#pragma unroll
+        for (int u = 0; u < kIdxPer; ++u) pg[u] = iv[u] < 0 ? 0 : bt[iv[u] / page_size];
+#pragma unroll
+        for (int u = 0; u < kIdxPer; ++u) iv[u] = iv[u] < 0 ? -1 : pg[u] * page_size + iv[u] % page_size;
+    }
+#pragma unroll
+    for (int u = 0; u < kIdxPer; ++u)
+        if (tid + u * kThreads < nrows) rows_s[tid + u * kThreads] = iv[u];
+
+    wait_vmcnt<0>();     // Q and the indices are in before any ring load is counted
     __syncthreads();
 
     // bf16: 16-byte LDS position s = 64*i + lane of a block holds row s / 73,
