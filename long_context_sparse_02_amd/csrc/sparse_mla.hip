@@ -414,17 +414,41 @@ __global__ __launch_bounds__(256) void sparse_mla_merge(LayerArgs L, int n_q,
     const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
     const int c = threadIdx.x & 63;              // float4 columns c and c + 64
     const float* pm = part_ml + ((int64_t)q * n_split * kHeads + h) * 2;
+    // Splits in batches of SB whose loads are all in flight together (a loop
+    // that uses each load before issuing the next waits out one memory
+    // latency per split); sums in split order as before.
+    constexpr int SB = 8;
     float mx = neg_inf();
-    for (int s = 0; s < n_split; ++s) mx = fmaxf(mx, pm[(int64_t)s * kHeads * 2]);
+    for (int s0 = 0; s0 < n_split; s0 += SB) {
+        float m[SB];
+#pragma unroll
+        for (int b = 0; b < SB; ++b) m[b] = s0 + b < n_split ? pm[(int64_t)(s0 + b) * kHeads * 2] : neg_inf();
+#pragma unroll
+        for (int b = 0; b < SB; ++b) mx = fmaxf(mx, m[b]);
+    }
     f32x4 a0 = {0.f, 0.f, 0.f, 0.f}, a1 = a0;
     float lsum = 0.f;
     if (mx != neg_inf()) {
-        for (int s = 0; s < n_split; ++s) {
-            const float wgt = exp2_(pm[(int64_t)s * kHeads * 2] - mx);
-            lsum += wgt * pm[(int64_t)s * kHeads * 2 + 1];
-            const f32x4* po = (const f32x4*)(part_o + (((int64_t)q * n_split + s) * kHeads + h) * kLat);
-            a0 += wgt * po[c];
-            a1 += wgt * po[c + 64];
+        for (int s0 = 0; s0 < n_split; s0 += SB) {
+            float m[SB], l[SB];
+            f32x4 x0[SB], x1[SB];
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {
+                const int s = min(s0 + b, n_split - 1);          // past the last split: not summed
+                m[b] = pm[(int64_t)s * kHeads * 2];
+                l[b] = pm[(int64_t)s * kHeads * 2 + 1];
+                const f32x4* po = (const f32x4*)(part_o + (((int64_t)q * n_split + s) * kHeads + h) * kLat);
+                x0[b] = po[c];
+                x1[b] = po[c + 64];
+            }
+#pragma unroll
+            for (int b = 0; b < SB; ++b) {                    // branch-free, so the loads stay batched
+                const bool ok = s0 + b < n_split;
+                const float wgt = exp2_(m[b] - mx);
+                lsum = ok ? lsum + wgt * l[b] : lsum;
+                a0 = ok ? a0 + wgt * x0[b] : a0;
+                a1 = ok ? a1 + wgt * x1[b] : a1;
+            }
         }
     }
     const float inv = lsum > 0.f ? 1.f / lsum : 0.f;
