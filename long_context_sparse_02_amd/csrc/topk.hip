@@ -657,6 +657,17 @@ __device__ __forceinline__ void merge_row(const uint8_t* __restrict__ lists, int
     int32_t* out = idx + (int64_t)q * kK;
     const uint8_t* in = lists + (size_t)q * n_lists * kListBytes;
     int nl = n_lists;
+    // The usual case, at most kSmall items in all: one gather (which sums the
+    // counts itself) and one selection, without a separate pass over the counts.
+    if (nl <= kThreads) {                                     // uniform
+        uint32_t v[kPerSmall], p[kPerSmall];
+        const int total = gather_lists<kPerSmall>(in, 0, nl, m, v, p);
+        if (total <= kSmall) {                                // uniform
+            auto em = [&](uint32_t slot, int, int r) { out[slot] = (int32_t)p[r]; };
+            write_final_pad(out, select_regs<kPerSmall, false>(v, m.sc, em));
+            return;
+        }
+    }
     // items of this row's lists (each count read once per list)
     uint32_t tot_local = 0;
     for (int l = threadIdx.x; l < nl; l += kThreads)
