@@ -476,12 +476,13 @@ def layer_pattern(n_layers=78):
 
 
 def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_stride=None,
-                scale=1.0 / 16.0, workspace=None, outs=None, block_table=None):
+                scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True):
     """The attention stack: indexers = [(q_idx, w, k_idx, q_scale, k_scale)] per full
     layer in layer order (scales None for bf16); layers = [(q_lat, q_rope, kv)] per
     layer. index_buf: int32 [n_full, n_q, k] (each full layer's indices kept) or
     [n_q, k] (one buffer reused). With block_table (int32 [batch, max_pages]) each
-    kv is a page pool [n_pages, page_size, 576]. Returns [(out, lse)] per layer."""
+    kv is a page pool [n_pages, page_size, 576]. score_buffer=False: every full
+    layer selects without a score buffer. Returns [(out, lse)] per layer."""
     L = lib()
     n_q = q_seq.shape[0]
     kv0 = layers[0][2]
@@ -503,9 +504,12 @@ def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_st
     if index_stride and index_buf.numel() < (n_full - 1) * index_stride + n_q * k:
         raise GsaError("index_buf is too small for one [n_q, k] buffer per full layer")
     fp8 = indexers[0][0].dtype == torch.uint8
-    if scores is None:
-        scores = torch.empty((n_q, (n_cap + 3) // 4 * 4), dtype=torch.float32, device=dev)
-    ld = scores.shape[1]
+    if not score_buffer:
+        scores, ld = None, (n_cap + 3) // 4 * 4
+    else:
+        if scores is None:
+            scores = torch.empty((n_q, (n_cap + 3) // 4 * 4), dtype=torch.float32, device=dev)
+        ld = scores.shape[1]
     if outs is None:
         outs = [(torch.empty((n_q, MLA_HEADS, LATENT_DIM), dtype=torch.float32, device=dev),
                  torch.empty((n_q, MLA_HEADS), dtype=torch.float32, device=dev)) for _ in layers]
@@ -522,7 +526,7 @@ def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_st
     d.n_layers, d.dt = len(layers), FP8_E4M3 if fp8 else BF16
     d.indexers = ctypes.cast(xs, ctypes.POINTER(_IndexerLayer))
     d.layers = ctypes.cast(arr, ctypes.POINTER(_MlaLayer))
-    d.scores_dev, d.ld_scores = scores.data_ptr(), ld
+    d.scores_dev, d.ld_scores = (None if scores is None else scores.data_ptr()), ld
     d.q_seq_dev, d.q_pos_dev = q_seq.data_ptr(), q_pos.data_ptr()
     d.n_q, d.batch, d.n_cap, d.k = n_q, batch, n_cap, k
     d.index_buf_dev, d.index_stride = index_buf.data_ptr(), index_stride

@@ -148,3 +148,22 @@ def test_group_without_score_buffer(dtype):
     for (o, s), (ob, sb), (wo, ws) in zip(outs_f, outs_b, oouts):
         assert np.array_equal(np32(o), np32(ob))
         assert float(np.max(np.abs(np32(o) - wo))) <= 1e-2
+
+
+@pytest.mark.parametrize("name", ["decode_b8_n1048576_fp8", "prefill_q4096_n131072_fp8", "decode_b64_n131072"])
+def test_indexer_topk_full_size_identical_to_buffered(name):
+    # the measured workloads at full size, from bench.py's own inputs: every
+    # row's indices without a score buffer equal the buffered path's
+    import bench
+    wl = W.WORKLOADS[name]
+    d = dev()
+    inp = bench.build_inputs(wl, 0, d)
+    q, w, k, qs, ks = inp["indexers"][0]
+    fused = gsa.indexer_topk(q, w, k, inp["q_seq"], inp["q_pos"], q_scale=qs, k_scale=ks)
+    ld = (wl.n_ctx + 3) // 4 * 4
+    gm = torch.empty((wl.n_q, gsa.group_max_ld(ld)), dtype=torch.float32, device=d)
+    s = gsa.indexer_score(q, w, k, inp["q_seq"], inp["q_pos"], q_scale=qs, k_scale=ks, group_max=gm)
+    buffered = gsa.topk(s, inp["q_pos"], group_max=gm)
+    torch.cuda.synchronize()
+    assert torch.equal(fused, buffered)
+    say(f"indexer_topk {name}: {wl.n_q} full-size rows identical to the buffered path")

@@ -24,7 +24,7 @@ def _stack_inputs(wl, seed, n_layers):
     return fulls, q_seq, q_pos, idx_in, mla_in
 
 
-def _run_stack(wl, seed, n_layers, dtype="bf16", index_stride=None):
+def _run_stack(wl, seed, n_layers, dtype="bf16", index_stride=None, score_buffer=True):
     fulls, q_seq, q_pos, idx_in, mla_in = _stack_inputs(wl, seed, n_layers)
     d = dev()
     indexers = []
@@ -43,7 +43,7 @@ def _run_stack(wl, seed, n_layers, dtype="bf16", index_stride=None):
     say(f"stack: {n_layers} layers ({len(fulls)} full), {dtype}, n_q={wl.n_q}, N={wl.n_ctx}, "
         f"index_stride={'0' if index_stride == 0 else 'n_q*k'}")
     outs = gsa.layer_stack(indexers, layers, q_seq.to(d), q_pos.to(d), index_buf,
-                           index_stride=index_stride)
+                           index_stride=index_stride, score_buffer=score_buffer)
     torch.cuda.synchronize()
     return fulls, q_seq, q_pos, idx_in, mla_in, index_buf, outs
 
@@ -82,3 +82,16 @@ def test_stack_fp8_indexer_matches_bf16_oracle():
     wl = W.WORKLOADS["group_b1_n4096_q4"]
     res = _run_stack(wl, 5, 7, dtype="fp8")
     _check_against_oracle(7, *res)
+
+
+def test_stack_without_score_buffer_matches_buffered():
+    # every full layer selecting without a score buffer: the same indices and
+    # outputs as the buffered stack, and the oracle's
+    wl = W.Workload("stack_nobuf", 2, 66_001, 2, 11, "bf16")
+    *_, buf_b, outs_b = _run_stack(wl, 6, 11)
+    res = _run_stack(wl, 6, 11, score_buffer=False)
+    buf_f, outs_f = res[-2], res[-1]
+    assert torch.equal(buf_f, buf_b)
+    for (ob, sb), (of, sf) in zip(outs_b, outs_f):
+        assert torch.equal(ob, of) and torch.equal(sb, sf)
+    _check_against_oracle(11, *res)
