@@ -406,28 +406,32 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__
     __shared__ Scratch sc;
     const int q = blockIdx.y, c = blockIdx.x;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int64_t len = row_len(q_pos, q, ld);
     const int64_t s0 = (int64_t)c * kChunk;
-    const int n = (int)max((int64_t)0, min(s0 + kChunk, len) - s0);
-    const uint32_t L = bound != nullptr ? uni(bound[q]) : 0u;
     const float* row = scores + (int64_t)q * ld + s0;
     // lane holds items kSeg*wave + 64r + lane: each wave load reads 256 contiguous bytes.
     // Loads are unconditional (clamped address) so all 32 are in flight together; a
     // branch around each would make the compiler wait for each one at the join.
     // Each score is read once: non-temporal loads (prefill top-k 1.7-3.4% faster).
+    // The clamp keeps the loads inside the row (ld), not inside the causal length,
+    // and no branch depends on it, so they do not wait for q_pos: positions past
+    // the length (a whole chunk, for short rows) are masked below.
     uint32_t v[kPer];                                         // 0: not a candidate
-    if (n > 0) {
+    int n;
+    uint32_t L;
+    {
+        const int lim = (int)min((int64_t)kChunk, ld - s0) - 1;
         float x[kPer];
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) x[r] = __builtin_nontemporal_load(row + min(kSeg * wave + 64 * r + lane, n - 1));
+        for (int r = 0; r < kPer; ++r) x[r] = __builtin_nontemporal_load(row + min(kSeg * wave + 64 * r + lane, lim));
+        asm volatile("" ::: "memory");                        // the row's length and bound are read after
+        const int64_t len = row_len(q_pos, q, ld);
+        n = (int)max((int64_t)0, min(s0 + kChunk, len) - s0);
+        L = bound != nullptr ? uni(bound[q]) : 0u;
 #pragma unroll
         for (int r = 0; r < kPer; ++r) {
             const uint32_t key = score_key(x[r]);
             v[r] = (kSeg * wave + 64 * r + lane < n && key >= L) ? key : 0u;
         }
-    } else {
-#pragma unroll
-        for (int r = 0; r < kPer; ++r) v[r] = 0u;
     }
     const bool full = n == kMaxItems && L == 0u;                // uniform
     if (n_chunks == 1) {
