@@ -387,6 +387,11 @@ __global__ __launch_bounds__(kThreads) void topk_bound(const float* __restrict__
         load(j, x0); load(j + 1, x1); load(j + 2, x2); load(j + 3, x3);
         take(j, x0); take(j + 1, x1); take(j + 2, x2); take(j + 3, x3);
     }
+    for (; j + 2 <= rg; j += 2) {                            // 2-round rows: one latency
+        float x0[kPerSmall], x1[kPerSmall];
+        load(j, x0); load(j + 1, x1);
+        take(j, x0); take(j + 1, x1);
+    }
     for (; j < rg; ++j) {
         float x0[kPerSmall];
         load(j, x0);
