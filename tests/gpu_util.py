@@ -38,5 +38,6 @@ def max_abs(a, b):
     a = np.asarray(a, np.float64)
     b = np.asarray(b, np.float64)
     both_inf = np.isinf(a) & np.isinf(b) & (np.sign(a) == np.sign(b))
-    d = np.where(both_inf, 0.0, np.abs(a - b))
+    with np.errstate(invalid="ignore"):                  # inf - inf where both_inf masks it
+        d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.max(d)) if d.size else 0.0
