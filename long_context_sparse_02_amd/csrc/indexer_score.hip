@@ -37,6 +37,7 @@ constexpr int kDim = 128;
 constexpr int kTile = 128;      // keys per LDS tile
 constexpr int kThreads = 256;   // 4 waves
 constexpr int kRing = 4;        // LDS tile slots
+constexpr int kStageKeys = 4096;  // longest chunk whose scores a one-query bf16 work-group keeps in LDS
 
 // Score stores of the streaming loops. The fp8 kernels write twice the score
 // bytes per key byte of the bf16 ones, and there the non-temporal hint measured
@@ -68,7 +69,7 @@ struct KeyTile {
 
 // NTK: the keys are read by this work-group only (one query block per
 // sequence), so they stream with the non-temporal hint.
-template <int QB, bool FP8, bool NTK>
+template <int QB, bool FP8, bool NTK, bool STAGE = false>
 __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
     const float* __restrict__ w, const uint8_t* __restrict__ k,
@@ -87,6 +88,13 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
     __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * T::kSlot];
+    // STAGE: the chunk's scores and group maxima collect in LDS (16.5 KiB beside
+    // the 128 KiB ring) and leave in one burst when the chunk ends, so that no
+    // global store is issued between the ring's DMAs (64 x 128K bf16 keys:
+    // 361-363 against 370 us)
+    static_assert(!STAGE || (QB == 1 && !FP8), "staged scores: one bf16 query per work-group");
+    __shared__ __attribute__((aligned(16))) float stage_sc[STAGE ? kStageKeys : 1];
+    __shared__ float stage_gm[STAGE ? kStageKeys / 32 : 1];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -159,7 +167,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
 #pragma unroll
         for (int p = 0; p < PPW; ++p) {
             const int j = (wave * PPW + p) / NSUBT;
-            stores += (j >= j0 && j < j1 && scores != nullptr) ? 1 : 0;
+            stores += (j >= j0 && j < j1 && scores != nullptr && !STAGE) ? 1 : 0;
         }
 
         auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
@@ -233,14 +241,39 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
                     res = (s <= apos[jj]) ? part : neg_inf();
                 }
                 if (scores != nullptr && g == 0 && s < c1)   // uniform pointer test
-                    store_score<FP8>(scores + (int64_t)(qb0 + j) * ld + s, res);
+                {
+                    if constexpr (STAGE) stage_sc[s - c0] = res;
+                    else store_score<FP8>(scores + (int64_t)(qb0 + j) * ld + s, res);
+                }
                 if (gmax != nullptr && s0 < c1) {                       // uniform
                     const uint32_t m = max_x32(score_key(s < c1 ? res : neg_inf()));
-                    if (lane == 0) gmax[(int64_t)(qb0 + j) * ldg + (s0 >> 5)] = key_value(m);
+                    if (lane == 0) {
+                        if constexpr (STAGE) stage_gm[(s0 - c0) >> 5] = key_value(m);
+                        else gmax[(int64_t)(qb0 + j) * ldg + (s0 >> 5)] = key_value(m);
+                    }
                 }
             }
         }
         ring_barrier();     // the next run refills slots this run's last tiles were read from
+        if constexpr (STAGE) {
+            // every position of [c0, c1) and every group there was written above
+            // (the masked ones as -inf); the launcher keeps c1 - c0 <= kStageKeys
+            __syncthreads();                             // the LDS writes of all waves are visible
+            const int len = (int)(c1 - c0);
+            if (scores != nullptr) {
+                float* dst = scores + (int64_t)qb0 * ld + c0;
+                if ((((uintptr_t)dst) & 15) == 0 && (len & 3) == 0) {
+                    for (int i = 4 * tid; i < len; i += 4 * kThreads)
+                        *(float4*)(dst + i) = *(const float4*)(stage_sc + i);
+                } else {
+                    for (int i = tid; i < len; i += kThreads) dst[i] = stage_sc[i];
+                }
+            }
+            if (gmax != nullptr) {
+                float* gd = gmax + (int64_t)qb0 * ldg + (c0 >> 5);
+                for (int i = tid; i < (len + 31) / 32; i += kThreads) gd[i] = stage_gm[i];
+            }
+        }
         j0 = j1;
     }
 }
@@ -665,11 +698,11 @@ hipError_t launch_mq(bool fp8, dim3 grid, hipStream_t st, const void* q, const f
     return hipGetLastError();
 }
 
-template <int QB, bool FP8, bool NT>
+template <int QB, bool FP8, bool NT, bool STAGE = false>
 void launch_qb_t(dim3 grid, hipStream_t st, const void* q, const float* qs, const float* w,
                  const void* k, const float* ks, const int32_t* q_seq, const int32_t* q_pos,
                  int n_q, int64_t n_cap, float* scores, int64_t ld, float* gmax, int chunk) {
-    hipLaunchKernelGGL((indexer_score_kernel<QB, FP8, NT>), grid, dim3(kThreads), 0, st, (const uint8_t*)q, qs, w,
+    hipLaunchKernelGGL((indexer_score_kernel<QB, FP8, NT, STAGE>), grid, dim3(kThreads), 0, st, (const uint8_t*)q, qs, w,
                        (const uint8_t*)k, ks, q_seq, q_pos, n_q, n_cap, scores, ld, gmax,
                        (ld + 31) / 32, chunk);
 }
@@ -679,6 +712,13 @@ hipError_t launch_qb(bool fp8, bool nt, dim3 grid, hipStream_t st, const void* q
                      const float* w, const void* k, const float* ks, const int32_t* q_seq,
                      const int32_t* q_pos, int n_q, int64_t n_cap, float* scores, int64_t ld,
                      float* gmax, int chunk) {
+    if constexpr (QB == 1) {
+        if (!fp8 && chunk <= kStageKeys) {                  // the chunk's scores fit in LDS
+            auto* g = nt ? launch_qb_t<1, false, true, true> : launch_qb_t<1, false, false, true>;
+            g(grid, st, q, qs, w, k, ks, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, chunk);
+            return hipGetLastError();
+        }
+    }
     auto* f = fp8 ? (nt ? launch_qb_t<QB, true, true> : launch_qb_t<QB, true, false>)
                   : (nt ? launch_qb_t<QB, false, true> : launch_qb_t<QB, false, false>);
     f(grid, st, q, qs, w, k, ks, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, chunk);
