@@ -124,6 +124,44 @@ def test_score_unsorted_sequences_and_positions(n_per):
     del perm
 
 
+def test_score_one_query_rows_past_the_query():
+    # one query per sequence at positions that leave partial tiles, whole tiles
+    # and whole chunks after it: the one-query kernel writes those positions as
+    # -inf (bf16 chunks this short collect the row in LDS and write it at the
+    # chunk end; fp8 stores as it goes); full rows and group maxima bit-exact
+    n_cap = 9000
+    pos = [37, 1023, 1024, 5000, 8191, n_cap - 1]
+    wl = W.Workload("past_query", len(pos), n_cap, 1, 1, "bf16")
+    q, w = W.indexer_queries(wl, 61, 0)
+    k = W.indexer_keys(wl, 61, 0)
+    q_seq = torch.arange(len(pos), dtype=torch.int32)
+    q_pos = torch.tensor(pos, dtype=torch.int32)
+    want = oracle.indexer_score(np32(q), np32(w), np32(k), np32(q_seq), np32(q_pos))
+    gm_want = oracle.group_max(want, n_cols=n_cap)
+    d = dev()
+    ld = (n_cap + 3) // 4 * 4 + 4
+    for dtype in ("bf16", "fp8"):
+        say(f"one-query rows past the query: {dtype}, positions {pos}")
+        scores = torch.full((len(pos), ld), 12345.0, device=d)
+        gmax = torch.full((len(pos), gsa.group_max_ld(ld)), 777.0, device=d)
+        if dtype == "fp8":
+            qc, qs = gsa.quantize_e4m3(q.to(d))
+            kc, ks = gsa.quantize_e4m3(k.to(d))
+            gsa.indexer_score(qc, w.to(d), kc, q_seq.to(d), q_pos.to(d), q_scale=qs, k_scale=ks,
+                              scores=scores, group_max=gmax)
+        else:
+            gsa.indexer_score(q.to(d), w.to(d), k.to(d), q_seq.to(d), q_pos.to(d), scores=scores,
+                              group_max=gmax)
+        torch.cuda.synchronize()
+        got, gm = np32(scores), np32(gmax)
+        ng = -(-n_cap // 32)
+        for i, p in enumerate(pos):
+            assert_scores_equal(got[i, :n_cap], want[i], f"{dtype} query at {p}")
+            assert np.all(np.isneginf(got[i, p + 1:n_cap])), f"{dtype} query at {p}: past positions"
+            assert_scores_equal(gm[i, :ng], gm_want[i], f"{dtype} query at {p} group maxima")
+        assert np.all(got[:, n_cap:] == 12345.0) and np.all(gm[:, ng:] == 777.0)
+
+
 def test_score_negative_weights_and_float_inputs():
     g = torch.Generator().manual_seed(9)
     q = (torch.randn((6, 32, 128), generator=g)).to(torch.bfloat16)
