@@ -629,17 +629,20 @@ __device__ __forceinline__ int gather_lists(const uint8_t* lists0, int l0, int n
 #pragma unroll
     for (int r = 0; r < PER; ++r) { v[r] = 0u; p[r] = 0u; }
     if ((uint32_t)(SEG * wave) < total) {                    // uniform: this wave holds items
+        // li[r]: the largest l with base[l] <= item r's index; the PER searches
+        // advance together, so each step issues PER independent LDS reads
         uint32_t li[PER];
 #pragma unroll
-        for (int r = 0; r < PER; ++r) {
-            const uint32_t i = min((uint32_t)(SEG * wave + 64 * r + lane), total - 1);
-            uint32_t lo = 0, span = 1u << steps;              // largest l with base[l] <= i
-            for (int t = 0; t < steps; ++t) {
-                span >>= 1;
-                const uint32_t mid = lo + span;
-                if (mid < (uint32_t)nl && m.base[min(mid, (uint32_t)nl)] <= i) lo = mid;
+        for (int r = 0; r < PER; ++r) li[r] = 0;
+        uint32_t span = 1u << steps;
+        for (int t = 0; t < steps; ++t) {
+            span >>= 1;
+#pragma unroll
+            for (int r = 0; r < PER; ++r) {
+                const uint32_t i = min((uint32_t)(SEG * wave + 64 * r + lane), total - 1);
+                const uint32_t mid = li[r] + span;
+                if (mid < (uint32_t)nl && m.base[min(mid, (uint32_t)nl)] <= i) li[r] = mid;
             }
-            li[r] = lo;
         }
         uint2 it[PER];
 #pragma unroll
