@@ -16,6 +16,7 @@ import pytest
 import torch
 
 import bench
+import long_context_sparse_02_amd as gsa
 import oracle
 import workloads as W
 from gpu_util import ATOL_LSE, ATOL_OUT, assert_scores_equal, dev, max_abs, np32, say
@@ -155,3 +156,37 @@ def test_prefill_rotated_fp8_full_size():
         have = set(np32(bufs["idx"][0, qi])) - {-1}
         assert len(want & have) >= 0.995 * len(want)
         say(f"{wl.name}: query {qi} tracks the oracle ({len(want & have)} of {len(want)} shared)")
+
+
+def test_decode_full_chunks_with_queries_inside_the_row():
+    # 64 x 128K bf16 keys with one query per sequence: the launch takes 4096-key
+    # chunks, which the one-query kernel collects whole in LDS before writing.
+    # The queries sit inside their rows (at 0, at tile and chunk edges, in the
+    # middle, at the end), so whole chunks and parts of chunks lie past them.
+    wl = W.WORKLOADS["decode_b64_n131072"]
+    d = dev()
+    k = W.indexer_keys(wl, SEED, 0, device=d)
+    q, w = W.indexer_queries(wl, SEED, 0, device=d)
+    g = torch.Generator().manual_seed(5)
+    pos = torch.randint(0, wl.n_ctx, (wl.n_q,), generator=g, dtype=torch.int32)
+    special = [0, 1, 127, 128, 4095, 4096, 4097, 8191, 65535, wl.n_ctx - 1]
+    pos[:len(special)] = torch.tensor(special, dtype=torch.int32)
+    q_seq = torch.arange(wl.n_q, dtype=torch.int32, device=d)
+    q_pos = pos.to(d)
+    say(f"full chunks, queries inside the row: n_q={wl.n_q}, N={wl.n_ctx}, positions {special} and random")
+    ld = wl.n_ctx
+    scores = torch.full((wl.n_q, ld), 12345.0, device=d)
+    gmax = torch.full((wl.n_q, gsa.group_max_ld(ld)), 777.0, device=d)
+    gsa.indexer_score(q, w, k, q_seq, q_pos, scores=scores, group_max=gmax)
+    torch.cuda.synchronize()
+    # every row: -inf exactly past its position, finite up to it (scores >= 0 here)
+    past = torch.arange(ld, device=d)[None, :] > q_pos[:, None].long()
+    assert bool(torch.isneginf(scores[past]).all()), "a position past its query is not -inf"
+    assert bool(torch.isfinite(scores[~past]).all()), "a causal position is not finite"
+    for i in [0, 2, 3, 4, 5, 6, 8, 9, 33]:
+        p = int(pos[i])
+        row = oracle.indexer_score(np32(q[i:i + 1]), np32(w[i:i + 1]), np32(k[i:i + 1]),
+                                   np.zeros(1, np.int32), np.array([p], np.int32))
+        assert_scores_equal(np32(scores[i]), row[0], f"query {i} at {p}")
+        assert_scores_equal(np32(gmax[i]), oracle.group_max(row, n_cols=ld)[0], f"query {i} at {p}: group maxima")
+    say("full chunks, queries inside the row: sampled rows match the oracle")
