@@ -41,7 +41,9 @@ typedef enum gsa_status {
     GSA_ERR_INVALID_ARG = 1,   /* null pointer, bad size, misalignment, ... */
     GSA_ERR_UNSUPPORTED = 2,   /* valid but not implemented (e.g. k != 2048) */
     GSA_ERR_WORKSPACE = 3,     /* workspace missing or too small */
-    GSA_ERR_HIP = 4            /* a HIP launch failed */
+    GSA_ERR_HIP = 4,           /* a HIP launch failed */
+    GSA_ERR_STALE_INDEX = 5    /* a shared-only group call's index buffer was not written for the
+                                  epoch, full layer and shape the call names (gsa_index_tag) */
 } gsa_status;
 
 typedef enum gsa_dtype {
@@ -196,7 +198,8 @@ gsa_status gsa_indexer_topk(gsa_dtype dt,
  * space; [Serving] §10: each layer gathers the selected entries of its own
  * K/V cache, then sparse attention).
  *
- * For query i, head h, selected rows s_j = idx[i, j] (entries < 0 skipped):
+ * For query i, head h, selected rows s_j = idx[i, j] (entries outside [0, n_cap)
+ * skipped, -1 in particular):
  *   z_j = scale * (q_lat[i,h,:] . c[s_j] + q_rope[i,h,:] . kr[s_j])
  *   out[i,h,:] = sum_j softmax(z)_j * c[s_j];  lse[i,h] = log sum_j exp(z_j)
  * (c = kv[..., :512], kr = kv[..., 512:]). A row with no valid index gives
@@ -204,8 +207,10 @@ gsa_status gsa_indexer_topk(gsa_dtype dt,
  *
  * q_lat_dev  bf16 [n_q, n_heads, 512]; q_rope_dev bf16 [n_q, n_heads, 64].
  * kv_dev     bf16 [batch, n_cap, 576] (packed 1152-byte rows).
- * q_seq_dev  int32 [n_q] in [0, batch). idx_dev int32 [n_q, k], each
- *            entry -1 or in [0, n_cap).
+ * q_seq_dev  int32 [n_q] in [0, batch). idx_dev int32 [n_q, k]: positions in
+ *            [0, n_cap); -1 pads, and any entry outside that range is skipped the
+ *            same way (an unsigned compare in the gather), so a stale or foreign
+ *            buffer cannot make the gather read outside the sequence's rows.
  * n_heads    must be 64. k must be 2048.
  * out_dev    fp32 [n_q, n_heads, 512]; lse_dev fp32 [n_q, n_heads] or NULL.
  * workspace_dev: at least gsa_mla_workspace_bytes(n_q, n_heads, k) bytes.
@@ -293,6 +298,32 @@ gsa_status gsa_sparse_mla_attn_fp8kv(const gsa_mla_layer* layers, int n_layers,
                                      int64_t n_cap, float scale, void* workspace_dev,
                                      size_t workspace_bytes, void* stream);
 
+/*
+ * gsa_index_tag — what an index buffer holds, kept by the caller on the host next
+ * to the buffer ([Serving] §10: a reused index cache is valid only for the prefix,
+ * positions and model revision it was computed for; [Arch] §2.4: shared layers and
+ * MTP steps read the buffer a full layer wrote). The library cannot read device
+ * memory to check a buffer, so the check is on this host record:
+ *   - a group call with compute_index = 1 and index_tag != NULL fills the record
+ *     in once its launches are enqueued (the buffer holds those indices when the
+ *     stream reaches them);
+ *   - a group call with compute_index = 0 and index_epoch != 0 compares the
+ *     record with its own description and returns GSA_ERR_STALE_INDEX, enqueuing
+ *     nothing, unless the buffer, epoch, full layer, n_q and k are equal and the
+ *     record's n_cap is at most the call's (every stored position is then inside
+ *     the call's caches).
+ * epoch is the caller's name for the prefix, positions and revision (any value
+ * but 0; 0 marks a record that describes nothing).
+ */
+typedef struct gsa_index_tag {
+    const int32_t* index_buf_dev;  /* the buffer the record describes */
+    uint64_t epoch;                /* the epoch of the call that wrote it; 0: nothing written */
+    int full_layer;                /* the full layer whose indexer wrote it */
+    int n_q;                       /* rows written */
+    int k;                         /* indices per row */
+    int64_t n_cap;                 /* positions of the writing call's caches */
+} gsa_index_tag;
+
 typedef struct gsa_group_desc {
     int compute_index;
     gsa_dtype dt;
@@ -310,6 +341,14 @@ typedef struct gsa_group_desc {
                                        indexer keys and scores (max_pages * page_size >= n_cap) */
     gsa_dtype kv_dt;                 /* GSA_BF16 (0): 1152-byte bf16 rows; GSA_FP8_E4M3: 656-byte
                                        FP8 latent rows (gsa_sparse_mla_attn_fp8kv) */
+    uint64_t index_epoch;            /* the caller's epoch of this call (gsa_index_tag); 0: the
+                                       buffer is not checked and a written record gets epoch 0 */
+    int index_layer;                 /* the full layer whose indices index_buf_dev holds: the
+                                       one this call's indexer is (compute_index = 1), or the
+                                       one whose buffer it reuses (compute_index = 0) */
+    gsa_index_tag* index_tag;        /* host record of index_buf_dev, or NULL: written when
+                                       compute_index = 1, checked when 0 (NULL with a non-zero
+                                       index_epoch is GSA_ERR_INVALID_ARG) */
 } gsa_group_desc;
 
 /* workspace of a group with n_layers attention layers (the full layer included) */
@@ -335,7 +374,8 @@ size_t gsa_mla_layers_workspace_bytes(int n_q, int n_heads, int k, int n_layers)
 /*
  * gsa_sparse_mla_attn_paged — gsa_sparse_mla_attn_layers over paged caches
  * (gsa_paged_kv above): each layers[l].kv_dev is that layer's page pool.
- * Indices are sequence positions, < max_pages * page_size. Same workspace as
+ * Indices are sequence positions; entries outside [0, max_pages * page_size) are
+ * skipped as -1 is. Same workspace as
  * gsa_sparse_mla_attn_layers; errors as there, plus GSA_ERR_INVALID_ARG for a
  * NULL or malformed paged_kv.
  */
@@ -401,6 +441,12 @@ typedef struct gsa_stack_desc {
     void* workspace_dev; size_t workspace_bytes;
     const gsa_paged_kv* paged_kv;   /* as in gsa_group_desc */
     gsa_dtype kv_dt;                 /* as in gsa_group_desc */
+    uint64_t index_epoch;            /* as in gsa_group_desc */
+    gsa_index_tag* index_tags;       /* NULL, or one host record per full layer (ordinal f):
+                                       record f describes full layer f's buffer once its group
+                                       is enqueued; a record whose buffer a later group of the
+                                       same call overwrites (index_stride = 0) is reset to
+                                       epoch 0 */
 } gsa_stack_desc;
 
 size_t gsa_stack_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads, int n_layers);

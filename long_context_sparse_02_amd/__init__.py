@@ -42,6 +42,15 @@ class _PagedKV(ctypes.Structure):
                 ("max_pages", ctypes.c_int), ("n_pages", ctypes.c_int64)]
 
 
+class IndexTag(ctypes.Structure):
+    """Host record of what an index buffer holds (gsa_index_tag): written by a
+    group call that computes the indices, checked by a shared-only call that
+    names a non-zero epoch (GsaError with GSA_ERR_STALE_INDEX on a mismatch)."""
+    _fields_ = [("index_buf_dev", ctypes.c_void_p), ("epoch", ctypes.c_uint64),
+                ("full_layer", ctypes.c_int), ("n_q", ctypes.c_int), ("k", ctypes.c_int),
+                ("n_cap", ctypes.c_int64)]
+
+
 class _GroupDesc(ctypes.Structure):
     _fields_ = [("compute_index", ctypes.c_int), ("dt", ctypes.c_int),
                 ("q_idx_dev", ctypes.c_void_p), ("q_scale_dev", ctypes.c_void_p),
@@ -53,7 +62,9 @@ class _GroupDesc(ctypes.Structure):
                 ("n_layers", ctypes.c_int), ("layers", ctypes.POINTER(_MlaLayer)),
                 ("n_heads", ctypes.c_int), ("scale", ctypes.c_float),
                 ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("paged_kv", ctypes.POINTER(_PagedKV)), ("kv_dt", ctypes.c_int)]
+                ("paged_kv", ctypes.POINTER(_PagedKV)), ("kv_dt", ctypes.c_int),
+                ("index_epoch", ctypes.c_uint64), ("index_layer", ctypes.c_int),
+                ("index_tag", ctypes.POINTER(IndexTag))]
 
 
 class _IndexerLayer(ctypes.Structure):
@@ -71,7 +82,8 @@ class _StackDesc(ctypes.Structure):
                 ("k", ctypes.c_int), ("index_buf_dev", ctypes.c_void_p),
                 ("index_stride", ctypes.c_int64), ("n_heads", ctypes.c_int), ("scale", ctypes.c_float),
                 ("workspace_dev", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t),
-                ("paged_kv", ctypes.POINTER(_PagedKV)), ("kv_dt", ctypes.c_int)]
+                ("paged_kv", ctypes.POINTER(_PagedKV)), ("kv_dt", ctypes.c_int),
+                ("index_epoch", ctypes.c_uint64), ("index_tags", ctypes.POINTER(IndexTag))]
 
 
 def _declare(lib):
@@ -407,12 +419,16 @@ def sparse_mla_attn_layers(layers, q_seq, idx, scale=1.0 / 16.0, outs=None, work
 
 def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_idx=None,
                      q_scale=None, k_scale=None, scores=None, compute_index=True,
-                     scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True):
+                     scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True,
+                     index_epoch=0, index_layer=0, index_tag=None):
     """One IndexShare group: layers = [(q_lat, q_rope, kv), ...], F layer first.
     With compute_index the F layer's indexer + top-k write index_buf, then every
     layer attends over it. With block_table (int32 [batch, max_pages]) each kv is
     a page pool [n_pages, page_size, 576]. score_buffer=False selects without a
-    score buffer (as indexer_topk). Returns [(out, lse)] per layer."""
+    score buffer (as indexer_topk). index_tag (an IndexTag) records what
+    index_buf holds: filled in when compute_index, checked against
+    (index_epoch, index_layer, shape) when not and index_epoch != 0.
+    Returns [(out, lse)] per layer."""
     L = lib()
     n_q = q_seq.shape[0]
     kv0 = layers[0][2]
@@ -462,6 +478,9 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     if pg is not None:
         d.paged_kv = ctypes.pointer(pg)
     d.kv_dt = FP8_E4M3 if _kv_fp8(kv0) else BF16
+    d.index_epoch, d.index_layer = index_epoch, index_layer
+    if index_tag is not None:
+        d.index_tag = ctypes.pointer(index_tag)
     _check(L.gsa_indexshare_group(ctypes.byref(d), _stream(dev)))
     return outs
 
@@ -476,13 +495,16 @@ def layer_pattern(n_layers=78):
 
 
 def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_stride=None,
-                scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True):
+                scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True,
+                index_epoch=0, index_tags=None):
     """The attention stack: indexers = [(q_idx, w, k_idx, q_scale, k_scale)] per full
     layer in layer order (scales None for bf16); layers = [(q_lat, q_rope, kv)] per
     layer. index_buf: int32 [n_full, n_q, k] (each full layer's indices kept) or
     [n_q, k] (one buffer reused). With block_table (int32 [batch, max_pages]) each
     kv is a page pool [n_pages, page_size, 576]. score_buffer=False: every full
-    layer selects without a score buffer. Returns [(out, lse)] per layer."""
+    layer selects without a score buffer. index_tags: None, or a ctypes array of
+    one IndexTag per full layer that the call fills in (see indexshare_group).
+    Returns [(out, lse)] per layer."""
     L = lib()
     n_q = q_seq.shape[0]
     kv0 = layers[0][2]
@@ -535,5 +557,10 @@ def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_st
     if pg is not None:
         d.paged_kv = ctypes.pointer(pg)
     d.kv_dt = FP8_E4M3 if _kv_fp8(kv0) else BF16
+    d.index_epoch = index_epoch
+    if index_tags is not None:
+        if len(index_tags) != n_full:
+            raise GsaError(f"index_tags must hold {n_full} records, got {len(index_tags)}")
+        d.index_tags = ctypes.cast(index_tags, ctypes.POINTER(IndexTag))
     _check(L.gsa_layer_stack(ctypes.byref(d), _stream(dev)))
     return outs

@@ -98,7 +98,7 @@ gsa_status check_mla(const void* q_lat, const void* q_rope, const void* kv, cons
     REQUIRE(n_q >= 1, "n_q must be >= 1 (got %d)", n_q);
     if (n_q > kMaxGridY) return fail(GSA_ERR_UNSUPPORTED, "n_q must be <= %d (got %d)", kMaxGridY, n_q);
     REQUIRE(batch >= 1, "batch must be >= 1 (got %d)", batch);
-    REQUIRE(n_cap >= 1, "n_cap must be >= 1");
+    REQUIRE(n_cap >= 1 && n_cap <= 0x7fffffff, "n_cap must be in [1, 2^31-1] (got %lld)", (long long)n_cap);
     if (n_heads != 64) return fail(GSA_ERR_UNSUPPORTED, "n_heads must be 64 (got %d)", n_heads);
     if (k != GSA_TOPK) return fail(GSA_ERR_UNSUPPORTED, "k must be %d (got %d)", GSA_TOPK, k);
     REQUIRE(scale > 0.f && scale < 1e30f, "scale must be positive and finite");
@@ -154,13 +154,14 @@ const char* gsa_status_string(gsa_status s) {
         case GSA_ERR_UNSUPPORTED: return "GSA_ERR_UNSUPPORTED";
         case GSA_ERR_WORKSPACE: return "GSA_ERR_WORKSPACE";
         case GSA_ERR_HIP: return "GSA_ERR_HIP";
+        case GSA_ERR_STALE_INDEX: return "GSA_ERR_STALE_INDEX";
     }
     return "GSA_ERR_UNKNOWN";
 }
 
 const char* gsa_last_error(void) { return g_err; }
 
-const char* gsa_version(void) { return "gsa 0.1 gfx950"; }
+const char* gsa_version(void) { return "gsa 0.2 gfx950"; }
 
 gsa_status gsa_quantize_e4m3(const void* x, int64_t n_blocks, uint8_t* codes, float* scales,
                              void* stream) {
@@ -355,6 +356,20 @@ gsa_status validate_group(const gsa_group_desc* d) {
         REQUIRE(n_cap_pg >= d->n_cap, "paged_kv holds %lld positions per sequence, fewer than n_cap %lld",
                 (long long)n_cap_pg, (long long)d->n_cap);
     }
+    REQUIRE(d->index_epoch == 0 || d->index_tag != nullptr, "index_epoch is set but index_tag is NULL");
+    if (!d->compute_index && d->index_epoch != 0) {
+        // the buffer must hold what this call names (Serving §10: a reused index
+        // cache is valid only for the prefix, positions and revision it was made for)
+        const gsa_index_tag& t = *d->index_tag;
+        if (t.epoch != d->index_epoch || t.index_buf_dev != d->index_buf_dev || t.full_layer != d->index_layer ||
+            t.n_q != d->n_q || t.k != d->k || t.n_cap > d->n_cap)
+            return fail(GSA_ERR_STALE_INDEX,
+                        "index buffer %p holds epoch %llu, full layer %d, n_q %d, k %d, n_cap %lld; the call "
+                        "names buffer %p, epoch %llu, full layer %d, n_q %d, k %d, n_cap %lld",
+                        (const void*)t.index_buf_dev, (unsigned long long)t.epoch, t.full_layer, t.n_q, t.k,
+                        (long long)t.n_cap, (const void*)d->index_buf_dev, (unsigned long long)d->index_epoch,
+                        d->index_layer, d->n_q, d->k, (long long)d->n_cap);
+    }
     if (d->compute_index) {
         const bool buffered = d->scores_dev != nullptr;        // else: selection without a score buffer
         gsa_status st = check_score(d->dt, d->q_idx_dev, d->q_scale_dev, d->w_dev, d->k_idx_dev,
@@ -413,6 +428,18 @@ gsa_status enqueue_group(const gsa_group_desc* d, hipStream_t s) {
 // full layer before it.
 bool layer_is_full(int i) { return i < 3 || i % 4 == 2; }
 
+// After a group that computed its indices was enqueued: the host record of its buffer.
+void write_tag(const gsa_group_desc* d) {
+    if (!d->compute_index || d->index_tag == nullptr) return;
+    gsa_index_tag& t = *d->index_tag;
+    t.index_buf_dev = d->index_buf_dev;
+    t.epoch = d->index_epoch;
+    t.full_layer = d->index_layer;
+    t.n_q = d->n_q;
+    t.k = d->k;
+    t.n_cap = d->n_cap;
+}
+
 }  // namespace
 
 extern "C" {
@@ -421,7 +448,10 @@ gsa_status gsa_indexshare_group(const gsa_group_desc* d, void* stream) {
     gsa_status st = validate_group(d);
     if (st != GSA_OK) return st;
     st = enqueue_group(d, (hipStream_t)stream);
-    if (st == GSA_OK) g_err[0] = 0;
+    if (st == GSA_OK) {
+        write_tag(d);
+        g_err[0] = 0;
+    }
     return st;
 }
 
@@ -461,6 +491,9 @@ gsa_status gsa_layer_stack(const gsa_stack_desc* d, void* stream) {
         g.workspace_dev = d->workspace_dev; g.workspace_bytes = d->workspace_bytes;
         g.paged_kv = d->paged_kv;
         g.kv_dt = d->kv_dt;
+        g.index_epoch = d->index_epoch;
+        g.index_layer = i;
+        g.index_tag = d->index_tags != nullptr ? &d->index_tags[f] : nullptr;
         return g;
     };
     for (int i = 0, f = 0; i < d->n_layers; ++i) {      // validate all before enqueuing any
@@ -476,9 +509,16 @@ gsa_status gsa_layer_stack(const gsa_stack_desc* d, void* stream) {
     }
     for (int i = 0, f = 0; i < d->n_layers; ++i) {
         if (!layer_is_full(i)) continue;
-        const gsa_group_desc g = group_at(i, f++);
+        const gsa_group_desc g = group_at(i, f);
         const gsa_status st = enqueue_group(&g, (hipStream_t)stream);
         if (st != GSA_OK) return st;
+        if (d->index_tags != nullptr) {
+            // a record of an earlier full layer whose buffer this group overwrote describes nothing now
+            for (int e = 0; e < f; ++e)
+                if (d->index_tags[e].index_buf_dev == g.index_buf_dev) d->index_tags[e].epoch = 0;
+            write_tag(&g);
+        }
+        ++f;
     }
     g_err[0] = 0;
     return GSA_OK;

@@ -185,6 +185,11 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         const int i = tid + u * kThreads;
         iv[u] = i < nrows ? idx[(int64_t)q * k + r0 + i] : -1;
     }
+    // positions outside [0, n_cap) (with a paged cache, outside the sequence's
+    // pages) are skipped as -1 is: one unsigned compare, so no index from a stale
+    // or foreign buffer makes the gather leave the sequence's rows
+#pragma unroll
+    for (int u = 0; u < kIdxPer; ++u) iv[u] = (uint32_t)iv[u] < (uint32_t)n_cap ? iv[u] : -1;
     if (block_table == nullptr) {
         kvs = kv + (int64_t)seq * n_cap * RB;
     } else {

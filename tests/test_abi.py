@@ -226,3 +226,58 @@ def test_stack_validates_every_group_before_launching():
     d.n_layers = 0
     assert L.gsa_layer_stack(ctypes.byref(d), None) == INVALID
     assert L.gsa_layer_stack(None, None) == INVALID
+
+
+STALE = 5
+
+
+def _s_only_group(tag, epoch, layer=6, n_q=8, n_cap=4096, buf=0x10000, break_layer=False):
+    """A shared-only group (attention over an existing index buffer) naming an
+    epoch and a full layer; the tag check happens before anything is enqueued.
+    break_layer: the attention layer lacks q_rope, a host check that comes after
+    the tag check, so the call never reaches a launch."""
+    L = gsa.lib()
+    layers = (gsa._MlaLayer * 1)()
+    layers[0] = gsa._MlaLayer(0x10000, None if break_layer else 0x10000, 0x10000, 0x10000, None)
+    d = gsa._GroupDesc()
+    d.compute_index = 0
+    d.q_seq_dev, d.index_buf_dev = 0x10000, buf
+    d.n_q, d.batch, d.n_cap, d.k = n_q, 1, n_cap, 2048
+    d.n_layers, d.layers = 1, ctypes.cast(layers, ctypes.POINTER(gsa._MlaLayer))
+    d.n_heads, d.scale = 64, 1 / 16
+    d.workspace_dev, d.workspace_bytes = 0x10000, 1 << 30
+    d.index_epoch, d.index_layer = epoch, layer
+    if tag is not None:
+        d.index_tag = ctypes.pointer(tag)
+    return L.gsa_indexshare_group(ctypes.byref(d), None), layers
+
+
+def test_stale_index_buffer_is_rejected_before_launching():
+    # the record of a buffer that full layer 6 wrote for 8 queries over 4096 positions at epoch 41
+    tag = gsa.IndexTag(0x10000, 41, 6, 8, 2048, 4096)
+    L = gsa.lib()
+    assert L.gsa_status_string(STALE) == b"GSA_ERR_STALE_INDEX"
+    for kw in (dict(epoch=42), dict(layer=10), dict(n_q=16), dict(n_cap=2048), dict(buf=0x20000)):
+        a = dict(epoch=41, layer=6, n_q=8, n_cap=4096, buf=0x10000)
+        a.update(kw)
+        st, _ = _s_only_group(tag, **a)
+        assert st == STALE, kw
+        assert b"epoch" in L.gsa_last_error()
+    never = gsa.IndexTag(0x10000, 0, 6, 8, 2048, 4096)            # epoch 0: describes nothing
+    assert _s_only_group(never, 41)[0] == STALE
+    assert _s_only_group(None, 41)[0] == INVALID                  # an epoch needs a record
+    assert b"index_tag is NULL" in L.gsa_last_error()
+
+
+def test_matching_index_tag_passes_the_check():
+    # a matching record (also with a longer call context than the writer's) passes
+    # the tag check: the call then stops at the attention layer's own host check,
+    # which comes after it (so nothing is launched on any machine)
+    L = gsa.lib()
+    tag = gsa.IndexTag(0x10000, 41, 6, 8, 2048, 4096)
+    for n_cap in (4096, 8192):
+        st, _ = _s_only_group(tag, 41, n_cap=n_cap, break_layer=True)
+        assert st == INVALID and b"layer 0: q_rope" in L.gsa_last_error(), (st, L.gsa_last_error())
+    # epoch 0 leaves the buffer unchecked, as before the tag existed
+    st, _ = _s_only_group(gsa.IndexTag(0x20000, 7, 1, 1, 2048, 1), 0, break_layer=True)
+    assert st == INVALID and b"layer 0: q_rope" in L.gsa_last_error()

@@ -303,6 +303,31 @@ def test_mla_scattered_invalid_indices_and_empty_rows():
     assert torch.all(out[1] == 0) and torch.all(torch.isneginf(lse[1]))
 
 
+def test_mla_out_of_range_indices_are_skipped_like_minus_one():
+    # entries past the cache (n_ctx, 2^30, 2^31 - 1) or below -1 are skipped by the
+    # gather exactly as -1 is: the same bits as the call with those entries set to -1
+    wl = W.Workload("mla_oob", 1, 3000, 4, 1, "bf16")
+    q_lat, q_rope = W.mla_queries(wl, 23, 0)
+    kv = W.mla_cache(wl, 23, 0)
+    q_seq, _ = W.query_layout(wl)
+    g = torch.Generator().manual_seed(23)
+    idx = torch.randint(0, 3000, (4, 2048), generator=g, dtype=torch.int32)
+    bad = torch.rand((4, 2048), generator=g) < 0.25
+    junk = torch.tensor([3000, 3001, 1 << 30, (1 << 31) - 1, -2, -(1 << 31)], dtype=torch.int32)
+    idx_bad = idx.clone()
+    idx_bad[bad] = junk[torch.randint(0, len(junk), (int(bad.sum()),), generator=g)]
+    idx_bad[3] = 5000                                     # a row with nothing in range
+    idx_clean = torch.where((idx_bad >= 0) & (idx_bad < 3000), idx_bad, torch.full_like(idx_bad, -1))
+    d = dev()
+    a = gsa.sparse_mla_attn(q_lat.to(d), q_rope.to(d), kv.to(d), q_seq.to(d), idx_bad.to(d))
+    b = gsa.sparse_mla_attn(q_lat.to(d), q_rope.to(d), kv.to(d), q_seq.to(d), idx_clean.to(d))
+    torch.cuda.synchronize()
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
+    assert torch.all(a[0][3] == 0) and torch.all(torch.isneginf(a[1][3]))
+    o_want, l_want = oracle.sparse_mla(np32(q_lat), np32(q_rope), np32(kv), np32(q_seq), np32(idx_clean), 1 / 16)
+    assert max_abs(np32(a[0]), o_want) <= ATOL_OUT and max_abs(np32(a[1]), l_want) <= ATOL_LSE
+
+
 def test_mla_short_prefix_equals_dense():
     # prefix <= 2048: top-k keeps every position, so sparse attention is dense attention
     def idx_fn(wl, g):
@@ -359,6 +384,35 @@ def test_group_s_only_call_reuses_buffer_and_is_deterministic():
     for (o1, s1), (o2, s2), (o3, s3) in zip(outs[1:], outs2, outs3):
         assert max_abs(np32(o1), np32(o2)) <= ATOL_OUT and max_abs(np32(s1), np32(s2)) <= ATOL_LSE
         assert torch.equal(o2, o3) and torch.equal(s2, s3)
+
+
+def test_group_index_tag_written_then_checked():
+    # the F call records what its buffer holds; an S-only call naming the same
+    # epoch and full layer runs (same bits as the unchecked call), any other
+    # epoch or layer is refused before anything is enqueued
+    wl = W.WORKLOADS["group_b1_n4096_q4"]
+    g = W.group_inputs(wl, 2, n_layers=4)
+    d = dev()
+    layers = [tuple(t.to(d) for t in L) for L in g.layers]
+    idx = torch.full((wl.n_q, 2048), -7, dtype=torch.int32, device=d)
+    tag = gsa.IndexTag()
+    gsa.indexshare_group(layers[:1], g.q_seq.to(d), idx, q_pos=g.q_pos.to(d), q_idx=g.q_idx.to(d),
+                         w=g.w.to(d), k_idx=g.k_idx.to(d), index_epoch=1234, index_layer=6, index_tag=tag)
+    assert (tag.index_buf_dev, tag.epoch, tag.full_layer, tag.n_q, tag.k, tag.n_cap) == \
+        (idx.data_ptr(), 1234, 6, wl.n_q, 2048, wl.n_ctx)
+    checked = gsa.indexshare_group(layers[1:], g.q_seq.to(d), idx, compute_index=False,
+                                   index_epoch=1234, index_layer=6, index_tag=tag)
+    plain = gsa.indexshare_group(layers[1:], g.q_seq.to(d), idx, compute_index=False)
+    torch.cuda.synchronize()
+    for (o1, s1), (o2, s2) in zip(checked, plain):
+        assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    before = [o.clone() for o, _ in checked]
+    for kw in (dict(index_epoch=1235, index_layer=6), dict(index_epoch=1234, index_layer=10)):
+        with pytest.raises(gsa.GsaError, match="GSA_ERR_STALE_INDEX"):
+            gsa.indexshare_group(layers[1:], g.q_seq.to(d), idx, compute_index=False, index_tag=tag,
+                                 outs=checked, **kw)
+    torch.cuda.synchronize()
+    assert all(torch.equal(o, b) for (o, _), b in zip(checked, before))   # nothing ran
 
 
 @pytest.mark.parametrize("n_layers,n_q,batch", [(3, 2, 1), (4, 8, 8), (9, 5, 2)])

@@ -24,7 +24,8 @@ def _stack_inputs(wl, seed, n_layers):
     return fulls, q_seq, q_pos, idx_in, mla_in
 
 
-def _run_stack(wl, seed, n_layers, dtype="bf16", index_stride=None, score_buffer=True):
+def _run_stack(wl, seed, n_layers, dtype="bf16", index_stride=None, score_buffer=True, index_tags=None,
+               index_epoch=0):
     fulls, q_seq, q_pos, idx_in, mla_in = _stack_inputs(wl, seed, n_layers)
     d = dev()
     indexers = []
@@ -43,7 +44,8 @@ def _run_stack(wl, seed, n_layers, dtype="bf16", index_stride=None, score_buffer
     say(f"stack: {n_layers} layers ({len(fulls)} full), {dtype}, n_q={wl.n_q}, N={wl.n_ctx}, "
         f"index_stride={'0' if index_stride == 0 else 'n_q*k'}")
     outs = gsa.layer_stack(indexers, layers, q_seq.to(d), q_pos.to(d), index_buf,
-                           index_stride=index_stride, score_buffer=score_buffer)
+                           index_stride=index_stride, score_buffer=score_buffer, index_tags=index_tags,
+                           index_epoch=index_epoch)
     torch.cuda.synchronize()
     return fulls, q_seq, q_pos, idx_in, mla_in, index_buf, outs
 
@@ -70,11 +72,32 @@ def test_stack_78_layers_matches_oracle():
 
 def test_stack_single_reused_buffer_gives_same_outputs():
     wl = W.WORKLOADS["group_b1_n4096_q4"]
-    *_, buf3, outs3 = _run_stack(wl, 4, 11)
-    *_, buf1, outs1 = _run_stack(wl, 4, 11, index_stride=0)
+    tags3 = (gsa.IndexTag * 5)()
+    tags1 = (gsa.IndexTag * 5)()
+    *_, buf3, outs3 = _run_stack(wl, 4, 11, index_tags=tags3, index_epoch=99)
+    *_, buf1, outs1 = _run_stack(wl, 4, 11, index_stride=0, index_tags=tags1, index_epoch=99)
     assert torch.equal(buf1, buf3[-1])             # the one buffer ends with the last full layer's
     for (o3, s3), (o1, s1) in zip(outs3, outs1):
         assert torch.equal(o3, o1) and torch.equal(s3, s1)
+    # records: one buffer per full layer (0, 1, 2, 6, 10) each described; with one
+    # reused buffer only the last full layer's record still describes it
+    step = wl.n_q * 2048 * 4
+    assert [(t.full_layer, t.epoch, t.index_buf_dev - buf3.data_ptr()) for t in tags3] == \
+        [(f, 99, j * step) for j, f in enumerate((0, 1, 2, 6, 10))]
+    assert [t.epoch for t in tags1] == [0, 0, 0, 0, 99] and tags1[4].full_layer == 10
+    # a shared-only call over full layer 6's buffer passes with its record, and is
+    # refused with layer 10's record
+    fulls, q_seq, q_pos, idx_in, mla_in = _stack_inputs(wl, 4, 11)
+    d = dev()
+    lay = [tuple(t.to(d) for t in mla_in[7])]
+    o = gsa.indexshare_group(lay, q_seq.to(d), buf3[3], compute_index=False, index_epoch=99, index_layer=6,
+                             index_tag=tags3[3])
+    torch.cuda.synchronize()
+    # (one layer splits its rows differently from the stack's four-layer launch)
+    assert max_abs(np32(o[0][0]), np32(outs3[7][0])) <= ATOL_OUT
+    with pytest.raises(gsa.GsaError, match="GSA_ERR_STALE_INDEX"):
+        gsa.indexshare_group(lay, q_seq.to(d), buf3[3], compute_index=False, index_epoch=99, index_layer=6,
+                             index_tag=tags3[4])
 
 
 def test_stack_fp8_indexer_matches_bf16_oracle():
