@@ -1,24 +1,31 @@
 #!/usr/bin/env python3
 """Benchmark of the DSA lightning indexer + IndexShare + sparse MLA hot path on one MI355X.
 
-One step = one pass of the measured unit over one batch of synthetic input:
-  group workloads   one IndexShare group: the full layer's indexer score and
+One step = one pass of the measured unit over one batch of synthetic input,
+issued as the C-ABI boundary call that runs it:
+  group workloads   gsa_indexshare_group: the full layer's indexer score and
                     top-2048, then absorbed sparse MLA for it and its 3 shared
                     layers (4 layers);
-  prefill workloads the full layer's indexer score and top-2048 (index buffer
-                    written), no attention;
-  stack workloads   the 78-layer attention stack: 21 full layers (score +
-                    top-2048 each) and 78 sparse MLA layers, in layer order.
-Default workload: decode, 64 sequences x 131072 cached tokens, one query per
-sequence (bf16 indexer, bf16 latent cache), one group per step.
+  prefill workloads gsa_indexshare_group with no attention layers: the full
+                    layer's indexer score and top-2048 (index buffer written);
+  stack workloads   gsa_layer_stack: 21 full layers (score + top-2048 each) and
+                    78 sparse MLA layers, in layer order.
 
-Prints ONE JSON line. `value` is query-tokens/s over the timed steps, inputs
-resident in HBM. `roofline` covers the kernel with the largest share of the
-step: algorithmic bytes per launch / its average launch time from HIP events
-recorded between the calls on the launch stream. `cpu_baseline` times the CPU
-oracle on a bounded sample of the same workload.
+By default every configuration is measured in turn (tiny group, decode 64 x
+128K, prefill 4096 x 128K bf16 and fp8, decode 8 x 1M fp8, the 78-layer stack),
+each one's inputs freed before the next. The headline fields of the ONE JSON
+line are the decode 64 x 128K group's; `workloads` holds every configuration's
+line. Per configuration:
+  ms_per_step / value  the boundary call timed whole (HIP events around the
+                       timed steps on the launch stream; inputs resident in HBM);
+  step_roofline        the step's algorithmic bytes (or the score's matrix work,
+                       for prefill) against the HBM (or MFMA) peak;
+  roofline             the kernel with the largest share of the step, from a
+                       separate pass that issues the same kernels as separate
+                       calls with HIP events between them;
+  cpu_baseline         the CPU oracle on a bounded sample of the same workload.
 
-    python bench.py [--gpus 1] [--steps 50] [--warmup 5] [--workload NAME]
+    python bench.py [--gpus 1] [--steps 20] [--warmup 5] [--workload NAME[,NAME...]]
     python bench.py --calibrate-copy     # plain 1 GiB device copy, for counter scaling
 """
 from __future__ import annotations
@@ -103,6 +110,14 @@ def launch_bytes(kind, wl, fp8):
             "sparse_mla": lambda: mla_bytes(wl)}[kind]()
 
 
+def step_bytes(wl, n_full, n_att):
+    """Algorithmic bytes of one step: every full layer's score inputs and index
+    write, and every attention layer's gather, queries, indices and output (the
+    score buffer between score and top-k is not algorithmic)."""
+    fp8 = wl.indexer_dtype in ("fp8", "fp8h")
+    return n_full * (score_bytes(wl, fp8) + wl.n_q * 2048 * 4) + n_att * mla_bytes(wl)
+
+
 def measured_traffic(kind, wl):
     """HBM bytes per launch of `kind` from the committed counter summary of this
     workload (FETCH_SIZE and WRITE_SIZE passes, copy-calibrated), or None when
@@ -123,17 +138,13 @@ def measured_traffic(kind, wl):
 
 
 # ---- inputs and the step ----------------------------------------------------------
-def build_inputs(wl, seed, dev, per_layer_dsa=False):
-    """Device inputs of the workload, drawn by the seeded generators in `workloads`.
-    per_layer_dsa: every layer is full (its own indexer and top-k), the schedule
-    IndexShare replaces."""
+def build_inputs(wl, seed, dev):
+    """Device inputs of the workload, drawn by the seeded generators in `workloads`."""
     t0 = time.time()
     q_seq, q_pos = W.query_layout(wl, dev)
     fp8 = wl.indexer_dtype in ("fp8", "fp8h")
     rot = wl.indexer_dtype == "fp8h"           # Hadamard-rotated fp8: the step quantises q
-    if per_layer_dsa:
-        src = list(range(wl.n_layers if wl.mla else 1))
-    elif is_stack(wl):
+    if is_stack(wl):
         src = gsa.layer_pattern(wl.n_layers)
     else:                                      # one group: layer 0 full, the rest shared
         src = [0] * (wl.n_layers if wl.mla else 1)
@@ -244,27 +255,67 @@ def make_step(wl, inp, dev, score_buffer=True):
     return step, bufs, [(k, b) for k, b, _ in calls]
 
 
-def run_bench(args):
-    wl = W.WORKLOADS[args.workload]
+def make_boundary_step(wl, inp, bufs, score_buffer=True):
+    """The measured unit as the one boundary call that runs it, over the same
+    buffers as make_step: gsa_indexshare_group (the group, or for prefill the
+    full layer alone) or gsa_layer_stack. The descriptor is marshalled once.
+    score_buffer=False: the full layers select without a score buffer."""
+    q_seq, q_pos = inp["q_seq"], inp["q_pos"]
+    lay = [inp["layers"][l] for l in range(len(inp["layers"]))]
+    scores = bufs["scores"] if score_buffer else None
+    if is_stack(wl):
+        call = gsa.prepare_stack(inp["indexers"], lay, q_seq, q_pos, bufs["idx"], scores=scores,
+                                 workspace=bufs["ws"], outs=bufs["outs"], scale=SCALE, score_buffer=score_buffer)
+    else:
+        q, w, k, qs, ks = inp["indexers"][0]
+        call = gsa.prepare_group(lay, q_seq, bufs["idx"][0], q_pos=q_pos, q_idx=q, w=w, k_idx=k, q_scale=qs,
+                                 k_scale=ks, scores=scores, workspace=bufs["ws"], outs=bufs["outs"],
+                                 scale=SCALE, score_buffer=score_buffer)
+    if not inp["rot"]:
+        return call
+    q, _, _, qs, _ = inp["indexers"][0]
+
+    def step():                      # the rotated fp8 indexer quantises this step's queries first
+        gsa.quantize_e4m3(inp["q_src"][0], hadamard=True, out=(q, qs))
+        call()
+    return step
+
+
+def time_steps(fn, steps, warmup):
+    """ms per call of fn over `steps` calls after `warmup`, from HIP events
+    recorded on the current stream (the binding launches there)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    t0.record()
+    for _ in range(steps):
+        fn()
+    t1.record()
+    torch.cuda.synchronize()
+    return t0.elapsed_time(t1) / steps, (time.perf_counter() - w0) * 1e3 / steps
+
+
+def measure(wl, args, cpu_seconds):
+    """One configuration: the boundary call timed whole, the per-kernel breakdown
+    pass, the rooflines and the CPU oracle's sample. Frees its inputs on return."""
     dev = torch.device("cuda", 0)
-    torch.cuda.set_device(dev)
-    inp = build_inputs(wl, args.seed, dev, per_layer_dsa=args.per_layer_dsa)
-    step, bufs, calls = make_step(wl, inp, dev, score_buffer=not args.no_score_buffer)
+    inp = build_inputs(wl, args.seed, dev)
+    step_b, bufs, calls = make_step(wl, inp, dev, score_buffer=not args.no_score_buffer)
+    whole = make_boundary_step(wl, inp, bufs, score_buffer=not args.no_score_buffer)
+    # ---- pass A: the boundary call, timed whole
+    ms_step, wall_ms = time_steps(whole, args.steps, args.warmup)
+    idx_whole = bufs["idx"].clone()
+    # ---- pass B: the same kernels as separate calls, events between them
     for _ in range(args.warmup):
-        step()
+        step_b()
     torch.cuda.synchronize()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(calls) + 1)] for _ in range(args.steps)]
-    t_start = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    w0 = time.perf_counter()
-    t_start.record()
     for i in range(args.steps):
-        step(evs[i])
-    t_end.record()
+        step_b(evs[i])
     torch.cuda.synchronize()
-    wall = time.perf_counter() - w0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
+    same = bool(torch.equal(idx_whole, bufs["idx"]))
     kinds = sorted({k for k, _ in calls}, key=[k for k, _ in calls].index)
     ms_kind = {k: 0.0 for k in kinds}           # per step
     bytes_kind = {k: 0 for k in kinds}          # per step
@@ -273,39 +324,59 @@ def run_bench(args):
         ms_kind[k] += float(np.mean([e[i].elapsed_time(e[i + 1]) for e in evs]))
         bytes_kind[k] += b
         launches[k] += 1
+    ms_split = float(np.mean([e[0].elapsed_time(e[-1]) for e in evs]))
     dom = max(ms_kind, key=ms_kind.get)
-    roof = roofline(dom, wl, inp["fp8"], bytes_kind[dom], ms_kind[dom], launches[dom])
-    value = wl.n_q / (ms_step / 1e3)
-    log(f"[bench] {args.steps} steps: {ms_step:.3f} ms/step (wall {wall / args.steps * 1e3:.3f}); " +
-        ", ".join(f"{k} {launches[k]}x {ms_kind[k] / launches[k] * 1e3:.1f} us" for k in kinds))
-    result = {
-        "metric": METRIC,
-        "value": round(value, 1),
-        "unit": "query-tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+    fp8 = inp["fp8"]
+    n_full, n_att = len(inp["full_layers"]), len(inp["layers"])
+    log(f"[bench] {wl.name}: {ms_step:.4f} ms/step as one boundary call (host {wall_ms:.4f} ms/step); "
+        f"as separate calls {ms_split:.4f} ms: " +
+        ", ".join(f"{k} {launches[k]}x {ms_kind[k] / launches[k] * 1e3:.1f} us" for k in kinds) +
+        ("" if same else "  [INDICES DIFFER BETWEEN THE TWO PASSES]"))
+    res = {
         "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "fp8" if inp["fp8"] else "bf16",
-        "data": "synthetic (seeded; integer indexer q/k in [-4,4], w in [1,4]; N(0,1) bf16 latents)",
-        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.n_ctx,
-                   "queries": wl.n_q, "full_layers": len(inp["full_layers"]),
-                   "attention_layers": len(inp["layers"]), "indexer": wl.indexer_dtype,
-                   "latent_cache": wl.kv_dtype,
-                   "topk": 2048, "mla_heads": 64, "seed": args.seed,
-                   "schedule": "per-layer DSA" if args.per_layer_dsa else "IndexShare",
+        "value": round(wl.n_q / (ms_step / 1e3), 1),
+        "unit": "query-tokens/s",
+        "dtype": "fp8" if fp8 else "bf16",
+        "config": {"workload": wl.name, "batch": wl.batch, "context": wl.n_ctx, "queries": wl.n_q,
+                   "full_layers": n_full, "attention_layers": n_att, "indexer": wl.indexer_dtype,
+                   "latent_cache": wl.kv_dtype, "topk": 2048, "mla_heads": 64, "seed": args.seed,
+                   "step": "gsa_layer_stack" if is_stack(wl) else "gsa_indexshare_group",
                    "score_buffer": not args.no_score_buffer},
-        "breakdown_ms_per_step": {k: round(v, 4) for k, v in ms_kind.items()},
-        "avg_launch_us": {k: round(ms_kind[k] / launches[k] * 1e3, 2) for k in kinds},
-        "achieved_GBs": {k: round(bytes_kind[k] / (ms_kind[k] / 1e3) / 1e9, 1) for k in kinds},
-        "roofline": roof,
+        "step_roofline": step_roofline(wl, fp8, n_full, n_att, ms_step),
+        "roofline": roofline(dom, wl, fp8, bytes_kind[dom], ms_kind[dom], launches[dom]),
+        "breakdown": {"ms_per_step_separate_calls": round(ms_split, 4),
+                      "avg_launch_us": {k: round(ms_kind[k] / launches[k] * 1e3, 2) for k in kinds},
+                      "launches_per_step": launches,
+                      "achieved_GBs": {k: round(bytes_kind[k] / (ms_kind[k] / 1e3) / 1e9, 1) for k in kinds},
+                      "indices_equal_to_boundary_call": same},
     }
-    if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(wl, inp, args)
-    return result
+    if cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(wl, inp, args, cpu_seconds)
+    log(f"[bench] {wl.name}: {res['value']:.1f} q-tok/s; step {res['step_roofline']['frac']:.3f} of "
+        f"{res['step_roofline']['bound']}; {dom} {res['roofline']['frac']:.3f} of {res['roofline']['bound']}")
+    del inp, bufs, calls, step_b, whole, idx_whole
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return res
+
+
+def step_roofline(wl, fp8, n_full, n_att, ms):
+    """The whole step against its bound: HBM for the decode and stack steps (all
+    their algorithmic bytes at the HBM peak), MFMA for prefill (the score's matrix
+    work at the peak of its input type; top-k and the index write ride along)."""
+    sec = ms / 1e3
+    if wl.mla:
+        nb = step_bytes(wl, n_full, n_att)
+        a = nb / sec / 1e9
+        return {"bound": "hbm", "achieved": round(a, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(a / HBM_PEAK_GBS, 4), "bytes_per_step": nb,
+                "roofline_ms": round(nb / (HBM_PEAK_GBS * 1e9) * 1e3, 4)}
+    fl = score_flops(wl) * n_full
+    peak = MFMA_PEAK_TFLOPS["fp8" if fp8 else "bf16"]
+    a = fl / sec / 1e12
+    return {"bound": "mfma", "achieved": round(a, 1), "peak": peak, "unit": "TFLOP/s",
+            "frac": round(a / peak, 4), "flops_per_step": fl,
+            "roofline_ms": round(fl / (peak * 1e12) * 1e3, 4)}
 
 
 def roofline(kind, wl, fp8, nbytes, ms, launches):
@@ -374,7 +445,7 @@ def host_rows(kv, b, sel):
     return rows[None], np.where(v, np.arange(len(sel)), -1)[None]
 
 
-def cpu_baseline(wl, inp, args):
+def cpu_baseline(wl, inp, args, cpu_seconds):
     """The CPU oracle on a bounded sample of the same workload: the first
     `--cpu-queries` queries through the whole measured unit (every full
     layer's score over all causal keys and top-2048, then every attention
@@ -386,7 +457,7 @@ def cpu_baseline(wl, inp, args):
     n = 0
     keys = {}
     for qi in range(min(args.cpu_queries, wl.n_q)):
-        if secs >= args.cpu_seconds:
+        if secs >= cpu_seconds:
             break
         n += 1
         b = int(inp["q_seq"][qi])
@@ -426,22 +497,30 @@ def calibrate_copy(args):
     print(json.dumps({"calibrate_copy_bytes": n, "launches": args.steps}))
 
 
+DEFAULT_SET = ["group_b1_n4096_q4", "decode_b64_n131072", "prefill_q4096_n131072", "prefill_q4096_n131072_fp8",
+               "decode_b8_n1048576_fp8", "stack78_b8_q8_n262144"]
+HEADLINE = "decode_b64_n131072"
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--seed", type=int, default=0)
-    ap.add_argument("--workload", default="decode_b64_n131072", choices=sorted(W.WORKLOADS))
-    ap.add_argument("--cpu-queries", type=int, default=1 << 30, help="most queries in the CPU sample")
+    ap.add_argument("--workload", default=",".join(DEFAULT_SET),
+                    help="comma-separated workloads (the first one in the list that is the 64 x 128K decode "
+                         "group, else the first, gives the headline fields); choices: " + ", ".join(W.WORKLOADS))
+    ap.add_argument("--cpu-queries", type=int, default=1 << 30, help="most queries in each CPU sample")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="the CPU sample stops at the first query that starts past this much oracle time")
+                    help="oracle seconds for the headline workload's CPU sample (it stops at the first query "
+                         "that starts past this much oracle time)")
+    ap.add_argument("--cpu-seconds-other", type=float, default=3.0,
+                    help="the same for every other workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true")
-    ap.add_argument("--per-layer-dsa", action="store_true",
-                    help="every layer full (own indexer + top-k): the schedule IndexShare replaces")
     ap.add_argument("--no-score-buffer", action="store_true",
-                    help="score + top-k as one gsa_indexer_topk call (no [n_q, n_ctx] score buffer)")
+                    help="full layers select without a score buffer (score + top-k as gsa_indexer_topk)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (this path is measured on a single MI355X); "
@@ -454,8 +533,41 @@ def main():
     if args.calibrate_copy:
         calibrate_copy(args)
         return
-    res = run_bench(args)
-    print(json.dumps(res), flush=True)
+    names = [n for n in args.workload.split(",") if n]
+    for n in names:
+        if n not in W.WORKLOADS:
+            ap.error(f"unknown workload {n}")
+    head = HEADLINE if HEADLINE in names else names[0]
+    torch.cuda.set_device(0)
+    t0 = time.perf_counter()
+    per = {}
+    for n in names:
+        secs = 0.0 if args.no_cpu_baseline else (args.cpu_seconds if n == head else args.cpu_seconds_other)
+        per[n] = measure(W.WORKLOADS[n], args, secs)
+        log(f"[bench] {n} done ({time.perf_counter() - t0:.1f}s since start)")
+    h = per[head]
+    result = {
+        "metric": METRIC,
+        "value": h["value"],
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": h["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": h["dtype"],
+        "data": "synthetic (seeded; integer indexer q/k in [-4,4], w in [1,4]; N(0,1) bf16 latents)",
+        "config": h["config"],
+        "step_roofline": h["step_roofline"],
+        "roofline": h["roofline"],
+        "breakdown": h["breakdown"],
+    }
+    if "cpu_baseline" in h:
+        result["cpu_baseline"] = h["cpu_baseline"]
+    result["workloads"] = per
+    print(json.dumps(result), flush=True)
 
 
 if __name__ == "__main__":

@@ -429,11 +429,41 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     index_buf holds: filled in when compute_index, checked against
     (index_epoch, index_layer, shape) when not and index_epoch != 0.
     Returns [(out, lse)] per layer."""
+    call = prepare_group(layers, q_seq, index_buf, q_pos, q_idx, w, k_idx, q_scale, k_scale, scores,
+                         compute_index, scale, workspace, outs, block_table, score_buffer, index_epoch,
+                         index_layer, index_tag)
+    call()
+    return call.outs
+
+
+class PreparedCall:
+    """A C-ABI call with its descriptor marshalled once: calling it enqueues the
+    same work again on the stream it was prepared for (the tensors it names must
+    stay alive; `keep` holds them and the ctypes arrays the descriptor points to)."""
+
+    def __init__(self, fn, desc, stream, outs, keep):
+        self.fn, self.desc, self.stream, self.outs, self.keep = fn, desc, stream, outs, keep
+
+    def __call__(self):
+        _check(self.fn(ctypes.byref(self.desc), self.stream))
+
+
+def prepare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_idx=None,
+                  q_scale=None, k_scale=None, scores=None, compute_index=True,
+                  scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True,
+                  index_epoch=0, index_layer=0, index_tag=None):
+    """indexshare_group's arguments marshalled into a PreparedCall (nothing is
+    enqueued until it is called). With no layers (compute_index only) the group
+    is the full layer's indexer and top-k alone."""
     L = lib()
     n_q = q_seq.shape[0]
-    kv0 = layers[0][2]
+    kv0 = layers[0][2] if layers else None
     pg = None
-    if block_table is None:
+    if kv0 is None:
+        if not compute_index:
+            raise GsaError("a group without attention layers must compute its indices")
+        batch, n_cap = k_idx.shape[0], k_idx.shape[1]
+    elif block_table is None:
         batch, n_cap = kv0.shape[0], kv0.shape[1]
     else:
         pg = _paged(block_table, kv0)
@@ -457,7 +487,7 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     for i, ((ql, qr, kv), (o, s)) in enumerate(zip(layers, outs)):
         arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
                            None if s is None else s.data_ptr())
-    nbytes = (group_workspace_bytes(n_q, ld, len(layers), k) if compute_index
+    nbytes = (group_workspace_bytes(n_q, ld, max(len(layers), 1), k) if compute_index
               else mla_layers_workspace_bytes(n_q, len(layers), MLA_HEADS, k))
     ws = _workspace(nbytes, dev, workspace)
     d = _GroupDesc()
@@ -477,12 +507,13 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
     if pg is not None:
         d.paged_kv = ctypes.pointer(pg)
-    d.kv_dt = FP8_E4M3 if _kv_fp8(kv0) else BF16
+    d.kv_dt = FP8_E4M3 if kv0 is not None and _kv_fp8(kv0) else BF16
     d.index_epoch, d.index_layer = index_epoch, index_layer
     if index_tag is not None:
         d.index_tag = ctypes.pointer(index_tag)
-    _check(L.gsa_indexshare_group(ctypes.byref(d), _stream(dev)))
-    return outs
+    keep = (layers, q_seq, index_buf, q_pos, q_idx, w, k_idx, q_scale, k_scale, scores, ws, outs, arr, pg,
+            block_table, index_tag)
+    return PreparedCall(L.gsa_indexshare_group, d, _stream(dev), outs, keep)
 
 
 def layer_pattern(n_layers=78):
@@ -497,6 +528,16 @@ def layer_pattern(n_layers=78):
 def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_stride=None,
                 scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True,
                 index_epoch=0, index_tags=None):
+    """The 78-layer attention stack (see prepare_stack); enqueued at once."""
+    call = prepare_stack(indexers, layers, q_seq, q_pos, index_buf, scores, index_stride, scale, workspace,
+                         outs, block_table, score_buffer, index_epoch, index_tags)
+    call()
+    return call.outs
+
+
+def prepare_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_stride=None,
+                  scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True,
+                  index_epoch=0, index_tags=None):
     """The attention stack: indexers = [(q_idx, w, k_idx, q_scale, k_scale)] per full
     layer in layer order (scales None for bf16); layers = [(q_lat, q_rope, kv)] per
     layer. index_buf: int32 [n_full, n_q, k] (each full layer's indices kept) or
@@ -504,7 +545,7 @@ def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_st
     kv is a page pool [n_pages, page_size, 576]. score_buffer=False: every full
     layer selects without a score buffer. index_tags: None, or a ctypes array of
     one IndexTag per full layer that the call fills in (see indexshare_group).
-    Returns [(out, lse)] per layer."""
+    Returns a PreparedCall (nothing enqueued yet); its .outs are [(out, lse)] per layer."""
     L = lib()
     n_q = q_seq.shape[0]
     kv0 = layers[0][2]
@@ -562,5 +603,5 @@ def layer_stack(indexers, layers, q_seq, q_pos, index_buf, scores=None, index_st
         if len(index_tags) != n_full:
             raise GsaError(f"index_tags must hold {n_full} records, got {len(index_tags)}")
         d.index_tags = ctypes.cast(index_tags, ctypes.POINTER(IndexTag))
-    _check(L.gsa_layer_stack(ctypes.byref(d), _stream(dev)))
-    return outs
+    keep = (indexers, layers, q_seq, q_pos, index_buf, scores, ws, outs, xs, arr, pg, block_table, index_tags)
+    return PreparedCall(L.gsa_layer_stack, d, _stream(dev), outs, keep)

@@ -50,3 +50,30 @@ def test_score_and_topk_without_a_buffer():
     pre = W.WORKLOADS["prefill_q4096_n131072"]
     r = bench.roofline("indexer_topk", pre, False, bench.launch_bytes("indexer_topk", pre, False), 6.0, 1)
     assert r["bound"] == "mfma" and r["kernel"] == "indexer_topk"
+
+
+def test_step_bytes_match_the_per_query_accounting():
+    # per query of a 1 F + 3 S decode group: keys (pos + 1) x 256 B (bf16) or
+    # x 132 B (fp8 + scale), q + w, the 8 KiB index write, and per layer
+    # 2048 x 1152 B gathered + 8 KiB of indices + 73,728 B of q + 128 KiB of output
+    per_layer = 2048 * 1152 + 8192 + 73_728 + 131_072
+    assert per_layer == 2_572_288
+    dec = W.WORKLOADS["decode_b64_n131072"]
+    assert bench.step_bytes(dec, 1, 4) == 64 * (131072 * 256 + 8320 + 8192 + 4 * per_layer) == 2_807_046_144
+    m1 = W.WORKLOADS["decode_b8_n1048576_fp8"]
+    assert bench.step_bytes(m1, 1, 4) == 8 * ((1 << 20) * 132 + 4352 + 8192 + 4 * per_layer) == 1_189_709_824
+    st = W.WORKLOADS["stack78_b8_q8_n262144"]
+    # 21 full layers read each sequence's keys once (its 8 queries share them); 78 attention layers
+    want = 21 * (8 * (1 << 18) * 256 + 64 * (8320 + 8192)) + 78 * 64 * per_layer
+    assert bench.step_bytes(st, 21, 78) == want
+    assert abs(want / 8e12 * 1e3 - 3.017) < 0.001          # the stack's 3.017 ms roofline
+
+
+def test_step_roofline_bounds():
+    m1 = W.WORKLOADS["decode_b8_n1048576_fp8"]
+    r = bench.step_roofline(m1, True, 1, 4, 0.248)
+    assert r["bound"] == "hbm" and abs(r["frac"] - 1_189_709_824 / 0.248e-3 / 8e12) < 1e-4
+    pre = W.WORKLOADS["prefill_q4096_n131072_fp8"]
+    r = bench.step_roofline(pre, True, 1, 0, 2.0)
+    assert r["bound"] == "mfma" and r["peak"] == 5000.0
+    assert abs(r["achieved"] - 528_484_352 * 32 * 128 * 2 / 2e-3 / 1e12) < 0.1
