@@ -4,23 +4,37 @@
 // highest-scoring history positions of each query as its sparse attention set.
 //
 // Order: (score descending, position ascending) is a strict total order on the
-// positions 0..pos of a row, so the top-k set is unique, and it is contained in
-// the union of the top-k sets of any partition of the row. The selection runs
-// as a tree over that fact:
-//   level 1  one work-group per 16K-score chunk: each wave holds 2048
-//            consecutive scores in registers (32 per lane) as order-preserving
-//            uint32 keys (-0 folded onto +0). The k-th largest key T is found
-//            by bisection over [min, max]: every step counts keys >= mid with
-//            one ballot and popcount per 64 keys plus an 8-wave sum, so no
-//            histogram or atomic is involved; ties at T keep the lowest
-//            positions. An ordered compaction (ballot ranks) writes the
-//            chunk's top-k as (key, position) pairs in position order;
-//   level 2+ one work-group merges up to 8 lists of a row (concatenated in
-//            chunk order, hence in position order) with the same selection,
-//            until one list remains.
-// The last level writes the positions (ascending) and pads with -1. The row is
-// read from HBM once; no counter or histogram is shared between work-groups,
-// so the result is the same on every run.
+// positions 0..pos of a row, so the top-k set is unique. Scores compare as
+// order-preserving uint32 keys (-0 folded onto +0).
+//
+// Selection core. select_regs holds the items of one 512-thread work-group in
+// registers and finds the k-th key by radix-histogram passes: each pass counts
+// the candidate keys (those in the exact key range of the bin chosen last)
+// into 256 bins per wave in LDS, linear in the score value while the range is
+// wide and then the top bits of key - lo, and keeps the bin where the count of
+// keys in it and above first reaches the number still needed. select_wide is
+// the same selection with one 2048-bin work-group histogram per pass (fewer
+// passes and barriers). Emission is an ordered ballot compaction, ties at the
+// threshold keeping the lowest positions.
+//
+// Bound. The largest score of every 32 positions (the score kernel writes these
+// group maxima) bounds the selection: with L the k-th largest group maximum, at
+// least k positions score >= L, so every selected score is >= L and lies in a
+// group whose maximum reaches L (about k groups, whatever the row length).
+//
+// Kernels:
+//   topk_row    rows of 64K to 1M positions: one work-group per row takes the
+//               row's maxima, L, the list of groups that reach it, those groups'
+//               scores only (each wave a contiguous share, compacted without
+//               work-group barriers) and the final selection, in one launch.
+//   topk_chunk + topk_merge
+//               other widths: one work-group per 16K-score chunk keeps its top
+//               k as a (key, position) list in position order (with a bound
+//               from topk_bound when the row has one), and one work-group per
+//               row merges the lists (their union holds the row's top k).
+//   topk_rescore
+//               the selection without a score buffer: the groups that reach the
+//               bound are rescored with the score kernel's arithmetic.
 #include <type_traits>
 
 #include "device_common.h"
@@ -53,15 +67,27 @@ struct Scratch {
     uint32_t pick[3];                           // chosen bin, count above it, count in it
 };
 
+// Reductions over the 64 lanes of a wave, every lane active, without LDS: the
+// two quad permutations and the half-row and row mirrors (DPP) combine the 16
+// lanes of a row, then the gfx950 permlane16 / permlane32 swaps combine rows
+// and halves (each step pairs disjoint lane sets, so the result is exact for a
+// sum as well as for min and max).
+template <typename Op>
+__device__ __forceinline__ uint32_t wave_reduce(uint32_t v, Op op) {
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // lane ^ 1
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // lane ^ 2
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // 7 - lane in 8
+    v = op(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // 15 - lane in 16
+    auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);                         // other row
+    v = op((uint32_t)r[0], (uint32_t)r[1]);
+    r = __builtin_amdgcn_permlane32_swap(v, v, false, false);                              // other half
+    return op((uint32_t)r[0], (uint32_t)r[1]);
+}
 __device__ __forceinline__ uint32_t wave_max(uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return max(a, b); });
 }
 __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o, 64));
-    return v;
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return min(a, b); });
 }
 // A value every lane of the wave holds (read from LDS after a barrier, or a
 // wave reduction), moved to a scalar register so that branches on it are
@@ -69,20 +95,30 @@ __device__ __forceinline__ uint32_t wave_min(uint32_t v) {
 __device__ __forceinline__ uint32_t uni(uint32_t v) { return __builtin_amdgcn_readfirstlane(v); }
 
 __device__ __forceinline__ uint32_t wave_sum(uint32_t v) {
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) v += (uint32_t)__shfl_xor((int)v, o, 64);
-    return v;
+    return wave_reduce(v, [](uint32_t a, uint32_t b) { return a + b; });
 }
 // number of set bits of `mask` in lanes below this one
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
 }
 
+// Work-group barrier for LDS traffic: this wave's LDS operations are complete
+// (lgkmcnt 0), then s_barrier. Unlike __syncthreads it does not wait for the
+// wave's global loads, so loads issued before a selection stay in flight
+// through its barriers. Global stores are not ordered by it: no wave reads
+// another wave's global stores inside a selection.
+__device__ __forceinline__ void sync_lds() {
+    __builtin_amdgcn_s_waitcnt(0xC07F);                         // lgkmcnt(0) only
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
 // Sum over the block of a per-wave value (uniform inside each wave).
 __device__ __forceinline__ uint32_t block_sum(uint32_t wave_val, Scratch& sc, uint32_t* before = nullptr) {
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     if (lane == 0) sc.wsum[wave] = wave_val;
-    __syncthreads();
+    sync_lds();
     uint32_t tot = 0, bef = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -90,7 +126,7 @@ __device__ __forceinline__ uint32_t block_sum(uint32_t wave_val, Scratch& sc, ui
         bef += w < wave ? t : 0u;
         tot += t;
     }
-    __syncthreads();
+    sync_lds();
     if (before) *before = bef;
     return tot;
 }
@@ -148,7 +184,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[PER], Scratch& sc
     mx = wave_max(mx);
     if (lane == 0) { sc.wmin[wave] = mn; sc.wmax[wave] = mx; }
     clear_hist(sc, 0);
-    __syncthreads();
+    sync_lds();
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) { mn = min(mn, sc.wmin[w]); mx = max(mx, sc.wmax[w]); }
     mn = uni(mn);
@@ -169,7 +205,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[PER], Scratch& sc
     int buf = 0;
     auto pick_bin = [&](uint32_t& b, uint32_t& above, uint32_t& tot_b) {
         // after the histogram of sc.hist[buf] is complete (uniform over the block)
-        __syncthreads();
+        sync_lds();
         clear_hist(sc, buf ^ 1);
         uint32_t tot = 0, sfx = 0;
         if (threadIdx.x < kBins) {
@@ -183,7 +219,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[PER], Scratch& sc
             }
             if (lane == 0) sc.wtot[wave] = sfx;
         }
-        __syncthreads();
+        sync_lds();
         if (threadIdx.x < kBins) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) sfx += w > wave ? sc.wtot[w] : 0u;
@@ -193,7 +229,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[PER], Scratch& sc
                 sc.pick[2] = tot;
             }
         }
-        __syncthreads();
+        sync_lds();
         b = uni(sc.pick[0]);
         above = uni(sc.pick[1]);
         tot_b = uni(sc.pick[2]);
@@ -251,10 +287,10 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[PER], Scratch& sc
         nlo = wave_min(nlo);
         nhi = wave_max(nhi);
         if (lane == 0) { sc.wmin[wave] = nlo; sc.wmax[wave] = nhi; }
-        __syncthreads();
+        sync_lds();
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) { nlo = min(nlo, sc.wmin[w]); nhi = max(nhi, sc.wmax[w]); }
-        __syncthreads();
+        sync_lds();
         lo = uni(nlo);
         hi = uni(nhi);
         if (in_bin == need) { whole = true; break; }
@@ -279,7 +315,7 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[PER], Scratch& sc
     if (!partial) { sel_w += in_bin_w; in_bin_w = 0; }
     // every wave's count of keys above T and of copies of T, from the histograms
     if (lane == 0) { sc.wsum[wave] = sel_w; sc.weq[wave] = in_bin_w; }
-    __syncthreads();
+    sync_lds();
     uint32_t slot = 0, eq_before = 0;
 #pragma unroll
     for (int w = 0; w < kWaves; ++w) {
@@ -308,6 +344,186 @@ __device__ __forceinline__ int select_regs(const uint32_t (&v)[PER], Scratch& sc
             if (s && my < (uint32_t)kK) emit(my, seg0 + 64 * r + lane, r);   // guard: never past k slots
             slot += __builtin_popcountll(sm);
         }
+    }
+    return kK;
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave, every lane active, without
+// LDS: shifts by 1, 2, 4 and 8 inside each row of 16 (lanes shifted in from
+// outside the row add 0), then row 15's sum into rows 1 and 3 and lane 31's
+// into rows 2 and 3 (DPP row broadcasts).
+__device__ __forceinline__ uint32_t wave_incl_scan(uint32_t v) {
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, true);   // row_shr:1
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, true);   // row_shr:2
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, true);   // row_shr:4
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, true);   // row_shr:8
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false);  // row_bcast:15
+    v += (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false);  // row_bcast:31
+    return v;
+}
+
+// The selection of select_regs (same items, same order, same result) with one
+// work-group histogram of 2048 bins per pass instead of a 256-bin histogram
+// per wave (the two views share Scratch::hist): each pass takes four
+// barriers, and integer-valued scores, whose candidates span a few thousand
+// units, usually resolve in one pass. Bins are linear in the score value while
+// the key range is wide, then the top 11 bits of key - lo; thread t owns bins
+// 4t .. 4t+3, and the bin holding the k-th key is found from a prefix sum over
+// the threads (a DPP scan inside each wave, the wave totals through LDS).
+constexpr int kWBins = kWaves * kBins;          // 2048
+
+template <int PER, typename Emit>
+__device__ __forceinline__ int select_wide(const uint32_t (&v)[PER], Scratch& sc, Emit emit,
+                                           uint32_t* t_out = nullptr) {
+    static_assert(kWBins == 4 * kThreads, "four bins per thread");
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    constexpr int SEG = 64 * PER;
+    const int seg0 = SEG * wave;
+    uint32_t* const H[2] = {&sc.hist[0][0][0], &sc.hist[1][0][0]};
+    // ---- count, min and max of the valid keys, one exchange
+    uint32_t c = 0, mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[r] != 0u));
+        if (v[r] != 0u) { mn = min(mn, v[r]); mx = max(mx, v[r]); }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) { sc.wsum[wave] = c; sc.wmin[wave] = mn; sc.wmax[wave] = mx; }
+    ((uint4*)H[0])[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    sync_lds();
+    uint32_t n_valid = 0, before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t x = sc.wsum[w];
+        n_valid += x;
+        before += w < wave ? x : 0u;
+        mn = min(mn, sc.wmin[w]);
+        mx = max(mx, sc.wmax[w]);
+    }
+    n_valid = uni(n_valid);
+    mn = uni(mn);
+    mx = uni(mx);
+    if (n_valid <= (uint32_t)kK && t_out == nullptr) {          // everything is kept
+        uint32_t slot = before;
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            const uint64_t m = __builtin_amdgcn_ballot_w64(v[r] != 0u);
+            if (v[r] != 0u) emit(slot + lanes_below(m), seg0 + 64 * r + lane, r);
+            slot += __builtin_popcountll(m);
+        }
+        return (int)n_valid;
+    }
+    // ---- the k-th largest key: candidates are the keys in [lo, hi] (the exact
+    // key range of the bin chosen last); a pass keeps the bin where the count of
+    // candidates in it and above first reaches `need`
+    uint32_t lo = mn, hi = mx, need = kK, in_bin = n_valid;
+    bool whole = false;                                         // the last bin was taken whole
+    int buf = 0;
+    while (lo != hi) {                                          // uniform
+        uint32_t* h = H[buf];
+        const float flo = key_value(lo), fspan = key_value(hi) - flo;
+        const bool by_value = hi - lo > 4u * kWBins && fspan > 1e-30f && fspan < 3.0e38f;
+        const float inv = by_value ? (float)kWBins / fspan : 0.f;
+        const int nb = 32 - __builtin_clz(hi - lo);
+        const int sh = nb > 11 ? nb - 11 : 0;
+        auto bin_of = [&](uint32_t key) __attribute__((always_inline)) {
+            return by_value ? min((int)((key_value(key) - flo) * inv), kWBins - 1) : (int)((key - lo) >> sh);
+        };
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            uint32_t key = v[r];
+            asm volatile("" : "+v"(key));                      // keep the bin math inside the loop
+            if (key != 0u && key >= lo && key <= hi) atomicAdd(&h[bin_of(key)], 1u);
+        }
+        ((uint4*)H[buf ^ 1])[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);   // for the next pass
+        sync_lds();
+        const uint4 hb = ((const uint4*)h)[threadIdx.x];
+        const uint32_t s4 = hb.x + hb.y + hb.z + hb.w;
+        const uint32_t incl = wave_incl_scan(s4);
+        if (lane == 63) sc.weq[wave] = incl;
+        sync_lds();
+        uint32_t above = 0;                                     // candidates in bins past this thread's 4
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) above += w > wave ? sc.weq[w] : 0u;
+        above += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;
+        const uint32_t cnt4[4] = {hb.w, hb.z, hb.y, hb.x};      // bins 4t+3 .. 4t
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (above < need && above + cnt4[q] >= need) {
+                sc.pick[0] = 4 * threadIdx.x + 3 - q;
+                sc.pick[1] = above;
+                sc.pick[2] = cnt4[q];
+            }
+            above += cnt4[q];
+        }
+        sync_lds();
+        const int b = (int)uni(sc.pick[0]);
+        need -= uni(sc.pick[1]);
+        in_bin = uni(sc.pick[2]);
+        uint32_t nlo = 0xffffffffu, nhi = 0u;
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            uint32_t key = v[r];
+            asm volatile("" : "+v"(key));
+            if (key != 0u && key >= lo && key <= hi && bin_of(key) == b) {
+                nlo = min(nlo, key);
+                nhi = max(nhi, key);
+            }
+        }
+        nlo = wave_min(nlo);
+        nhi = wave_max(nhi);
+        if (lane == 0) { sc.wmin[wave] = nlo; sc.wmax[wave] = nhi; }
+        sync_lds();
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) { nlo = min(nlo, sc.wmin[w]); nhi = max(nhi, sc.wmax[w]); }
+        lo = uni(nlo);
+        hi = uni(nhi);
+        buf ^= 1;
+        if (in_bin == need) { whole = true; break; }
+    }
+    const uint32_t T = lo;
+    if (t_out != nullptr) {
+        *t_out = T;
+        return 0;
+    }
+    // ---- emission: keys above T, then the first `need` copies of T (all of them
+    // when the bin was taken whole or need = in_bin), in item order
+    const bool partial = !whole && need != in_bin;
+    uint32_t sel_w = 0, eq_w = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        sel_w += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[r] != 0u && (partial ? v[r] > T : v[r] >= T)));
+        eq_w += partial ? __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[r] == T)) : 0;
+    }
+    if (lane == 0) { sc.wsum[wave] = sel_w; sc.weq[wave] = eq_w; }
+    sync_lds();
+    uint32_t slot = 0, eq_before = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        if (w < wave) {
+            const uint32_t eq = sc.weq[w];
+            const uint32_t taken = partial ? min(eq, need > eq_before ? need - eq_before : 0u) : 0u;
+            slot += sc.wsum[w] + taken;
+            eq_before += eq;
+        }
+    }
+    uint32_t eq_run = eq_before;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        bool sl;
+        if (!partial) {
+            sl = v[r] != 0u && v[r] >= T;
+        } else {
+            const bool in = v[r] != 0u;
+            const uint64_t eqm = __builtin_amdgcn_ballot_w64(in && v[r] == T);
+            sl = in && (v[r] > T || (v[r] == T && eq_run + lanes_below(eqm) < need));
+            eq_run += __builtin_popcountll(eqm);
+        }
+        const uint64_t sm = __builtin_amdgcn_ballot_w64(sl);
+        const uint32_t my = slot + lanes_below(sm);
+        if (sl && my < (uint32_t)kK) emit(my, seg0 + 64 * r + lane, r);   // never past k slots
+        slot += __builtin_popcountll(sm);
     }
     return kK;
 }
@@ -451,6 +667,326 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__
         const int cnt = full ? select_regs<kPer, true>(v, sc, em) : select_regs<kPer, false>(v, sc, em);
         if (threadIdx.x == 0) *(uint32_t*)Lst = (uint32_t)cnt;
     }
+}
+
+// ---- One work-group per row ---------------------------------------------------
+// For rows of up to 512 * GPL groups whose group maxima are known. The top-k
+// set lies in the groups whose maximum reaches the bound L, and with L the
+// kK-th largest maximum those are about kK groups whatever the row length
+// (kK x 128 bytes of scores), so one work-group selects the row from its maxima
+// and those groups' scores alone, with no list in global memory and no second
+// launch:
+//   1. every group maximum of the row into registers (group 512 i + t in
+//      thread t, round i); L = the kK-th largest of 4096 items, each the
+//      largest of GPL / 8 of a thread's maxima: at least kK positions score
+//      >= L, so every selected score is >= L. Fewer than kK items (a row of
+//      fewer groups): no bound.
+//   2. the groups whose maximum reaches L, in position order, into an LDS list
+//      (ballot ranks inside a round, per-wave counts for the offsets).
+//   3. those groups' scores, 512 groups (16K scores) per batch, the next
+//      batch's loads in flight while the current one is selected (the
+//      selection's barriers wait for LDS traffic only): a batch's keys >= thr
+//      are cut to their top kK (all of them, the usual case, pass straight
+//      through) and appended to a candidate list in position order. A list
+//      of more than kK is first cut to its top kK, and thr becomes one above
+//      the kK-th key: a later position with that key loses the tie.
+//   4. the list's top kK, written as ascending positions, -1 padded.
+template <int GPL>
+__global__ __launch_bounds__(kThreads) void topk_row(const float* __restrict__ scores, int64_t ld,
+                                                     const int32_t* __restrict__ q_pos,
+                                                     const float* __restrict__ gmax, int64_t ldg,
+                                                     int32_t* __restrict__ idx) {
+    constexpr int kMaxGroups = kThreads * GPL;
+    constexpr int IPL = kPerSmall;                 // bound items per thread: 4096 in all
+    constexpr int GPI = GPL / IPL;                 // maxima per item
+    static_assert(GPL % IPL == 0 && kMaxGroups <= 65536, "GPL");
+    constexpr int kWaveCap = 2 * kK / kWaves;      // candidates a wave's part holds (512)
+    constexpr int kWords = kMaxGroups / 64;
+    constexpr int kEnt = 128;                      // candidate-holding loads per wave per half sub-batch
+    struct Lds {
+        Scratch sc;
+        uint2 pend[2 * kK];                        // candidates (key, position), in position order
+        uint2 ptrash[kThreads];                    // where a lane writes what it does not keep
+        uint64_t bitmap[kWords];                   // passing groups, bit g % 64 of word g / 64
+        f32x4 ent_x[kWaves][kEnt];                 // per wave: loads that hold a candidate (scores,
+        int ent_p[kWaves][kEnt];                   // first position)
+        uint32_t wtot[kWaves];
+        uint32_t wmin[kWaves];
+        uint32_t wcnt[kWaves];                     // candidates per wave part (all ones: overflow)
+        uint16_t glist[kMaxGroups];                // passing groups, in position order
+    };
+    __shared__ __attribute__((aligned(16))) Lds s;
+    const int q = blockIdx.x;
+    const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+    const int64_t len = row_len(q_pos, q, ld);
+    const int ng = (int)((len + kGroup - 1) / kGroup);          // groups with a causal position
+    const float* grow = gmax + (int64_t)q * ldg;
+    const float* srow = scores + (int64_t)q * ld;
+    int32_t* out = idx + (int64_t)q * kK;
+
+    // ---- 1. the maxima and the bound
+    uint32_t gk[GPL];                                           // 0: no causal group
+#pragma unroll
+    for (int i = 0; i < GPL; ++i)
+        gk[i] = score_key(__builtin_nontemporal_load(grow + min(kThreads * i + t, ng - 1)));
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) gk[i] = kThreads * i + t < ng ? gk[i] : 0u;
+    uint32_t L = 0u;
+    {
+        uint32_t it[IPL];
+        uint32_t c = 0;
+#pragma unroll
+        for (int k = 0; k < IPL; ++k) {
+            uint32_t m = 0u;
+#pragma unroll
+            for (int j = 0; j < GPI; ++j) m = max(m, gk[GPI * k + j]);
+            it[k] = m;
+            c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(m != 0u));
+        }
+        const uint32_t n_items = uni(block_sum(uni(c), s.sc));
+        if (n_items >= (uint32_t)kK) select_wide<IPL>(it, s.sc, [](uint32_t, int, int) {}, &L);
+        L = uni(L);
+    }
+    // ---- 2. the groups that reach it, in position order. Round i's ballot in
+    // wave w covers groups 512 i + 64 w .. + 63: word 8 i + w of a bitmap in LDS.
+    // Thread t then owns bits GPL t .. GPL t + GPL - 1 (groups GPL t ..) and
+    // writes its groups after those of the lower threads (a scan of the counts).
+#pragma unroll
+    for (int i = 0; i < GPL; ++i) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(gk[i] != 0u && gk[i] >= L);
+        if (lane == 0) s.bitmap[kWaves * i + wave] = m;
+    }
+    sync_lds();
+    uint32_t base;
+    {
+        uint64_t word = s.bitmap[(t * GPL) / 64] >> ((t * GPL) % 64);
+        if constexpr (GPL < 64) word &= (1ull << GPL) - 1ull;
+        const uint32_t cw = (uint32_t)__builtin_popcountll(word);
+        const uint32_t incl = wave_incl_scan(cw);
+        if (lane == 63) s.wtot[wave] = incl;
+        sync_lds();
+        uint32_t before = 0, total = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) {
+            const uint32_t x = s.wtot[w];
+            before += w < wave ? x : 0u;
+            total += x;
+        }
+        uint32_t o = before + incl - cw;
+        while (word != 0ull) {                                  // about 5 groups per word at the bound
+            s.glist[o++] = (uint16_t)(GPL * t + __builtin_ctzll(word));
+            word &= word - 1;
+        }
+        base = total;
+    }
+    const int P = (int)uni(base);                               // >= kK with a bound, else ng
+    sync_lds();
+
+    // ---- 3. candidates of the passing groups. Usual case: wave w streams its own
+    // contiguous share of the list, 64 groups (2048 scores, 32 per lane) at a
+    // time with the next 64 in flight, and appends its keys >= L in position
+    // order to its own part of the LDS candidate list, without work-group
+    // barriers. The shares are contiguous and in order, so the parts,
+    // concatenated, are in position order.
+    auto gpos = [&](int gi, int e) __attribute__((always_inline)) {
+        return (int64_t)s.glist[min(gi, max(P, 1) - 1)] * kGroup + e;
+    };
+    {
+        const int gs = (int)(((int64_t)P * wave) / kWaves), ge = (int)(((int64_t)P * (wave + 1)) / kWaves);
+        uint2* part = s.pend + kWaveCap * wave;
+        uint32_t cnt = 0;
+        bool over = false;
+        const int nsb = (ge - gs + 63) / 64;
+        // sub-batch j, load r: lane l reads scores 4 (l % 8) .. + 3 of group
+        // gs + 64 j + 8 r + l / 8 (16 bytes; a start past the row's last full
+        // 4 is moved back to ld - 4, and its positions are masked by len).
+        // Scores are compared as floats against the bound's value (the order of
+        // the keys; -0 equals +0 as floats), so only the kept ones are turned
+        // into keys, at the end; the part holds (score bits, position).
+        constexpr int NL = 8;                                   // 16-byte loads per lane per sub-batch
+        const float Lf = L == 0u ? neg_inf() : key_value(L);
+        auto sb_groups = [&](int j, int (&g)[NL]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < NL; ++r) g[r] = s.glist[min(gs + 64 * j + 8 * r + (lane >> 3), ge - 1)];
+        };
+        auto sb_load = [&](const int (&g)[NL], f32x4 (&x)[NL]) __attribute__((always_inline)) {
+#pragma unroll
+            for (int r = 0; r < NL; ++r) {
+                const int64_t p = min((int64_t)g[r] * kGroup + 4 * (lane & 7), ld - 4);
+                x[r] = __builtin_nontemporal_load((const f32x4*)(srow + p));
+            }
+        };
+        const int len32 = (int)len;
+        f32x4 x[NL];
+        int g[NL];
+        if (nsb > 0) {
+            sb_groups(0, g);
+            sb_load(g, x);
+        }
+        for (int j = 0; j < nsb; ++j) {                        // uniform in the wave
+            f32x4 xc[NL];
+            int lim[NL], p0[NL];                                // positions p0 .. p0 + lim - 1 count
+#pragma unroll
+            for (int r = 0; r < NL; ++r) {
+                xc[r] = x[r];
+                p0[r] = g[r] * kGroup + 4 * (lane & 7);
+                lim[r] = gs + 64 * j + 8 * r + (lane >> 3) < ge ? len32 - p0[r] : 0;
+            }
+            if (j + 1 < nsb) {                                  // in flight while this one is compacted
+                sb_groups(j + 1, g);
+                sb_load(g, x);
+            }
+            // two levels, per half sub-batch: (a) the loads whose largest score
+            // reaches the bound (about 1 in 6) go, in order, to this wave's entry
+            // list; (b) lane e of a round of 64 entries keeps that entry's scores
+            // >= the bound after those of the lower lanes (a wave scan of the
+            // counts), in position order
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                uint32_t ecnt = 0;
+#pragma unroll
+                for (int r = 4 * h; r < 4 * h + 4; ++r) {
+                    const float m4 = fmaxf(fmaxf(xc[r][0], xc[r][1]), fmaxf(xc[r][2], xc[r][3]));
+                    const bool b = m4 >= Lf && lim[r] > 0;
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(b);
+                    const uint32_t slot = ecnt + lanes_below(m);
+                    if (b && slot < (uint32_t)kEnt) {
+                        s.ent_x[wave][slot] = xc[r];
+                        s.ent_p[wave][slot] = p0[r];
+                    }
+                    ecnt += (uint32_t)__builtin_popcountll(m);
+                }
+                over = over || ecnt > (uint32_t)kEnt;
+                for (uint32_t k = 0; k < ecnt && !over; k += 64) {      // uniform
+                    const uint32_t ei = min(k + lane, (uint32_t)kEnt - 1);
+                    const f32x4 xe = s.ent_x[wave][ei];
+                    const int pe = s.ent_p[wave][ei];
+                    const int le = k + lane < ecnt ? len32 - pe : 0;
+                    uint32_t f[4], c = 0;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        f[e] = (xe[e] >= Lf && e < le) ? 1u : 0u;
+                        c += f[e];
+                    }
+                    const uint32_t incl = wave_incl_scan(c);
+                    const uint32_t n = (uint32_t)__builtin_amdgcn_readlane((int)incl, 63);
+                    over = over || cnt + n > (uint32_t)kWaveCap;
+                    uint32_t at = cnt + incl - c;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        uint2* dst = (f[e] != 0u && !over) ? part + at : s.ptrash + t;
+                        *dst = make_uint2(__float_as_uint(xe[e]), (uint32_t)(pe + e));
+                        at += f[e];
+                    }
+                    cnt += n;
+                }
+            }
+        }
+        if (lane == 0) s.wcnt[wave] = over ? 0xffffffffu : cnt;
+    }
+    sync_lds();
+    uint32_t off[kWaves + 1];
+    bool any_over = false;
+    off[0] = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        const uint32_t c = s.wcnt[w];
+        any_over = any_over || c == 0xffffffffu;
+        off[w + 1] = off[w] + (c == 0xffffffffu ? 0u : c);
+    }
+    if (!any_over) {                                            // uniform
+        // ---- 4. the top kK of the concatenated parts (at most kWaves * kWaveCap = 4096)
+        uint32_t pv[kPerSmall], pp[kPerSmall];
+#pragma unroll
+        for (int r = 0; r < kPerSmall; ++r) {
+            const uint32_t i = 64 * kPerSmall * wave + 64 * r + lane;
+            int w = 0;
+#pragma unroll
+            for (int u = 1; u < kWaves; ++u) w += i >= off[u] ? 1 : 0;
+            const uint2 e = s.pend[kWaveCap * w + min(i - off[w], (uint32_t)kWaveCap - 1)];
+            pv[r] = i < off[kWaves] ? score_key(__uint_as_float(e.x)) : 0u;
+            pp[r] = e.y;
+        }
+        const int cnt = select_wide<kPerSmall>(pv, s.sc, [&](uint32_t slot, int, int r) {
+            out[slot] = (int32_t)pp[r];
+        });
+        write_final_pad(out, cnt);
+        return;
+    }
+
+    // ---- Fallback (a part overflowed: ties at the bound, or a row too short for
+    // one): the list's groups again, 512 per batch: item (r, lane) of wave w is
+    // position lane % 32 of group glist[512 b + 64 w + 2 r + lane / 32]; a
+    // batch's keys >= thr are cut to their top kK and appended to the candidate
+    // list in position order; a list of more than kK is first cut to its top kK
+    // and thr becomes one above the kK-th key (a later position with that key
+    // loses the tie).
+    auto load = [&](int b, float (&x)[kPer]) __attribute__((always_inline)) {
+#pragma unroll
+        for (int r = 0; r < kPer; ++r)
+            x[r] = __builtin_nontemporal_load(
+                srow + min(gpos(kThreads * b + 64 * wave + 2 * r + (lane >> 5), lane & 31), len - 1));
+    };
+    const int nb = (P + kThreads - 1) / kThreads;
+    uint32_t thr = L, npend = 0;
+    float x[kPer];
+    sync_lds();                                                 // every wave is done with the parts
+    if (nb > 0) load(0, x);
+    for (int b = 0; b < nb; ++b) {                              // uniform
+        uint32_t v[kPer];
+#pragma unroll
+        for (int r = 0; r < kPer; ++r) {
+            const int gi = kThreads * b + 64 * wave + 2 * r + (lane >> 5);
+            const uint32_t key = score_key(x[r]);
+            v[r] = (gi < P && gpos(gi, lane & 31) < len && key >= thr) ? key : 0u;
+        }
+        if (b + 1 < nb) load(b + 1, x);                         // in flight during this batch's selection
+        if (npend > (uint32_t)kK) {                             // uniform: cut the list to its top kK
+            sync_lds();                                         // the list is complete
+            uint32_t pv[kPerSmall], pp[kPerSmall];
+#pragma unroll
+            for (int r = 0; r < kPerSmall; ++r) {
+                const uint32_t i = 64 * kPerSmall * wave + 64 * r + lane;
+                const uint2 e = s.pend[min(i, npend - 1)];
+                pv[r] = i < npend ? e.x : 0u;
+                pp[r] = e.y;
+            }
+            uint32_t mn = 0xffffffffu;
+            // every thread read its items before the selection's first barrier, and
+            // nothing is emitted before it, so the list is rewritten in place
+            select_wide<kPerSmall>(pv, s.sc, [&](uint32_t slot, int, int r) {
+                s.pend[slot] = make_uint2(pv[r], pp[r]);
+                mn = min(mn, pv[r]);
+            });
+            mn = wave_min(mn);
+            if (lane == 0) s.wmin[wave] = mn;
+            sync_lds();
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w) mn = min(mn, s.wmin[w]);
+            thr = uni(mn) + 1u;                                 // the kK-th key, plus one
+            npend = kK;
+        }
+        const uint32_t at = npend;
+        sync_lds();                                             // the last selection's readers of sc are done
+        npend += (uint32_t)select_wide<kPer>(v, s.sc, [&](uint32_t slot, int i, int r) {
+            s.pend[at + slot] = make_uint2(v[r], (uint32_t)gpos(kThreads * b + (i >> 5), i & 31));
+        });
+        npend = uni(npend);
+    }
+    // the list's top kK
+    sync_lds();
+    uint32_t pv[kPerSmall], pp[kPerSmall];
+#pragma unroll
+    for (int r = 0; r < kPerSmall; ++r) {
+        const uint32_t i = 64 * kPerSmall * wave + 64 * r + lane;
+        const uint2 e = s.pend[min(i, max(npend, 1u) - 1)];
+        pv[r] = i < npend ? e.x : 0u;
+        pp[r] = e.y;
+    }
+    const int cnt = select_wide<kPerSmall>(pv, s.sc, [&](uint32_t slot, int, int r) {
+        out[slot] = (int32_t)pp[r];
+    });
+    write_final_pad(out, cnt);
 }
 
 // ---- Selection without a score buffer ----------------------------------------
@@ -746,6 +1282,8 @@ int n_chunks_of(int64_t ld) { return (int)((ld + kChunk - 1) / kChunk); }
 // Rows of at least kK full groups exist only when ld >= kK * kGroup.
 bool bounded(int64_t ld) { return ld >= (int64_t)kK * kGroup; }
 
+constexpr int kRowMaxGpl = 64;                  // topk_row: rows of up to 512 * 64 groups (2^20 positions)
+
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
 }  // namespace
@@ -779,6 +1317,19 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, in
     if (nc == 1) {
         hipLaunchKernelGGL(topk_chunk, dim3(1, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, 1,
                            (const uint32_t*)nullptr, (uint8_t*)nullptr, idx);
+        return hipGetLastError();
+    }
+    const int64_t ldg = group_max_ld(ld);
+    if (bounded(ld) && ldg <= (int64_t)kThreads * kRowMaxGpl) {
+        // rows of 64K to 1M positions: one work-group per row, over the group maxima
+        if (group_max == nullptr) {
+            float* gm = topk_group_max_area(ws, n_q, ld);
+            hipLaunchKernelGGL(topk_group_max, dim3(nc, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, gm, ldg);
+            group_max = gm;
+        }
+        const int gpl = ldg <= kThreads * 8 ? 8 : ldg <= kThreads * 16 ? 16 : ldg <= kThreads * 32 ? 32 : 64;
+        auto* kern = gpl == 8 ? topk_row<8> : gpl == 16 ? topk_row<16> : gpl == 32 ? topk_row<32> : topk_row<64>;
+        hipLaunchKernelGGL(kern, dim3(n_q), dim3(kThreads), 0, st, scores, ld, q_pos, group_max, ldg, idx);
         return hipGetLastError();
     }
     uint8_t* p = (uint8_t*)ws;

@@ -255,6 +255,17 @@ def test_topk_one_million_row():
     assert np.array_equal(idx, want)
 
 
+@pytest.mark.parametrize("n", [(1 << 20) - 28, 600_004])
+def test_topk_wide_rows_of_every_kind(n):
+    # rows up to 2^20 positions (one work-group per row over up to 32K group
+    # maxima; 2^20 - 28 leaves an odd number of maxima per row), each score
+    # distribution in one call, rows long and short, ties at the bound
+    rows = [W.score_matrix(kind, 1, n, seed=40 + i)[0] for i, kind in enumerate(W.SCORE_KINDS)]
+    s = torch.stack(rows + rows[:3])
+    pos = torch.tensor([n - 1, n - 2, n // 2, 65_535, 200_001, 70_000, 64_000, 3], dtype=torch.int32)
+    _topk_case(s, pos, f"wide rows n={n}")
+
+
 def test_topk_ld_padding_is_ignored():
     s = W.score_matrix("normal", 3, 5000, seed=2)
     s[:, 4990:] = 1e30                                 # beyond every q_pos: must not be selected
