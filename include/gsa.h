@@ -356,6 +356,24 @@ size_t gsa_group_workspace_bytes(int n_q, int64_t ld_scores, int k, int n_heads,
 gsa_status gsa_indexshare_group(const gsa_group_desc* desc, void* stream);
 
 /*
+ * gsa_indexshare_group_noalloc — gsa_indexshare_group for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops, and
+ * harnesses that forbid allocation. It takes no workspace: desc->workspace_dev
+ * and workspace_bytes are ignored, and the group runs on a static device scratch
+ * of gsa_noalloc_scratch_bytes() bytes (64 MiB) that the library holds on every
+ * GPU it runs on until the process ends. It calls no allocating routine. On the
+ * first call on a device it looks up that device's scratch address (once).
+ * Results are those of gsa_indexshare_group on the same descriptor (same kernels;
+ * the kernels need no scratch contents on entry).
+ * All calls on one GPU share its scratch: calls that overlap on one GPU (other
+ * streams, other threads) race and must not be issued.
+ * Errors: as gsa_indexshare_group; GSA_ERR_WORKSPACE when the group needs more
+ * than the scratch holds (e.g. thousands of queries over 128K positions).
+ */
+size_t gsa_noalloc_scratch_bytes(void);
+gsa_status gsa_indexshare_group_noalloc(const gsa_group_desc* desc, void* stream);
+
+/*
  * gsa_sparse_mla_attn_layers — gsa_sparse_mla_attn for n_layers layers that
  * attend over the same index buffer, the layers of one IndexShare group
  * ([Serving] §10: the indexer runs once per group, then every layer gathers

@@ -112,6 +112,8 @@ def _declare(lib):
                                           I, I, I, I, I64, F, P, SZ, P]),
         "gsa_quantize_latent_fp8": (I, [P, I64, P, P]),
         "gsa_indexshare_group": (I, [ctypes.POINTER(_GroupDesc), P]),
+        "gsa_indexshare_group_noalloc": (I, [ctypes.POINTER(_GroupDesc), P]),
+        "gsa_noalloc_scratch_bytes": (SZ, []),
         "gsa_layer_pattern": (I, [I, P]),
         "gsa_layer_stack": (I, [ctypes.POINTER(_StackDesc), P]),
     }
@@ -420,7 +422,7 @@ def sparse_mla_attn_layers(layers, q_seq, idx, scale=1.0 / 16.0, outs=None, work
 def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_idx=None,
                      q_scale=None, k_scale=None, scores=None, compute_index=True,
                      scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True,
-                     index_epoch=0, index_layer=0, index_tag=None):
+                     index_epoch=0, index_layer=0, index_tag=None, noalloc=False):
     """One IndexShare group: layers = [(q_lat, q_rope, kv), ...], F layer first.
     With compute_index the F layer's indexer + top-k write index_buf, then every
     layer attends over it. With block_table (int32 [batch, max_pages]) each kv is
@@ -428,10 +430,12 @@ def indexshare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k
     score buffer (as indexer_topk). index_tag (an IndexTag) records what
     index_buf holds: filled in when compute_index, checked against
     (index_epoch, index_layer, shape) when not and index_epoch != 0.
-    Returns [(out, lse)] per layer."""
+    noalloc: run as gsa_indexshare_group_noalloc (the library's static scratch
+    instead of a workspace; pass outs, and scores unless score_buffer=False, to
+    allocate nothing here either). Returns [(out, lse)] per layer."""
     call = prepare_group(layers, q_seq, index_buf, q_pos, q_idx, w, k_idx, q_scale, k_scale, scores,
                          compute_index, scale, workspace, outs, block_table, score_buffer, index_epoch,
-                         index_layer, index_tag)
+                         index_layer, index_tag, noalloc)
     call()
     return call.outs
 
@@ -451,10 +455,11 @@ class PreparedCall:
 def prepare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_idx=None,
                   q_scale=None, k_scale=None, scores=None, compute_index=True,
                   scale=1.0 / 16.0, workspace=None, outs=None, block_table=None, score_buffer=True,
-                  index_epoch=0, index_layer=0, index_tag=None):
+                  index_epoch=0, index_layer=0, index_tag=None, noalloc=False):
     """indexshare_group's arguments marshalled into a PreparedCall (nothing is
     enqueued until it is called). With no layers (compute_index only) the group
-    is the full layer's indexer and top-k alone."""
+    is the full layer's indexer and top-k alone. noalloc: the call is
+    gsa_indexshare_group_noalloc and no workspace is passed."""
     L = lib()
     n_q = q_seq.shape[0]
     kv0 = layers[0][2] if layers else None
@@ -487,9 +492,12 @@ def prepare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_id
     for i, ((ql, qr, kv), (o, s)) in enumerate(zip(layers, outs)):
         arr[i] = _MlaLayer(ql.data_ptr(), qr.data_ptr(), kv.data_ptr(), o.data_ptr(),
                            None if s is None else s.data_ptr())
-    nbytes = (group_workspace_bytes(n_q, ld, max(len(layers), 1), k) if compute_index
-              else mla_layers_workspace_bytes(n_q, len(layers), MLA_HEADS, k))
-    ws = _workspace(nbytes, dev, workspace)
+    if noalloc:
+        ws = None
+    else:
+        nbytes = (group_workspace_bytes(n_q, ld, max(len(layers), 1), k) if compute_index
+                  else mla_layers_workspace_bytes(n_q, len(layers), MLA_HEADS, k))
+        ws = _workspace(nbytes, dev, workspace)
     d = _GroupDesc()
     d.compute_index = 1 if compute_index else 0
     d.dt = FP8_E4M3 if fp8 else BF16
@@ -504,7 +512,8 @@ def prepare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_id
     d.index_buf_dev = index_buf.data_ptr()
     d.n_layers, d.layers = len(layers), ctypes.cast(arr, ctypes.POINTER(_MlaLayer))
     d.n_heads, d.scale = MLA_HEADS, scale
-    d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
+    if ws is not None:
+        d.workspace_dev, d.workspace_bytes = ws.data_ptr(), ws.numel()
     if pg is not None:
         d.paged_kv = ctypes.pointer(pg)
     d.kv_dt = FP8_E4M3 if kv0 is not None and _kv_fp8(kv0) else BF16
@@ -513,7 +522,8 @@ def prepare_group(layers, q_seq, index_buf, q_pos=None, q_idx=None, w=None, k_id
         d.index_tag = ctypes.pointer(index_tag)
     keep = (layers, q_seq, index_buf, q_pos, q_idx, w, k_idx, q_scale, k_scale, scores, ws, outs, arr, pg,
             block_table, index_tag)
-    return PreparedCall(L.gsa_indexshare_group, d, _stream(dev), outs, keep)
+    fn = L.gsa_indexshare_group_noalloc if noalloc else L.gsa_indexshare_group
+    return PreparedCall(fn, d, _stream(dev), outs, keep)
 
 
 def layer_pattern(n_layers=78):

@@ -4,6 +4,8 @@
 #include <stdarg.h>
 #include <stdio.h>
 
+#include <mutex>
+
 #include "../../include/gsa.h"
 #include "launch.h"
 
@@ -341,6 +343,37 @@ size_t gsa_stack_workspace_bytes(int n_q, int64_t ld, int k, int n_heads, int n_
 
 namespace {
 
+// ---- The group call without a workspace argument ------------------------------
+// Its workspace is this file-scope device array: every GPU the library runs on
+// holds its own copy (at its own address) until the process ends. Host code must
+// not pass the array's name to a kernel (on the host it is a stand-in, not a
+// device address): the address of the current device's copy is taken once per
+// device with hipGetSymbolAddress and used instead.
+constexpr size_t kScratchBytes = (size_t)64 << 20;
+static __device__ __attribute__((aligned(256))) uint8_t scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The current device's copy of `scratch` (looked up on the first call on that device).
+gsa_status scratch_for_current_device(void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(GSA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= kMaxDevices) return fail(GSA_ERR_UNSUPPORTED, "device %d: at most %d devices", dev, kMaxDevices);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || p == nullptr)
+            return fail(GSA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return GSA_OK;
+}
+
 // Host-side checks of one group; enqueues nothing.
 gsa_status validate_group(const gsa_group_desc* d) {
     if (d == nullptr) return fail(GSA_ERR_INVALID_ARG, "desc is NULL");
@@ -450,6 +483,39 @@ gsa_status gsa_indexshare_group(const gsa_group_desc* d, void* stream) {
     st = enqueue_group(d, (hipStream_t)stream);
     if (st == GSA_OK) {
         write_tag(d);
+        g_err[0] = 0;
+    }
+    return st;
+}
+
+size_t gsa_noalloc_scratch_bytes(void) { return kScratchBytes; }
+
+gsa_status gsa_indexshare_group_noalloc(const gsa_group_desc* d, void* stream) {
+    if (d == nullptr) return fail(GSA_ERR_INVALID_ARG, "desc is NULL");
+    // the workspace this group needs (the same rule as gsa_group_workspace_bytes;
+    // without a score buffer the top-k rows span n_cap rounded up to 4)
+    size_t need = 0;
+    if (d->n_layers >= 1) need = gsa_mla_layers_workspace_bytes(d->n_q, d->n_heads, d->k, d->n_layers);
+    if (d->compute_index) {
+        const int64_t ld = d->scores_dev != nullptr ? d->ld_scores : gsa::indexer_topk_ld(d->n_cap);
+        const size_t t = (d->n_q >= 1 && ld >= 1 && d->k == GSA_TOPK) ? gsa::topk_workspace_bytes(d->n_q, ld, d->k) : 0;
+        need = t > need ? t : need;
+    }
+    if (need > kScratchBytes)
+        return fail(GSA_ERR_WORKSPACE,
+                    "the group call without a workspace argument has a %zu-byte static scratch; this group needs %zu",
+                    kScratchBytes, need);
+    void* ws = nullptr;
+    gsa_status st = scratch_for_current_device(&ws);
+    if (st != GSA_OK) return st;
+    gsa_group_desc g = *d;
+    g.workspace_dev = ws;
+    g.workspace_bytes = kScratchBytes;
+    st = validate_group(&g);
+    if (st != GSA_OK) return st;
+    st = enqueue_group(&g, (hipStream_t)stream);
+    if (st == GSA_OK) {
+        write_tag(&g);
         g_err[0] = 0;
     }
     return st;
