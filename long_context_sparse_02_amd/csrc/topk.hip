@@ -691,18 +691,17 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__
 //      of more than kK is first cut to its top kK, and thr becomes one above
 //      the kK-th key: a later position with that key loses the tie.
 //   4. the list's top kK, written as ascending positions, -1 padded.
-template <int GPL>
-__global__ __launch_bounds__(kThreads) void topk_row(const float* __restrict__ scores, int64_t ld,
-                                                     const int32_t* __restrict__ q_pos,
-                                                     const float* __restrict__ gmax, int64_t ldg,
-                                                     int32_t* __restrict__ idx) {
+template <int GPL, int kEnt>
+__device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, int64_t ld,
+                                              const int32_t* __restrict__ q_pos,
+                                              const float* __restrict__ gmax, int64_t ldg,
+                                              int32_t* __restrict__ idx) {
     constexpr int kMaxGroups = kThreads * GPL;
     constexpr int IPL = kPerSmall;                 // bound items per thread: 4096 in all
     constexpr int GPI = GPL / IPL;                 // maxima per item
     static_assert(GPL % IPL == 0 && kMaxGroups <= 65536, "GPL");
     constexpr int kWaveCap = 2 * kK / kWaves;      // candidates a wave's part holds (512)
     constexpr int kWords = kMaxGroups / 64;
-    constexpr int kEnt = 128;                      // candidate-holding loads per wave per half sub-batch
     struct Lds {
         Scratch sc;
         uint2 pend[2 * kK];                        // candidates (key, position), in position order
@@ -842,15 +841,15 @@ __global__ __launch_bounds__(kThreads) void topk_row(const float* __restrict__ s
             // >= the bound after those of the lower lanes (a wave scan of the
             // counts), in position order
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
+            for (int h = 0; h < NL / 4; ++h) {
                 uint32_t ecnt = 0;
 #pragma unroll
                 for (int r = 4 * h; r < 4 * h + 4; ++r) {
-                    const float m4 = fmaxf(fmaxf(xc[r][0], xc[r][1]), fmaxf(xc[r][2], xc[r][3]));
-                    const bool b = m4 >= Lf && lim[r] > 0;
-                    const uint64_t m = __builtin_amdgcn_ballot_w64(b);
+                    const bool b = (xc[r][0] >= Lf) | (xc[r][1] >= Lf) | (xc[r][2] >= Lf) | (xc[r][3] >= Lf);
+                    const bool bl = b & (lim[r] > 0);
+                    const uint64_t m = __builtin_amdgcn_ballot_w64(bl);
                     const uint32_t slot = ecnt + lanes_below(m);
-                    if (b && slot < (uint32_t)kEnt) {
+                    if (bl & (slot < (uint32_t)kEnt)) {
                         s.ent_x[wave][slot] = xc[r];
                         s.ent_p[wave][slot] = p0[r];
                     }
@@ -865,7 +864,7 @@ __global__ __launch_bounds__(kThreads) void topk_row(const float* __restrict__ s
                     uint32_t f[4], c = 0;
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
-                        f[e] = (xe[e] >= Lf && e < le) ? 1u : 0u;
+                        f[e] = ((xe[e] >= Lf) & (e < le)) ? 1u : 0u;
                         c += f[e];
                     }
                     const uint32_t incl = wave_incl_scan(c);
@@ -987,6 +986,24 @@ __global__ __launch_bounds__(kThreads) void topk_row(const float* __restrict__ s
         out[slot] = (int32_t)pp[r];
     });
     write_final_pad(out, cnt);
+}
+
+// kEnt: candidate-holding loads a wave's entry list holds per half sub-batch.
+// The default build keeps one work-group per CU (about 215 registers); the
+// capped build (128 registers, spills in the rare paths, 72 KiB of LDS) runs two
+// per CU, for launches of many rows (prefill).
+template <int GPL>
+__global__ __launch_bounds__(kThreads) void topk_row(const float* __restrict__ scores, int64_t ld,
+                                                     const int32_t* __restrict__ q_pos,
+                                                     const float* __restrict__ gmax, int64_t ldg,
+                                                     int32_t* __restrict__ idx) {
+    topk_row_body<GPL, 128>(scores, ld, q_pos, gmax, ldg, idx);
+}
+template <int GPL>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_row_wide(
+    const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_pos,
+    const float* __restrict__ gmax, int64_t ldg, int32_t* __restrict__ idx) {
+    topk_row_body<GPL, 64>(scores, ld, q_pos, gmax, ldg, idx);
 }
 
 // ---- Selection without a score buffer ----------------------------------------
@@ -1328,7 +1345,8 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, in
             group_max = gm;
         }
         const int gpl = ldg <= kThreads * 8 ? 8 : ldg <= kThreads * 16 ? 16 : ldg <= kThreads * 32 ? 32 : 64;
-        auto* kern = gpl == 8 ? topk_row<8> : gpl == 16 ? topk_row<16> : gpl == 32 ? topk_row<32> : topk_row<64>;
+        auto* kern = gpl == 8 ? (n_q >= kWideRows ? topk_row_wide<8> : topk_row<8>)
+                   : gpl == 16 ? topk_row<16> : gpl == 32 ? topk_row<32> : topk_row<64>;
         hipLaunchKernelGGL(kern, dim3(n_q), dim3(kThreads), 0, st, scores, ld, q_pos, group_max, ldg, idx);
         return hipGetLastError();
     }
