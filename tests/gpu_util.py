@@ -1,4 +1,5 @@
 """Helpers shared by the GPU parity tests (marshalling between torch and numpy)."""
+import os
 import sys
 
 import numpy as np
@@ -41,3 +42,15 @@ def max_abs(a, b):
     with np.errstate(invalid="ignore"):                  # inf - inf where both_inf masks it
         d = np.where(both_inf, 0.0, np.abs(a - b))
     return float(np.max(d)) if d.size else 0.0
+
+
+# Largest attention errors against the oracle per test (printed at the end of the
+# run by conftest.py, so that a run's log records the margin under the bar).
+ERRORS = {}
+
+
+def note(eo, el=0.0):
+    """Record the max-abs output and lse errors of an attention check for the running test."""
+    label = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
+    a, b = ERRORS.get(label, (0.0, 0.0))
+    ERRORS[label] = (max(a, float(eo)), max(b, float(el)))

@@ -10,7 +10,7 @@ import torch
 import long_context_sparse_02_amd as gsa
 import oracle
 import workloads as W
-from gpu_util import ATOL_LSE, ATOL_OUT, dev, max_abs, np32, say
+from gpu_util import ATOL_LSE, ATOL_OUT, dev, max_abs, np32, say, note
 
 pytestmark = pytest.mark.gpu
 
@@ -78,6 +78,7 @@ def test_fp8kv_attention_matches_oracle(n_q, batch, n_layers):
         wo, ws = oracle.sparse_mla(np32(ql), np32(qr), deq, np32(q_seq), np32(idx), 1 / 16)
         eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
         say(f"  layer {l}: out err {eo:.2e} lse err {el:.2e}")
+        note(eo, el)
         assert eo <= ATOL_OUT and el <= ATOL_LSE
 
 
@@ -116,4 +117,6 @@ def test_fp8kv_group_and_stack_match_oracle():
                                              np32(gi.q_pos), deq)
     assert np.array_equal(np32(idx), oidx)
     for (o, s), (wo, ws) in zip(outs, oouts):
-        assert max_abs(np32(o), wo) <= ATOL_OUT and max_abs(np32(s), ws) <= ATOL_LSE
+        eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
+        note(eo, el)
+        assert eo <= ATOL_OUT and el <= ATOL_LSE

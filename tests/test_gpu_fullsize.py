@@ -19,7 +19,7 @@ import bench
 import long_context_sparse_02_amd as gsa
 import oracle
 import workloads as W
-from gpu_util import ATOL_LSE, ATOL_OUT, assert_scores_equal, dev, max_abs, np32, say
+from gpu_util import ATOL_LSE, ATOL_OUT, assert_scores_equal, dev, max_abs, np32, say, note
 
 pytestmark = pytest.mark.gpu
 SEED = 11
@@ -94,6 +94,7 @@ def check_sampled_queries(wl, inp, bufs, qis, mla_layers, full_ordinals):
                                      np.zeros(1, np.int32), local, bench.SCALE)
             go, gs = bufs["outs"][l]
             eo, el = max_abs(np32(go[qi:qi + 1]), o), max_abs(np32(gs[qi:qi + 1]), s)
+            note(eo, el)
             assert eo <= ATOL_OUT and el <= ATOL_LSE, f"{wl.name} query {qi} layer {l}: {eo:.2e} {el:.2e}"
         say(f"{wl.name}: query {qi} (seq {b}, pos {pos[0]}) matches the oracle")
 

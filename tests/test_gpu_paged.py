@@ -10,7 +10,7 @@ import torch
 import long_context_sparse_02_amd as gsa
 import oracle
 import workloads as W
-from gpu_util import ATOL_LSE, ATOL_OUT, dev, max_abs, np32, say
+from gpu_util import ATOL_LSE, ATOL_OUT, dev, max_abs, np32, say, note
 
 pytestmark = pytest.mark.gpu
 
@@ -68,6 +68,7 @@ def test_paged_attention_matches_contiguous_and_oracle(page_size, n_layers, n_q,
         wo, ws = oracle.sparse_mla(np32(ql), np32(qr), view, np32(q_seq), np32(idx), 1 / 16)
         eo, el = max_abs(np32(op), wo), max_abs(np32(sp), ws)
         say(f"  layer {l}: out err {eo:.2e} lse err {el:.2e}")
+        note(eo, el)
         assert eo <= ATOL_OUT and el <= ATOL_LSE
 
 

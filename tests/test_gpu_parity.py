@@ -9,7 +9,7 @@ import torch
 import long_context_sparse_02_amd as gsa
 import oracle
 import workloads as W
-from gpu_util import ATOL_LSE, ATOL_OUT, assert_scores_equal, dev, max_abs, np32, say
+from gpu_util import ATOL_LSE, ATOL_OUT, assert_scores_equal, dev, max_abs, np32, say, note
 
 pytestmark = pytest.mark.gpu
 
@@ -292,6 +292,7 @@ def _mla_case(n_q, batch, n_ctx, seed, idx_fn=None):
     o_want, l_want = oracle.sparse_mla(np32(q_lat), np32(q_rope), np32(kv), np32(q_seq), np32(idx), 1 / 16)
     eo, el = max_abs(np32(out), o_want), max_abs(np32(lse), l_want)
     say(f"mla n_q={n_q}: max|out-oracle|={eo:.2e} max|lse-oracle|={el:.2e}")
+    note(eo, el)
     assert eo <= ATOL_OUT and el <= ATOL_LSE
     return out, lse
 
@@ -336,7 +337,9 @@ def test_mla_out_of_range_indices_are_skipped_like_minus_one():
     assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
     assert torch.all(a[0][3] == 0) and torch.all(torch.isneginf(a[1][3]))
     o_want, l_want = oracle.sparse_mla(np32(q_lat), np32(q_rope), np32(kv), np32(q_seq), np32(idx_clean), 1 / 16)
-    assert max_abs(np32(a[0]), o_want) <= ATOL_OUT and max_abs(np32(a[1]), l_want) <= ATOL_LSE
+    eo, el = max_abs(np32(a[0]), o_want), max_abs(np32(a[1]), l_want)
+    note(eo, el)
+    assert eo <= ATOL_OUT and el <= ATOL_LSE
 
 
 def test_mla_short_prefix_equals_dense():
@@ -371,6 +374,7 @@ def _group_case(wl, seed, dtype="bf16"):
     for l, ((o, s), (wo, ws)) in enumerate(zip(outs, oouts)):
         eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
         say(f"group layer {l}: max|out|err={eo:.2e} lse err={el:.2e}")
+        note(eo, el)
         assert eo <= ATOL_OUT and el <= ATOL_LSE
     return idx, outs
 
@@ -450,5 +454,6 @@ def test_sparse_mla_layers_launch_matches_oracle(n_layers, n_q, batch):
         wo, ws = oracle.sparse_mla(np32(ql), np32(qr), np32(kv), np32(q_seq), np32(idx), 1 / 16)
         eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
         say(f"layers launch {n_layers}x{n_q}: layer {l} out err {eo:.2e} lse err {el:.2e}")
+        note(eo, el)
         assert eo <= ATOL_OUT and el <= ATOL_LSE
     del q_pos

@@ -9,7 +9,7 @@ import torch
 import long_context_sparse_02_amd as gsa
 import oracle
 import workloads as W
-from gpu_util import ATOL_LSE, ATOL_OUT, dev, max_abs, np32, say
+from gpu_util import ATOL_LSE, ATOL_OUT, dev, max_abs, np32, say, note
 
 pytestmark = pytest.mark.gpu
 
@@ -60,6 +60,7 @@ def _check_against_oracle(n_layers, fulls, q_seq, q_pos, idx_in, mla_in, index_b
     for l, ((o, s), (wo, ws)) in enumerate(zip(outs, o_outs)):
         eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
         worst = max(worst, eo, el)
+        note(eo, el)
         assert eo <= ATOL_OUT and el <= ATOL_LSE, f"layer {l}: out err {eo:.2e}, lse err {el:.2e}"
     say(f"stack: all {n_layers} layers within tolerance, worst {worst:.2e}")
 

@@ -10,7 +10,7 @@ import torch
 import long_context_sparse_02_amd as gsa
 import oracle
 import workloads as W
-from gpu_util import ATOL_LSE, ATOL_OUT, dev, max_abs, np32, say
+from gpu_util import ATOL_LSE, ATOL_OUT, dev, max_abs, np32, say, note
 
 pytestmark = pytest.mark.gpu
 
@@ -59,7 +59,9 @@ def test_noalloc_group_matches_the_workspace_call_twice():
         assert np.array_equal(np32(idx_n), want_idx)
         for l, (ql, qr, kv) in enumerate(g.layers):
             o, s = oracle.sparse_mla(np32(ql), np32(qr), np32(kv), np32(g.q_seq), want_idx, 1 / 16)
-            assert max_abs(np32(outs_n[l][0]), o) <= ATOL_OUT and max_abs(np32(outs_n[l][1]), s) <= ATOL_LSE
+            eo, el = max_abs(np32(outs_n[l][0]), o), max_abs(np32(outs_n[l][1]), s)
+            note(eo, el)
+            assert eo <= ATOL_OUT and el <= ATOL_LSE
 
 
 def test_noalloc_group_rejects_what_the_scratch_cannot_hold():
