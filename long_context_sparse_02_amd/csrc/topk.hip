@@ -35,6 +35,8 @@
 //   topk_rescore
 //               the selection without a score buffer: the groups that reach the
 //               bound are rescored with the score kernel's arithmetic.
+#include <atomic>
+#include <chrono>
 #include <type_traits>
 
 #include "device_common.h"
@@ -669,33 +671,62 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__
     }
 }
 
-// ---- One work-group per row ---------------------------------------------------
+// ---- One work-group per row, or a few per row -------------------------------
 // For rows of up to 512 * GPL groups whose group maxima are known. The top-k
 // set lies in the groups whose maximum reaches the bound L, and with L the
 // kK-th largest maximum those are about kK groups whatever the row length
-// (kK x 128 bytes of scores), so one work-group selects the row from its maxima
-// and those groups' scores alone, with no list in global memory and no second
-// launch:
+// (kK x 128 bytes of scores), so a row is selected from its maxima and those
+// groups' scores alone:
 //   1. every group maximum of the row into registers (group 512 i + t in
 //      thread t, round i); L = the kK-th largest of 4096 items, each the
 //      largest of GPL / 8 of a thread's maxima: at least kK positions score
 //      >= L, so every selected score is >= L. Fewer than kK items (a row of
 //      fewer groups): no bound.
-//   2. the groups whose maximum reaches L, in position order, into an LDS list
-//      (ballot ranks inside a round, per-wave counts for the offsets).
-//   3. those groups' scores, 512 groups (16K scores) per batch, the next
-//      batch's loads in flight while the current one is selected (the
-//      selection's barriers wait for LDS traffic only): a batch's keys >= thr
-//      are cut to their top kK (all of them, the usual case, pass straight
-//      through) and appended to a candidate list in position order. A list
-//      of more than kK is first cut to its top kK, and thr becomes one above
-//      the kK-th key: a later position with that key loses the tie.
-//   4. the list's top kK, written as ascending positions, -1 padded.
-template <int GPL, int kEnt>
+//   2. the groups whose maximum reaches L, in position order, into an LDS list.
+//   3. the scores of a contiguous share of the list, each wave its own part of
+//      the share, compacted into per-wave candidate parts in position order.
+//   4. the top kK of the candidates, written as ascending positions, -1 padded.
+// Split rows (few rows per launch): work-groups (q, p), p < pn, all find the
+// same L and list, each streams share p of the list (step 3) and writes its
+// candidates to its region of the workspace, then sets its flag to the
+// launch's tag; a work-group that then finds every flag of the row set runs
+// step 4 over all regions (two may, with identical results) and clears the
+// flags, so a replay of the same launch starts clean and a workspace of any
+// prior contents works. The hand-over uses device-scope stores and loads
+// (written through to, and read from, the device's coherence point), and each
+// wave waits for its stores to complete before the flag is set, so no L2
+// write-back (a release fence: microseconds per wave) is needed. A part that
+// overflows (ties at the bound, rows without one), or more than 2 kK / pn
+// candidates in a share, sends the row to a batched fallback over the whole
+// list in the work-group that runs step 4.
+struct SplitArgs {
+    unsigned long long* flags;   // [row][share]: the tag of the launch that filled the share
+    uint8_t* regions;            // [row][share]: candidate count, then (score bits, position) pairs
+    unsigned long long tag;      // this launch's tag (never 0)
+    int pn;                      // shares per row: 2, 4 or 8
+};
+constexpr int kMaxShares = 8;
+constexpr size_t kRegionHead = 128;
+constexpr size_t kRegionBytes = kRegionHead + (size_t)2 * kK * sizeof(uint2);
+
+__device__ __forceinline__ void store_dev(unsigned long long* p, unsigned long long v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ unsigned long long load_dev(const unsigned long long* p) {
+    return __hip_atomic_load(const_cast<unsigned long long*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// this wave's stores and loads are complete (also a compiler barrier)
+__device__ __forceinline__ void drain_vm() {
+    asm volatile("" ::: "memory");
+    wait_vmcnt<0>();
+    asm volatile("" ::: "memory");
+}
+
+template <int GPL, int kEnt, bool kSplit>
 __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, int64_t ld,
                                               const int32_t* __restrict__ q_pos,
                                               const float* __restrict__ gmax, int64_t ldg,
-                                              int32_t* __restrict__ idx) {
+                                              int32_t* __restrict__ idx, const SplitArgs& sa) {
     constexpr int kMaxGroups = kThreads * GPL;
     constexpr int IPL = kPerSmall;                 // bound items per thread: 4096 in all
     constexpr int GPI = GPL / IPL;                 // maxima per item
@@ -716,6 +747,7 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
     };
     __shared__ __attribute__((aligned(16))) Lds s;
     const int q = blockIdx.x;
+    const int share = kSplit ? (int)blockIdx.y : 0, pn = kSplit ? sa.pn : 1;
     const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
     const int64_t len = row_len(q_pos, q, ld);
     const int ng = (int)((len + kGroup - 1) / kGroup);          // groups with a causal position
@@ -782,16 +814,17 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
     sync_lds();
 
     // ---- 3. candidates of the passing groups. Usual case: wave w streams its own
-    // contiguous share of the list, 64 groups (2048 scores, 32 per lane) at a
-    // time with the next 64 in flight, and appends its keys >= L in position
-    // order to its own part of the LDS candidate list, without work-group
-    // barriers. The shares are contiguous and in order, so the parts,
-    // concatenated, are in position order.
+    // contiguous part of the work-group's share of the list, 64 groups (2048
+    // scores, 32 per lane) at a time with the next 64 in flight, and appends its
+    // keys >= L in position order to its own part of the LDS candidate list,
+    // without work-group barriers. The parts and shares are contiguous and in
+    // order, so the parts, concatenated, are in position order.
     auto gpos = [&](int gi, int e) __attribute__((always_inline)) {
         return (int64_t)s.glist[min(gi, max(P, 1) - 1)] * kGroup + e;
     };
     {
-        const int gs = (int)(((int64_t)P * wave) / kWaves), ge = (int)(((int64_t)P * (wave + 1)) / kWaves);
+        const int64_t s0 = (int64_t)P * share / pn, s1 = (int64_t)P * (share + 1) / pn;
+        const int gs = (int)(s0 + (s1 - s0) * wave / kWaves), ge = (int)(s0 + (s1 - s0) * (wave + 1) / kWaves);
         uint2* part = s.pend + kWaveCap * wave;
         uint32_t cnt = 0;
         bool over = false;
@@ -893,7 +926,73 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
         any_over = any_over || c == 0xffffffffu;
         off[w + 1] = off[w] + (c == 0xffffffffu ? 0u : c);
     }
-    if (!any_over) {                                            // uniform
+    if constexpr (kSplit) {
+        // ---- hand-over: this share's candidates (compacted, in position order)
+        // and their count (all ones: a part overflowed) to its region, then its flag
+        uint8_t* reg = sa.regions + ((size_t)q * pn + share) * kRegionBytes;
+        unsigned long long* ent = (unsigned long long*)(reg + kRegionHead);
+        unsigned long long* flag = sa.flags + (size_t)q * pn;
+        const uint32_t total = off[kWaves];
+        if (!any_over) {
+            for (uint32_t i = t; i < total; i += kThreads) {
+                int w = 0;
+#pragma unroll
+                for (int u = 1; u < kWaves; ++u) w += i >= off[u] ? 1 : 0;
+                const uint2 e = s.pend[kWaveCap * w + (i - off[w])];
+                store_dev(ent + i, ((unsigned long long)e.y << 32) | e.x);
+            }
+        }
+        if (t == 0) store_dev((unsigned long long*)reg, any_over ? 0xffffffffull : (unsigned long long)total);
+        drain_vm();                                             // every store of this wave is complete
+        sync_lds();                                             // ... and of every wave
+        if (wave == 0) {                                        // lane u reads share u's flag
+            if (lane == 0) store_dev(flag + share, sa.tag);
+            drain_vm();
+            const unsigned long long f = load_dev(flag + (lane < pn ? lane : 0));
+            const uint64_t set = __builtin_amdgcn_ballot_w64(lane >= pn || f == sa.tag);
+            if (lane == 0) s.wtot[0] = set == ~0ull ? 1u : 0u;
+        }
+        sync_lds();
+        if (uni(s.wtot[0]) == 0u) return;                       // uniform: a later share finishes the row
+        // ---- 4. the top kK of every share's candidates: share u's first W
+        // entries are items u W .. u W + W - 1, in position order across shares
+        static_assert(2 * kK == 1 << 12, "two selections' worth of items is 2^12");
+        const int wsh = 12 - __builtin_ctz((unsigned)pn);       // W = 2 kK / pn = 2^wsh
+        const int W = 1 << wsh;
+        const uint8_t* rrow = sa.regions + (size_t)q * pn * kRegionBytes;
+        unsigned long long x[kPerSmall];
+#pragma unroll
+        for (int r = 0; r < kPerSmall; ++r) {
+            const int i = 64 * kPerSmall * wave + 64 * r + lane;     // < 2 kK = pn W
+            x[r] = load_dev((const unsigned long long*)(rrow + (size_t)(i >> wsh) * kRegionBytes + kRegionHead) +
+                            (i & (W - 1)));
+        }
+        uint32_t cnt_u[kMaxShares];
+#pragma unroll
+        for (int u = 0; u < kMaxShares; ++u)
+            cnt_u[u] = (uint32_t)load_dev((const unsigned long long*)(rrow + (size_t)(u < pn ? u : 0) * kRegionBytes));
+        bool fits = true;
+#pragma unroll
+        for (int u = 0; u < kMaxShares; ++u) fits = fits && cnt_u[u] <= (uint32_t)W;   // all ones: overflow
+        if (t < pn) store_dev(flag + t, 0ull);                  // every share has arrived: clear for the next launch
+        if (fits) {                                             // uniform
+            uint32_t pv[kPerSmall], pp[kPerSmall];
+#pragma unroll
+            for (int r = 0; r < kPerSmall; ++r) {
+                const int i = 64 * kPerSmall * wave + 64 * r + lane;
+                uint32_t c = cnt_u[0];
+#pragma unroll
+                for (int u = 1; u < kMaxShares; ++u) c = (i >> wsh) == u ? cnt_u[u] : c;
+                pv[r] = (uint32_t)(i & (W - 1)) < c ? score_key(__uint_as_float((uint32_t)x[r])) : 0u;
+                pp[r] = (uint32_t)(x[r] >> 32);
+            }
+            const int cnt = select_wide<kPerSmall>(pv, s.sc, [&](uint32_t slot, int, int r) {
+                out[slot] = (int32_t)pp[r];
+            });
+            write_final_pad(out, cnt);
+            return;
+        }
+    } else if (!any_over) {                                     // uniform
         // ---- 4. the top kK of the concatenated parts (at most kWaves * kWaveCap = 4096)
         uint32_t pv[kPerSmall], pp[kPerSmall];
 #pragma unroll
@@ -914,28 +1013,32 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
     }
 
     // ---- Fallback (a part overflowed: ties at the bound, or a row too short for
-    // one): the list's groups again, 512 per batch: item (r, lane) of wave w is
-    // position lane % 32 of group glist[512 b + 64 w + 2 r + lane / 32]; a
-    // batch's keys >= thr are cut to their top kK and appended to the candidate
-    // list in position order; a list of more than kK is first cut to its top kK
-    // and thr becomes one above the kK-th key (a later position with that key
-    // loses the tie).
-    auto load = [&](int b, float (&x)[kPer]) __attribute__((always_inline)) {
+    // one; split rows: also more than 2 kK candidates in all): the whole list's
+    // groups again, 256 per batch (a smaller batch keeps this rare path's
+    // registers below the usual path's): item (r, lane) of wave w is position
+    // lane % 32 of group glist[256 b + 32 w + 2 r + lane / 32]; a batch's keys
+    // >= thr are cut to their top kK and appended to the candidate list in
+    // position order; a list of more than kK is first cut to its top kK and thr
+    // becomes one above the kK-th key (a later position with that key loses the
+    // tie).
+    constexpr int kFb = 16;                                     // items per lane
+    constexpr int kGb = kThreads * kFb / kGroup;                // groups per batch
+    auto load = [&](int b, float (&x)[kFb]) __attribute__((always_inline)) {
 #pragma unroll
-        for (int r = 0; r < kPer; ++r)
+        for (int r = 0; r < kFb; ++r)
             x[r] = __builtin_nontemporal_load(
-                srow + min(gpos(kThreads * b + 64 * wave + 2 * r + (lane >> 5), lane & 31), len - 1));
+                srow + min(gpos(kGb * b + 2 * kFb * wave + 2 * r + (lane >> 5), lane & 31), len - 1));
     };
-    const int nb = (P + kThreads - 1) / kThreads;
+    const int nb = (P + kGb - 1) / kGb;
     uint32_t thr = L, npend = 0;
-    float x[kPer];
+    float x[kFb];
     sync_lds();                                                 // every wave is done with the parts
     if (nb > 0) load(0, x);
     for (int b = 0; b < nb; ++b) {                              // uniform
-        uint32_t v[kPer];
+        uint32_t v[kFb];
 #pragma unroll
-        for (int r = 0; r < kPer; ++r) {
-            const int gi = kThreads * b + 64 * wave + 2 * r + (lane >> 5);
+        for (int r = 0; r < kFb; ++r) {
+            const int gi = kGb * b + 2 * kFb * wave + 2 * r + (lane >> 5);
             const uint32_t key = score_key(x[r]);
             v[r] = (gi < P && gpos(gi, lane & 31) < len && key >= thr) ? key : 0u;
         }
@@ -967,8 +1070,8 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
         }
         const uint32_t at = npend;
         sync_lds();                                             // the last selection's readers of sc are done
-        npend += (uint32_t)select_wide<kPer>(v, s.sc, [&](uint32_t slot, int i, int r) {
-            s.pend[at + slot] = make_uint2(v[r], (uint32_t)gpos(kThreads * b + (i >> 5), i & 31));
+        npend += (uint32_t)select_wide<kFb>(v, s.sc, [&](uint32_t slot, int i, int r) {
+            s.pend[at + slot] = make_uint2(v[r], (uint32_t)gpos(kGb * b + (i >> 5), i & 31));
         });
         npend = uni(npend);
     }
@@ -997,13 +1100,21 @@ __global__ __launch_bounds__(kThreads) void topk_row(const float* __restrict__ s
                                                      const int32_t* __restrict__ q_pos,
                                                      const float* __restrict__ gmax, int64_t ldg,
                                                      int32_t* __restrict__ idx) {
-    topk_row_body<GPL, 128>(scores, ld, q_pos, gmax, ldg, idx);
+    topk_row_body<GPL, 128, false>(scores, ld, q_pos, gmax, ldg, idx, SplitArgs{});
 }
 template <int GPL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_row_wide(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_pos,
     const float* __restrict__ gmax, int64_t ldg, int32_t* __restrict__ idx) {
-    topk_row_body<GPL, 64>(scores, ld, q_pos, gmax, ldg, idx);
+    topk_row_body<GPL, 64, false>(scores, ld, q_pos, gmax, ldg, idx, SplitArgs{});
+}
+// grid (rows, shares)
+template <int GPL>
+__global__ __launch_bounds__(kThreads) void topk_row_split(const float* __restrict__ scores, int64_t ld,
+                                                           const int32_t* __restrict__ q_pos,
+                                                           const float* __restrict__ gmax, int64_t ldg,
+                                                           int32_t* __restrict__ idx, SplitArgs sa) {
+    topk_row_body<GPL, 128, true>(scores, ld, q_pos, gmax, ldg, idx, sa);
 }
 
 // ---- Selection without a score buffer ----------------------------------------
@@ -1303,6 +1414,31 @@ constexpr int kRowMaxGpl = 64;                  // topk_row: rows of up to 512 *
 
 size_t align256(size_t b) { return (b + 255) & ~(size_t)255; }
 
+bool row_path(int64_t ld) { return bounded(ld) && group_max_ld(ld) <= (int64_t)kThreads * kRowMaxGpl; }
+
+// Shares per row for the row kernels: launches of at most 128 rows split each
+// row in 2, 4 or 8 so that at most 256 work-groups (one per CU) run.
+int row_shares(int n_q) {
+    int p = 1;
+    while (2 * p <= kMaxShares && n_q * 2 * p <= 256) p *= 2;
+    return p;
+}
+
+// Split-row area of the workspace, after the bounds and the group maxima: the
+// flags, then the regions.
+size_t split_offset(int n_q, int64_t ld) {
+    return align256((size_t)n_q * 4) + align256((size_t)n_q * group_max_ld(ld) * 4);
+}
+
+// Launch tags: a new one per launch, from a per-process start that differs
+// between processes; never 0 (a cleared flag).
+unsigned long long next_tag() {
+    static std::atomic<unsigned long long> counter{
+        (unsigned long long)std::chrono::steady_clock::now().time_since_epoch().count() * 0x9E3779B97F4A7C15ull};
+    const unsigned long long t = counter.fetch_add(1ull);
+    return t != 0ull ? t : counter.fetch_add(1ull);
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int n_q, int64_t ld, int k) {
@@ -1318,6 +1454,11 @@ size_t topk_workspace_bytes(int n_q, int64_t ld, int k) {
     for (int64_t n = level_lists(nc); ; n = level_lists(n)) {       // merge fallback rounds
         b += (size_t)n_q * n * kListBytes;
         if (n <= 1) break;
+    }
+    const int pn = row_shares(n_q);
+    if (row_path(ld) && pn > 1) {                                   // split rows: counters and regions
+        const size_t sp = split_offset(n_q, ld) + align256((size_t)n_q * pn * 8) + (size_t)n_q * pn * kRegionBytes;
+        b = b > sp ? b : sp;
     }
     return b;
 }
@@ -1337,14 +1478,24 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, in
         return hipGetLastError();
     }
     const int64_t ldg = group_max_ld(ld);
-    if (bounded(ld) && ldg <= (int64_t)kThreads * kRowMaxGpl) {
-        // rows of 64K to 1M positions: one work-group per row, over the group maxima
+    if (row_path(ld)) {
+        // rows of 64K to 1M positions: one work-group per row (or per share of a
+        // row), over the group maxima
         if (group_max == nullptr) {
             float* gm = topk_group_max_area(ws, n_q, ld);
             hipLaunchKernelGGL(topk_group_max, dim3(nc, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, gm, ldg);
             group_max = gm;
         }
         const int gpl = ldg <= kThreads * 8 ? 8 : ldg <= kThreads * 16 ? 16 : ldg <= kThreads * 32 ? 32 : 64;
+        const int pn = row_shares(n_q);
+        if (pn > 1) {
+            uint8_t* sp = (uint8_t*)ws + split_offset(n_q, ld);
+            const SplitArgs sa{(unsigned long long*)sp, sp + align256((size_t)n_q * pn * 8), next_tag(), pn};
+            auto* kern = gpl == 8 ? topk_row_split<8> : gpl == 16 ? topk_row_split<16>
+                       : gpl == 32 ? topk_row_split<32> : topk_row_split<64>;
+            hipLaunchKernelGGL(kern, dim3(n_q, pn), dim3(kThreads), 0, st, scores, ld, q_pos, group_max, ldg, idx, sa);
+            return hipGetLastError();
+        }
         auto* kern = gpl == 8 ? (n_q >= kWideRows ? topk_row_wide<8> : topk_row<8>)
                    : gpl == 16 ? topk_row<16> : gpl == 32 ? topk_row<32> : topk_row<64>;
         hipLaunchKernelGGL(kern, dim3(n_q), dim3(kThreads), 0, st, scores, ld, q_pos, group_max, ldg, idx);

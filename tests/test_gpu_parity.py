@@ -274,6 +274,83 @@ def test_topk_ld_padding_is_ignored():
     assert np.array_equal(idx, oracle.topk_select(np32(s), np32(pos), 2048))
 
 
+def test_topk_split_rows_workspace_of_any_contents():
+    # launches of few rows split each row over several work-groups that hand
+    # their candidates over through the workspace: the workspace may hold
+    # anything beforehand (the arrival counters carry a launch tag) and is
+    # reused call after call
+    n = 300_000
+    s = W.score_matrix("normal", 5, n, seed=51)
+    pos = torch.tensor([n - 1, 250_000, 65_536 + 5, 100_000, n - 7], dtype=torch.int32)
+    d = dev()
+    want = oracle.topk_select(np32(s), np32(pos), 2048)
+    sd, pd = s.to(d), pos.to(d)
+    g = torch.Generator().manual_seed(52)
+    ws = torch.randint(0, 256, (gsa.topk_workspace_bytes(5, n),), dtype=torch.uint8, generator=g).to(d)
+    for rep in range(3):
+        assert np.array_equal(np32(gsa.topk(sd, pd, workspace=ws)), want), f"random workspace, call {rep}"
+    for fill in (255, 0):
+        ws.fill_(fill)
+        assert np.array_equal(np32(gsa.topk(sd, pd, workspace=ws)), want), f"workspace of {fill}s"
+    say("top-k split rows: random, all-ones and zero workspaces, repeated calls")
+
+
+def test_topk_split_rows_replayed_in_a_graph():
+    # a captured launch keeps its tag: every replay must find the counters it
+    # left (reset by the last arrival), with other launches on the same
+    # workspace between the replays
+    n = 200_000
+    s = W.score_matrix("int_ties", 4, n, seed=53)
+    s2 = W.score_matrix("normal", 4, n, seed=54)
+    pos = torch.tensor([n - 1, 150_000, 70_000, n - 3], dtype=torch.int32)
+    d = dev()
+    sd, s2d, pd = s.to(d), s2.to(d), pos.to(d)
+    want = oracle.topk_select(np32(s), np32(pos), 2048)
+    want2 = oracle.topk_select(np32(s2), np32(pos), 2048)
+    idx = torch.empty((4, 2048), dtype=torch.int32, device=d)
+    ws = torch.empty(gsa.topk_workspace_bytes(4, n), dtype=torch.uint8, device=d)
+    gsa.topk(sd, pd, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        gsa.topk(sd, pd, idx=idx, workspace=ws)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        idx.fill_(-7)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(np32(idx), want), f"replay {rep}"
+        assert np.array_equal(np32(gsa.topk(s2d, pd, workspace=ws)), want2), f"eager call after replay {rep}"
+    say("top-k split rows: 3 graph replays, each followed by an eager call on the same workspace")
+
+
+def test_topk_split_rows_with_more_candidates_than_one_selection_takes():
+    # every group's maximum is 1.0, so every group reaches the bound: one 1.0
+    # per group fills each wave's part exactly and the shares together hold 16x
+    # what the final selection takes; two per group overflow the parts; both go
+    # to the fallback over the whole list
+    n = 1 << 20
+    s = torch.zeros((3, n))
+    gi = torch.arange(n // 32)
+    s[0, gi * 32 + gi % 32] = 1.0
+    s[1, gi * 32] = 1.0
+    s[1, gi * 32 + 31] = 1.0
+    s[2] = W.score_matrix("normal", 1, n, seed=55)[0]
+    pos = torch.tensor([n - 1, n - 1, 700_000], dtype=torch.int32)
+    _topk_case(s, pos, "every group at the bound")
+
+
+def test_topk_row_kernel_without_split():
+    # 128..511 rows: one work-group per row, the default build
+    n, rows = 70_000, 130
+    parts = [W.score_matrix(kind, rows, n, seed=61) for kind in ("normal", "int_ties", "few_values")]
+    s = torch.stack([parts[i % 3][i] for i in range(rows)])
+    g = torch.Generator().manual_seed(62)
+    pos = torch.randint(66_000, n, (rows,), generator=g, dtype=torch.int32)
+    pos[::9] = n - 1
+    _topk_case(s, pos, f"{rows} rows, one work-group each", with_max=False)
+
+
 # ------------------------------------------------------------------ sparse MLA
 def _mla_case(n_q, batch, n_ctx, seed, idx_fn=None):
     wl = W.Workload("mla", batch, n_ctx, n_q // batch, 1, "bf16")
