@@ -530,6 +530,169 @@ __device__ __forceinline__ int select_wide(const uint32_t (&v)[PER], Scratch& sc
     return kK;
 }
 
+// Bound of the row kernels: a key L such that at least kK valid items are >= L,
+// in one histogram pass: the exact lower edge (in key space) of the one of 2048
+// equal key ranges between the smallest and largest item that holds the kK-th
+// largest item. Looser than the kK-th largest item by less than one range; 0
+// (no bound) with fewer than kK valid items (key 0: no item). `largest` is
+// the largest item (0 without one).
+template <int PER>
+__device__ __forceinline__ uint32_t bound_one_pass(const uint32_t (&v)[PER], Scratch& sc, uint32_t& largest) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    uint32_t* const h = &sc.hist[0][0][0];
+    uint32_t c = 0, mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(v[r] != 0u));
+        if (v[r] != 0u) { mn = min(mn, v[r]); mx = max(mx, v[r]); }
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) { sc.wsum[wave] = c; sc.wmin[wave] = mn; sc.wmax[wave] = mx; }
+    ((uint4*)h)[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);
+    sync_lds();
+    uint32_t n = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        n += sc.wsum[w];
+        mn = min(mn, sc.wmin[w]);
+        mx = max(mx, sc.wmax[w]);
+    }
+    n = uni(n);
+    mn = uni(mn);
+    mx = uni(mx);
+    largest = mx;
+    if (n < (uint32_t)kK) return 0u;                            // uniform
+    if (mn == mx) return mn;
+    const int nb = 32 - __builtin_clz(mx - mn);
+    const int sh = nb > 11 ? nb - 11 : 0;                       // (key - mn) >> sh < 2048
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        uint32_t key = v[r];
+        asm volatile("" : "+v"(key));
+        if (key != 0u) atomicAdd(&h[(key - mn) >> sh], 1u);
+    }
+    sync_lds();
+    const uint4 hb = ((const uint4*)h)[threadIdx.x];
+    const uint32_t incl = wave_incl_scan(hb.x + hb.y + hb.z + hb.w);
+    if (lane == 63) sc.weq[wave] = incl;
+    sync_lds();
+    uint32_t above = 0;                                         // items in bins past this thread's 4
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) above += w > wave ? sc.weq[w] : 0u;
+    above += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;
+    const uint32_t cnt4[4] = {hb.w, hb.z, hb.y, hb.x};          // bins 4t+3 .. 4t
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        if (above < (uint32_t)kK && above + cnt4[q] >= (uint32_t)kK) sc.pick[0] = 4 * threadIdx.x + 3 - q;
+        above += cnt4[q];
+    }
+    sync_lds();
+    return mn + (uni(sc.pick[0]) << sh);
+}
+
+// The top kK of the candidates v (keys, 0: none; item i = 64 PER wave + 64 r +
+// lane in position order, positions p), n of them valid and every key in [lo,
+// hi], written to out[] as ascending positions. One histogram pass over 2048
+// equal key ranges of [lo, hi] finds the range that holds the kK-th largest
+// key; one wave ranks that range's items by (key descending, item ascending),
+// which names the last selected item (T, iT): an item is selected iff its key
+// exceeds T, or equals T and the item is not after iT. A range of more than 64
+// items (heavy ties) goes to select_wide. The caller zeroes sc.hist[0] before
+// a barrier that precedes the call. Returns the number written.
+template <int PER>
+__device__ __forceinline__ int select_final(const uint32_t (&v)[PER], const uint32_t (&p)[PER], uint32_t lo,
+                                            uint32_t hi, uint32_t n, int32_t* out, Scratch& sc) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int seg0 = 64 * PER * wave;
+    uint32_t T = 1u, iT = 0xffffffffu;                          // n <= kK: every valid item
+    if (n > (uint32_t)kK) {                                     // uniform
+        uint32_t* const h = &sc.hist[0][0][0];
+        const int nb = hi > lo ? 32 - __builtin_clz(hi - lo) : 0;
+        const int sh = nb > 11 ? nb - 11 : 0;                   // (key - lo) >> sh < 2048
+        // (clamped, so keys outside [lo, hi], which valid inputs never hold, stay in bounds)
+        auto range = [&](uint32_t key) { return min((key - lo) >> sh, (uint32_t)(kWBins - 1)); };
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            uint32_t key = v[r];
+            asm volatile("" : "+v"(key));
+            if (key != 0u) atomicAdd(&h[range(key)], 1u);
+        }
+        if (threadIdx.x == 0) sc.wtot[0] = 0u;                  // the range's item count, below
+        sync_lds();
+        const uint4 hb = ((const uint4*)h)[threadIdx.x];
+        const uint32_t incl = wave_incl_scan(hb.x + hb.y + hb.z + hb.w);
+        if (lane == 63) sc.weq[wave] = incl;
+        sync_lds();
+        uint32_t above = 0;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) above += w > wave ? sc.weq[w] : 0u;
+        above += (uint32_t)__builtin_amdgcn_readlane((int)incl, 63) - incl;
+        const uint32_t cnt4[4] = {hb.w, hb.z, hb.y, hb.x};      // ranges 4t+3 .. 4t
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            if (above < (uint32_t)kK && above + cnt4[q] >= (uint32_t)kK) {
+                sc.pick[0] = 4 * threadIdx.x + 3 - q;
+                sc.pick[1] = above;
+                sc.pick[2] = cnt4[q];
+            }
+            above += cnt4[q];
+        }
+        sync_lds();
+        const uint32_t b = uni(sc.pick[0]), need = (uint32_t)kK - uni(sc.pick[1]), nin = uni(sc.pick[2]);
+        if (nin > 64u)                                          // uniform: heavy ties at the threshold
+            return select_wide<PER>(v, sc, [&](uint32_t slot, int, int r) { out[slot] = (int32_t)p[r]; });
+        uint32_t* const lst = &sc.hist[1][0][0];                // (key, item) of the range's items
+#pragma unroll
+        for (int r = 0; r < PER; ++r) {
+            if (v[r] != 0u && range(v[r]) == b) {
+                const uint32_t at = atomicAdd(&sc.wtot[0], 1u);
+                lst[2 * at] = v[r];
+                lst[2 * at + 1] = (uint32_t)(seg0 + 64 * r + lane);
+            }
+        }
+        sync_lds();
+        if (wave == 0) {
+            const uint32_t kl = lane < (int)nin ? lst[2 * lane] : 0u;
+            const uint32_t il = lane < (int)nin ? lst[2 * lane + 1] : 0xffffffffu;
+            uint32_t rank = 0;                                  // items of the range before this one
+            for (uint32_t m = 0; m < nin; ++m) {                // uniform
+                const uint32_t km = (uint32_t)__builtin_amdgcn_readlane((int)kl, (int)m);
+                const uint32_t im = (uint32_t)__builtin_amdgcn_readlane((int)il, (int)m);
+                rank += (km > kl || (km == kl && im < il)) ? 1u : 0u;
+            }
+            if (lane < (int)nin && rank == need - 1u) {
+                sc.pick[0] = kl;
+                sc.pick[1] = il;
+            }
+        }
+        sync_lds();
+        T = uni(sc.pick[0]);
+        iT = uni(sc.pick[1]);
+    }
+    // ---- emission in item order
+    bool sl[PER];
+    uint32_t c = 0;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const uint32_t i = (uint32_t)(seg0 + 64 * r + lane);
+        sl[r] = v[r] != 0u && (v[r] > T || (v[r] == T && i <= iT));
+        c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(sl[r]));
+    }
+    if (lane == 0) sc.wsum[wave] = c;
+    sync_lds();
+    uint32_t slot = 0;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) slot += w < wave ? sc.wsum[w] : 0u;
+#pragma unroll
+    for (int r = 0; r < PER; ++r) {
+        const uint64_t m = __builtin_amdgcn_ballot_w64(sl[r]);
+        if (sl[r]) out[slot + lanes_below(m)] = (int32_t)p[r];
+        slot += __builtin_popcountll(m);
+    }
+    return (int)min(n, (uint32_t)kK);
+}
+
 __device__ __forceinline__ void write_final_pad(int32_t* out, int count) {
     for (int j = count + threadIdx.x; j < kK; j += kThreads) out[j] = -1;
 }
@@ -725,19 +888,19 @@ __device__ __forceinline__ void drain_vm() {
 template <int GPL, int kEnt, bool kSplit>
 __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, int64_t ld,
                                               const int32_t* __restrict__ q_pos,
-                                              const float* __restrict__ gmax, int64_t ldg,
+                                              const float* __restrict__ gmax, int64_t ldg, bool al16,
                                               int32_t* __restrict__ idx, const SplitArgs& sa) {
     constexpr int kMaxGroups = kThreads * GPL;
     constexpr int IPL = kPerSmall;                 // bound items per thread: 4096 in all
     constexpr int GPI = GPL / IPL;                 // maxima per item
     static_assert(GPL % IPL == 0 && kMaxGroups <= 65536, "GPL");
     constexpr int kWaveCap = 2 * kK / kWaves;      // candidates a wave's part holds (512)
-    constexpr int kWords = kMaxGroups / 64;
+    constexpr int R4 = GPL / 4;                    // rounds of 4 groups per thread
     struct Lds {
         Scratch sc;
         uint2 pend[2 * kK];                        // candidates (key, position), in position order
         uint2 ptrash[kThreads];                    // where a lane writes what it does not keep
-        uint64_t bitmap[kWords];                   // passing groups, bit g % 64 of word g / 64
+        alignas(16) uint8_t nib[kMaxGroups / 4];   // passing groups: 4 per byte, bit g % 4
         f32x4 ent_x[kWaves][kEnt];                 // per wave: loads that hold a candidate (scores,
         int ent_p[kWaves][kEnt];                   // first position)
         uint32_t wtot[kWaves];
@@ -755,43 +918,75 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
     const float* srow = scores + (int64_t)q * ld;
     int32_t* out = idx + (int64_t)q * kK;
 
-    // ---- 1. the maxima and the bound
-    uint32_t gk[GPL];                                           // 0: no causal group
+    // ---- 1. the maxima and the bound. Round i of thread t holds groups
+    // 2048 i + 4 t .. + 3: one 16-byte load when the maxima rows are 16-byte
+    // aligned (al16), else four 4-byte loads; gk[4 i + c] is group 2048 i + 4 t + c.
+    // The work-groups of a split row all read the row's maxima, so they are
+    // cached loads there, and non-temporal ones otherwise.
+    auto load_maxima = [&](uint32_t (&g)[GPL]) __attribute__((always_inline)) {
+        if (al16) {                                             // uniform
 #pragma unroll
-    for (int i = 0; i < GPL; ++i)
-        gk[i] = score_key(__builtin_nontemporal_load(grow + min(kThreads * i + t, ng - 1)));
+            for (int i = 0; i < R4; ++i) {
+                const f32x4* a = (const f32x4*)(grow + min(2048 * i + 4 * t, (int)ldg - 4));
+                const f32x4 x = kSplit ? *a : __builtin_nontemporal_load(a);
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) gk[i] = kThreads * i + t < ng ? gk[i] : 0u;
-    uint32_t L = 0u;
+                for (int c = 0; c < 4; ++c) g[4 * i + c] = score_key(x[c]);
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < R4; ++i)
+#pragma unroll
+                for (int c = 0; c < 4; ++c) {
+                    const float* a = grow + min(2048 * i + 4 * t + c, max(ng - 1, 0));
+                    g[4 * i + c] = score_key(kSplit ? *a : __builtin_nontemporal_load(a));
+                }
+        }
+#pragma unroll
+        for (int i = 0; i < R4; ++i)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) g[4 * i + c] = 2048 * i + 4 * t + c < ng ? g[4 * i + c] : 0u;   // 0: no causal group
+    };
+    uint32_t gk[GPL];
+    load_maxima(gk);
+    uint32_t L, Mx;                                             // the bound, the largest maximum
     {
         uint32_t it[IPL];
-        uint32_t c = 0;
 #pragma unroll
         for (int k = 0; k < IPL; ++k) {
             uint32_t m = 0u;
 #pragma unroll
             for (int j = 0; j < GPI; ++j) m = max(m, gk[GPI * k + j]);
             it[k] = m;
-            c += __builtin_popcountll(__builtin_amdgcn_ballot_w64(m != 0u));
         }
-        const uint32_t n_items = uni(block_sum(uni(c), s.sc));
-        if (n_items >= (uint32_t)kK) select_wide<IPL>(it, s.sc, [](uint32_t, int, int) {}, &L);
-        L = uni(L);
+        L = bound_one_pass<IPL>(it, s.sc, Mx);
     }
-    // ---- 2. the groups that reach it, in position order. Round i's ballot in
-    // wave w covers groups 512 i + 64 w .. + 63: word 8 i + w of a bitmap in LDS.
-    // Thread t then owns bits GPL t .. GPL t + GPL - 1 (groups GPL t ..) and
-    // writes its groups after those of the lower threads (a scan of the counts).
+    // ---- 2. the groups of words w0 .. w1 - 1 (64 groups each) that reach L, in
+    // position order: every thread writes a 4-bit mask per round (a byte in
+    // LDS), then lists the groups of a few consecutive masks after those of the
+    // lower threads (a scan of the counts). Returns their number.
+    auto build_list = [&](const uint32_t (&g)[GPL], int w0, int w1) __attribute__((always_inline)) {
+        const int g0 = 64 * w0, g1 = 64 * w1;
 #pragma unroll
-    for (int i = 0; i < GPL; ++i) {
-        const uint64_t m = __builtin_amdgcn_ballot_w64(gk[i] != 0u && gk[i] >= L);
-        if (lane == 0) s.bitmap[kWaves * i + wave] = m;
-    }
-    sync_lds();
-    uint32_t base;
-    {
-        uint64_t word = s.bitmap[(t * GPL) / 64] >> ((t * GPL) % 64);
-        if constexpr (GPL < 64) word &= (1ull << GPL) - 1ull;
+        for (int i = 0; i < R4; ++i) {
+            if (2048 * (i + 1) <= g0 || 2048 * i >= g1) continue;   // uniform: round outside the words
+            const int b = 2048 * i + 4 * t;
+            uint32_t m = 0u;
+#pragma unroll
+            for (int c = 0; c < 4; ++c) m |= (g[4 * i + c] != 0u && g[4 * i + c] >= L) ? 1u << c : 0u;
+            if (b >= g0 && b < g1) s.nib[(b - g0) >> 2] = (uint8_t)m;
+        }
+        sync_lds();
+        // thread t takes mask bytes t B .. t B + B - 1 (groups g0 + 4 t B ..): few
+        // per thread, so that dense lists (half the groups of a 128K row) are
+        // written by many threads at once
+        const int nbytes = (g1 - g0) >> 2;
+        int B = 1;
+        while (B * kThreads < nbytes) B <<= 1;                  // <= 16
+        uint64_t word = 0ull;
+        for (int k = 0; k < B; ++k) {
+            const int j = t * B + k;
+            if (j < nbytes) word |= (uint64_t)s.nib[j] << (4 * k);
+        }
         const uint32_t cw = (uint32_t)__builtin_popcountll(word);
         const uint32_t incl = wave_incl_scan(cw);
         if (lane == 63) s.wtot[wave] = incl;
@@ -805,26 +1000,28 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
         }
         uint32_t o = before + incl - cw;
         while (word != 0ull) {                                  // about 5 groups per word at the bound
-            s.glist[o++] = (uint16_t)(GPL * t + __builtin_ctzll(word));
+            s.glist[o++] = (uint16_t)(g0 + 4 * B * t + __builtin_ctzll(word));
             word &= word - 1;
         }
-        base = total;
-    }
-    const int P = (int)uni(base);                               // >= kK with a bound, else ng
-    sync_lds();
+        sync_lds();
+        return (int)uni(total);
+    };
+    // this work-group's words: the row's, or (split rows) its share of them
+    const int nwr = (ng + 63) / 64;
+    int P = build_list(gk, kSplit ? (int)((int64_t)nwr * share / pn) : 0,
+                       kSplit ? (int)((int64_t)nwr * (share + 1) / pn) : nwr);   // >= kK with a bound, else ng
 
     // ---- 3. candidates of the passing groups. Usual case: wave w streams its own
-    // contiguous part of the work-group's share of the list, 64 groups (2048
-    // scores, 32 per lane) at a time with the next 64 in flight, and appends its
-    // keys >= L in position order to its own part of the LDS candidate list,
-    // without work-group barriers. The parts and shares are contiguous and in
+    // contiguous part of the list, 64 groups (2048 scores, 32 per lane) at a
+    // time with the next 64 in flight, and appends its keys >= L in position
+    // order to its own part of the LDS candidate list, without work-group
+    // barriers. The parts (and the shares of a split row) are contiguous and in
     // order, so the parts, concatenated, are in position order.
     auto gpos = [&](int gi, int e) __attribute__((always_inline)) {
         return (int64_t)s.glist[min(gi, max(P, 1) - 1)] * kGroup + e;
     };
     {
-        const int64_t s0 = (int64_t)P * share / pn, s1 = (int64_t)P * (share + 1) / pn;
-        const int gs = (int)(s0 + (s1 - s0) * wave / kWaves), ge = (int)(s0 + (s1 - s0) * (wave + 1) / kWaves);
+        const int gs = (int)(((int64_t)P * wave) / kWaves), ge = (int)(((int64_t)P * (wave + 1)) / kWaves);
         uint2* part = s.pend + kWaveCap * wave;
         uint32_t cnt = 0;
         bool over = false;
@@ -916,6 +1113,7 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
         }
         if (lane == 0) s.wcnt[wave] = over ? 0xffffffffu : cnt;
     }
+    ((uint4*)&s.sc.hist[0][0][0])[t] = make_uint4(0u, 0u, 0u, 0u);   // for step 4
     sync_lds();
     uint32_t off[kWaves + 1];
     bool any_over = false;
@@ -945,6 +1143,7 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
         if (t == 0) store_dev((unsigned long long*)reg, any_over ? 0xffffffffull : (unsigned long long)total);
         drain_vm();                                             // every store of this wave is complete
         sync_lds();                                             // ... and of every wave
+        ((uint4*)&s.sc.hist[0][0][0])[t] = make_uint4(0u, 0u, 0u, 0u);   // for step 4
         if (wave == 0) {                                        // lane u reads share u's flag
             if (lane == 0) store_dev(flag + share, sa.tag);
             drain_vm();
@@ -976,7 +1175,7 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
         for (int u = 0; u < kMaxShares; ++u) fits = fits && cnt_u[u] <= (uint32_t)W;   // all ones: overflow
         if (t < pn) store_dev(flag + t, 0ull);                  // every share has arrived: clear for the next launch
         if (fits) {                                             // uniform
-            uint32_t pv[kPerSmall], pp[kPerSmall];
+            uint32_t pv[kPerSmall], pp[kPerSmall], n = 0;
 #pragma unroll
             for (int r = 0; r < kPerSmall; ++r) {
                 const int i = 64 * kPerSmall * wave + 64 * r + lane;
@@ -986,9 +1185,9 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
                 pv[r] = (uint32_t)(i & (W - 1)) < c ? score_key(__uint_as_float((uint32_t)x[r])) : 0u;
                 pp[r] = (uint32_t)(x[r] >> 32);
             }
-            const int cnt = select_wide<kPerSmall>(pv, s.sc, [&](uint32_t slot, int, int r) {
-                out[slot] = (int32_t)pp[r];
-            });
+#pragma unroll
+            for (int u = 0; u < kMaxShares; ++u) n += cnt_u[u];
+            const int cnt = select_final<kPerSmall>(pv, pp, L == 0u ? 1u : L, Mx, n, out, s.sc);
             write_final_pad(out, cnt);
             return;
         }
@@ -1005,9 +1204,7 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
             pv[r] = i < off[kWaves] ? score_key(__uint_as_float(e.x)) : 0u;
             pp[r] = e.y;
         }
-        const int cnt = select_wide<kPerSmall>(pv, s.sc, [&](uint32_t slot, int, int r) {
-            out[slot] = (int32_t)pp[r];
-        });
+        const int cnt = select_final<kPerSmall>(pv, pp, L == 0u ? 1u : L, Mx, off[kWaves], out, s.sc);
         write_final_pad(out, cnt);
         return;
     }
@@ -1029,10 +1226,15 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
             x[r] = __builtin_nontemporal_load(
                 srow + min(gpos(kGb * b + 2 * kFb * wave + 2 * r + (lane >> 5), lane & 31), len - 1));
     };
+    sync_lds();                                                 // every wave is done with the parts
+    if constexpr (kSplit) {                                     // the list holds this share's groups: the row's
+        uint32_t g[GPL];
+        load_maxima(g);
+        P = build_list(g, 0, nwr);
+    }
     const int nb = (P + kGb - 1) / kGb;
     uint32_t thr = L, npend = 0;
     float x[kFb];
-    sync_lds();                                                 // every wave is done with the parts
     if (nb > 0) load(0, x);
     for (int b = 0; b < nb; ++b) {                              // uniform
         uint32_t v[kFb];
@@ -1098,23 +1300,23 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
 template <int GPL>
 __global__ __launch_bounds__(kThreads) void topk_row(const float* __restrict__ scores, int64_t ld,
                                                      const int32_t* __restrict__ q_pos,
-                                                     const float* __restrict__ gmax, int64_t ldg,
+                                                     const float* __restrict__ gmax, int64_t ldg, int al16,
                                                      int32_t* __restrict__ idx) {
-    topk_row_body<GPL, 128, false>(scores, ld, q_pos, gmax, ldg, idx, SplitArgs{});
+    topk_row_body<GPL, 128, false>(scores, ld, q_pos, gmax, ldg, al16 != 0, idx, SplitArgs{});
 }
 template <int GPL>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void topk_row_wide(
     const float* __restrict__ scores, int64_t ld, const int32_t* __restrict__ q_pos,
-    const float* __restrict__ gmax, int64_t ldg, int32_t* __restrict__ idx) {
-    topk_row_body<GPL, 64, false>(scores, ld, q_pos, gmax, ldg, idx, SplitArgs{});
+    const float* __restrict__ gmax, int64_t ldg, int al16, int32_t* __restrict__ idx) {
+    topk_row_body<GPL, 64, false>(scores, ld, q_pos, gmax, ldg, al16 != 0, idx, SplitArgs{});
 }
 // grid (rows, shares)
 template <int GPL>
 __global__ __launch_bounds__(kThreads) void topk_row_split(const float* __restrict__ scores, int64_t ld,
                                                            const int32_t* __restrict__ q_pos,
-                                                           const float* __restrict__ gmax, int64_t ldg,
+                                                           const float* __restrict__ gmax, int64_t ldg, int al16,
                                                            int32_t* __restrict__ idx, SplitArgs sa) {
-    topk_row_body<GPL, 128, true>(scores, ld, q_pos, gmax, ldg, idx, sa);
+    topk_row_body<GPL, 128, true>(scores, ld, q_pos, gmax, ldg, al16 != 0, idx, sa);
 }
 
 // ---- Selection without a score buffer ----------------------------------------
@@ -1487,18 +1689,20 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, in
             group_max = gm;
         }
         const int gpl = ldg <= kThreads * 8 ? 8 : ldg <= kThreads * 16 ? 16 : ldg <= kThreads * 32 ? 32 : 64;
+        const int al16 = ldg % 4 == 0 && ((uintptr_t)group_max & 15u) == 0 ? 1 : 0;   // 16-byte maxima loads
         const int pn = row_shares(n_q);
         if (pn > 1) {
             uint8_t* sp = (uint8_t*)ws + split_offset(n_q, ld);
             const SplitArgs sa{(unsigned long long*)sp, sp + align256((size_t)n_q * pn * 8), next_tag(), pn};
             auto* kern = gpl == 8 ? topk_row_split<8> : gpl == 16 ? topk_row_split<16>
                        : gpl == 32 ? topk_row_split<32> : topk_row_split<64>;
-            hipLaunchKernelGGL(kern, dim3(n_q, pn), dim3(kThreads), 0, st, scores, ld, q_pos, group_max, ldg, idx, sa);
+            hipLaunchKernelGGL(kern, dim3(n_q, pn), dim3(kThreads), 0, st, scores, ld, q_pos, group_max, ldg, al16, idx,
+                               sa);
             return hipGetLastError();
         }
         auto* kern = gpl == 8 ? (n_q >= kWideRows ? topk_row_wide<8> : topk_row<8>)
                    : gpl == 16 ? topk_row<16> : gpl == 32 ? topk_row<32> : topk_row<64>;
-        hipLaunchKernelGGL(kern, dim3(n_q), dim3(kThreads), 0, st, scores, ld, q_pos, group_max, ldg, idx);
+        hipLaunchKernelGGL(kern, dim3(n_q), dim3(kThreads), 0, st, scores, ld, q_pos, group_max, ldg, al16, idx);
         return hipGetLastError();
     }
     uint8_t* p = (uint8_t*)ws;
