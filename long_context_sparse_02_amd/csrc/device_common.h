@@ -123,6 +123,42 @@ __device__ __forceinline__ void ring_barrier() {
     asm volatile("" ::: "memory");
 }
 
+// Scalar-base forms: lane l's source is base + off (base wave-uniform, in an
+// SGPR pair; off a 32-bit lane offset), which saves the 64-bit address
+// arithmetic of every load when the lane offsets are computed once per ring.
+template <bool NT>
+__device__ __forceinline__ void lds_dma16_so(const void* base, uint32_t off, uint32_t lds_base) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1 nt"
+                     :
+                     : "v"(off), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, %1"
+                     :
+                     : "v"(off), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "m0");
+}
+template <bool NT>
+__device__ __forceinline__ void lds_dma4_so(const void* base, uint32_t off, uint32_t lds_base) {
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t sb = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    if constexpr (NT)
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1 nt"
+                     :
+                     : "v"(off), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "m0");
+    else
+        asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tglobal_load_lds_dword %0, %1"
+                     :
+                     : "v"(off), "s"(sb), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+                     : "m0");
+}
+
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding)
 template <int N>
 __device__ __forceinline__ void wait_vmcnt() {
@@ -131,14 +167,19 @@ __device__ __forceinline__ void wait_vmcnt() {
 }
 
 // Run-time count: waits until at most n (clamped to [0, 63]) vector-memory
-// operations of this wave are outstanding. A smaller n only waits longer.
-template <int N = 63>
+// operations of this wave are outstanding. A smaller n only waits longer. The
+// count is an immediate of s_waitcnt, so n (wave-uniform: pass it through
+// readfirstlane, or the branches become exec-masked vector compares) selects
+// one of 64 instructions by a binary dispatch of six scalar branches (a
+// linear chain cost ~560 cycles per call at the counts the streaming rings use).
+template <int LO = 0, int HI = 63>
 __device__ __forceinline__ void wait_vmcnt_le(int n) {
-    if constexpr (N == 0) {
-        wait_vmcnt<0>();
+    if constexpr (LO == HI) {
+        wait_vmcnt<LO>();
     } else {
-        if (n >= N) wait_vmcnt<N>();
-        else wait_vmcnt_le<N - 1>(n);
+        constexpr int MID = (LO + HI + 1) / 2;
+        if (n >= MID) wait_vmcnt_le<MID, HI>(n);
+        else wait_vmcnt_le<LO, MID - 1>(n);
     }
 }
 

@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     __shared__ float stage_gm[STAGE ? kStageKeys / 32 : 1];
 
     const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave: uniform (SGPR)
     const int n = lane & 31, g = lane >> 5;
     const int qb0 = blockIdx.y * QB;
     const int64_t c0 = (int64_t)blockIdx.x * chunk;
@@ -143,6 +143,17 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     // DMA instructions per tile issued by this wave (wave 0 also moves the fp8 scales)
     const int per = T::kDmaPerWave + ((FP8 && wave == 0) ? T::kScaleDma : 0);
     const uint32_t ring_base = (uint32_t)(uintptr_t)(lds_u8*)ring;
+    // lane offsets (bytes from a tile's first key row) of this wave's DMAs:
+    // DMA i moves rows 8i .. (fp8) or 4i .. (bf16), and lane l's 16-byte chunk
+    // lands at the XOR-swizzled place of its row
+    uint32_t doff[T::kDmaPerWave];
+#pragma unroll
+    for (int jd = 0; jd < T::kDmaPerWave; ++jd) {
+        const int i = wave * T::kDmaPerWave + jd;
+        const int r = i * T::kRowsPerDma + lane / T::kChunks;
+        const int c = (lane % T::kChunks) ^ (r & (T::kChunks - 1));
+        doff[jd] = (uint32_t)(r * T::kRowBytes + 16 * c);
+    }
 
     // Queries of the block are processed in runs that share a sequence.
     int j0 = 0;
@@ -173,6 +184,20 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
         auto issue = [&](int ti, int slot) __attribute__((always_inline)) {
             const int64_t t0 = c0 + (int64_t)ti * T::kKeys;
             const uint32_t dst = ring_base + slot * T::kSlot;
+            if (t0 + T::kKeys <= c1) {                   // uniform: a whole tile, scalar base + lane offsets
+                const uint8_t* base = kb + t0 * T::kRowBytes;
+#pragma unroll
+                for (int jd = 0; jd < T::kDmaPerWave; ++jd)
+                    lds_dma16_so<NTK>(base, doff[jd], dst + 1024 * (wave * T::kDmaPerWave + jd));
+                if constexpr (FP8) {
+                    if (wave == 0) {
+#pragma unroll
+                        for (int h = 0; h < T::kScaleDma; ++h)
+                            lds_dma4_so<NTK>(ksb + t0, 4 * (64 * h + lane), dst + T::kBytes + 256 * h);
+                    }
+                }
+                return;
+            }
 #pragma unroll
             for (int jd = 0; jd < T::kDmaPerWave; ++jd) {
                 const int i = wave * T::kDmaPerWave + jd;
@@ -204,49 +229,66 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
                 // DMAs of tiles ti+1 .. min(na, ti+kRing-1)-1 and the score stores of
                 // the iterations since tile ti was issued
                 const int later = min(na, ti + kRing - 1) - ti - 1;
-                wait_vmcnt_le<63>(later * per + stores * min(ti, kRing - 1));
+                wait_vmcnt_le(__builtin_amdgcn_readfirstlane(later * per + stores * min(ti, kRing - 1)));
                 ring_barrier();   // every wave's part of tile ti landed; tile ti-1's readers are done
                 if (ti + kRing - 1 < na) issue(ti + kRing - 1, (ti + kRing - 1) % kRing);
+            }
+            // this wave's pairs: the MFMAs of every pair first, then every pair's head
+            // sums, so that one pair's sums run while the next pair's MFMAs occupy
+            // the matrix core (no branch between them); a pair outside the run or
+            // the causal range is computed anyway, from whatever the slot holds,
+            // and discarded (the last tiles of a query only)
+            f32x16 acc[PPW];
+#pragma unroll
+            for (int p = 0; p < PPW; ++p) {
+                const int pp = wave * PPW + p;
+                const int nt = pp % NSUBT;
+                const int jj = pp / NSUBT - jw0;         // 0: one query per wave
+                const int row = nt * 32 + n;
+                acc[p] = f32x16{};
+#pragma unroll
+                for (int t = 0; t < KSTEPS; ++t) {
+                    if constexpr (FP8) {
+                        const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(tile + T::off(row, 4 * g + 2 * t));
+                        const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(tile + T::off(row, 4 * g + 2 * t + 1));
+                        const i32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                        const float ks = *(const __attribute__((address_space(3))) float*)(tile + T::kBytes + 4 * row);
+                        acc[p] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                            a[jj][t], b, acc[p], 0, 0, 0, a_e8[jj], 0, e8m0_of(ks));
+                    } else {
+                        const bf16x8 b = *(const __attribute__((address_space(3))) bf16x8*)(tile + T::off(row, 8 * g + t));
+                        acc[p] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jj][t], b, acc[p], 0, 0, 0);
+                    }
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);          // keep every MFMA ahead of the head sums
+            float res[PPW];                              // every pair's sums before any branch
+#pragma unroll
+            for (int p = 0; p < PPW; ++p) {
+                const int pp = wave * PPW + p;
+                const int jj = pp / NSUBT - jw0;
+                const int64_t s = t0 + (pp % NSUBT) * 32 + n;
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)             // relu on the bit pattern: exact, one instruction
+                    part = fmaf(wr[jj][i], __int_as_float(max(__float_as_int(acc[p][i]), 0)), part);
+                part = sum_x32(part);
+                res[p] = (active && s <= apos[jj]) ? part : neg_inf();
             }
 #pragma unroll
             for (int p = 0; p < PPW; ++p) {
                 const int pp = wave * PPW + p;
                 const int j = pp / NSUBT, nt = pp % NSUBT;
-                const int jj = j - jw0;
                 if (j < j0 || j >= j1) continue;         // other run (wave-uniform)
                 const int64_t s0 = t0 + nt * 32;
                 const int64_t s = s0 + n;
-                float res = neg_inf();
-                if (active && s0 <= apos[jj]) {
-                    f32x16 acc = {};
-                    const int row = nt * 32 + n;
-#pragma unroll
-                    for (int t = 0; t < KSTEPS; ++t) {
-                        if constexpr (FP8) {
-                            const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(tile + T::off(row, 4 * g + 2 * t));
-                            const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(tile + T::off(row, 4 * g + 2 * t + 1));
-                            const i32x8 b = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-                            const float ks = *(const __attribute__((address_space(3))) float*)(tile + T::kBytes + 4 * row);
-                            acc = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                                a[jj][t], b, acc, 0, 0, 0, a_e8[jj], 0, e8m0_of(ks));
-                        } else {
-                            const bf16x8 b = *(const __attribute__((address_space(3))) bf16x8*)(tile + T::off(row, 8 * g + t));
-                            acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[jj][t], b, acc, 0, 0, 0);
-                        }
-                    }
-                    float part = 0.f;
-#pragma unroll
-                    for (int i = 0; i < 16; ++i) part = fmaf(wr[jj][i], fmaxf(acc[i], 0.f), part);
-                    part = sum_x32(part);
-                    res = (s <= apos[jj]) ? part : neg_inf();
-                }
                 if (scores != nullptr && g == 0 && s < c1)   // uniform pointer test
                 {
-                    if constexpr (STAGE) stage_sc[s - c0] = res;
-                    else store_score<FP8>(scores + (int64_t)(qb0 + j) * ld + s, res);
+                    if constexpr (STAGE) stage_sc[s - c0] = res[p];
+                    else store_score<FP8>(scores + (int64_t)(qb0 + j) * ld + s, res[p]);
                 }
                 if (gmax != nullptr && s0 < c1) {                       // uniform
-                    const uint32_t m = max_x32(score_key(s < c1 ? res : neg_inf()));
+                    const uint32_t m = max_x32(score_key(s < c1 ? res[p] : neg_inf()));
                     if (lane == 0) {
                         if constexpr (STAGE) stage_gm[(s0 - c0) >> 5] = key_value(m);
                         else gmax[(int64_t)(qb0 + j) * ldg + (s0 >> 5)] = key_value(m);
@@ -425,7 +467,7 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
             const bool active = ti < na;
             if (active) {
                 const int later = min(na, ti + kRingMq - 1) - ti - 1;
-                wait_vmcnt_le<63>(later * per + stores * min(ti, kRingMq - 1));
+                wait_vmcnt_le(__builtin_amdgcn_readfirstlane(later * per + stores * min(ti, kRingMq - 1)));
                 ring_barrier();
                 if (ti + kRingMq - 1 < na) issue(ti + kRingMq - 1, (ti + kRingMq - 1) % kRingMq);
             }

@@ -1421,7 +1421,8 @@ __global__ __launch_bounds__(kThreads) void topk_rescore(
                 }
                 float part = 0.f;
 #pragma unroll
-                for (int i = 0; i < 16; ++i) part = fmaf(wr[i], fmaxf(acc[i], 0.f), part);
+                for (int i = 0; i < 16; ++i)               // relu on the bit pattern, as the score kernels
+                    part = fmaf(wr[i], __int_as_float(max(__float_as_int(acc[i]), 0)), part);
                 part = sum_x32(part);
                 const int64_t s = w0 + 32 * js[b] + n;
                 const uint32_t key = score_key(part);
