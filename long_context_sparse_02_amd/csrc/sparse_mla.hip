@@ -93,6 +93,18 @@ __shared__ f32x4 g_xs[kWaves][2][64];           // partial S^T of each wave (2 K
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+// Largest value over the 16 lanes of a row (DPP: two quad permutations, the
+// half-row and row mirrors), in every lane of the row.
+__device__ __forceinline__ float max_row16(float v) {
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
+    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+    return v;
+}
+
 // Per-layer operands of one launch (kernel argument, indexed by blockIdx.z):
 // the layers of an IndexShare group share the index buffer and are independent
 // otherwise, so one launch covers all of them.
@@ -133,7 +145,7 @@ template <bool FP8KV>
 __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     LayerArgs L, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ idx, int k,
     int n_q, int64_t n_cap, const int32_t* __restrict__ block_table, int page_size, int max_pages,
-    float scale_log2, int rows_per_split, float* __restrict__ part_o_all,
+    float scale_log2, int rows_per_split, _Float16* __restrict__ part_o_all,
     float* __restrict__ part_ml_all) {
     // this work-group's layer (uniform): its operands and its part of the workspace
     const int layer = blockIdx.z;
@@ -142,8 +154,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     const uint8_t* __restrict__ kv = L.kv[layer];
     float* __restrict__ out = L.out[layer];
     float* __restrict__ lse = L.lse[layer];
-    float* __restrict__ part_o = part_o_all + (size_t)layer * n_q * gridDim.x * kHeads * kLat;
-    float* __restrict__ part_ml = part_ml_all + (size_t)layer * n_q * gridDim.x * kHeads * 2;
+    _Float16* __restrict__ part_o = part_o_all + (size_t)layer * n_q * gridDim.x * kHeads * kLat;
+    float* __restrict__ part_ml = part_ml_all + (size_t)layer * n_q * gridDim.x * kHeads * 4;
     int32_t* rows_s = g_rows;
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const int l16 = lane & 15, g = lane >> 4;
@@ -390,16 +402,34 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             lse[(int64_t)q * kHeads + head] =
                 l_tot > 0.f ? (m_run + log2f(l_tot)) * 0.69314718055994531f : neg_inf();
     } else {
-        float* po = part_o + ((int64_t)q * n_split + split) * kHeads * kLat;
+        // the split's unnormalised O in fp16 with a power-of-two scale per (head,
+        // latent half): 2^-e puts the largest |O| of the half in [2^14, 2^15), so
+        // every value keeps 11 significant bits relative to that largest one
+        // whatever the cache's magnitudes (half the bytes of fp32 partials,
+        // written here and read by the merge)
+        int ex[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float mx = 0.f;
+#pragma unroll
+            for (int d = 0; d < 16; ++d) mx = fmaxf(mx, fabsf(o[d][i]));
+            mx = max_row16(mx);                          // the 16 lanes of the row hold the half's dims
+            ex[i] = __builtin_amdgcn_frexp_expf(mx) - 15;
+        }
+        _Float16* po = part_o + ((int64_t)q * n_split + split) * kHeads * kLat;
 #pragma unroll
         for (int d = 0; d < 16; ++d)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                po[(16 * hg + 4 * g + i) * kLat + dim0 + 16 * d + l16] = o[d][i];
+                po[(16 * hg + 4 * g + i) * kLat + dim0 + 16 * d + l16] = (_Float16)__builtin_amdgcn_ldexpf(o[d][i], -ex[i]);
+        float* pm = part_ml + ((int64_t)q * n_split + split) * kHeads * 4;
+        if (l16 == 0) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) pm[4 * (16 * hg + 4 * g + i) + 2 + hf] = (float)ex[i];
+        }
         if (g == 0 && hf == 0) {
-            float* pm = part_ml + ((int64_t)q * n_split + split) * kHeads * 2;
-            pm[2 * head] = m_run;
-            pm[2 * head + 1] = l_tot;
+            pm[4 * head] = m_run;
+            pm[4 * head + 1] = l_tot;
         }
     }
 }
@@ -407,18 +437,18 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 // Combine the per-split partial results with their log-sum-exp. Grid
 // (n_q, 16): a work-group merges 4 heads x 512 dims of one query.
 __global__ __launch_bounds__(256) void sparse_mla_merge(LayerArgs L, int n_q,
-                                                             const float* __restrict__ part_o_all,
+                                                             const _Float16* __restrict__ part_o_all,
                                                              const float* __restrict__ part_ml_all,
                                                              int n_split) {
     const int layer = blockIdx.z;
     float* __restrict__ out = L.out[layer];
     float* __restrict__ lse = L.lse[layer];
-    const float* __restrict__ part_o = part_o_all + (size_t)layer * n_q * n_split * kHeads * kLat;
-    const float* __restrict__ part_ml = part_ml_all + (size_t)layer * n_q * n_split * kHeads * 2;
+    const _Float16* __restrict__ part_o = part_o_all + (size_t)layer * n_q * n_split * kHeads * kLat;
+    const float* __restrict__ part_ml = part_ml_all + (size_t)layer * n_q * n_split * kHeads * 4;
     const int q = blockIdx.x;
     const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
-    const int c = threadIdx.x & 63;              // float4 columns c and c + 64
-    const float* pm = part_ml + ((int64_t)q * n_split * kHeads + h) * 2;
+    const int c = threadIdx.x & 63;              // dims 4c .. 4c + 3 of each latent half
+    const float* pm = part_ml + ((int64_t)q * n_split * kHeads + h) * 4;
     // Splits in batches of SB whose loads are all in flight together (a loop
     // that uses each load before issuing the next waits out one memory
     // latency per split); sums in split order as before.
@@ -427,7 +457,7 @@ __global__ __launch_bounds__(256) void sparse_mla_merge(LayerArgs L, int n_q,
     for (int s0 = 0; s0 < n_split; s0 += SB) {
         float m[SB];
 #pragma unroll
-        for (int b = 0; b < SB; ++b) m[b] = s0 + b < n_split ? pm[(int64_t)(s0 + b) * kHeads * 2] : neg_inf();
+        for (int b = 0; b < SB; ++b) m[b] = s0 + b < n_split ? pm[(int64_t)(s0 + b) * kHeads * 4] : neg_inf();
 #pragma unroll
         for (int b = 0; b < SB; ++b) mx = fmaxf(mx, m[b]);
     }
@@ -435,24 +465,27 @@ __global__ __launch_bounds__(256) void sparse_mla_merge(LayerArgs L, int n_q,
     float lsum = 0.f;
     if (mx != neg_inf()) {
         for (int s0 = 0; s0 < n_split; s0 += SB) {
-            float m[SB], l[SB];
-            f32x4 x0[SB], x1[SB];
+            f32x4 ml[SB];                                      // m, l, exponents of the two halves
+            f16x4 x0[SB], x1[SB];
 #pragma unroll
             for (int b = 0; b < SB; ++b) {
                 const int s = min(s0 + b, n_split - 1);          // past the last split: not summed
-                m[b] = pm[(int64_t)s * kHeads * 2];
-                l[b] = pm[(int64_t)s * kHeads * 2 + 1];
-                const f32x4* po = (const f32x4*)(part_o + (((int64_t)q * n_split + s) * kHeads + h) * kLat);
+                ml[b] = *(const f32x4*)(pm + (int64_t)s * kHeads * 4);
+                const f16x4* po = (const f16x4*)(part_o + (((int64_t)q * n_split + s) * kHeads + h) * kLat);
                 x0[b] = po[c];
                 x1[b] = po[c + 64];
             }
 #pragma unroll
             for (int b = 0; b < SB; ++b) {                    // branch-free, so the loads stay batched
                 const bool ok = s0 + b < n_split;
-                const float wgt = exp2_(m[b] - mx);
-                lsum = ok ? lsum + wgt * l[b] : lsum;
-                a0 = ok ? a0 + wgt * x0[b] : a0;
-                a1 = ok ? a1 + wgt * x1[b] : a1;
+                const float wgt = exp2_(ml[b][0] - mx);
+                const float w0 = __builtin_amdgcn_ldexpf(wgt, (int)ml[b][2]);
+                const float w1 = __builtin_amdgcn_ldexpf(wgt, (int)ml[b][3]);
+                const f32x4 y0 = {(float)x0[b][0], (float)x0[b][1], (float)x0[b][2], (float)x0[b][3]};
+                const f32x4 y1 = {(float)x1[b][0], (float)x1[b][1], (float)x1[b][2], (float)x1[b][3]};
+                lsum = ok ? lsum + wgt * ml[b][1] : lsum;
+                a0 = ok ? a0 + w0 * y0 : a0;
+                a1 = ok ? a1 + w1 * y1 : a1;
             }
         }
     }
@@ -479,7 +512,7 @@ size_t mla_workspace_bytes(int n_q, int n_heads, int k, int n_layers) {
     const int per = n_layers < kMaxLayersPerLaunch ? n_layers : kMaxLayersPerLaunch;
     const int s = choose_split(n_q * per, k);
     if (s == 1) return 0;
-    return (size_t)per * n_q * s * kHeads * (kLat + 2) * sizeof(float);
+    return (size_t)per * n_q * s * kHeads * (kLat * sizeof(_Float16) + 4 * sizeof(float));
 }
 
 hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, const int32_t* q_seq,
@@ -502,8 +535,8 @@ hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, co
         const int per = n_layers < kMaxLayersPerLaunch ? n_layers : kMaxLayersPerLaunch;
         const int s = choose_split(n_q * per, k);
         const int rows = k / s;
-        float* part_o = (float*)ws;
-        float* part_ml = s > 1 ? part_o + (size_t)per * n_q * s * kHeads * kLat : nullptr;
+        _Float16* part_o = (_Float16*)ws;
+        float* part_ml = s > 1 ? (float*)(part_o + (size_t)per * n_q * s * kHeads * kLat) : nullptr;
         if (fp8_kv)
             hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq,
                                idx, k, n_q, n_cap, block_table, page_size, max_pages, scale_log2, rows,
