@@ -859,9 +859,10 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__
 // (written through to, and read from, the device's coherence point), and each
 // wave waits for its stores to complete before the flag is set, so no L2
 // write-back (a release fence: microseconds per wave) is needed. A part that
-// overflows (ties at the bound, rows without one), or more than 2 kK / pn
-// candidates in a share, sends the row to a batched fallback over the whole
-// list in the work-group that runs step 4.
+// overflows (ties at the bound, rows without one), or more than 2 kK
+// candidates in all, sends the row to a batched fallback over the whole list
+// in the work-group that runs step 4; a share with more than its window of
+// 2 kK / pn candidates costs one more round trip to load them compacted.
 struct SplitArgs {
     unsigned long long* flags;   // [row][share]: the tag of the launch that filled the share
     uint8_t* regions;            // [row][share]: candidate count, then (score bits, position) pairs
@@ -1166,27 +1167,51 @@ __device__ __forceinline__ void topk_row_body(const float* __restrict__ scores, 
             x[r] = load_dev((const unsigned long long*)(rrow + (size_t)(i >> wsh) * kRegionBytes + kRegionHead) +
                             (i & (W - 1)));
         }
-        uint32_t cnt_u[kMaxShares];
+        uint32_t cnt_u[kMaxShares];                             // 0 past the row's shares
 #pragma unroll
-        for (int u = 0; u < kMaxShares; ++u)
-            cnt_u[u] = (uint32_t)load_dev((const unsigned long long*)(rrow + (size_t)(u < pn ? u : 0) * kRegionBytes));
-        bool fits = true;
+        for (int u = 0; u < kMaxShares; ++u) {
+            const uint32_t c = (uint32_t)load_dev((const unsigned long long*)(rrow + (size_t)(u < pn ? u : 0) * kRegionBytes));
+            cnt_u[u] = u < pn ? c : 0u;
+        }
+        bool fits = true, over = false;                         // every share in its window; a part overflowed
+        uint32_t n = 0;
 #pragma unroll
-        for (int u = 0; u < kMaxShares; ++u) fits = fits && cnt_u[u] <= (uint32_t)W;   // all ones: overflow
+        for (int u = 0; u < kMaxShares; ++u) {
+            over = over || cnt_u[u] == 0xffffffffu;
+            fits = fits && cnt_u[u] <= (uint32_t)W;
+            n += cnt_u[u] == 0xffffffffu ? 0u : cnt_u[u];
+        }
         if (t < pn) store_dev(flag + t, 0ull);                  // every share has arrived: clear for the next launch
-        if (fits) {                                             // uniform
-            uint32_t pv[kPerSmall], pp[kPerSmall], n = 0;
+        if (!over && n <= (uint32_t)(2 * kK)) {                 // uniform
+            if (!fits) {
+                // a share holds more than its window (candidates clustered in
+                // part of the row): load again, compacted, item i being entry i -
+                // roff[u] of share u
+                uint32_t roff[kMaxShares + 1];
+                roff[0] = 0;
+#pragma unroll
+                for (int u = 0; u < kMaxShares; ++u) roff[u + 1] = roff[u] + cnt_u[u];
+#pragma unroll
+                for (int r = 0; r < kPerSmall; ++r) {
+                    const uint32_t i = 64 * kPerSmall * wave + 64 * r + lane;
+                    int u = 0;
+#pragma unroll
+                    for (int j = 1; j < kMaxShares; ++j) u += (j < pn && i >= roff[j]) ? 1 : 0;
+                    x[r] = load_dev((const unsigned long long*)(rrow + (size_t)u * kRegionBytes + kRegionHead) +
+                                    min(i - roff[u], (uint32_t)(2 * kK - 1)));
+                }
+            }
+            uint32_t pv[kPerSmall], pp[kPerSmall];
 #pragma unroll
             for (int r = 0; r < kPerSmall; ++r) {
                 const int i = 64 * kPerSmall * wave + 64 * r + lane;
                 uint32_t c = cnt_u[0];
 #pragma unroll
                 for (int u = 1; u < kMaxShares; ++u) c = (i >> wsh) == u ? cnt_u[u] : c;
-                pv[r] = (uint32_t)(i & (W - 1)) < c ? score_key(__uint_as_float((uint32_t)x[r])) : 0u;
+                const bool valid = fits ? (uint32_t)(i & (W - 1)) < c : (uint32_t)i < n;
+                pv[r] = valid ? score_key(__uint_as_float((uint32_t)x[r])) : 0u;
                 pp[r] = (uint32_t)(x[r] >> 32);
             }
-#pragma unroll
-            for (int u = 0; u < kMaxShares; ++u) n += cnt_u[u];
             const int cnt = select_final<kPerSmall>(pv, pp, L == 0u ? 1u : L, Mx, n, out, s.sc);
             write_final_pad(out, cnt);
             return;

@@ -340,6 +340,32 @@ def test_topk_split_rows_with_more_candidates_than_one_selection_takes():
     _topk_case(s, pos, "every group at the bound")
 
 
+@pytest.mark.parametrize("n,rows", [(1 << 20, 3), (131_072, 40)])
+def test_topk_split_rows_with_candidates_clustered_in_one_share(n, rows):
+    # scores rising with the position (recent positions score higher, as in
+    # attention): every candidate lies in the row's last share, far more than
+    # its window of 4096 / shares; a few rows are i.i.d. for contrast
+    g = torch.Generator().manual_seed(71)
+    pos_f = torch.arange(n, dtype=torch.float32)
+    s = pos_f[None, :] / 64.0 + torch.randint(0, 8, (rows, n), generator=g).float()
+    s[1] = W.score_matrix("normal", 1, n, seed=72)[0]
+    pos = torch.full((rows,), n - 1, dtype=torch.int32)
+    pos[2] = n - 5000
+    _topk_case(s, pos, f"clustered candidates n={n} rows={rows}")
+
+
+def test_topk_four_shares_with_short_rows():
+    # 40 rows: four shares per row; short rows (no bound, or fewer than 2048
+    # candidates in all) beside full ones
+    n, rows = 131_072, 40
+    s = torch.stack([W.score_matrix(("normal", "int_ties", "few_values")[i % 3], 1, n, seed=80 + i)[0]
+                     for i in range(rows)])
+    pos = torch.full((rows,), n - 1, dtype=torch.int32)
+    pos[0:8] = torch.tensor([0, 1, 100, 2046, 2047, 2048, 3000, 4095], dtype=torch.int32)
+    pos[8:12] = torch.tensor([65_535, 65_536, 70_000, 100_000], dtype=torch.int32)
+    _topk_case(s, pos, f"{rows} rows with short ones")
+
+
 def test_topk_row_kernel_without_split():
     # 128..511 rows: one work-group per row, the default build
     n, rows = 70_000, 130
