@@ -18,6 +18,7 @@ import torch
 import bench
 import long_context_sparse_02_amd as gsa
 import oracle
+import rounding
 import workloads as W
 from gpu_util import ATOL_LSE, ATOL_OUT, assert_scores_equal, dev, max_abs, np32, say, note
 
@@ -140,9 +141,10 @@ def test_stack78_full_size():
 
 def test_prefill_rotated_fp8_full_size():
     # Hadamard-rotated fp8 indexer: the selection is exact for the scores the
-    # kernel produced (all properties above), and the sampled queries' scores and
-    # sets track the oracle's rotated-fp8 scores (not bit-exact: rotated values
-    # are not integers, so fp32 accumulation rounds)
+    # kernel produced (all properties above); the sampled queries' scores are
+    # within 1e-4 (1 + |s|) of the oracle's rotated-fp8 scores (rotated values
+    # are not integers, so fp32 accumulation rounds), and their sets are the
+    # oracle's except among positions that bound leaves open
     wl, inp, bufs = run_unit("prefill_q4096_n131072_fp8h")
     check_selection_properties(bufs["scores"], bufs["idx"][0], inp["q_pos"], wl.n_ctx)
     for qi in [0, 2047, 4095]:
@@ -153,10 +155,9 @@ def test_prefill_rotated_fp8_full_size():
         fin = np.isfinite(row)
         assert np.array_equal(np.isfinite(got), fin)
         assert np.all(np.abs(got[fin] - row[fin]) <= 1e-4 * (1 + np.abs(row[fin])))
-        want = set(oracle.topk_select(row[None], pos, 2048)[0]) - {-1}
-        have = set(np32(bufs["idx"][0, qi])) - {-1}
-        assert len(want & have) >= 0.995 * len(want)
-        say(f"{wl.name}: query {qi} tracks the oracle ({len(want & have)} of {len(want)} shared)")
+        # the set differs from the oracle's only where the score bound leaves it open
+        n_band = rounding.check_selection_within_bound(np32(bufs["idx"][0, qi]), row, 2048, 1e-4)
+        say(f"{wl.name}: query {qi}: selection fixed by the bound except {n_band} positions at the threshold")
 
 
 def test_decode_full_chunks_with_queries_inside_the_row():

@@ -26,20 +26,18 @@ def test_rotated_quantiser_bit_exact_on_integer_inputs():
 
 
 def test_rotated_quantiser_on_float_inputs():
-    # bf16 N(0,1) blocks with spread exponents: the staged fp32 sums can differ
-    # from the once-rounded exact sum in the last bit, which may move a code by
-    # one step at a rounding boundary; the scales follow the block maximum
+    # bf16 N(0,1) blocks with spread exponents: the kernel's staged float32
+    # butterflies may differ from the oracle's once-rounded sums in the last
+    # bits, within the bound of tests/rounding.py; every code and scale whose
+    # decision that bound fixes must be the oracle's exactly
+    import rounding
     g = torch.Generator().manual_seed(8)
     x = (torch.randn((4096, 128), generator=g) * torch.exp2(torch.randint(-6, 6, (4096, 1), generator=g).float()))
     x = x.to(torch.bfloat16)
     codes, scales = gsa.quantize_e4m3(x.to(dev()), hadamard=True)
-    oc, osc = oracle.quantize_blocks_hadamard(np32(x))
-    got = np32(codes).astype(np.int64)
-    diff = np.abs(got - oc.astype(np.int64))
-    n_bad = int(np.count_nonzero(diff))
-    say(f"rotated codes differing from the oracle: {n_bad} of {diff.size}")
-    assert np.all(diff <= 1) and n_bad <= diff.size // 1000
-    assert np.mean(np32(scales).astype(np.float64) == osc[..., 0]) > 0.999
+    n, n_open, n_scale_open = rounding.check_rotated_codes(np32(codes), np32(scales), np32(x))
+    say(f"rotated codes: {n} compared, {n_open} at an open boundary, {n_scale_open} blocks with an open scale")
+    assert n >= x.numel() - 128 * n_scale_open          # only blocks with an open scale may be skipped
 
 
 def test_rotated_fp8_score_and_topk():
@@ -62,9 +60,10 @@ def test_rotated_fp8_score_and_topk():
     # zero can land on either side
     err = np.abs(got[fin] - want[fin])
     assert np.all(err <= 1e-4 * (1.0 + np.abs(want[fin]))), err.max()
-    # the selection is exact for the scores it was given, and near the oracle's
+    # the selection is exact for the scores it was given
     assert np.array_equal(np32(idx), oracle.topk_select(np32(scores), np32(q_pos), 2048))
-    osel = oracle.topk_select(want, np32(q_pos), 2048)
+    # and it differs from the oracle's own selection only among positions whose
+    # oracle scores the 1e-4 bound leaves at the threshold
+    import rounding
     for i in range(wl.n_q):
-        a, b = set(np32(idx)[i]) - {-1}, set(osel[i]) - {-1}
-        assert len(a & b) >= 0.995 * len(b), f"query {i}: {len(a & b)} of {len(b)}"
+        rounding.check_selection_within_bound(np32(idx)[i], want[i], 2048, 1e-4)

@@ -203,3 +203,29 @@ def test_kth_group_max_bounds_the_kth_score():
         if gm.shape[1] < k:
             continue
         assert np.sort(gm[0])[::-1][k - 1] <= np.sort(s[0])[::-1][k - 1]
+
+
+def test_selection_bound_check_accepts_perturbed_scores_and_rejects_wrong_sets():
+    # the check the rotated-fp8 GPU tests use: a selection made from scores
+    # within tau (1 + |s|) of the oracle's passes it; swapping a clearly
+    # selected position for a clearly unselected one fails it
+    import rounding
+    rng = np.random.default_rng(4)
+    n, k, tau = 20000, 2048, 1e-4
+    want = rng.standard_normal(n) * 3.0
+    want[-100:] = -np.inf                                   # masked tail
+    want[500:540] = np.sort(want[~np.isinf(want)])[-k]      # ties at the threshold
+    pos = np.array([n - 101], np.int32)
+    noisy = want + tau * (1.0 + np.abs(np.where(np.isinf(want), 0.0, want))) * rng.uniform(-1, 1, n)
+    sel = oracle.topk_select(noisy[None], pos, k)[0]
+    n_band = rounding.check_selection_within_bound(sel, want, k, tau)
+    assert n_band >= 40
+    order = np.argsort(-np.where(np.isinf(want), -1e30, want))
+    bad = sel.copy()
+    bad[bad == order[0]] = order[-200]                      # best position out, a poor one in
+    with pytest.raises(AssertionError):
+        rounding.check_selection_within_bound(bad, want, k, tau)
+    # rows with at most k causal positions select them all
+    short = want.copy()
+    short[100:] = -np.inf
+    assert rounding.check_selection_within_bound(np.arange(100), short, k, tau) == 0

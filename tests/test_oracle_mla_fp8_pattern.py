@@ -353,6 +353,50 @@ def test_rotation_closed_forms():
     assert np.array_equal(oracle.rotate_blocks(x2)[0, 128:], want) and not oracle.rotate_blocks(x2)[0, :128].any()
 
 
+def _spread_bf16_blocks(n=4096, seed=8):
+    # bf16 N(0,1) blocks, each row scaled by its own power of two in [2^-6, 2^5]
+    g = torch.Generator().manual_seed(seed)
+    x = torch.randn((n, 128), generator=g) * torch.exp2(torch.randint(-6, 6, (n, 1), generator=g).float())
+    return x.to(torch.bfloat16)
+
+
+def test_staged_rotation_bound_holds_on_a_staged_float32_rotation():
+    # The exact check of the rotated quantiser's codes rests on the error bound
+    # of a staged float32 rotation (tests/rounding.py). A second staged
+    # computation, quantised by the oracle's rule, must pass it; it does differ
+    # from the oracle's once-rounded sums, so the bound is exercised.
+    import rounding
+    x = _spread_bf16_blocks().float().numpy()
+    y = rounding.staged_rotation_fp32(x)
+    assert np.any(y != oracle.rotate_blocks(x))
+    codes, scales = oracle.quantize_blocks(y.astype(np.float64))
+    n, n_open, n_scale_open = rounding.check_rotated_codes(codes, scales[..., 0], x)
+    assert n == x.size
+    assert n_open < x.size // 100 and n_scale_open < x.shape[0] // 100
+
+
+def test_staged_rotation_check_rejects_wrong_codes_and_scales():
+    import rounding
+    x = _spread_bf16_blocks(256, seed=9).float().numpy()
+    codes, scales = oracle.quantize_blocks_hadamard(x)
+    rounding.check_rotated_codes(codes, scales[..., 0], x)
+    y = oracle.rotate_blocks(x).astype(np.float64)
+    delta = rounding.staged_rotation_bound(x)[..., 0]
+    # a code one step off where the bound fixes it
+    lo = oracle.e4m3_encode((y - delta[:, None]) / scales)
+    hi = oracle.e4m3_encode((y + delta[:, None]) / scales)
+    r, c = np.argwhere((lo == hi) & ((codes & 0x7F) > 0) & ((codes & 0x7F) < 0x7E))[0]
+    bad = codes.copy()
+    bad[r, c] += 1
+    with pytest.raises(AssertionError):
+        rounding.check_rotated_codes(bad, scales[..., 0], x)
+    # a block scale doubled where the block maximum is far from a scale step
+    bad_s = scales[..., 0].copy()
+    bad_s[r] *= 2.0
+    with pytest.raises(AssertionError):
+        rounding.check_rotated_codes(codes, bad_s, x)
+
+
 def test_rotation_keeps_dot_products_and_inverts_itself():
     rng = np.random.default_rng(2)
     q = rng.standard_normal((50, 128))
