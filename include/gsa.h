@@ -122,6 +122,12 @@ gsa_status gsa_quantize_e4m3_hadamard(const void* x_dev, int64_t n_blocks,
  *            pass over scores that cannot be selected.
  * Errors: null pointers, n_q < 1, batch < 1, n_cap < 1, bad ld, bad dtype,
  *         missing scales for FP8, n_cap > 2^31 - 1.
+ * Concurrency: FP8 calls with one query per sequence, a query count dividing
+ * 256, n_cap a multiple of 1024 and n_q * n_cap >= 2^23 hand out key chunks
+ * through per-query counters in a static device array of 64 slots (no
+ * allocation; every launch leaves its slot at zero). Such a launch takes a
+ * new slot each call: at most 63 other such launches may start on the same
+ * device while one runs.
  */
 gsa_status gsa_indexer_score(gsa_dtype dt,
                              const void* q_dev, const float* q_scale_dev, const float* w_dev,

@@ -24,6 +24,7 @@
 // swizzled inside their key row, which makes the MFMA-layout ds_read_b128
 // conflict-free. Queries of one sequence that share a work-group (QB of them)
 // reuse each key tile from LDS.
+#include <mutex>
 #include <type_traits>
 
 #include "device_common.h"
@@ -319,6 +320,210 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
             }
         }
         j0 = j1;
+    }
+}
+
+// ---- fp8 decode rows on a persistent grid --------------------------------------
+// One query per sequence, fp8 keys, rows of whole 1024-key chunks: 256
+// work-groups, one per CU; work-group b serves query (b/8 + 32 (b%8)) mod n_q
+// (so a query's work-groups sit on every XCD) and takes its query's chunks one
+// by one from a per-query counter until the counter passes the row's chunk
+// count. With equal chunks handed out in launch order (two rounds of 16K-key
+// work-groups) the CUs stop at different times: the second round's last
+// work-groups run alone for about 7% of the launch; here every CU keeps taking
+// 1024-key chunks until none are left, and the ring runs on across chunks.
+//
+// The counters are a static array of kDynSlots slots of 256, zero when the
+// library loads; a launch uses the slot its tag selects, and the work-group
+// whose grab comes last (each work-group fails exactly once, so the last grab
+// returns chunks + work-groups - 1) sets the counter back to zero, so every
+// launch finds its counters at zero. Launches running at the same time must use
+// different slots: at most kDynSlots - 1 other launches may start while one runs.
+//
+// Waves 0-3 move, score and store the keys as in the one-query kernel. A fifth
+// wave only takes the grabs: a grab is an atomic add whose result the compiler
+// waits for with the wave's whole memory counter, which in a wave with DMAs or
+// score stores in flight would wait for those too. It grabs the chunk of slot
+// s + 2 when slot s starts and posts it to LDS one slot later; the other waves
+// read it there.
+constexpr int kDynChunk = 1024;                 // keys per grab (4 tiles)
+constexpr int kDynWGs = 256;
+constexpr int kDynSlots = 64;
+constexpr int kDynMaxQ = 256;
+constexpr int kDynThreads = kThreads + 64;      // four streaming waves and the grabbing wave
+__device__ int g_dyn_ctr[kDynSlots * kDynMaxQ];
+
+__global__ __launch_bounds__(kDynThreads) void indexer_score_dyn(
+    const uint8_t* __restrict__ q, const float* __restrict__ q_scale,
+    const float* __restrict__ w, const uint8_t* __restrict__ k,
+    const float* __restrict__ k_scale, const int32_t* __restrict__ q_seq,
+    const int32_t* __restrict__ q_pos, int n_q, int64_t n_cap,
+    float* __restrict__ scores, int64_t ld, float* __restrict__ gmax, int64_t ldg, int* __restrict__ ctr) {
+    using T = KeyTile<true, 256>;
+    constexpr int TPC = kDynChunk / T::kKeys;   // tiles per chunk
+    static_assert(TPC >= kRing - 1, "a tile issued kRing - 1 ahead is at most one chunk ahead");
+    constexpr int NSUBT = T::kKeys / 32;        // 32-key subtiles per tile
+    constexpr int PPW = NSUBT / 4;              // subtiles per streaming wave
+    constexpr int KSTEPS = 2;
+    constexpr int kGrab = 4;                    // the grabbing wave
+    typedef __attribute__((address_space(3))) uint8_t lds_u8;
+    typedef __attribute__((address_space(1))) int gint;
+    __shared__ __attribute__((aligned(16))) uint8_t ring[kRing * T::kSlot];
+    __shared__ int chq[4];                      // chunk of slot s at chq[s % 4], -1: none
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int n = lane & 31, g = lane >> 5;
+    const int b = blockIdx.x;
+    const int qi = ((b >> 3) + 32 * (b & 7)) % n_q;
+    const int wgs = (int)gridDim.x / n_q;       // work-groups of this query
+    const int nch = (int)(n_cap / kDynChunk);
+    // the counter's address in a vector register: the compiler's atomic
+    // optimizer, which rewrites an add at a uniform address into one lane's add
+    // plus a broadcast of its result (a wait for the result right after the
+    // add), leaves it alone; a global (not generic) pointer, so the add counts
+    // in vmcnt only
+    uint64_t cnt_addr = (uint64_t)(uintptr_t)(ctr + qi);
+    asm volatile("" : "+v"(cnt_addr));
+    gint* const cnt = (gint*)cnt_addr;
+
+    int pend = 0;                               // grabbing wave, lane 0: the grab in flight
+    bool more = true;                           // no grab of this work-group has failed yet
+    if (wave == kGrab && lane == 0) pend = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    // grabbing wave: post the grab in flight as the chunk of slot `sl`, and grab
+    // again while chunks remain
+    auto post = [&](int sl) __attribute__((always_inline)) {
+        if (wave == kGrab) {
+            if (lane == 0) {
+                const int v = more ? pend : nch;
+                const bool ok = v >= 0 && v < nch;              // (any other value: no chunk)
+                if (more && !ok && v == nch + wgs - 1)          // the last grab of this launch
+                    __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                chq[sl & 3] = ok ? v : -1;
+                if (ok) pend = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                more = ok;
+            }
+            more = __builtin_amdgcn_readfirstlane(more ? 1 : 0) != 0;
+            __builtin_amdgcn_s_waitcnt(0xC07F);          // lgkmcnt(0): the posted chunk is in LDS
+        }
+    };
+
+    i32x8 a[KSTEPS];
+    float wr[16];
+    int apos = 0, a_e8 = 127, seq = 0;
+    if (wave < kGrab) {
+        apos = q_pos[qi];
+        seq = q_seq[qi];
+        const uint8_t* qh = q + ((int64_t)qi * kHeads + n) * T::kRowBytes;
+#pragma unroll
+        for (int t = 0; t < KSTEPS; ++t) {
+            const i32x4* p = (const i32x4*)(qh + 64 * g + 32 * t);
+            const i32x4 lo = p[0], hi = p[1];
+            a[t] = i32x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        }
+#pragma unroll
+        for (int i = 0; i < 16; ++i) wr[i] = w[(int64_t)qi * kHeads + 8 * (i >> 2) + 4 * g + (i & 3)];
+        a_e8 = e8m0_of(q_scale[(int64_t)qi * kHeads + n]);
+        wait_vmcnt<0>();   // operands are in registers before any ring load is counted
+    }
+    post(0);
+    __syncthreads();
+
+    const uint8_t* kb = k + (int64_t)seq * n_cap * T::kRowBytes;
+    const float* ksb = k_scale + (int64_t)seq * n_cap;
+    // DMA instructions per tile issued by this wave (wave 0 also moves the scales)
+    const int per = wave < kGrab ? T::kDmaPerWave + (wave == 0 ? T::kScaleDma : 0) : 0;
+    const uint32_t ring_base = (uint32_t)(uintptr_t)(lds_u8*)ring;
+    uint32_t doff[T::kDmaPerWave];
+#pragma unroll
+    for (int jd = 0; jd < T::kDmaPerWave; ++jd) {
+        const int i = wave * T::kDmaPerWave + jd;
+        const int r = i * T::kRowsPerDma + lane / T::kChunks;
+        const int c = (lane % T::kChunks) ^ (r & (T::kChunks - 1));
+        doff[jd] = (uint32_t)(r * T::kRowBytes + 16 * c);
+    }
+    auto issue = [&](int64_t t0, int slot) __attribute__((always_inline)) {   // a whole tile inside the row
+        if (wave >= kGrab) return;
+        const uint32_t dst = ring_base + slot * T::kSlot;
+        const uint8_t* base = kb + t0 * T::kRowBytes;
+#pragma unroll
+        for (int jd = 0; jd < T::kDmaPerWave; ++jd)
+            lds_dma16_so<true>(base, doff[jd], dst + 1024 * (wave * T::kDmaPerWave + jd));
+        if (wave == 0) {
+#pragma unroll
+            for (int h = 0; h < T::kScaleDma; ++h)
+                lds_dma4_so<true>(ksb + t0, 4 * (64 * h + lane), dst + T::kBytes + 256 * h);
+        }
+    };
+
+    // tiles are numbered u = 0, 1, ... over this work-group's chunks: tile u is
+    // tile u % TPC of the chunk of slot u / TPC
+    int cc = __builtin_amdgcn_readfirstlane(chq[0]);   // chunk being computed
+    int ic = cc;                                        // chunk being issued
+    int issued = 0;
+    if (cc >= 0) {
+#pragma unroll
+        for (int p = 0; p < kRing - 1; ++p) issue((int64_t)cc * kDynChunk + (int64_t)p * T::kKeys, p);
+        issued = kRing - 1;
+    }
+    const int stores = (scores != nullptr) ? PPW : 0;     // score stores per tile and streaming wave
+    for (int u = 0; cc >= 0; ++u) {
+        const int ut = u % TPC;
+        if (wave < kGrab) {
+            // later issued: the DMAs of tiles u+1 .. issued-1 and the score stores
+            // of the iterations since tile u was issued
+            wait_vmcnt_le(__builtin_amdgcn_readfirstlane((issued - u - 1) * per + stores * min(u, kRing - 1)));
+        }
+        ring_barrier();   // every wave's part of tile u landed; tile u-1's readers are done
+        if (ut == 0) post(u / TPC + 1);
+        {
+            const int un = u + kRing - 1;        // the tile to issue now
+            if (un % TPC == 0) ic = ic >= 0 ? __builtin_amdgcn_readfirstlane(chq[(un / TPC) & 3]) : -1;
+            if (ic >= 0) {
+                issue((int64_t)ic * kDynChunk + (int64_t)(un % TPC) * T::kKeys, un % kRing);
+                ++issued;
+            }
+        }
+        if (wave < kGrab) {
+            const int64_t t0 = (int64_t)cc * kDynChunk + (int64_t)ut * T::kKeys;
+            const lds_u8* tile = (const lds_u8*)ring + (u % kRing) * T::kSlot;
+            f32x16 acc[PPW];
+#pragma unroll
+            for (int p = 0; p < PPW; ++p) {
+                const int row = (wave * PPW + p) * 32 + n;
+                acc[p] = f32x16{};
+#pragma unroll
+                for (int t = 0; t < KSTEPS; ++t) {
+                    const i32x4 lo = *(const __attribute__((address_space(3))) i32x4*)(tile + T::off(row, 4 * g + 2 * t));
+                    const i32x4 hi = *(const __attribute__((address_space(3))) i32x4*)(tile + T::off(row, 4 * g + 2 * t + 1));
+                    const i32x8 bb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                    const float ks = *(const __attribute__((address_space(3))) float*)(tile + T::kBytes + 4 * row);
+                    acc[p] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a[t], bb, acc[p], 0, 0, 0, a_e8, 0, e8m0_of(ks));
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            float res[PPW];
+#pragma unroll
+            for (int p = 0; p < PPW; ++p) {
+                const int64_t sk = t0 + (wave * PPW + p) * 32 + n;
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                    part = fmaf(wr[i], __int_as_float(max(__float_as_int(acc[p][i]), 0)), part);
+                part = sum_x32(part);
+                res[p] = sk <= apos ? part : neg_inf();
+            }
+#pragma unroll
+            for (int p = 0; p < PPW; ++p) {
+                const int64_t s0 = t0 + (wave * PPW + p) * 32;
+                if (scores != nullptr && g == 0) store_score<true>(scores + (int64_t)qi * ld + s0 + n, res[p]);
+                if (gmax != nullptr) {
+                    const uint32_t m = max_x32(score_key(res[p]));
+                    if (lane == 0) gmax[(int64_t)qi * ldg + (s0 >> 5)] = key_value(m);
+                }
+            }
+        }
+        if ((u + 1) % TPC == 0) cc = __builtin_amdgcn_readfirstlane(chq[((u + 1) / TPC) & 3]);
     }
 }
 
@@ -769,6 +974,28 @@ hipError_t launch_qb(bool fp8, bool nt, dim3 grid, hipStream_t st, const void* q
     return hipGetLastError();
 }
 
+// The current device's copy of g_dyn_ctr (host code must not use the array's
+// name as a device address; its address is looked up once per device).
+constexpr int kMaxDevices = 64;
+std::mutex g_dyn_mu;
+int* g_dyn_ptr[kMaxDevices] = {};
+hipError_t dyn_counters(int** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_dyn_mu);
+    if (g_dyn_ptr[dev] == nullptr) {
+        void* p = nullptr;
+        e = hipGetSymbolAddress(&p, HIP_SYMBOL(g_dyn_ctr));
+        if (e != hipSuccess) return e;
+        if (p == nullptr) return hipErrorInvalidSymbol;
+        g_dyn_ptr[dev] = (int*)p;
+    }
+    *out = g_dyn_ptr[dev];
+    return hipSuccess;
+}
+
 }  // namespace
 
 hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, const float* w,
@@ -802,6 +1029,18 @@ hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, c
     // blocks of a chunk share its keys through L2; the multi-query kernel keeps
     // plain loads (compute bound; the hint measured 1% slower there).
     const bool nt = (per_seq + qb - 1) / qb <= 1;
+    // fp8 decode whose rows are whole 1024-key chunks, with at least 32K keys
+    // per CU and a query count dividing 256: the persistent grid
+    if (qb == 1 && fp8 && nt && n_q <= kDynMaxQ && kDynWGs % n_q == 0 && n_cap % kDynChunk == 0 &&
+        (int64_t)n_q * n_cap >= (int64_t)kDynWGs * 32768 && n_cap / kDynChunk < (1 << 30) - kDynWGs) {
+        int* ctr = nullptr;
+        const hipError_t e = dyn_counters(&ctr);
+        if (e != hipSuccess) return e;
+        ctr += (launch_tag() % kDynSlots) * kDynMaxQ;
+        hipLaunchKernelGGL(indexer_score_dyn, dim3(kDynWGs), dim3(kDynThreads), 0, stream, (const uint8_t*)q, q_scale, w,
+                           (const uint8_t*)k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, (ld + 31) / 32, ctr);
+        return hipGetLastError();
+    }
     switch (qb) {
         case 16: return launch_mq<16>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, (int)chunk);
         case 8: return launch_mq<8>(fp8, grid, stream, q, q_scale, w, k, k_scale, q_seq, q_pos, n_q, n_cap, scores, ld, gmax, (int)chunk);

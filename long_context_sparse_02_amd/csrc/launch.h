@@ -8,6 +8,11 @@
 
 namespace gsa {
 
+// A new tag per call: a per-process 64-bit sequence from a start that differs
+// between processes, never 0. Kernels that hand work over through device
+// memory mark it with the tag of their launch.
+unsigned long long launch_tag();
+
 // rotate: multiply each 128-element block by the orthonormal Hadamard matrix first.
 hipError_t launch_quantize_e4m3(const void* x, int64_t n_blocks, uint8_t* codes, float* scales,
                                 bool rotate, hipStream_t stream);

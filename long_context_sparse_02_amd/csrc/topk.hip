@@ -1669,6 +1669,8 @@ unsigned long long next_tag() {
 
 }  // namespace
 
+unsigned long long launch_tag() { return next_tag(); }
+
 size_t topk_workspace_bytes(int n_q, int64_t ld, int k) {
     (void)k;
     const int nc = n_chunks_of(ld);

@@ -162,6 +162,54 @@ def test_score_one_query_rows_past_the_query():
         assert np.all(got[:, n_cap:] == 12345.0) and np.all(gm[:, ng:] == 777.0)
 
 
+def test_score_persistent_fp8_grid_repeated_calls():
+    # fp8 decode over 8 rows of 2^20 keys runs on the persistent grid: 256
+    # work-groups taking 1024-key chunks from per-query counters that every
+    # launch leaves at zero. Queries sit inside their rows (at 0, at chunk
+    # edges, mid-row, at the end); the buffers start as NaN, so a chunk that no
+    # work-group took shows; 70 calls use every counter slot at least once and
+    # each must equal the first bit for bit; sampled rows are bit-exact against
+    # the oracle, every row is -inf past its query, and every row's group
+    # maxima are those of its scores.
+    n_cap = 1 << 20
+    pos = [0, 1023, 1024, 333_333, 524_287, 524_288, 1_000_000, n_cap - 1]
+    wl = W.Workload("grid_fp8", len(pos), n_cap, 1, 1, "fp8")
+    d = dev()
+    q, w = W.indexer_queries(wl, 71, 0)
+    k = W.indexer_keys(wl, 71, 0, device=d)
+    sample = [0, 2, 5, 7]
+    k_host = {b: np32(k[b]) for b in sample}
+    q_seq = torch.arange(len(pos), dtype=torch.int32, device=d)
+    q_pos = torch.tensor(pos, dtype=torch.int32, device=d)
+    qc, qs = gsa.quantize_e4m3(q.to(d))
+    kc, ks = gsa.quantize_e4m3(k)
+    del k
+    wd = w.to(d)
+    scores = torch.empty((len(pos), n_cap), device=d)
+    gmax = torch.empty((len(pos), gsa.group_max_ld(n_cap)), device=d)
+    first = None
+    for call in range(70):
+        scores.fill_(float("nan"))
+        gmax.fill_(float("nan"))
+        gsa.indexer_score(qc, wd, kc, q_seq, q_pos, q_scale=qs, k_scale=ks, scores=scores, group_max=gmax)
+        if first is None:
+            first = (scores.clone(), gmax.clone())
+            assert not bool(torch.isnan(first[0]).any()) and not bool(torch.isnan(first[1]).any())
+        else:
+            assert torch.equal(scores, first[0]) and torch.equal(gmax, first[1]), f"call {call}"
+    torch.cuda.synchronize()
+    got, gm = np32(first[0]), np32(first[1])
+    for i, p in enumerate(pos):
+        assert np.all(np.isneginf(got[i, p + 1:])), f"query at {p}: past positions"
+        assert np.all(np.isfinite(got[i, :p + 1])), f"query at {p}: causal positions"
+    assert_scores_equal(gm.ravel(), oracle.group_max(got).ravel(), "group maxima of the scores")
+    for b in sample:
+        say(f"persistent fp8 grid: oracle row {b} (query at {pos[b]})")
+        want = oracle.indexer_score(np32(q[b:b + 1]), np32(w[b:b + 1]), k_host[b][None],
+                                    np.zeros(1, np.int32), np.array([pos[b]], np.int32))[0]
+        assert_scores_equal(got[b], want, f"row {b}")
+
+
 def test_score_negative_weights_and_float_inputs():
     g = torch.Generator().manual_seed(9)
     q = (torch.randn((6, 32, 128), generator=g)).to(torch.bfloat16)
