@@ -22,11 +22,24 @@
 // least k positions score >= L, so every selected score is >= L and lies in a
 // group whose maximum reaches L (about k groups, whatever the row length).
 //
+// Final selection. The candidates that pass the bound have keys in [L, largest
+// maximum], both known: select_final finds the 2048th key with one histogram
+// pass over 2048 equal key ranges and one wave's rank of the range holding it
+// (more than 64 items there, heavy ties: select_wide), then keeps every key
+// above that item and the equal ones not after it.
+//
 // Kernels:
 //   topk_row    rows of 64K to 1M positions: one work-group per row takes the
 //               row's maxima, L, the list of groups that reach it, those groups'
 //               scores only (each wave a contiguous share, compacted without
 //               work-group barriers) and the final selection, in one launch.
+//   topk_row_split
+//               the same for launches of at most 128 rows, each row split over
+//               2, 4 or 8 work-groups: every share bounds the whole row, lists
+//               and streams its own part of the groups, and hands its
+//               candidates over through the workspace (write-through stores,
+//               then a flag set to the launch's tag); the share that finds every
+//               flag of its row set runs the final selection and clears them.
 //   topk_chunk + topk_merge
 //               other widths: one work-group per 16K-score chunk keeps its top
 //               k as a (key, position) list in position order (with a bound
