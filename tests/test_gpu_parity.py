@@ -210,6 +210,45 @@ def test_score_persistent_fp8_grid_repeated_calls():
         assert_scores_equal(got[b], want, f"row {b}")
 
 
+@pytest.mark.parametrize("n_q,n_cap", [(1, 1 << 23), (256, 1 << 15), (32, 1 << 18)])
+def test_score_persistent_fp8_grid_query_counts(n_q, n_cap):
+    # the persistent grid at the ends of its range: one query (all 256
+    # work-groups on one counter), 256 queries (one work-group each) and 32;
+    # queries at random positions inside their rows, buffers starting as NaN,
+    # two calls in a row equal, sampled rows bit-exact against the oracle
+    wl = W.Workload("grid_q%d" % n_q, n_q, n_cap, 1, 1, "fp8")
+    d = dev()
+    g = torch.Generator().manual_seed(73 + n_q)
+    pos = torch.randint(0, n_cap, (n_q,), generator=g)
+    pos[0] = n_cap - 1
+    q, w = W.indexer_queries(wl, 74, 0)
+    k = W.indexer_keys(wl, 74, 0, device=d)
+    sample = sorted({0, n_q // 2, n_q - 1})
+    k_host = {b: np32(k[b]) for b in sample}
+    qc, qs = gsa.quantize_e4m3(q.to(d))
+    kc, ks = gsa.quantize_e4m3(k)
+    del k
+    q_seq = torch.arange(n_q, dtype=torch.int32, device=d)
+    q_pos = pos.to(torch.int32).to(d)
+    outs = []
+    for _ in range(2):
+        scores = torch.full((n_q, n_cap), float("nan"), device=d)
+        gmax = torch.full((n_q, gsa.group_max_ld(n_cap)), float("nan"), device=d)
+        gsa.indexer_score(qc, w.to(d), kc, q_seq, q_pos, q_scale=qs, k_scale=ks, scores=scores, group_max=gmax)
+        outs.append((scores, gmax))
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    got, gm = np32(outs[0][0]), np32(outs[0][1])
+    assert not np.isnan(got).any() and not np.isnan(gm).any()
+    assert_scores_equal(gm.ravel(), oracle.group_max(got).ravel(), "group maxima of the scores")
+    for b in sample:
+        p = int(pos[b])
+        assert np.all(np.isneginf(got[b, p + 1:])), f"query at {p}: past positions"
+        want = oracle.indexer_score(np32(q[b:b + 1]), np32(w[b:b + 1]), k_host[b][None],
+                                    np.zeros(1, np.int32), np.array([p], np.int32))[0]
+        assert_scores_equal(got[b], want, f"row {b}")
+
+
 def test_score_negative_weights_and_float_inputs():
     g = torch.Generator().manual_seed(9)
     q = (torch.randn((6, 32, 128), generator=g)).to(torch.bfloat16)
