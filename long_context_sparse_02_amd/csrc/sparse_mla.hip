@@ -15,7 +15,8 @@
 // two waves of a head group split both contractions: each takes Q.K over half
 // of the 576 dims and P.V over half of the 512 latent dims, and they swap
 // their fp32 partial scores through LDS (a + b == b + a, so both hold the
-// identical S and run the identical softmax). Per wave that is 36 registers
+// identical S and run the identical softmax); the swap waits on the
+// partner's flag only, not on the whole work-group. Per wave that is 36 registers
 // of Q and 64 of O, which leaves room for two waves per SIMD; the LDS reads
 // per 32-row block (each head group reads the block once for Q.K and once
 // for P.V) are what bounds this kernel.
@@ -90,6 +91,7 @@ __shared__ __attribute__((aligned(16))) uint8_t g_stage[kRing * kStageBuf];
 __shared__ __attribute__((aligned(16))) uint8_t g_blk[kBuf];
 __shared__ int32_t g_rows[kMaxRows];
 __shared__ f32x4 g_xs[kWaves][2][64];           // partial S^T of each wave (2 KiB per wave)
+__shared__ int g_xflag[kWaves];                  // the block (+1) whose partial S^T each wave has posted
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -217,6 +219,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     for (int u = 0; u < kIdxPer; ++u)
         if (tid + u * kThreads < nrows) rows_s[tid + u * kThreads] = iv[u];
 
+    if (lane == 0) g_xflag[wave] = 0;
     wait_vmcnt<0>();     // Q and the indices are in before any ring load is counted
     __syncthreads();
 
@@ -307,10 +310,19 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             }
         }
         // swap partial scores with the partner wave (same heads, other half)
+        // (a flag per wave instead of a work-group barrier: only the two waves of
+        // a head group wait for each other; the barrier of the next block keeps
+        // a wave from overwriting its scores before the partner has read them)
         g_xs[wave][0][lane] = sacc[0];
         g_xs[wave][1][lane] = sacc[1];
-        wait_lgkm0();
-        ring_barrier();
+        __hip_atomic_store(&g_xflag[wave], b + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // bounded: a post that never came would leave wrong scores, never a hang
+        for (int spin = 0; spin < (1 << 22); ++spin) {
+            const int f = __builtin_amdgcn_readfirstlane(
+                __hip_atomic_load(&g_xflag[wave ^ 4], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+            if (f == b + 1) break;
+            __builtin_amdgcn_s_sleep(1);
+        }
         sacc[0] += g_xs[wave ^ 4][0][lane];
         sacc[1] += g_xs[wave ^ 4][1][lane];
         float z[8];
