@@ -214,8 +214,9 @@ def test_score_persistent_fp8_grid_repeated_calls():
 def test_score_persistent_fp8_grid_query_counts(n_q, n_cap):
     # the persistent grid at the ends of its range: one query (all 256
     # work-groups on one counter), 256 queries (one work-group each) and 32;
-    # queries at random positions inside their rows, buffers starting as NaN,
-    # two calls in a row equal, sampled rows bit-exact against the oracle
+    # queries at random positions inside their rows, rows padded past n_cap,
+    # buffers starting as NaN, two calls in a row equal (the second without
+    # group maxima), sampled rows bit-exact against the oracle
     wl = W.Workload("grid_q%d" % n_q, n_q, n_cap, 1, 1, "fp8")
     d = dev()
     g = torch.Generator().manual_seed(73 + n_q)
@@ -230,15 +231,23 @@ def test_score_persistent_fp8_grid_query_counts(n_q, n_cap):
     del k
     q_seq = torch.arange(n_q, dtype=torch.int32, device=d)
     q_pos = pos.to(torch.int32).to(d)
+    # rows padded past n_cap (those columns must stay untouched); the second
+    # call writes no group maxima
+    ld = n_cap + 8
     outs = []
-    for _ in range(2):
-        scores = torch.full((n_q, n_cap), float("nan"), device=d)
-        gmax = torch.full((n_q, gsa.group_max_ld(n_cap)), float("nan"), device=d)
-        gsa.indexer_score(qc, w.to(d), kc, q_seq, q_pos, q_scale=qs, k_scale=ks, scores=scores, group_max=gmax)
+    for call in range(2):
+        scores = torch.full((n_q, ld), float("nan"), device=d)
+        gmax = torch.full((n_q, gsa.group_max_ld(ld)), float("nan"), device=d)
+        gsa.indexer_score(qc, w.to(d), kc, q_seq, q_pos, q_scale=qs, k_scale=ks, scores=scores,
+                          group_max=gmax if call == 0 else None)
         outs.append((scores, gmax))
     torch.cuda.synchronize()
-    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
-    got, gm = np32(outs[0][0]), np32(outs[0][1])
+    assert bool(torch.isnan(outs[0][0][:, n_cap:]).all()), "columns past n_cap written"
+    assert bool(torch.isnan(outs[1][1]).all()), "group maxima written without a buffer"
+    assert torch.equal(outs[0][0][:, :n_cap], outs[1][0][:, :n_cap])
+    ng = n_cap // 32
+    assert bool(torch.isnan(outs[0][1][:, ng:]).all())
+    got, gm = np32(outs[0][0][:, :n_cap]), np32(outs[0][1][:, :ng])
     assert not np.isnan(got).any() and not np.isnan(gm).any()
     assert_scores_equal(gm.ravel(), oracle.group_max(got).ravel(), "group maxima of the scores")
     for b in sample:
