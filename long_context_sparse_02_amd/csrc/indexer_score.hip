@@ -24,6 +24,12 @@
 // swizzled inside their key row, which makes the MFMA-layout ds_read_b128
 // conflict-free. Queries of one sequence that share a work-group (QB of them)
 // reuse each key tile from LDS.
+//
+// Kernels: indexer_score_kernel (one or two queries per work-group, a 2D grid
+// of equal key chunks); indexer_score_dyn (fp8 decode with one query per
+// sequence on a persistent grid that hands out 1024-key chunks through
+// self-resetting counters); indexer_score_mq (4, 8 or 16 queries of one
+// sequence per work-group, MTP verify and chunked prefill).
 #include <mutex>
 #include <type_traits>
 
