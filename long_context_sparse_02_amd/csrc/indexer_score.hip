@@ -1024,9 +1024,15 @@ hipError_t launch_indexer_score(bool fp8, const void* q, const float* q_scale, c
     // multi-query cap is 64K keys: each work-group first loads the A operands
     // of its 16 queries (128 KiB), and 4096 x 128K-key prefill measured 1.3-2.1%
     // faster than with 16K (32K: 1%; 128K: mixed).
+    // Launches too small to give every CU a 1024-key chunk (a few short rows)
+    // go down to one LDS tile per work-group: their time is one work-group's
+    // start-up and ring fill, so more and shorter chunks finish sooner.
     const int64_t min_wg = qb >= 4 ? 256 : fp8 ? 512 : 2048;
+    const int64_t min_chunk = qb >= 4 ? (fp8 ? 512 : 256) : (fp8 ? 256 : 128);
     int64_t chunk = qb >= 4 ? 65536 : 16384;
     while (chunk > 1024 && n_qblk * ((n_cap + chunk - 1) / chunk) < min_wg) chunk >>= 1;
+    if (n_qblk * ((n_cap + chunk - 1) / chunk) < 256)
+        while (chunk > min_chunk && n_qblk * ((n_cap + chunk - 1) / chunk) < 256) chunk >>= 1;
     const dim3 grid((unsigned)((n_cap + chunk - 1) / chunk), (unsigned)n_qblk);
     // One query block per sequence (decode): every key is read by one
     // work-group only, so the one-query kernel streams its keys with the
