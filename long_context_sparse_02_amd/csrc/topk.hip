@@ -40,6 +40,8 @@
 //               candidates over through the workspace (write-through stores,
 //               then a flag set to the launch's tag); the share that finds every
 //               flag of its row set runs the final selection and clears them.
+//   topk_small  rows of at most 4096 positions: one work-group per row, the
+//               row's smallest and largest key bounding select_final.
 //   topk_chunk + topk_merge
 //               other widths: one work-group per 16K-score chunk keeps its top
 //               k as a (key, position) list in position order (with a bound
@@ -845,6 +847,55 @@ __global__ __launch_bounds__(kThreads) void topk_chunk(const float* __restrict__
         const int cnt = full ? select_regs<kPer, true>(v, sc, em) : select_regs<kPer, false>(v, sc, em);
         if (threadIdx.x == 0) *(uint32_t*)Lst = (uint32_t)cnt;
     }
+}
+
+// Rows of at most 4096 positions (kPerSmall = 8 per lane): the smallest and
+// largest valid keys of the row bound select_final's one histogram pass, so the
+// row needs one reduction and one selection instead of select_regs' passes
+// (4 rows of 4096 positions: 10.9 against 19.7 us per call).
+__global__ __launch_bounds__(kThreads) void topk_small(const float* __restrict__ scores, int64_t ld,
+                                                       const int32_t* __restrict__ q_pos,
+                                                       int32_t* __restrict__ idx) {
+    __shared__ Scratch sc;
+    const int q = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const float* row = scores + (int64_t)q * ld;
+    const int lim = (int)ld - 1;
+    float x[kPerSmall];
+#pragma unroll
+    for (int r = 0; r < kPerSmall; ++r)                         // clamped, unconditional: all in flight
+        x[r] = __builtin_nontemporal_load(row + min(64 * kPerSmall * wave + 64 * r + lane, lim));
+    asm volatile("" ::: "memory");
+    const int n = (int)row_len(q_pos, q, ld);
+    uint32_t v[kPerSmall], pos[kPerSmall];
+    uint32_t mn = 0xffffffffu, mx = 0u;
+#pragma unroll
+    for (int r = 0; r < kPerSmall; ++r) {
+        const int i = 64 * kPerSmall * wave + 64 * r + lane;    // item i = position i
+        const uint32_t key = score_key(x[r]);
+        const bool ok = i < n;
+        v[r] = ok ? key : 0u;
+        pos[r] = (uint32_t)i;
+        mn = ok ? min(mn, key) : mn;
+        mx = ok ? max(mx, key) : mx;
+    }
+    mn = wave_min(mn);
+    mx = wave_max(mx);
+    if (lane == 0) {
+        sc.wmin[wave] = mn;
+        sc.wmax[wave] = mx;
+    }
+    ((uint4*)&sc.hist[0][0][0])[threadIdx.x] = make_uint4(0u, 0u, 0u, 0u);   // for select_final
+    sync_lds();
+    uint32_t lo = 0xffffffffu, hi = 0u;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+        lo = min(lo, sc.wmin[w]);
+        hi = max(hi, sc.wmax[w]);
+    }
+    int32_t* out = idx + (int64_t)q * kK;
+    const int cnt = select_final<kPerSmall>(v, pos, lo, hi, (uint32_t)n, out, sc);
+    write_final_pad(out, cnt);
 }
 
 // ---- One work-group per row, or a few per row -------------------------------
@@ -1716,8 +1767,11 @@ hipError_t launch_topk(const float* scores, int64_t ld, const int32_t* q_pos, in
     (void)k;
     const int nc = n_chunks_of(ld);
     if (nc == 1) {
-        hipLaunchKernelGGL(topk_chunk, dim3(1, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, 1,
-                           (const uint32_t*)nullptr, (uint8_t*)nullptr, idx);
+        if (ld <= (int64_t)kPerSmall * kThreads)                // rows of at most 4096 positions
+            hipLaunchKernelGGL(topk_small, dim3(n_q), dim3(kThreads), 0, st, scores, ld, q_pos, idx);
+        else
+            hipLaunchKernelGGL(topk_chunk, dim3(1, n_q), dim3(kThreads), 0, st, scores, ld, q_pos, 1,
+                               (const uint32_t*)nullptr, (uint8_t*)nullptr, idx);
         return hipGetLastError();
     }
     const int64_t ldg = group_max_ld(ld);

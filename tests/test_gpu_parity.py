@@ -290,6 +290,25 @@ def test_topk_matches_oracle(kind):
         assert np.array_equal(got[i], want[i]), f"{kind} row {i} (pos {int(pos[i])})"
 
 
+@pytest.mark.parametrize("kind", W.SCORE_KINDS)
+@pytest.mark.parametrize("n", [64, 2048, 2052, 3000, 4092, 4096])
+def test_topk_short_rows_match_oracle(kind, n):
+    # rows of at most 4096 positions take the one-pass selection bounded by the
+    # row's own smallest and largest key: every score kind (ties at the
+    # threshold, all equal, signed zeros, a few values), rows shorter than,
+    # equal to and just past 2048, rows ending anywhere in the buffer
+    cand = [n - 1, 0, 1, 2046, 2047, 2048, 2049, n // 2, 4000]
+    pos = torch.tensor(sorted({p for p in cand if 0 <= p < n}), dtype=torch.int32)
+    s = W.score_matrix(kind, pos.numel(), n, seed=9 + n)
+    d = dev()
+    idx = gsa.topk(s.to(d), pos.to(d))
+    torch.cuda.synchronize()
+    want = oracle.topk_select(np32(s), np32(pos), 2048)
+    got = np32(idx)
+    for i in range(pos.numel()):
+        assert np.array_equal(got[i], want[i]), f"{kind} n={n} row {i} (pos {int(pos[i])})"
+
+
 def _topk_case(s, pos, label, with_max=True):
     """gsa.topk with the group maxima computed inside, and (with_max) with the
     oracle's maxima passed in; both against the oracle."""
