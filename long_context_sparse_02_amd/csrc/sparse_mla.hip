@@ -448,6 +448,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 
 // Combine the per-split partial results with their log-sum-exp. Grid
 // (n_q, 16): a work-group merges 4 heads x 512 dims of one query.
+template <int SB>
 __global__ __launch_bounds__(256) void sparse_mla_merge(LayerArgs L, int n_q,
                                                              const _Float16* __restrict__ part_o_all,
                                                              const float* __restrict__ part_ml_all,
@@ -461,10 +462,9 @@ __global__ __launch_bounds__(256) void sparse_mla_merge(LayerArgs L, int n_q,
     const int h = 4 * blockIdx.y + (threadIdx.x >> 6);
     const int c = threadIdx.x & 63;              // dims 4c .. 4c + 3 of each latent half
     const float* pm = part_ml + ((int64_t)q * n_split * kHeads + h) * 4;
-    // Splits in batches of SB whose loads are all in flight together (a loop
-    // that uses each load before issuing the next waits out one memory
-    // latency per split); sums in split order as before.
-    constexpr int SB = 8;
+    // Splits in batches of SB (8, or 16 when there are 16 or more) whose loads
+    // are all in flight together (a loop that uses each load before issuing the
+    // next waits out one memory latency per split); sums in split order.
     float mx = neg_inf();
     for (int s0 = 0; s0 < n_split; s0 += SB) {
         float m[SB];
@@ -558,7 +558,8 @@ hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, co
                                idx, k, n_q, n_cap, block_table, page_size, max_pages, scale_log2, rows,
                                part_o, part_ml);
         if (s > 1)
-            hipLaunchKernelGGL(sparse_mla_merge, dim3(n_q, kHeads / 4, nl), dim3(256), 0, st, L, n_q,
+            hipLaunchKernelGGL(s >= 16 ? sparse_mla_merge<16> : sparse_mla_merge<8>, dim3(n_q, kHeads / 4, nl),
+                               dim3(256), 0, st, L, n_q,
                                part_o, part_ml, s);
         const hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
