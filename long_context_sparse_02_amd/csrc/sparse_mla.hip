@@ -295,6 +295,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     float m_run = neg_inf();      // running max (log2 units) of head `head`
     float l_part = 0.f;           // this lane's share of the running sum
 
+    const int nblk = nrows / kBlk;
     auto compute = [&](int b, const lds_u8* buf) __attribute__((always_inline)) {
         // rows of this block with a valid index (bit r), one LDS read per lane
         const uint64_t valid = __builtin_amdgcn_ballot_w64(rows_s[b * kBlk + (lane & 31)] >= 0);
@@ -316,6 +317,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         g_xs[wave][0][lane] = sacc[0];
         g_xs[wave][1][lane] = sacc[1];
         __hip_atomic_store(&g_xflag[wave], b + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+        // the gathers of block b + kRing - 1 into the slot the barrier freed, issued
+        // here so that their issue (which stalls while the memory system drains
+        // earlier requests) overlaps the partner's post rather than delaying Q.K
+        if (b + kRing - 1 < nblk) issue(b + kRing - 1, (b + kRing - 1) % kRing);
         // bounded: a post that never came would leave wrong scores, never a hang
         for (int spin = 0; spin < (1 << 22); ++spin) {
             const int f = __builtin_amdgcn_readfirstlane(
@@ -375,7 +380,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         }
     };
 
-    const int nblk = nrows / kBlk;
 #pragma unroll
     for (int p = 0; p < kRing - 1; ++p)
         if (p < nblk) issue(p, p);
@@ -386,7 +390,6 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         if (big) wait_block<DMA_HI>(later);
         else wait_block<DMA_LO>(later);
         ring_barrier();    // every wave's part of block b is in; block b-1's readers are done
-        if (b + kRing - 1 < nblk) issue(b + kRing - 1, (b + kRing - 1) % kRing);
         if constexpr (FP8KV) {
             widen(b % kRing);
             wait_lgkm0();
