@@ -708,11 +708,14 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                 };
                 // One permlane32 swap of the two queries' partial sums leaves query
                 // jw0 + g's score of key s0 + n in lane 32g + n: one add and one store
-                // serve both queries, and one 32-lane max gives both group maxima
-                // (+0.0f turns a -0.0 maximum into +0.0). Split in four parts that
-                // the fp8 step places between its (64-cycle) MFMAs.
+                // serve both queries, and one 32-lane max gives both group maxima. The
+                // max runs on order-preserving integer keys (-0.0 folded into +0.0), one
+                // DPP max instruction per step, as in the other score kernels: a float
+                // max with a DPP operand costs a move and two canonicalisations more.
+                // Split in four parts that the fp8 step places between its (64-cycle)
+                // MFMAs.
                 static_assert(QPW == 2, "the finish pairs two queries");
-                struct Fin { float sc; float m; int64_t s0; };
+                struct Fin { float sc; uint32_t m; int64_t s0; };
                 auto fin_a = [&](int ns, const float (&part)[QPW], Fin& f) __attribute__((always_inline)) {
                     f.s0 = t0 + (sub0 + ns) * 32;
                     const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(part[0]),
@@ -723,22 +726,22 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                 };
                 auto fin_b = [&](Fin& f) __attribute__((always_inline)) {
                     if (gmax == nullptr) return;               // uniform
-                    float v = f.sc;
-                    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xb1, 0xf, 0xf, false)));
-                    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4e, 0xf, 0xf, false)));
+                    uint32_t v = score_key(f.sc);
+                    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // lane ^ 1
+                    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // lane ^ 2
                     f.m = v;
                 };
                 auto fin_c = [&](Fin& f) __attribute__((always_inline)) {
                     if (gmax == nullptr) return;
-                    float v = f.m;
-                    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xf, 0xf, false)));
-                    v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xf, 0xf, false)));
+                    uint32_t v = f.m;
+                    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // 7 - lane in 8
+                    v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // 15 - lane in 16
                     f.m = v;
                 };
                 auto fin_d = [&](Fin& f) __attribute__((always_inline)) {
                     if (gmax == nullptr) return;
-                    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(f.m), __float_as_uint(f.m), false, false);
-                    const float m = fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])) + 0.0f;
+                    const auto r = __builtin_amdgcn_permlane16_swap(f.m, f.m, false, false);        // other row
+                    const float m = key_value(max((uint32_t)r[0], (uint32_t)r[1]));
                     if (n == 0) gmax[(int64_t)(qb0 + jw0 + g) * ldg + (f.s0 >> 5)] = m;
                 };
                 auto finish = [&](int ns, const float (&part)[QPW]) __attribute__((always_inline)) {
