@@ -302,13 +302,21 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         // partial S^T over this wave's 9 K-steps: rows 16tt + 4g + i, head l16
         f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
         const lds_u8* arow = buf + l16 * kPitch + 16 * g + 64 * 9 * hf;
+        // fragment e = 2j + tt (K-step j, rows 16tt..): the first 8 are read before
+        // any MFMA and each later one 8 MFMAs ahead of its use; the scheduling
+        // fence keeps the compiler from pulling those reads back next to their
+        // MFMAs, which left the LDS latency exposed every second MFMA
+        bf16x8 af[18];
+        auto frag = [&](int e) __attribute__((always_inline)) {
+            af[e] = *(const __attribute__((address_space(3))) bf16x8*)(arow + 16 * (e & 1) * kPitch + 64 * (e >> 1));
+        };
 #pragma unroll
-        for (int j = 0; j < 9; ++j) {
+        for (int e = 0; e < 8; ++e) frag(e);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const bf16x8 a = *(const __attribute__((address_space(3))) bf16x8*)(arow + 16 * tt * kPitch + 64 * j);
-                sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qr[j], sacc[tt], 0, 0, 0);
-            }
+        for (int e = 0; e < 18; ++e) {
+            if (e + 8 < 18) frag(e + 8);
+            sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[e], qr[e >> 1], sacc[e & 1], 0, 0, 0);
         }
         // swap partial scores with the partner wave (same heads, other half)
         // (a flag per wave instead of a work-group barrier: only the two waves of
