@@ -11,15 +11,23 @@
 //
 // One work-group (8 waves) takes one query and a contiguous slice of its
 // selected rows ("split"); slices are merged with their log-sum-exp when a
-// query is split. Wave w serves heads 16*(w%4) .. +15 and latent half w/4; the
-// two waves of a head group split both contractions: each takes Q.K over half
-// of the 576 dims and P.V over half of the 512 latent dims, and they swap
-// their fp32 partial scores through LDS (a + b == b + a, so both hold the
-// identical S and run the identical softmax); the swap waits on the
-// partner's flag only, not on the whole work-group. Per wave that is 36 registers
-// of Q and 64 of O, which leaves room for two waves per SIMD; the LDS reads
-// per 32-row block (each head group reads the block once for Q.K and once
-// for P.V) are what bounds this kernel.
+// query is split. Wave w serves heads 16*(w%4) .. +15 and latent half w/4 of
+// P.V; the two waves of a head group (w, w^4) split Q.K in one of two ways and
+// swap through LDS, waiting on the partner's flag only, not on the whole
+// work-group:
+//   dim pair  each takes Q.K over half of the 576 dims for all 32 rows of a
+//             block and they swap their fp32 partial scores (a + b == b + a, so
+//             both hold the identical S and run the identical softmax); 36
+//             registers of Q per wave.
+//   row pair  each takes Q.K over all 576 dims for 16 of the 32 rows, runs the
+//             softmax of its own rows only, and they swap their bf16 P with the
+//             running max each proposes (the larger one is the pair's: where it
+//             moved, which is rare, each side rescales); half the softmax work
+//             and half the swapped bytes, for 72 registers of Q, whose loads
+//             double: the layout of slices of 1024 rows or more.
+// Either way 64 registers of O per wave, which leaves room for two waves per
+// SIMD; the LDS reads per 32-row block (each head group reads the block once
+// for Q.K and once for P.V) are what bounds this kernel.
 // FP8 latent cache ("GLM-5.2 总览" tbl-glm52-config: ~656 bytes per token and
 // layer with per-group scales; glossary: E4M3 on the 512-dim latent): rows of
 // [512 E4M3 | 4 fp32 scales | 64 bf16 RoPE] are gathered into a staging ring
@@ -70,6 +78,7 @@ constexpr int kRing = 3;                        // LDS blocks in the ring
 constexpr int kMaxRows = 2048;
 constexpr float kRescale = 8.0f;                // lazy-rescale threshold (log2 units)
 constexpr int kMaxLayersPerLaunch = 8;
+constexpr int kRowPairRows = 1024;              // shortest slice for the row-pair layout
 
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
@@ -91,7 +100,12 @@ __shared__ __attribute__((aligned(16))) uint8_t g_stage[kRing * kStageBuf];
 __shared__ __attribute__((aligned(16))) uint8_t g_blk[kBuf];
 __shared__ int32_t g_rows[kMaxRows];
 __shared__ f32x4 g_xs[kWaves][2][64];           // partial S^T of each wave (2 KiB per wave)
-__shared__ int g_xflag[kWaves];                  // the block (+1) whose partial S^T each wave has posted
+__shared__ int g_xflag[kWaves];                  // the block (+1) whose swap post each wave has made
+// row-pair layout: each wave's bf16 P of its 16 rows, the running max it was
+// computed with, and (at the end) its row sums, per head
+__shared__ bf16x4 g_xp[kWaves][64];
+__shared__ float g_xm[kWaves][16];
+__shared__ float g_xl[kWaves][16];
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
@@ -143,7 +157,7 @@ __device__ __forceinline__ void wait_block(int later) {
     else wait_vmcnt<0>();
 }
 
-template <bool FP8KV>
+template <bool FP8KV, bool RP>
 __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     LayerArgs L, const int32_t* __restrict__ q_seq, const int32_t* __restrict__ idx, int k,
     int n_q, int64_t n_cap, const int32_t* __restrict__ block_table, int page_size, int max_pages,
@@ -167,17 +181,19 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     const int nrows = rows_per_split;
     const int seq = q_seq[q];
     // Q as the B operand: head 16*hg + l16, K-steps t = 9*hf .. 9*hf+8 of the
-    // 576 dims (dims 32t + 8g .. +8; steps 16 and 17 are the RoPE dims). Issued
-    // before the index loads, so that the two latencies overlap (the index
-    // stores to LDS wait for every earlier load); the fence keeps that order.
+    // 576 dims (row-pair layout: all 18), dims 32t + 8g .. +8; steps 16 and 17
+    // are the RoPE dims. Issued before the index loads, so that the two
+    // latencies overlap (the index stores to LDS wait for every earlier load);
+    // the fence keeps that order.
     const int head = 16 * hg + l16;
-    bf16x8 qr[9];
+    constexpr int QS = RP ? 18 : 9;
+    bf16x8 qr[QS];
     {
         const uint8_t* ql = q_lat + ((int64_t)q * kHeads + head) * (kLat * 2);
         const uint8_t* qp = q_rope + ((int64_t)q * kHeads + head) * (64 * 2);
 #pragma unroll
-        for (int j = 0; j < 9; ++j) {
-            const int t = 9 * hf + j;
+        for (int j = 0; j < QS; ++j) {
+            const int t = RP ? j : 9 * hf + j;
             qr[j] = t < 16 ? *(const bf16x8*)(ql + 2 * (32 * t + 8 * g))
                            : *(const bf16x8*)(qp + 2 * (32 * (t - 16) + 8 * g));
         }
@@ -299,80 +315,181 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     auto compute = [&](int b, const lds_u8* buf) __attribute__((always_inline)) {
         // rows of this block with a valid index (bit r), one LDS read per lane
         const uint64_t valid = __builtin_amdgcn_ballot_w64(rows_s[b * kBlk + (lane & 31)] >= 0);
-        // partial S^T over this wave's 9 K-steps: rows 16tt + 4g + i, head l16
-        f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-        const lds_u8* arow = buf + l16 * kPitch + 16 * g + 64 * 9 * hf;
-        // fragment e = 2j + tt (K-step j, rows 16tt..): the first 8 are read before
-        // any MFMA and each later one 8 MFMAs ahead of its use; the scheduling
-        // fence keeps the compiler from pulling those reads back next to their
-        // MFMAs, which left the LDS latency exposed every second MFMA
-        bf16x8 af[18];
-        auto frag = [&](int e) __attribute__((always_inline)) {
-            af[e] = *(const __attribute__((address_space(3))) bf16x8*)(arow + 16 * (e & 1) * kPitch + 64 * (e >> 1));
-        };
+        bf16x8 pa;
+        if constexpr (RP) {
+            // S^T of this wave's 16 rows (16hf + 4g + i) and head l16 over all 576 dims,
+            // as two accumulation chains (K-steps 0-8 and 9-17) added at the end
+            f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            const lds_u8* arow = buf + (16 * hf + l16) * kPitch + 16 * g;
+            // fragment e: chain e & 1, its K-step e >> 1; the first 8 are read before
+            // any MFMA and each later one 8 MFMAs ahead of its use
+            bf16x8 af[18];
+            auto frag = [&](int e) __attribute__((always_inline)) {
+                af[e] = *(const __attribute__((address_space(3))) bf16x8*)(arow + 64 * (9 * (e & 1) + (e >> 1)));
+            };
 #pragma unroll
-        for (int e = 0; e < 8; ++e) frag(e);
-        __builtin_amdgcn_sched_barrier(0);
+            for (int e = 0; e < 8; ++e) frag(e);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int e = 0; e < 18; ++e) {
-            if (e + 8 < 18) frag(e + 8);
-            sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[e], qr[e >> 1], sacc[e & 1], 0, 0, 0);
-        }
-        // swap partial scores with the partner wave (same heads, other half)
-        // (a flag per wave instead of a work-group barrier: only the two waves of
-        // a head group wait for each other; the barrier of the next block keeps
-        // a wave from overwriting its scores before the partner has read them)
-        g_xs[wave][0][lane] = sacc[0];
-        g_xs[wave][1][lane] = sacc[1];
-        __hip_atomic_store(&g_xflag[wave], b + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-        // the gathers of block b + kRing - 1 into the slot the barrier freed, issued
-        // here so that their issue (which stalls while the memory system drains
-        // earlier requests) overlaps the partner's post rather than delaying Q.K
-        if (b + kRing - 1 < nblk) issue(b + kRing - 1, (b + kRing - 1) % kRing);
-        // bounded: a post that never came would leave wrong scores, never a hang
-        for (int spin = 0; spin < (1 << 22); ++spin) {
-            const int f = __builtin_amdgcn_readfirstlane(
-                __hip_atomic_load(&g_xflag[wave ^ 4], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
-            if (f == b + 1) break;
-            __builtin_amdgcn_s_sleep(1);
-        }
-        sacc[0] += g_xs[wave ^ 4][0][lane];
-        sacc[1] += g_xs[wave ^ 4][1][lane];
-        float z[8];
-        float mb = neg_inf();
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
+            for (int e = 0; e < 18; ++e) {
+                if (e + 8 < 18) frag(e + 8);
+                sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[e], qr[9 * (e & 1) + (e >> 1)], sacc[e & 1], 0, 0, 0);
+            }
+            const f32x4 sc = sacc[0] + sacc[1];
+            // this wave's rows: scores, the block max of the head, the max this wave
+            // proposes (moved only past the lazy-rescale margin) and P against it
+            float z[4], p[4];
+            float mb = neg_inf();
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int r = 16 * tt + 4 * g + i;
+                const int r = 16 * hf + 4 * g + i;
                 const bool ok = (valid >> r) & 1u;
-                const float v = ok ? sacc[tt][i] * scale_log2 : neg_inf();
-                z[tt * 4 + i] = v;
-                mb = fmaxf(mb, v);
+                z[i] = ok ? sc[i] * scale_log2 : neg_inf();
+                mb = fmaxf(mb, z[i]);
             }
-        mb = max_x16(mb);
-        mb = max_x32(mb);
-        const bool move = mb > m_run + kRescale;
-        if (__builtin_amdgcn_ballot_w64(move) != 0) {   // wave-uniform branch, rare
-            const float m_new = move ? mb : m_run;
-            const float alpha = move ? exp2_(m_run - m_new) : 1.f;   // exp2(-inf) = 0
-            l_part *= alpha;
-            m_run = m_new;
-            float al[4];
+            mb = max_x32(max_x16(mb));
+            const float mo = mb > m_run + kRescale ? mb : m_run;
+            {
+                const float mu = mo == neg_inf() ? 0.f : mo;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
+                for (int i = 0; i < 4; ++i) p[i] = exp2_(z[i] - mu);
+            }
+            // hand the partner (same heads, other 16 rows) this wave's P and proposal
+            // (flag f1; a second post in the rare case below sets f1 + 1). The
+            // barrier of the next block keeps a wave from overwriting its post before
+            // the partner has read it; the polls are bounded, so a post that never
+            // came would leave wrong results, never a hang.
+            const int f1 = 2 * (b + 1);
+            g_xp[wave][lane] = bf16x4{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+            if (g == 0) g_xm[wave][l16] = mo;
+            __hip_atomic_store(&g_xflag[wave], f1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            // the gathers of block b + kRing - 1 into the slot the barrier freed, issued
+            // here so that their issue (which stalls while the memory system drains
+            // earlier requests) overlaps the partner's post
+            if (b + kRing - 1 < nblk) issue(b + kRing - 1, (b + kRing - 1) % kRing);
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                const int f = __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(&g_xflag[wave ^ 4], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+                if (f >= f1) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            bf16x4 px = g_xp[wave ^ 4][lane];
+            const float mx = g_xm[wave ^ 4][l16];
+            // the pair's max is the larger proposal (both waves see the same two, so
+            // both take the branch below or neither). Where it moved (rare): O and
+            // the sums are rescaled, and both waves compute P against it again and
+            // swap once more, so that P is rounded once, as in the dim-pair layout.
+            const float mf = fmaxf(mo, mx);
+            if (__builtin_amdgcn_ballot_w64(mf != m_run) != 0) {     // wave-uniform branch, rare
+                const float alpha = mf != m_run ? exp2_(m_run - mf) : 1.f;   // exp2(-inf) = 0
+                l_part *= alpha;
+                m_run = mf;
+                float al[4];
 #pragma unroll
-            for (int d = 0; d < 16; ++d)
+                for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
 #pragma unroll
-                for (int i = 0; i < 4; ++i) o[d][i] *= al[i];
-        }
-        const float m_use = m_run == neg_inf() ? 0.f : m_run;
-        bf16x8 pa;
+                for (int d = 0; d < 16; ++d)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            const float p = exp2_(z[e] - m_use);
-            l_part += p;
-            pa[e] = (__bf16)p;
+                    for (int i = 0; i < 4; ++i) o[d][i] *= al[i];
+                const float mu = mf == neg_inf() ? 0.f : mf;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) p[i] = exp2_(z[i] - mu);
+                // (the partner discards what it read of the first post)
+                g_xp[wave][lane] = bf16x4{(__bf16)p[0], (__bf16)p[1], (__bf16)p[2], (__bf16)p[3]};
+                __hip_atomic_store(&g_xflag[wave], f1 + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+                for (int spin = 0; spin < (1 << 22); ++spin) {
+                    const int f = __builtin_amdgcn_readfirstlane(
+                        __hip_atomic_load(&g_xflag[wave ^ 4], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+                    if (f == f1 + 1) break;
+                    __builtin_amdgcn_s_sleep(1);
+                }
+                px = g_xp[wave ^ 4][lane];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) l_part += p[i];
+            // P as the A operand: K index e < 4 is row 4g + e (rows 0-15), e >= 4 row
+            // 16 + 4g + e - 4 (rows 16-31)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const __bf16 own = (__bf16)p[i];
+                pa[i] = hf == 0 ? own : px[i];
+                pa[4 + i] = hf == 0 ? px[i] : own;
+            }
+        } else {
+            // partial S^T over this wave's 9 K-steps: rows 16tt + 4g + i, head l16
+            f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+            const lds_u8* arow = buf + l16 * kPitch + 16 * g + 64 * 9 * hf;
+            // fragment e = 2j + tt (K-step j, rows 16tt..): the first 8 are read before
+            // any MFMA and each later one 8 MFMAs ahead of its use; the scheduling
+            // fence keeps the compiler from pulling those reads back next to their
+            // MFMAs, which left the LDS latency exposed every second MFMA
+            bf16x8 af[18];
+            auto frag = [&](int e) __attribute__((always_inline)) {
+                af[e] = *(const __attribute__((address_space(3))) bf16x8*)(arow + 16 * (e & 1) * kPitch + 64 * (e >> 1));
+            };
+#pragma unroll
+            for (int e = 0; e < 8; ++e) frag(e);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int e = 0; e < 18; ++e) {
+                if (e + 8 < 18) frag(e + 8);
+                sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[e], qr[e >> 1], sacc[e & 1], 0, 0, 0);
+            }
+            // swap partial scores with the partner wave (same heads, other half)
+            // (a flag per wave instead of a work-group barrier: only the two waves of
+            // a head group wait for each other; the barrier of the next block keeps
+            // a wave from overwriting its scores before the partner has read them)
+            g_xs[wave][0][lane] = sacc[0];
+            g_xs[wave][1][lane] = sacc[1];
+            __hip_atomic_store(&g_xflag[wave], b + 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+            // the gathers of block b + kRing - 1 into the slot the barrier freed, issued
+            // here so that their issue (which stalls while the memory system drains
+            // earlier requests) overlaps the partner's post rather than delaying Q.K
+            if (b + kRing - 1 < nblk) issue(b + kRing - 1, (b + kRing - 1) % kRing);
+            // bounded: a post that never came would leave wrong scores, never a hang
+            for (int spin = 0; spin < (1 << 22); ++spin) {
+                const int f = __builtin_amdgcn_readfirstlane(
+                    __hip_atomic_load(&g_xflag[wave ^ 4], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP));
+                if (f == b + 1) break;
+                __builtin_amdgcn_s_sleep(1);
+            }
+            sacc[0] += g_xs[wave ^ 4][0][lane];
+            sacc[1] += g_xs[wave ^ 4][1][lane];
+            float z[8];
+            float mb = neg_inf();
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int r = 16 * tt + 4 * g + i;
+                    const bool ok = (valid >> r) & 1u;
+                    const float v = ok ? sacc[tt][i] * scale_log2 : neg_inf();
+                    z[tt * 4 + i] = v;
+                    mb = fmaxf(mb, v);
+                }
+            mb = max_x16(mb);
+            mb = max_x32(mb);
+            const bool move = mb > m_run + kRescale;
+            if (__builtin_amdgcn_ballot_w64(move) != 0) {   // wave-uniform branch, rare
+                const float m_new = move ? mb : m_run;
+                const float alpha = move ? exp2_(m_run - m_new) : 1.f;   // exp2(-inf) = 0
+                l_part *= alpha;
+                m_run = m_new;
+                float al[4];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) al[i] = __shfl(alpha, 4 * g + i, 64);
+#pragma unroll
+                for (int d = 0; d < 16; ++d)
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) o[d][i] *= al[i];
+            }
+            const float m_use = m_run == neg_inf() ? 0.f : m_run;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float p = exp2_(z[e] - m_use);
+                l_part += p;
+                pa[e] = (__bf16)p;
+            }
         }
         // P.V over this wave's 256 latent dims: O[heads][16 dims] += P[heads][32 rows] *
         // V[32 rows][16 dims]. The V operand of lane (dim l16, group g) is rows
@@ -408,7 +525,15 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         }
     }
 
-    const float l_tot = sum_x32(sum_x16(l_part));
+    // the head's sum over the slice (row-pair layout: this wave's rows plus the
+    // partner's, added in row-half order so that both hold the same value)
+    float l_tot = sum_x32(sum_x16(l_part));
+    if constexpr (RP) {
+        if (g == 0) g_xl[wave][l16] = l_tot;
+        __syncthreads();
+        const float lx = g_xl[wave ^ 4][l16];
+        l_tot = hf == 0 ? l_tot + lx : lx + l_tot;
+    }
     const int dim0 = 256 * hf;
     if (n_split == 1) {
         const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -560,14 +685,13 @@ hipError_t launch_sparse_mla_layers(const MlaLayerPtrs* layers, int n_layers, co
         const int rows = k / s;
         _Float16* part_o = (_Float16*)ws;
         float* part_ml = s > 1 ? (float*)(part_o + (size_t)per * n_q * s * kHeads * kLat) : nullptr;
-        if (fp8_kv)
-            hipLaunchKernelGGL(sparse_mla_kernel<true>, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq,
-                               idx, k, n_q, n_cap, block_table, page_size, max_pages, scale_log2, rows,
-                               part_o, part_ml);
-        else
-            hipLaunchKernelGGL(sparse_mla_kernel<false>, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq,
-                               idx, k, n_q, n_cap, block_table, page_size, max_pages, scale_log2, rows,
-                               part_o, part_ml);
+        // slices of at least kRowPairRows rows take the row-pair layout; shorter ones
+        // the dim-pair layout, whose work-groups load half as many Q bytes
+        const bool rp = rows >= kRowPairRows;
+        auto* kern = fp8_kv ? (rp ? sparse_mla_kernel<true, true> : sparse_mla_kernel<true, false>)
+                            : (rp ? sparse_mla_kernel<false, true> : sparse_mla_kernel<false, false>);
+        hipLaunchKernelGGL(kern, dim3(s, n_q, nl), dim3(kThreads), 0, st, L, q_seq, idx, k, n_q, n_cap,
+                           block_table, page_size, max_pages, scale_log2, rows, part_o, part_ml);
         if (s > 1)
             hipLaunchKernelGGL(s >= 16 ? sparse_mla_merge<16> : sparse_mla_merge<8>, dim3(n_q, kHeads / 4, nl),
                                dim3(256), 0, st, L, n_q,

@@ -6,8 +6,10 @@ import numpy as np
 import torch
 
 # Attention tolerance: bf16 inputs, fp32 accumulation, P rounded to bf16 before
-# P.V (relative error <= 2^-9 per weight); outputs are O(0.1), so the expected
-# max-abs error is ~1e-3. The bar is 1e-2 max-abs.
+# P.V (relative error <= 2^-8 per weight, the bf16 unit roundoff); on unit-scale
+# caches the outputs are O(0.1) and the rounding errors of many weights average
+# out, so the expected max-abs error is ~1e-3. The bar is 1e-2 max-abs (a test
+# whose data make the softmax peaked states its own bound).
 ATOL_OUT = 1e-2
 ATOL_LSE = 1e-2
 
@@ -49,8 +51,9 @@ def max_abs(a, b):
 ERRORS = {}
 
 
-def note(eo, el=0.0):
-    """Record the max-abs output and lse errors of an attention check for the running test."""
+def note(eo, el=0.0, bar=ATOL_OUT):
+    """Record the max-abs output and lse errors of an attention check for the
+    running test, with the output bar it was held to."""
     label = os.environ.get("PYTEST_CURRENT_TEST", "?").split(" ")[0]
-    a, b = ERRORS.get(label, (0.0, 0.0))
-    ERRORS[label] = (max(a, float(eo)), max(b, float(el)))
+    a, b, c = ERRORS.get(label, (0.0, 0.0, float(bar)))
+    ERRORS[label] = (max(a, float(eo)), max(b, float(el)), min(c, float(bar)))

@@ -675,3 +675,51 @@ def test_sparse_mla_layers_launch_matches_oracle(n_layers, n_q, batch):
         note(eo, el)
         assert eo <= ATOL_OUT and el <= ATOL_LSE
     del q_pos
+
+
+def test_mla_row_pair_layout_rescales_and_edge_rows():
+    # 4 layers x 32 queries: 128 (query, layer) units, each query split into 2
+    # slices of 1024 rows, which takes the row-pair layout (each wave of a pair
+    # scores 16 of a block's 32 rows). The RoPE half of the cache rows grows with
+    # the position (up to 11x), so rows taken in ascending order raise the running
+    # max block after block: on the CPU, 1.6 later rescales per head on average,
+    # some moving in both row halves at once; descending order puts the largest
+    # rows first. Edge rows: every index -1; a single valid index; one row half of
+    # every block empty (the first, or the second).
+    n_layers, n_q, batch, n_ctx = 4, 32, 2, 5000
+    wl = W.Workload("mla_rp", batch, n_ctx, n_q // batch, n_layers, "bf16")
+    q_seq = torch.arange(n_q, dtype=torch.int32) % batch
+    g = torch.Generator().manual_seed(91)
+    idx = torch.stack([torch.sort(torch.randperm(n_ctx, generator=g)[:2048])[0] for _ in range(n_q)]).to(torch.int32)
+    idx[1] = torch.flip(idx[1], [0])
+    idx[2] = -1
+    idx[3] = -1
+    idx[3, 1500] = 4321
+    second_half = (torch.arange(2048) // 16) % 2 == 1
+    idx[4, second_half] = -1
+    idx[5, ~second_half] = -1
+    grow = 1.0 + torch.arange(n_ctx, dtype=torch.float32) / 500.0
+    layers_cpu = []
+    for l in range(n_layers):
+        ql, qr = W.mla_queries(wl, 9, l)
+        kv = W.mla_cache(wl, 9, l).float()
+        kv[..., 512:] *= grow[None, :, None]
+        layers_cpu.append((ql, qr, kv.to(torch.bfloat16)))
+    d = dev()
+    layers = [tuple(t.to(d) for t in L) for L in layers_cpu]
+    outs = gsa.sparse_mla_attn_layers(layers, q_seq.to(d), idx.to(d), 1 / 16)
+    torch.cuda.synchronize()
+    for l, ((o, s), (ql, qr, kv)) in enumerate(zip(outs, layers_cpu)):
+        wo, ws = oracle.sparse_mla(np32(ql), np32(qr), np32(kv), np32(q_seq), np32(idx), 1 / 16)
+        eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
+        # These scores are large, so the softmax is peaked and few rows carry each
+        # output: the 1e-2 bar of the unit-scale cases no longer bounds the error.
+        # Bound from the arithmetic instead: out = sum_j p_j v_j / l with l the exact
+        # fp32 sum and P rounded to bf16 (unit roundoff 2^-8), so the error is at
+        # most 2^-8 max|v|; the 2 slices' partials are fp16 with a power-of-two
+        # scale per (head, latent half), adding at most 2^-11 max|v|.
+        tol = 1.05 * (2.0 ** -8 + 2.0 ** -11) * float(kv[..., :512].float().abs().max())
+        say(f"row-pair layout: layer {l} out err {eo:.2e} (bound {tol:.2e}) lse err {el:.2e}")
+        note(eo, el, bar=tol)
+        assert eo <= tol and el <= ATOL_LSE
+        assert torch.all(o[2] == 0) and torch.all(torch.isneginf(s[2]))
