@@ -22,7 +22,7 @@
 //   row pair  each takes Q.K over all 576 dims for 16 of the 32 rows, runs the
 //             softmax of its own rows only, and they swap their bf16 P with the
 //             running max each proposes (the larger one is the pair's: where it
-//             moved, which is rare, each side rescales); half the softmax work
+//             moved, which is rare, both recompute P and swap again); half the softmax work
 //             and half the swapped bytes, for 72 registers of Q, whose loads
 //             double: the layout of slices of 1024 rows or more.
 // Either way 64 registers of O per wave, which leaves room for two waves per
@@ -30,9 +30,16 @@
 // for Q.K and once for P.V) are what bounds this kernel.
 // FP8 latent cache ("GLM-5.2 总览" tbl-glm52-config: ~656 bytes per token and
 // layer with per-group scales; glossary: E4M3 on the 512-dim latent): rows of
-// [512 E4M3 | 4 fp32 scales | 64 bf16 RoPE] are gathered into a staging ring
-// and widened to the bf16 block layout (one scaled conversion per two codes)
-// before the same compute.
+// [512 E4M3 | 4 fp32 scales | 64 bf16 RoPE] are gathered into a ring as they
+// are. The row-pair layout computes on them there: Q.K's K operand converts 8
+// codes with the row's group scale (exact), and P.V reads V with the 8-bit
+// transpose read, converts it unscaled and takes the rows' scales into P
+// instead (a power of two, so P.V forms the products of the dequantised rows),
+// with half the LDS bytes of a bf16 block. The dim-pair layout (short slices,
+// where those conversions per wave cost more than they save) widens each
+// block to the bf16 layout first (one scaled conversion per two codes, a
+// barrier) and runs the bf16 compute. Both give the outputs of the
+// dequantised rows bit for bit.
 // Per 32-row block:
 //   gather  global_load_lds_dwordx4 copies the block's 32 x 1152 bytes straight
 //           into LDS (no staging registers); each wave instruction moves 1 KiB
@@ -84,9 +91,7 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
 // FP8 latent rows ([512 E4M3 | 4 fp32 scales | 64 bf16 RoPE], 656 bytes): the
-// gather lands them unpadded in a staging ring, and every block is widened to
-// the bf16 layout above (exact: code x power-of-two scale) before the same
-// compute runs on it.
+// gather lands them unpadded in their own ring.
 constexpr int kRowBytesF8 = 656;
 constexpr int kChunksF8 = kRowBytesF8 / 16;     // 41
 constexpr int kDmaF8 = (kBlk * kRowBytesF8 + 1023) / 1024;   // 21
@@ -108,6 +113,20 @@ __shared__ float g_xm[kWaves][16];
 __shared__ float g_xl[kWaves][16];
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef int v2i __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i lds_v2i;
+
+// 8 E4M3 codes (bytes 0..7 of c) times the power-of-two scale s, as 8 bf16
+// (exact: 4 significand bits and a power of two fit bf16), in byte order.
+__device__ __forceinline__ bf16x8 fp8x8_to_bf16(v2i c, float s) {
+    const auto a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c[0], s, false);
+    const auto b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c[0], s, true);
+    const auto d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c[1], s, false);
+    const auto e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)c[1], s, true);
+    return bf16x8{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+}
 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 
@@ -272,7 +291,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             lds_dma16(src, dst + 1024 * (i0 + j));
         }
     };
-    // FP8: widen staging slot `slot` into g_blk in the bf16 row layout. Thread t
+    // FP8, dim-pair layout: widen staging slot `slot` into g_blk in the bf16 row
+    // layout, for the bf16 compute. Thread t
     // converts codes 32*(t%16) .. +31 of row t/16 with that group's scale (the
     // scaled conversion is exact for a power-of-two scale); threads 0-255 move
     // the RoPE dims (16 bytes each).
@@ -312,6 +332,29 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     float l_part = 0.f;           // this lane's share of the running sum
 
     const int nblk = nrows / kBlk;
+    // FP8 rows read in place (row-pair layout); the dim-pair layout widens them first
+    constexpr bool F8IN = FP8KV && RP;
+    // The A operand of K-step t for the row at `rp` (this lane's dims 32t + 8g ..
+    // +7): bf16 rows are read as they are; FP8 rows hold 8 codes there (steps of
+    // the latent dims, converted with the row's group scale by kval) or, past the
+    // latent, the bf16 RoPE key.
+    auto kraw = [&](const lds_u8* rp, int t) __attribute__((always_inline)) -> i32x4 {
+        if constexpr (F8IN) {
+            if (t < 16) {
+                const v2i c = *(const lds_v2i*)(rp + 32 * t + 8 * g);
+                return i32x4{c[0], c[1], 0, 0};
+            }
+            return *(const __attribute__((address_space(3))) i32x4*)(rp + 528 + 64 * (t - 16) + 16 * g);
+        } else {
+            return *(const __attribute__((address_space(3))) i32x4*)(rp + 64 * t);
+        }
+    };
+    auto kval = [&](const i32x4& raw, int t, const f32x4& srow) __attribute__((always_inline)) -> bf16x8 {
+        if constexpr (F8IN) {
+            if (t < 16) return fp8x8_to_bf16(v2i{raw[0], raw[1]}, srow[t >> 2]);
+        }
+        return __builtin_bit_cast(bf16x8, raw);
+    };
     auto compute = [&](int b, const lds_u8* buf) __attribute__((always_inline)) {
         // rows of this block with a valid index (bit r), one LDS read per lane
         const uint64_t valid = __builtin_amdgcn_ballot_w64(rows_s[b * kBlk + (lane & 31)] >= 0);
@@ -320,12 +363,17 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             // S^T of this wave's 16 rows (16hf + 4g + i) and head l16 over all 576 dims,
             // as two accumulation chains (K-steps 0-8 and 9-17) added at the end
             f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            const lds_u8* arow = buf + (16 * hf + l16) * kPitch + 16 * g;
+            const lds_u8* arow = F8IN ? buf + (16 * hf + l16) * kRowBytesF8
+                                       : buf + (16 * hf + l16) * kPitch + 16 * g;
+            // FP8 rows: the row's four group scales, for the conversion of its codes
+            f32x4 srw{};
+            if constexpr (F8IN) srw = *(const __attribute__((address_space(3))) f32x4*)(arow + 512);
             // fragment e: chain e & 1, its K-step e >> 1; the first 8 are read before
             // any MFMA and each later one 8 MFMAs ahead of its use
-            bf16x8 af[18];
+            i32x4 af[18];
             auto frag = [&](int e) __attribute__((always_inline)) {
-                af[e] = *(const __attribute__((address_space(3))) bf16x8*)(arow + 64 * (9 * (e & 1) + (e >> 1)));
+                const int t = 9 * (e & 1) + (e >> 1);
+                af[e] = kraw(arow, t);
             };
 #pragma unroll
             for (int e = 0; e < 8; ++e) frag(e);
@@ -333,7 +381,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 #pragma unroll
             for (int e = 0; e < 18; ++e) {
                 if (e + 8 < 18) frag(e + 8);
-                sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[e], qr[9 * (e & 1) + (e >> 1)], sacc[e & 1], 0, 0, 0);
+                const int t = 9 * (e & 1) + (e >> 1);
+                sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kval(af[e], t, srw), qr[t], sacc[e & 1], 0, 0, 0);
             }
             const f32x4 sc = sacc[0] + sacc[1];
             // this wave's rows: scores, the block max of the head, the max this wave
@@ -418,14 +467,14 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         } else {
             // partial S^T over this wave's 9 K-steps: rows 16tt + 4g + i, head l16
             f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            const lds_u8* arow = buf + l16 * kPitch + 16 * g + 64 * 9 * hf;
+            const lds_u8* arow = buf + l16 * kPitch + 16 * g;
             // fragment e = 2j + tt (K-step j, rows 16tt..): the first 8 are read before
             // any MFMA and each later one 8 MFMAs ahead of its use; the scheduling
             // fence keeps the compiler from pulling those reads back next to their
             // MFMAs, which left the LDS latency exposed every second MFMA
-            bf16x8 af[18];
+            i32x4 af[18];
             auto frag = [&](int e) __attribute__((always_inline)) {
-                af[e] = *(const __attribute__((address_space(3))) bf16x8*)(arow + 16 * (e & 1) * kPitch + 64 * (e >> 1));
+                af[e] = kraw(arow + 16 * (e & 1) * kPitch, 9 * hf + (e >> 1));
             };
 #pragma unroll
             for (int e = 0; e < 8; ++e) frag(e);
@@ -433,7 +482,8 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
 #pragma unroll
             for (int e = 0; e < 18; ++e) {
                 if (e + 8 < 18) frag(e + 8);
-                sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(af[e], qr[e >> 1], sacc[e & 1], 0, 0, 0);
+                sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kval(af[e], 9 * hf + (e >> 1), f32x4{}), qr[e >> 1],
+                                                                      sacc[e & 1], 0, 0, 0);
             }
             // swap partial scores with the partner wave (same heads, other half)
             // (a flag per wave instead of a work-group barrier: only the two waves of
@@ -493,15 +543,43 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         }
         // P.V over this wave's 256 latent dims: O[heads][16 dims] += P[heads][32 rows] *
         // V[32 rows][16 dims]. The V operand of lane (dim l16, group g) is rows
-        // {4g..4g+3, 16+4g..16+4g+3}: two transpose reads in which lane j of the group
-        // supplies row 4g + j/4 (+16), dims 16d + 4(j%4) .. +3.
-        const lds_u8* vb = buf + (4 * g + (l16 >> 2)) * kPitch + 8 * (l16 & 3) + 512 * hf;
+        // {4g..4g+3, 16+4g..16+4g+3} (K index e of P is row R(e): 4g + e, then
+        // 16 + 4g + e - 4).
+        if constexpr (!F8IN) {
+            // two 16-bit transpose reads in which lane j of the group supplies row
+            // 4g + j/4 (+16), dims 16d + 4(j%4) .. +3
+            const lds_u8* vb = buf + (4 * g + (l16 >> 2)) * kPitch + 8 * (l16 & 3) + 512 * hf;
 #pragma unroll
-        for (int d = 0; d < 16; ++d) {
-            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 32 * d));
-            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 16 * kPitch + 32 * d));
-            const bf16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[d], 0, 0, 0);
+            for (int d = 0; d < 16; ++d) {
+                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 32 * d));
+                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 16 * kPitch + 32 * d));
+                const bf16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[d], 0, 0, 0);
+            }
+        } else {
+            // one 8-bit transpose read: lane j of the group supplies row R(j/2), codes
+            // of dims 16d + 8(j%2) .. +7, and gets back the 8 codes of dim 16d + j,
+            // byte e from row R(e); they convert unscaled. The rows' group scales
+            // multiply P instead (a power of two: exact, and P.V's products are those
+            // of the dequantised rows): pa for the half's first 128 dims, pb for the
+            // second.
+            const int k = l16 >> 1;
+            const int rsrc = k < 4 ? 4 * g + k : 12 + 4 * g + k;
+            const lds_u8* vb = buf + rsrc * kRowBytesF8 + 256 * hf + 8 * (l16 & 1);
+            bf16x8 pb;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int r = e < 4 ? 4 * g + e : 12 + 4 * g + e;
+                const f32x2 sc = *(const __attribute__((address_space(3))) f32x2*)(buf + r * kRowBytesF8 + 512 + 8 * hf);
+                const float pv = (float)pa[e];
+                pb[e] = (__bf16)(pv * sc[1]);
+                pa[e] = (__bf16)(pv * sc[0]);
+            }
+#pragma unroll
+            for (int d = 0; d < 16; ++d) {
+                const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + 16 * d));
+                o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d < 8 ? pa : pb, fp8x8_to_bf16(c, 1.0f), o[d], 0, 0, 0);
+            }
         }
     };
 
@@ -515,13 +593,13 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         if (big) wait_block<DMA_HI>(later);
         else wait_block<DMA_LO>(later);
         ring_barrier();    // every wave's part of block b is in; block b-1's readers are done
-        if constexpr (FP8KV) {
+        if constexpr (FP8KV && !RP) {
             widen(b % kRing);
             wait_lgkm0();
             ring_barrier();    // the widened block is complete
             compute(b, (const lds_u8*)g_blk);
         } else {
-            compute(b, (const lds_u8*)g_ring + (b % kRing) * kBuf);
+            compute(b, (const lds_u8*)ring + (b % kRing) * SLOT);
         }
     }
 

@@ -82,6 +82,27 @@ def test_fp8kv_attention_matches_oracle(n_q, batch, n_layers):
         assert eo <= ATOL_OUT and el <= ATOL_LSE
 
 
+@pytest.mark.parametrize("n_q,batch,n_layers", [(64, 4, 2), (8, 2, 4)])
+def test_fp8kv_attention_equals_bf16_attention_on_dequantised_rows(n_q, batch, n_layers):
+    # 64 x 2: 1024-row slices, the row-pair layout, which computes on the FP8
+    # rows in place (codes converted with their group scale for Q.K; V unscaled,
+    # the scales carried by P); 8 x 4: 256-row slices, the dim-pair layout, which
+    # widens each block first. Either way the MFMAs see the products of the
+    # dequantised rows, so attention over the bf16 rows that dequantisation gives
+    # (exact: a 4-bit significand times a power of two) is the same, bit for bit.
+    q_seq, idx, layers_cpu, layers, outs = _attn_case(n_q, batch, 2500, n_layers, seed=40 + n_q)
+    d = dev()
+    deq_layers = []
+    for (ql, qr, kv8) in layers:
+        deq = torch.from_numpy(oracle.dequantize_latent(kv8.cpu().numpy()).astype(np.float32))
+        assert torch.equal(deq.to(torch.bfloat16).float(), deq)          # exact in bf16
+        deq_layers.append((ql, qr, deq.to(torch.bfloat16).to(d)))
+    ref = gsa.sparse_mla_attn_layers(deq_layers, q_seq.to(d), idx.to(d), 1 / 16)
+    torch.cuda.synchronize()
+    for l, ((o, s), (ro, rs)) in enumerate(zip(outs, ref)):
+        assert torch.equal(o, ro) and torch.equal(s, rs), f"layer {l}: max |diff| {float((o - ro).abs().max()):.3e}"
+
+
 def test_fp8kv_paged_matches_contiguous():
     q_seq, idx, layers_cpu, layers, outs = _attn_case(6, 3, 2500, 2, seed=11)
     ps = 32
