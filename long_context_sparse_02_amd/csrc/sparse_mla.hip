@@ -45,10 +45,11 @@
 //           into LDS (no staging registers); each wave instruction moves 1 KiB
 //           of whole 128-byte lines. A ring of kRing LDS blocks keeps
 //           kRing - 1 blocks in flight per CU. Rows sit at a 1184-byte pitch
-//           (32 bytes of padding) with pairs of 16-byte chunks swapped in half
-//           the rows (swz), which keeps the reads of Q.K and of P.V free of
-//           bank conflicts and lets every LDS address be one base register
-//           plus an immediate. Indices of -1 load a static zero row.
+//           (32 bytes of padding), at which the SQ_LDS_BANK_CONFLICT counter
+//           reads zero for Q.K's 16-row reads and P.V's transpose reads alike
+//           (with 16 bytes of padding both conflicted, 17.8M cycles per
+//           128K launch), and every LDS address is one base register plus an
+//           immediate. Indices of -1 load a static zero row.
 //   Q.K     S^T (rows x heads) on v_mfma_f32_16x16x32_bf16 with Q resident in
 //           registers; in that layout a lane holds 8 rows of one head, so the
 //           softmax max/sum need only two cross-lane steps.
@@ -115,13 +116,6 @@ __shared__ float g_xl[kWaves][16];
 
 __device__ __forceinline__ float exp2_(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// bf16 block layout: 16-byte chunk c of row r sits at chunk c ^ swz(r) of the
-// row's 74 (rows 4-11 and 20-27 swap each pair of chunks). With the 1184-byte
-// pitch this keeps both of the compute's LDS read patterns free of bank
-// conflicts: Q.K's 16 rows x 16 bytes and P.V's transpose reads of 4 rows x
-// 32 bytes per 16 lanes (with a 1168-byte pitch and no swap the latter met
-// 2-way conflicts). swz(r + 16) == swz(r).
-__device__ __forceinline__ int swz(int r) { return ((r >> 2) ^ (r >> 3)) & 1; }
 
 typedef int v2i __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -287,7 +281,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         for (int j = 0; j < DMA_HI; ++j) {              // every index read first, one wait
             const int pos = 64 * (i0 + j) + lane;
             const int row = pos / UNIT;
-            const int c = FP8KV ? pos - row * UNIT : (pos - row * UNIT) ^ swz(row);   // the chunk this slot holds
+            const int c = pos - row * UNIT;
             srow[j] = (j < nload && row < kBlk && c < ROW_CHUNKS) ? rows_s[b * kBlk + row] : -1;
         }
 #pragma unroll
@@ -295,7 +289,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             if (j == DMA_HI - 1 && !big) break;
             const int pos = 64 * (i0 + j) + lane;
             const int row = pos / UNIT;
-            const int c = FP8KV ? pos - row * UNIT : (pos - row * UNIT) ^ swz(row);
+            const int c = pos - row * UNIT;
             const uint8_t* src = srow[j] >= 0 ? kvs + (int64_t)srow[j] * RB + 16 * c : g_zero_row;
             lds_dma16(src, dst + 1024 * (i0 + j));
         }
@@ -326,10 +320,10 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         }
         lds_u8* dr = (lds_u8*)g_blk + r * kPitch + 64 * j;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) *(__attribute__((address_space(3))) i32x4*)(dr + 16 * (e ^ swz(r))) = w[e];
+        for (int e = 0; e < 4; ++e) *(__attribute__((address_space(3))) i32x4*)(dr + 16 * e) = w[e];
         if (tid < 256) {
             const int r2 = tid >> 3, c = tid & 7;
-            *(__attribute__((address_space(3))) i32x4*)((lds_u8*)g_blk + r2 * kPitch + 1024 + 16 * (c ^ swz(r2))) =
+            *(__attribute__((address_space(3))) i32x4*)((lds_u8*)g_blk + r2 * kPitch + 1024 + 16 * c) =
                 *(const __attribute__((address_space(3))) i32x4*)(st + r2 * kRowBytesF8 + 528 + 16 * c);
         }
     };
@@ -373,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             // as two accumulation chains (K-steps 0-8 and 9-17) added at the end
             f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
             const lds_u8* arow = F8IN ? buf + (16 * hf + l16) * kRowBytesF8
-                                       : buf + (16 * hf + l16) * kPitch + 16 * (g ^ swz(l16));
+                                       : buf + (16 * hf + l16) * kPitch + 16 * g;
             // FP8 rows: the row's four group scales, for the conversion of its codes
             f32x4 srw{};
             if constexpr (F8IN) srw = *(const __attribute__((address_space(3))) f32x4*)(arow + 512);
@@ -476,7 +470,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         } else {
             // partial S^T over this wave's 9 K-steps: rows 16tt + 4g + i, head l16
             f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            const lds_u8* arow = buf + l16 * kPitch + 16 * (g ^ swz(l16));
+            const lds_u8* arow = buf + l16 * kPitch + 16 * g;
             // fragment e = 2j + tt (K-step j, rows 16tt..): the first 8 are read before
             // any MFMA and each later one 8 MFMAs ahead of its use; the scheduling
             // fence keeps the compiler from pulling those reads back next to their
@@ -557,8 +551,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         if constexpr (!F8IN) {
             // two 16-bit transpose reads in which lane j of the group supplies row
             // 4g + j/4 (+16), dims 16d + 4(j%4) .. +3
-            const int rv = 4 * g + (l16 >> 2);
-            const lds_u8* vb = buf + rv * kPitch + 16 * (((l16 & 3) >> 1) ^ swz(rv)) + 8 * (l16 & 1) + 512 * hf;
+            const lds_u8* vb = buf + (4 * g + (l16 >> 2)) * kPitch + 8 * (l16 & 3) + 512 * hf;
 #pragma unroll
             for (int d = 0; d < 16; ++d) {
                 const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 32 * d));
