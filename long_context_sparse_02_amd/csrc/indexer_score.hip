@@ -68,9 +68,17 @@ struct KeyTile {
     static constexpr int kScaleDma = FP8 ? KEYS / 64 : 0;       // 256-byte DMAs of fp32 scales
     static constexpr int kScaleBytes = 256 * kScaleDma;
     static constexpr int kSlot = kBytes + kScaleBytes;
-    // byte offset of logical chunk c of tile row r (XOR swizzle over the row's chunks)
+    // Chunk c of tile row r is stored at chunk c ^ swz(r) of the row. A 16-byte
+    // read of 16 consecutive rows (16 lanes) then touches 16 distinct chunks
+    // of the 64 banks: a bf16 row spans all 64 (256 bytes), so r mod 16 spreads
+    // them; an fp8 row spans 32, and rows r and r + 1 sit in the two halves, so
+    // (r / 2) mod 8 spreads the 8 rows of each half (r mod 8 put rows r and
+    // r + 8 on the same banks: 3 conflict cycles per LDS read in the FP8 decode
+    // kernel).
+    __device__ static __forceinline__ int swz(int r) { return FP8 ? (r >> 1) & 7 : r & (kChunks - 1); }
+    // byte offset of logical chunk c of tile row r
     __device__ static __forceinline__ int off(int r, int c) {
-        return r * kRowBytes + ((c ^ (r & (kChunks - 1))) << 4);
+        return r * kRowBytes + ((c ^ swz(r)) << 4);
     }
 };
 
@@ -158,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
     for (int jd = 0; jd < T::kDmaPerWave; ++jd) {
         const int i = wave * T::kDmaPerWave + jd;
         const int r = i * T::kRowsPerDma + lane / T::kChunks;
-        const int c = (lane % T::kChunks) ^ (r & (T::kChunks - 1));
+        const int c = (lane % T::kChunks) ^ T::swz(r);
         doff[jd] = (uint32_t)(r * T::kRowBytes + 16 * c);
     }
 
@@ -210,7 +218,7 @@ __global__ __launch_bounds__(kThreads) void indexer_score_kernel(
                 const int i = wave * T::kDmaPerWave + jd;
                 const int r = i * T::kRowsPerDma + lane / T::kChunks;
                 const int p = lane % T::kChunks;                     // physical chunk in the row
-                const int c = p ^ (r & (T::kChunks - 1));            // logical chunk stored there
+                const int c = p ^ T::swz(r);            // logical chunk stored there
                 const int64_t krow = min(t0 + r, c1 - 1);            // rows past the chunk: any valid row
                 lds_dma16_t<NTK>(kb + krow * T::kRowBytes + 16 * c, dst + 1024 * i);
             }
@@ -445,7 +453,7 @@ __global__ __launch_bounds__(kDynThreads) void indexer_score_dyn(
     for (int jd = 0; jd < T::kDmaPerWave; ++jd) {
         const int i = wave * T::kDmaPerWave + jd;
         const int r = i * T::kRowsPerDma + lane / T::kChunks;
-        const int c = (lane % T::kChunks) ^ (r & (T::kChunks - 1));
+        const int c = (lane % T::kChunks) ^ T::swz(r);
         doff[jd] = (uint32_t)(r * T::kRowBytes + 16 * c);
     }
     auto issue = [&](int64_t t0, int slot) __attribute__((always_inline)) {   // a whole tile inside the row
@@ -656,7 +664,7 @@ __global__ __launch_bounds__(kMqThreads) void indexer_score_mq(
                 const int i = wave * kDmaPerWave + jd;
                 const int r = i * T::kRowsPerDma + lane / T::kChunks;
                 const int p = lane % T::kChunks;
-                const int c = p ^ (r & (T::kChunks - 1));
+                const int c = p ^ T::swz(r);
                 const int64_t krow = min(t0 + r, c1 - 1);
                 lds_dma16(kb + krow * T::kRowBytes + 16 * c, dst + 1024 * i);
             }
