@@ -96,7 +96,8 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // gather lands them unpadded in their own ring.
 constexpr int kRowBytesF8 = 656;
 constexpr int kChunksF8 = kRowBytesF8 / 16;     // 41
-constexpr int kDmaF8 = (kBlk * kRowBytesF8 + 1023) / 1024;   // 21
+constexpr int kPitchF8 = 656;                   // staging row pitch
+constexpr int kDmaF8 = (kBlk * kPitchF8 + 1023) / 1024;   // 21
 constexpr int kStageBuf = kDmaF8 * 1024;
 constexpr int kDmaLoF8 = kDmaF8 / kWaves;       // 2
 constexpr int kDmaHiF8 = kDmaLoF8 + 1;          // 3
@@ -267,7 +268,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     constexpr int DMA_BIG = FP8KV ? kDmaBigF8 : kDmaBig;
     constexpr int DMA_HI = FP8KV ? kDmaHiF8 : kDmaHi;
     constexpr int DMA_LO = FP8KV ? kDmaLoF8 : kDmaLo;
-    constexpr int UNIT = FP8KV ? kChunksF8 : kChunksPerPitch;    // 16-byte units per LDS row
+    constexpr int UNIT = FP8KV ? kPitchF8 / 16 : kChunksPerPitch;    // 16-byte units per LDS row
     constexpr int ROW_CHUNKS = FP8KV ? kChunksF8 : kChunksPerRow;
     constexpr int SLOT = FP8KV ? kStageBuf : kBuf;
     uint8_t* const ring = FP8KV ? g_stage : g_ring;
@@ -302,7 +303,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
     auto widen = [&](int slot) __attribute__((always_inline)) {
         const lds_u8* st = (const lds_u8*)g_stage + slot * kStageBuf;
         const int r = tid >> 4, j = tid & 15;
-        const lds_u8* sr = st + r * kRowBytesF8;
+        const lds_u8* sr = st + r * kPitchF8;
         const i32x4 c0 = *(const __attribute__((address_space(3))) i32x4*)(sr + 32 * j);
         const i32x4 c1 = *(const __attribute__((address_space(3))) i32x4*)(sr + 32 * j + 16);
         const float sc = *(const __attribute__((address_space(3))) float*)(sr + 512 + 4 * (j >> 2));
@@ -324,7 +325,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         if (tid < 256) {
             const int r2 = tid >> 3, c = tid & 7;
             *(__attribute__((address_space(3))) i32x4*)((lds_u8*)g_blk + r2 * kPitch + 1024 + 16 * c) =
-                *(const __attribute__((address_space(3))) i32x4*)(st + r2 * kRowBytesF8 + 528 + 16 * c);
+                *(const __attribute__((address_space(3))) i32x4*)(st + r2 * kPitchF8 + 528 + 16 * c);
         }
     };
 
@@ -366,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             // S^T of this wave's 16 rows (16hf + 4g + i) and head l16 over all 576 dims,
             // as two accumulation chains (K-steps 0-8 and 9-17) added at the end
             f32x4 sacc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
-            const lds_u8* arow = F8IN ? buf + (16 * hf + l16) * kRowBytesF8
+            const lds_u8* arow = F8IN ? buf + (16 * hf + l16) * kPitchF8
                                        : buf + (16 * hf + l16) * kPitch + 16 * g;
             // FP8 rows: the row's four group scales, for the conversion of its codes
             f32x4 srw{};
@@ -568,12 +569,12 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             // second.
             const int k = l16 >> 1;
             const int rsrc = k < 4 ? 4 * g + k : 12 + 4 * g + k;
-            const lds_u8* vb = buf + rsrc * kRowBytesF8 + 256 * hf + 8 * (l16 & 1);
+            const lds_u8* vb = buf + rsrc * kPitchF8 + 256 * hf + 8 * (l16 & 1);
             bf16x8 pb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
                 const int r = e < 4 ? 4 * g + e : 12 + 4 * g + e;
-                const f32x2 sc = *(const __attribute__((address_space(3))) f32x2*)(buf + r * kRowBytesF8 + 512 + 8 * hf);
+                const f32x2 sc = *(const __attribute__((address_space(3))) f32x2*)(buf + r * kPitchF8 + 512 + 8 * hf);
                 const float pv = (float)pa[e];
                 pb[e] = (__bf16)(pv * sc[1]);
                 pa[e] = (__bf16)(pv * sc[0]);
