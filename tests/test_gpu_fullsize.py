@@ -111,7 +111,8 @@ def run_unit(name):
     return wl, inp, bufs
 
 
-@pytest.mark.parametrize("name", ["decode_b64_n131072", "decode_b8_n1048576_fp8", "decode_b8_n1048576_fp8_kv8"])
+@pytest.mark.parametrize("name", ["decode_b64_n131072", "decode_b64_n131072_kv8", "decode_b8_n1048576_fp8",
+                                  "decode_b8_n1048576_fp8_kv8"])
 def test_group_full_size(name):
     wl, inp, bufs = run_unit(name)
     check_selection_properties(bufs["scores"], bufs["idx"][0], inp["q_pos"], wl.n_ctx)
