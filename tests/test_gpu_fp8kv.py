@@ -141,3 +141,44 @@ def test_fp8kv_group_and_stack_match_oracle():
         eo, el = max_abs(np32(o), wo), max_abs(np32(s), ws)
         note(eo, el)
         assert eo <= ATOL_OUT and el <= ATOL_LSE
+
+
+def test_fp8kv_row_pair_layout_rescales_and_edge_rows():
+    # The row-pair layout on FP8 rows in place, under the conditions that stress
+    # it: 4 layers x 32 queries split into two 1024-row slices; RoPE keys that
+    # grow with the position (the running max moves block after block, in one or
+    # both row halves at once), one query in descending order; edge rows (every
+    # index -1, a single valid index, one row half of every block empty). The
+    # result must be bf16 attention over the dequantised rows, bit for bit, with
+    # the empty query's output zero and its lse -inf.
+    n_layers, n_q, batch, n_ctx = 4, 32, 2, 5000
+    wl = W.Workload("fp8kv_rp", batch, n_ctx, n_q // batch, n_layers, "bf16")
+    q_seq = torch.arange(n_q, dtype=torch.int32) % batch
+    g = torch.Generator().manual_seed(93)
+    idx = torch.stack([torch.sort(torch.randperm(n_ctx, generator=g)[:2048])[0] for _ in range(n_q)]).to(torch.int32)
+    idx[1] = torch.flip(idx[1], [0])
+    idx[2] = -1
+    idx[3] = -1
+    idx[3, 700] = 4321
+    second_half = (torch.arange(2048) // 16) % 2 == 1
+    idx[4, second_half] = -1
+    idx[5, ~second_half] = -1
+    grow = 1.0 + torch.arange(n_ctx, dtype=torch.float32) / 500.0
+    d = dev()
+    layers, deq_layers = [], []
+    for l in range(n_layers):
+        ql, qr = W.mla_queries(wl, 11, l)
+        kv = W.mla_cache(wl, 11, l).float()
+        kv[..., 512:] *= grow[None, :, None]
+        kv8 = oracle.quantize_latent(kv.to(torch.bfloat16).float().numpy())
+        deq = torch.from_numpy(oracle.dequantize_latent(kv8).astype(np.float32))
+        assert torch.equal(deq.to(torch.bfloat16).float(), deq)          # exact in bf16
+        layers.append((ql.to(d), qr.to(d), torch.from_numpy(kv8).to(d)))
+        deq_layers.append((ql.to(d), qr.to(d), deq.to(torch.bfloat16).to(d)))
+    outs = gsa.sparse_mla_attn_layers(layers, q_seq.to(d), idx.to(d), 1 / 16)
+    ref = gsa.sparse_mla_attn_layers(deq_layers, q_seq.to(d), idx.to(d), 1 / 16)
+    torch.cuda.synchronize()
+    for l, ((o, s), (ro, rs)) in enumerate(zip(outs, ref)):
+        assert torch.equal(o, ro) and torch.equal(s, rs), f"layer {l}: max |diff| {float((o - ro).abs().max()):.3e}"
+        assert torch.all(o[2] == 0) and torch.all(torch.isneginf(s[2]))
+    say("FP8 row-pair layout: 4 layers bit-identical to bf16 attention on the dequantised rows")
