@@ -363,6 +363,18 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         // rows of this block with a valid index (bit r), one LDS read per lane
         const uint64_t valid = __builtin_amdgcn_ballot_w64(rows_s[b * kBlk + (lane & 31)] >= 0);
         bf16x8 pa;
+        // row-pair layout, bf16 rows: P.V's first kVPre V fragments, read between
+        // Q.K and the softmax so that they load while the softmax and the swap run
+        constexpr int kVPre = 8;
+        bf16x8 vpre[kVPre];
+        const lds_u8* const vb = buf + (4 * g + (l16 >> 2)) * kPitch + 8 * (l16 & 3) + 512 * hf;
+        auto vfrag = [&](int d) __attribute__((always_inline)) {
+            // two 16-bit transpose reads in which lane j of the group supplies row
+            // 4g + j/4 (+16), dims 16d + 4(j%4) .. +3
+            const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 32 * d));
+            const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 16 * kPitch + 32 * d));
+            return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        };
         if constexpr (RP) {
             // S^T of this wave's 16 rows (16hf + 4g + i) and head l16 over all 576 dims,
             // as two accumulation chains (K-steps 0-8 and 9-17) added at the end
@@ -387,6 +399,11 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
                 if (e + 8 < 18) frag(e + 8);
                 const int t = 9 * (e & 1) + (e >> 1);
                 sacc[e & 1] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kval(af[e], t, srw), qr[t], sacc[e & 1], 0, 0, 0);
+            }
+            if constexpr (!F8IN) {
+#pragma unroll
+                for (int d = 0; d < kVPre; ++d) vpre[d] = vfrag(d);
+                __builtin_amdgcn_sched_barrier(0);
             }
             const f32x4 sc = sacc[0] + sacc[1];
             // this wave's rows: scores, the block max of the head, the max this wave
@@ -550,14 +567,9 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
         // {4g..4g+3, 16+4g..16+4g+3} (K index e of P is row R(e): 4g + e, then
         // 16 + 4g + e - 4).
         if constexpr (!F8IN) {
-            // two 16-bit transpose reads in which lane j of the group supplies row
-            // 4g + j/4 (+16), dims 16d + 4(j%4) .. +3
-            const lds_u8* vb = buf + (4 * g + (l16 >> 2)) * kPitch + 8 * (l16 & 3) + 512 * hf;
 #pragma unroll
             for (int d = 0; d < 16; ++d) {
-                const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 32 * d));
-                const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb + 16 * kPitch + 32 * d));
-                const bf16x8 bv = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+                const bf16x8 bv = RP && d < kVPre ? vpre[d < kVPre ? d : 0] : vfrag(d);
                 o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, bv, o[d], 0, 0, 0);
             }
         } else {
@@ -569,7 +581,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             // second.
             const int k = l16 >> 1;
             const int rsrc = k < 4 ? 4 * g + k : 12 + 4 * g + k;
-            const lds_u8* vb = buf + rsrc * kPitchF8 + 256 * hf + 8 * (l16 & 1);
+            const lds_u8* vb8 = buf + rsrc * kPitchF8 + 256 * hf + 8 * (l16 & 1);
             bf16x8 pb;
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
@@ -581,7 +593,7 @@ __global__ __launch_bounds__(kThreads) void sparse_mla_kernel(
             }
 #pragma unroll
             for (int d = 0; d < 16; ++d) {
-                const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb + 16 * d));
+                const v2i c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i*)(vb8 + 16 * d));
                 o[d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(d < 8 ? pa : pb, fp8x8_to_bf16(c, 1.0f), o[d], 0, 0, 0);
             }
         }
